@@ -1,0 +1,304 @@
+#!/usr/bin/env python3
+"""Throughput of the gfx950 dense GEMM library on one MI355X.
+
+One step = one GEMM call C = alpha*A*B + beta*C on the headline workload
+(BF16 inputs, FP32 accumulate/output, M = N = K = 8192), inputs already
+resident in HBM.  W untimed warm-up calls (the pages ask for warm-up before
+quoting numbers: dilfish.github.io 5.7), then K timed calls bracketed by
+device synchronisation, timed with HIP events on the stream the kernels run
+on.  TFLOP/s = 2MNK / time (chongfengling.github.io section 1 counts K
+multiplies and K adds per output; 2*2048^3 = 17.18e9 in its section 2.5).
+
+The same JSON line carries, under "also", the FP32 4096^3 case (against the
+fp32 matrix-core peak) and the skinny decode-shaped case M=8, N=28672,
+K=8192 (against HBM bandwidth: its time is the time to stream B once,
+dilfish.github.io 5.1 GEMV row), plus:
+  * "roofline": the dominant kernel's algorithmic FLOP per launch over its
+    measured launch time, against the published MI355X peak;
+  * "cpu_baseline": the CPU oracle timed on a bounded row sample of the same
+    workload on this host's cores (a reported baseline, not a target).
+
+Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
+       python bench.py --only bf16_8192 --no-cpu   (one workload, for profiling)
+       python bench.py --copy-calibration          (copy kernel of known size)
+"""
+
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import math
+import os
+import re
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+METRIC = "GEMM TFLOPS + % of MI355X roofline (FP32 4096^3, BF16 8192^3, skinny GB/s)"
+
+# Published MI355X peaks (dense, no sparsity): matrix cores bf16 2.5 PFLOP/s,
+# fp32 157.3 TFLOP/s; HBM3E 8 TB/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+HBM_PEAK_GBS = 8000.0
+
+PRIMARY = "bf16_8192"
+SECONDARY = ["f32_4096", "bf16_skinny_8x28672x8192"]
+
+# Kernel (source file) that dominates each workload's time, for the roofline.
+DOMINANT = {
+    "bf16_8192": ("mfma_bf16_kernel", "k_mfma_bf16.hip"),
+    "f32_4096": ("mfma_f32_kernel", "k_mfma_f32.hip"),
+    "bf16_skinny_8x28672x8192": ("skinny_bf16_kernel", "k_skinny.hip"),
+}
+
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
+
+
+def log(*a):
+    print(*a, file=sys.stderr, flush=True)
+
+
+# ------------------------------------------------------------ cost model
+
+def gemm_flops(M: int, N: int, K: int) -> int:
+    """K multiplies and K adds per output element."""
+    return 2 * M * N * K
+
+
+def algorithmic_bytes(M: int, N: int, K: int, in_bytes: int, beta: float) -> int:
+    """Read A and B once, write C once (and read it once when beta != 0)."""
+    return (M * K + K * N) * in_bytes + M * N * 4 * (2 if beta != 0 else 1)
+
+
+def arithmetic_intensity(flops: float, nbytes: float) -> float:
+    return flops / nbytes
+
+
+def naive_lane_view_intensity(K: int, in_bytes: int = 4) -> float:
+    """One lane per output reads a row of A and a column of B: 2K FLOP over
+    2K loads (dilfish.github.io 5.2; chongfengling.github.io 2.3)."""
+    return (2 * K) / (2 * K * in_bytes)
+
+
+def tile_intensity(T: int, in_bytes: int = 4) -> float:
+    """A T x T tile per K-slice of T: 2T^3 FLOP over 2T^2 loaded elements
+    (dilfish.github.io 5.3)."""
+    return (2 * T ** 3) / (2 * T * T * in_bytes)
+
+
+def naive_load_requests(M: int, N: int, K: int, wave: int) -> int:
+    """Vector load instructions of the one-lane-per-output kernel: each
+    wavefront issues one load of A and one of B per k."""
+    return 2 * K * (M * N // wave)
+
+
+# ------------------------------------------------------------ measurement
+
+def source_digest(fname: str) -> str:
+    h = hashlib.sha256()
+    for f in (fname, "gemm_common.hpp"):
+        with open(os.path.join(ROOT, "dense_gemm_tuning_amd", "csrc", f), "rb") as fh:
+            h.update(fh.read())
+    return h.hexdigest()[:16]
+
+
+def read_traffic(workload: str):
+    """HBM bytes per launch from the committed counter summary, or None when
+    absent or taken on a different version of the kernel source."""
+    if not os.path.exists(TRAFFIC_FILE):
+        return None
+    kern, src = DOMINANT[workload]
+    want = source_digest(src)
+    pat = re.compile(r"^traffic\s+workload=(\S+)\s+kernel=(\S+)\s+src=(\S+)\s+"
+                     r"fetch_bytes=(\d+)\s+write_bytes=(\d+)", re.M)
+    for m in pat.finditer(open(TRAFFIC_FILE).read()):
+        if m.group(1) == workload and m.group(3) == want:
+            return int(m.group(4)) + int(m.group(5))
+    return None
+
+
+def to_dev(torch, x, dtype):
+    import numpy as np
+    if dtype == "bf16":
+        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    return torch.from_numpy(np.ascontiguousarray(x)).cuda()
+
+
+def time_workload(torch, dgt, w, steps, warmup, copies=1):
+    """Average and spread of one GEMM call's duration (ms) on the current stream."""
+    import gemm_inputs as gi
+    t0 = time.perf_counter()
+    A, B, C0 = gi.make_inputs(w)
+    log(f"[{w.name}] inputs generated in {time.perf_counter() - t0:.1f} s")
+    dA = [to_dev(torch, A, w.dtype) for _ in range(copies)]
+    dB = [to_dev(torch, B, w.dtype) for _ in range(copies)]
+    dC = (torch.from_numpy(C0).cuda() if C0 is not None
+          else torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda"))
+    stream = torch.cuda.current_stream()
+    sptr = stream.cuda_stream
+    fn = dgt.gemm_bf16 if w.dtype == "bf16" else dgt.gemm_f32
+
+    def launch(i):
+        st = fn(w.M, w.N, w.K, w.alpha, dA[i % copies].data_ptr(), w.K,
+                dB[i % copies].data_ptr(), w.N, w.beta, dC.data_ptr(), w.N, sptr)
+        if st != 0:
+            raise RuntimeError(dgt.gemm_status_string(st))
+
+    for i in range(warmup):
+        launch(i)
+    torch.cuda.synchronize()
+    ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    ev[0].record(stream)
+    for i in range(steps):
+        launch(i)
+        ev[i + 1].record(stream)
+    torch.cuda.synchronize()
+    per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
+    total = ev[0].elapsed_time(ev[steps])
+    res = {"ms_avg": total / steps, "ms_median": per[len(per) // 2],
+           "ms_min": per[0], "ms_max": per[-1]}
+    del dA, dB, dC
+    torch.cuda.empty_cache()
+    return res, (A, B, C0)
+
+
+def roofline(w, ms_avg):
+    kern, _ = DOMINANT[w.name]
+    fl = gemm_flops(w.M, w.N, w.K)
+    by = algorithmic_bytes(w.M, w.N, w.K, 2 if w.dtype == "bf16" else 4, w.beta)
+    traffic = read_traffic(w.name)
+    if w.name.startswith("bf16_skinny"):
+        ach = by / (ms_avg * 1e-3) / 1e9
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
+                "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
+                "traffic": traffic, "kernel": kern, "algorithmic_bytes": by}
+    ach = fl / (ms_avg * 1e-3) / 1e12
+    peak = PEAK_TFLOPS[w.dtype]
+    return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+            "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+            "kernel": kern, "algorithmic_flops": fl}
+
+
+def cpu_baseline(w, A, B, C0, target_s=12.0):
+    """The oracle as it stands, on a row sample sized for ~target_s seconds."""
+    import oracle
+    oracle.build(force=False)
+    rows = 8
+    while True:
+        t0 = time.perf_counter()
+        oracle.gemm(A[:rows], B, None if C0 is None else C0[:rows], w.alpha, w.beta, w.dtype)
+        dt = time.perf_counter() - t0
+        if dt >= target_s / 3 or rows >= w.M:
+            break
+        rows = min(w.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3))))
+    fl = gemm_flops(rows, w.N, w.K)
+    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+            "cores": oracle.num_threads(), "kind": "oracle",
+            "sample": f"first {rows} of {w.M} rows of {w.name} "
+                      f"({rows}x{w.N}x{w.K}, {dt:.1f} s incl. fp64 widening of B)"}
+
+
+def copy_calibration(torch, nbytes=1 << 30, reps=5):
+    """A plain device copy of known size, for scaling HBM byte counters."""
+    src = torch.ones(nbytes // 4, dtype=torch.float32, device="cuda")
+    dst = torch.empty_like(src)
+    for _ in range(reps):
+        dst.copy_(src)
+    torch.cuda.synchronize()
+    print(json.dumps({"copy_calibration_bytes_read": nbytes,
+                      "copy_calibration_bytes_written": nbytes, "reps": reps}))
+
+
+def main(argv=None):
+    ap = argparse.ArgumentParser(description=__doc__,
+                                 formatter_class=argparse.RawDescriptionHelpFormatter)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--only", default=None, help="time a single workload")
+    ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--copy-calibration", action="store_true")
+    args = ap.parse_args(argv)
+
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU only (got --gpus {args.gpus}); the GEMM "
+              "shards by rows or columns with no exchange, so N GPUs run N "
+              "independent copies of the single-GPU kernel.", file=sys.stderr)
+        return 2
+
+    import torch
+    import dense_gemm_tuning_amd as dgt
+    import gemm_inputs as gi
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        return 1
+    torch.cuda.set_device(0)
+    dgt.library()  # fail loudly if the HIP library is missing
+
+    if args.copy_calibration:
+        copy_calibration(torch)
+        return 0
+
+    names = [args.only] if args.only else [PRIMARY] + SECONDARY
+    results = {}
+    for name in names:
+        w = gi.WORKLOADS[name]
+        copies = 2 if name.startswith("bf16_skinny") else 1  # B > 256 MB cache
+        log(f"[{name}] {w.M}x{w.N}x{w.K} {w.dtype}: warmup {args.warmup}, steps {args.steps}")
+        res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies)
+        res["roofline"] = roofline(w, res["ms_avg"])
+        res["tflops"] = gemm_flops(w.M, w.N, w.K) / (res["ms_avg"] * 1e-3) / 1e12
+        log(f"[{name}] {res['ms_avg']:.4f} ms  {res['tflops']:.1f} TFLOP/s  "
+            f"roofline frac {res['roofline']['frac']:.3f}")
+        results[name] = (w, res, inputs)
+
+    head = names[0]
+    w, res, (A, B, C0) = results[head]
+    cpu = None
+    if not args.no_cpu:
+        log("[cpu] timing the oracle on a row sample ...")
+        cpu = cpu_baseline(w, A, B, C0)
+        log(f"[cpu] {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+
+    also = []
+    for name in names[1:]:
+        w2, r2, _ = results[name]
+        entry = {"workload": name, "M": w2.M, "N": w2.N, "K": w2.K, "dtype": w2.dtype,
+                 "ms_per_step": round(r2["ms_avg"], 5),
+                 "tflops": round(r2["tflops"], 2), "roofline": r2["roofline"]}
+        if name.startswith("bf16_skinny"):
+            entry["gbs"] = r2["roofline"]["achieved"]
+        also.append(entry)
+
+    line = {
+        "metric": METRIC,
+        "value": round(res["tflops"], 2),
+        "unit": "TFLOP/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(res["ms_avg"], 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": w.dtype,
+        "data": "synthetic (seeded SplitMix64; bf16 N(0,1) / fp32 uniform[-1,1))",
+        "config": {"workload": head, "M": w.M, "N": w.N, "K": w.K,
+                   "alpha": w.alpha, "beta": w.beta,
+                   "inputs": w.dtype, "accumulate": "f32", "output": "f32"},
+        "launch_ms": {k: round(res[k], 5) for k in ("ms_median", "ms_min", "ms_max")},
+        "roofline": res["roofline"],
+        "cpu_baseline": cpu,
+        "also": also,
+    }
+    print(json.dumps(line), flush=True)
+    return 0
+
+
+if __name__ == "__main__":
+    sys.exit(main())

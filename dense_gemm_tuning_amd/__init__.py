@@ -1,0 +1,165 @@
+"""Python binding of the gfx950 dense GEMM library (``libdgt_gemm.so``).
+
+Argument marshalling only: every function forwards to the C entry point of
+the same name in ``include/dgt_gemm.h``; all arithmetic happens in the HIP
+kernels behind it.  Pointers are device addresses passed as Python ints,
+``stream`` is a ``hipStream_t`` as an int (0 = null stream).  Each function
+returns the library's status code (0 = GEMM_OK); ``check`` turns a non-zero
+status into an exception.
+
+``gemm(A, B, C, alpha, beta, variant)`` is a convenience for torch tensors on
+the GPU: it reads shapes, leading dimensions (``stride(0)``) and
+``torch.cuda.current_stream()`` and calls ``gemm_f32`` / ``gemm_bf16`` (or the
+``_variant`` forms).  Torch is used for memory and streams only.
+
+There is no fallback: if the library has not been built, every call raises.
+"""
+
+from __future__ import annotations
+
+import ctypes
+import os
+
+LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "lib",
+                        "libdgt_gemm.so")
+
+GEMM_OK = 0
+GEMM_ERR_DIM = -1
+GEMM_ERR_LD = -2
+GEMM_ERR_NULL = -3
+GEMM_ERR_OVERLAP = -4
+GEMM_ERR_VARIANT = -5
+GEMM_ERR_LAUNCH = -6
+
+VARIANT_AUTO = 0
+VARIANT_NAIVE = 1
+VARIANT_LDS = 2
+VARIANT_MFMA = 3
+VARIANT_SKINNY = 4
+VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
+            "mfma": VARIANT_MFMA, "skinny": VARIANT_SKINNY}
+
+# Every symbol the header declares (the tests check the library exports them).
+EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f32_variant", "gemm_bf16_variant",
+           "gemm_select_variant", "gemm_status_string", "gemm_abi_version")
+
+_lib = None
+
+
+class GemmError(RuntimeError):
+    def __init__(self, status: int):
+        super().__init__(gemm_status_string(status))
+        self.status = status
+
+
+def _load() -> ctypes.CDLL:
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(
+                f"HIP GEMM library not built ({LIB_PATH} missing); run "
+                "`python -m dense_gemm_tuning_amd.build` or "
+                "`python -c 'import __graft_entry__ as g; g.build()'`")
+        lib = ctypes.CDLL(LIB_PATH)
+        i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
+        core = [i, i, i, f, p, i, p, i, f, p, i, p]
+        for name in ("gemm_f32", "gemm_bf16"):
+            fn = getattr(lib, name)
+            fn.restype = i
+            fn.argtypes = core
+        for name in ("gemm_f32_variant", "gemm_bf16_variant"):
+            fn = getattr(lib, name)
+            fn.restype = i
+            fn.argtypes = [i, *core]
+        lib.gemm_select_variant.restype = i
+        lib.gemm_select_variant.argtypes = [i] * 7
+        lib.gemm_status_string.restype = ctypes.c_char_p
+        lib.gemm_status_string.argtypes = [i]
+        lib.gemm_abi_version.restype = i
+        lib.gemm_abi_version.argtypes = []
+        _lib = lib
+    return _lib
+
+
+def library() -> ctypes.CDLL:
+    """The loaded ctypes handle (raises if the library is not built)."""
+    return _load()
+
+
+def gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return _load().gemm_f32(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_bf16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return _load().gemm_bf16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                     stream=0) -> int:
+    return _load().gemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta,
+                                    C, ldc, stream)
+
+
+def gemm_bf16_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                      stream=0) -> int:
+    return _load().gemm_bf16_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta,
+                                     C, ldc, stream)
+
+
+def gemm_select_variant(dtype_is_bf16, M, N, K, lda, ldb, ldc) -> int:
+    return _load().gemm_select_variant(int(bool(dtype_is_bf16)), M, N, K, lda, ldb, ldc)
+
+
+def gemm_status_string(status: int) -> str:
+    return _load().gemm_status_string(status).decode()
+
+
+def gemm_abi_version() -> int:
+    return _load().gemm_abi_version()
+
+
+def check(status: int) -> None:
+    if status != GEMM_OK:
+        raise GemmError(status)
+
+
+def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
+         stream=None) -> int:
+    """C <- alpha*A*B + beta*C on torch tensors (row-major, unit column stride).
+
+    A and B are float32 or bfloat16 (bf16 bits are passed as-is), C float32.
+    Returns the status code; the work is queued on ``stream`` (default: torch's
+    current stream) and not waited for.
+    """
+    import torch
+
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16):
+        raise TypeError("A and B must both be float32 or both bfloat16")
+    if C.dtype != torch.float32:
+        raise TypeError("C must be float32")
+    for t in (A, B, C):
+        if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
+            raise ValueError("operands must be 2-D row-major with unit column stride")
+        if t.numel() > 0 and not t.is_cuda:
+            raise ValueError("operands must be GPU tensors")
+    M, K = A.shape
+    K2, N = B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"C {tuple(C.shape)}")
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    # a single-row operand's row stride is never used; report a legal one
+    lda = A.stride(0) if M > 1 else max(A.stride(0), K, 1)
+    ldb = B.stride(0) if K > 1 else max(B.stride(0), N, 1)
+    ldc = C.stride(0) if M > 1 else max(C.stride(0), N, 1)
+    args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
+            float(beta), C.data_ptr(), ldc, stream)
+    bf16 = A.dtype == torch.bfloat16
+    if variant == VARIANT_AUTO:
+        return (gemm_bf16 if bf16 else gemm_f32)(*args)
+    return (gemm_bf16_variant if bf16 else gemm_f32_variant)(variant, *args)

@@ -1,0 +1,192 @@
+// k_lds.hip -- LDS-staged macro tiles with per-lane register tiles on the
+// vector ALU (the rung below the matrix cores).
+//
+// A workgroup owns a 128 x 128 tile of C and walks K in slices of 16.  Each
+// slice of A (128 x 16) and B (16 x 128) is fetched once with coalesced
+// 128-bit loads and parked in LDS, where every lane of the workgroup reuses
+// it (dilfish.github.io section 5.3; elainafan.one "Shared Memory Tiling").
+// Each lane owns 8 x 8 outputs and, per k, reads 8 values of A and 8 of B
+// from LDS for 64 FMAs, four FMAs per LDS read (dilfish.github.io 5.4); with
+// a 128-wide tile the global-side intensity is 32 FLOP/B (same section).
+//
+// Double buffering (dilfish.github.io 5.4, "software pipeline"): the next
+// slice is loaded from global memory into registers while the current one is
+// consumed from LDS, then written to the other LDS buffer; one barrier per
+// slice suffices because a buffer is only rewritten one slice after its last
+// read (the second barrier the pages insist on, dilfish.github.io 5.7 and
+// elainafan.one after the tiled listing, is the previous slice's barrier).
+//
+// LDS layout: A is stored transposed (k-major, As[k][m]) so that a lane's
+// 4 consecutive m are one 128-bit read; rows are padded by 4 floats (132
+// floats), which makes the transposing writes land on distinct banks
+// (dilfish.github.io 5.7 and qwbw.cn's "Pad" row on padding the second
+// dimension).  Ragged shapes: out-of-range loads are zero-filled and stores
+// masked (dilfish.github.io 5.7; elainafan.one masked tiled listing).
+#include "gemm_common.hpp"
+
+namespace dgt {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 16, PAD = 4, NT = 256;
+
+template <typename T> struct Chunk;
+template <> struct Chunk<float> {
+    static constexpr int V = 4;  // elements per 16-byte chunk
+    __device__ static void unpack(const uint4& u, float* o) {
+        o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
+        o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
+    }
+};
+template <> struct Chunk<uint16_t> {
+    static constexpr int V = 8;
+    __device__ static void unpack(const uint4& u, float* o) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
+            o[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
+        }
+    }
+};
+
+// Load the 16-byte chunk [col, col+V) of one row, zero-filling whatever lies
+// outside the row range or beyond `limit` columns.
+template <typename T, bool kVec>
+__device__ __forceinline__ void load_chunk(const T* rowp, int col, int limit,
+                                           bool row_ok, float* out) {
+    constexpr int V = Chunk<T>::V;
+    if (!row_ok) {
+#pragma unroll
+        for (int v = 0; v < V; ++v) out[v] = 0.0f;
+        return;
+    }
+    if (kVec && col + V <= limit) {
+        Chunk<T>::unpack(*reinterpret_cast<const uint4*>(rowp + col), out);
+    } else {
+#pragma unroll
+        for (int v = 0; v < V; ++v)
+            out[v] = (col + v < limit) ? load_in(rowp + col + v) : 0.0f;
+    }
+}
+
+template <typename T, bool kVec>
+__global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
+    __shared__ float As[2][BK][BM + PAD];
+    __shared__ float Bs[2][BK][BN + PAD];
+    constexpr int V = Chunk<T>::V;
+    constexpr int A_CPR = BK / V;            // chunks per row of the A slice
+    constexpr int A_CH = BM * A_CPR / NT;    // chunks per lane
+    constexpr int B_CPR = BN / V;
+    constexpr int B_CH = BK * B_CPR / NT;
+
+    const int tid = threadIdx.x;
+    const int m0 = (blockIdx.x / tiles_n) * BM;
+    const int n0 = (blockIdx.x % tiles_n) * BN;
+    const T* A = static_cast<const T*>(p.A);
+    const T* B = static_cast<const T*>(p.B);
+
+    float ra[A_CH][V], rb[B_CH][V];
+
+    auto load_slice = [&](int k0) {
+#pragma unroll
+        for (int c = 0; c < A_CH; ++c) {
+            const int f = tid + NT * c, r = f / A_CPR, q = f % A_CPR;
+            const int row = m0 + r;
+            const bool ok = row < p.M;
+            load_chunk<T, kVec>(A + (int64_t)(ok ? row : 0) * p.lda, k0 + q * V,
+                                p.K, ok, ra[c]);
+        }
+#pragma unroll
+        for (int c = 0; c < B_CH; ++c) {
+            const int f = tid + NT * c, r = f / B_CPR, q = f % B_CPR;
+            const int krow = k0 + r;
+            const bool ok = krow < p.K;
+            load_chunk<T, kVec>(B + (int64_t)(ok ? krow : 0) * p.ldb, n0 + q * V,
+                                p.N, ok, rb[c]);
+        }
+    };
+    auto store_slice = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < A_CH; ++c) {
+            const int f = tid + NT * c, r = f / A_CPR, q = f % A_CPR;
+#pragma unroll
+            for (int v = 0; v < V; ++v) As[buf][q * V + v][r] = ra[c][v];
+        }
+#pragma unroll
+        for (int c = 0; c < B_CH; ++c) {
+            const int f = tid + NT * c, r = f / B_CPR, q = f % B_CPR;
+#pragma unroll
+            for (int v = 0; v < V; ++v) Bs[buf][r][q * V + v] = rb[c][v];
+        }
+    };
+
+    const int ty = tid / 16, tx = tid % 16;
+    float acc[8][8];
+#pragma unroll
+    for (int i = 0; i < 8; ++i)
+#pragma unroll
+        for (int j = 0; j < 8; ++j) acc[i][j] = 0.0f;
+
+    const int nk = (p.K + BK - 1) / BK;
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nk) load_slice((t + 1) * BK);
+#pragma unroll 2
+        for (int k = 0; k < BK; ++k) {
+            float a[8], b[8];
+            *reinterpret_cast<float4*>(&a[0]) = *reinterpret_cast<const float4*>(&As[buf][k][ty * 4]);
+            *reinterpret_cast<float4*>(&a[4]) = *reinterpret_cast<const float4*>(&As[buf][k][64 + ty * 4]);
+            *reinterpret_cast<float4*>(&b[0]) = *reinterpret_cast<const float4*>(&Bs[buf][k][tx * 4]);
+            *reinterpret_cast<float4*>(&b[4]) = *reinterpret_cast<const float4*>(&Bs[buf][k][64 + tx * 4]);
+#pragma unroll
+            for (int i = 0; i < 8; ++i)
+#pragma unroll
+                for (int j = 0; j < 8; ++j) acc[i][j] = fmaf(a[i], b[j], acc[i][j]);
+        }
+        if (t + 1 < nk) store_slice(buf ^ 1);
+        __syncthreads();
+    }
+
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const int row = m0 + (i < 4 ? ty * 4 + i : 64 + ty * 4 + (i - 4));
+        if (row >= p.M) continue;
+        float* crow = p.C + (int64_t)row * p.ldc;
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int col = n0 + (j < 4 ? tx * 4 + j : 64 + tx * 4 + (j - 4));
+            if (col < p.N) crow[col] = epilogue(acc[i][j], p.alpha, p.beta, crow + col);
+        }
+    }
+}
+
+template <typename T>
+hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
+    const int tiles_n = (p.N + BN - 1) / BN;
+    const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool vec = rows_16b_aligned(p.A, p.lda, sizeof(T)) &&
+                     rows_16b_aligned(p.B, p.ldb, sizeof(T));
+    if (vec)
+        hipLaunchKernelGGL((lds_kernel<T, true>), dim3((unsigned)blocks), dim3(NT),
+                           0, s, p, tiles_n);
+    else
+        hipLaunchKernelGGL((lds_kernel<T, false>), dim3((unsigned)blocks), dim3(NT),
+                           0, s, p, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_lds_f32(const GemmParams& p, hipStream_t s) {
+    return launch_lds<float>(p, s);
+}
+hipError_t launch_lds_bf16(const GemmParams& p, hipStream_t s) {
+    return launch_lds<uint16_t>(p, s);
+}
+
+}  // namespace dgt

@@ -1,0 +1,212 @@
+// k_mfma_bf16.hip -- BF16-input / FP32-accumulate GEMM on the CDNA4 matrix
+// cores.
+//
+// The pages' matrix-unit rung (dilfish.github.io 5.5 WMMA listing; qwbw.cn
+// Level 2 and its double-buffering row) feeds 16-bit inputs to the matrix
+// unit and accumulates in fp32.  Here every wavefront owns a 128 x 128 tile
+// of C built from 4 x 4 v_mfma_f32_32x32x16_bf16 instructions (256 fp32
+// accumulators per lane, held in the accumulation registers for the whole K
+// loop); four wavefronts in a 2 x 2 grid cover a 256 x 256 workgroup tile,
+// so a 64-deep K slice of A and B (64 KiB) is read from memory once and
+// reused 256 times per element from LDS (dilfish.github.io 5.3-5.4: tile
+// size sets the arithmetic intensity, 2*256*256*64 / 65536 B = 128 FLOP/B
+// here).  The products of two bf16 values are exact in fp32.
+//
+// Operand layout.  The MFMA takes, per lane, 8 consecutive k of one row of
+// A and 8 consecutive k of one column of B.  A is row-major (k contiguous),
+// so its 16-byte chunks go to LDS unchanged.  B is row-major K x N (n
+// contiguous): each lane loads an 8 (k) x 8 (n) block as eight 16-byte row
+// pieces and transposes it in registers (byte permutes), then writes eight
+// 16-byte column pieces, so B sits in LDS as N x 64 with k contiguous.  The
+// pages warn that a fragment declared in the wrong major order still "looks
+// right" (dilfish.github.io 5.5); the tests check with permutation and
+// rank-1 inputs that rows and columns are not swapped.
+//
+// LDS layout (both operands): rows of 64 bf16 = eight 16-byte chunks; chunk
+// q of row r is stored at position q ^ ((r ^ (r >> 3)) & 7).  Eight lanes
+// reading the same chunk of 8 consecutive rows, and eight lanes writing
+// rows 8 apart, both land on 8 distinct 16-byte bank groups (the XOR form
+// of the padding remedy of dilfish.github.io 5.7 / qwbw.cn "Pad").
+//
+// Pipeline: the next K slice is loaded from global memory into registers
+// while the current one is consumed from LDS; it is then written to the other
+// LDS buffer (two 64 KiB stages in the 160 KiB LDS), one barrier per
+// slice (dilfish.github.io 5.4 double buffering; 5.7 second barrier).
+// Ragged shapes: zero-filled loads and masked stores; shapes that are tile
+// multiples with 16-byte aligned rows use an unchecked specialisation.
+#include "gemm_common.hpp"
+
+namespace dgt {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 64, NT = 256;
+constexpr int CPR = BK / 8;  // 16-byte chunks per LDS row (8)
+
+__device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
+
+// 8 bf16 at [col, col+8) of one row as a 16-byte chunk, zero outside.
+template <bool kVec, bool kGuard>
+__device__ __forceinline__ uint4 load8(const uint16_t* rowp, int col, int limit,
+                                       bool row_ok) {
+    if (!kGuard) return *reinterpret_cast<const uint4*>(rowp + col);
+    if (!row_ok) return make_uint4(0, 0, 0, 0);
+    if (kVec && col + 8 <= limit) return *reinterpret_cast<const uint4*>(rowp + col);
+    uint32_t w[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t lo = (col + 2 * i < limit) ? rowp[col + 2 * i] : 0u;
+        const uint32_t hi = (col + 2 * i + 1 < limit) ? rowp[col + 2 * i + 1] : 0u;
+        w[i] = lo | (hi << 16);
+    }
+    return make_uint4(w[0], w[1], w[2], w[3]);
+}
+
+__device__ __forceinline__ uint32_t word(const uint4& v, int i) {
+    return i == 0 ? v.x : i == 1 ? v.y : i == 2 ? v.z : v.w;
+}
+
+// Column j (0..7) of the 8 x 8 bf16 block r[0..7] (row k = index, 8 n per
+// row) as 8 k-consecutive values: dword e holds rows 2e (low) and 2e+1.
+__device__ __forceinline__ uint4 column8(const uint4 (&r)[8], int j) {
+    uint32_t o[4];
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = word(r[2 * e], j >> 1), hi = word(r[2 * e + 1], j >> 1);
+        o[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u))
+                       : ((lo & 0xffffu) | (hi << 16));
+    }
+    return make_uint4(o[0], o[1], o[2], o[3]);
+}
+
+__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
+    return __builtin_bit_cast(bf16x8, v);
+}
+
+template <bool kVec, bool kGuard>
+__global__ __launch_bounds__(NT, 1) void mfma_bf16_kernel(GemmParams p, int tiles_n) {
+    __shared__ uint4 As[2][BM * CPR];
+    __shared__ uint4 Bt[2][BN * CPR];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int m0 = (blockIdx.x / tiles_n) * BM;
+    const int n0 = (blockIdx.x % tiles_n) * BN;
+    const uint16_t* A = static_cast<const uint16_t*>(p.A);
+    const uint16_t* B = static_cast<const uint16_t*>(p.B);
+
+    // A: chunk i of this lane covers row (tid>>3) + 32*i, chunk q = tid&7.
+    // B: this lane covers rows 8*g .. 8*g+7 (g = tid>>5) of the slice and
+    //    columns 8*c .. 8*c+7 (c = tid&31).
+    const int aq = tid & 7, arow = tid >> 3;
+    const int bc = tid & 31, bg = tid >> 5;
+    uint4 ra[8], rb[8];
+
+    auto load_slice = [&](int k0) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = m0 + arow + 32 * i;
+            const bool ok = row < p.M;
+            ra[i] = load8<kVec, kGuard>(A + (int64_t)(ok ? row : 0) * p.lda,
+                                        k0 + 8 * aq, p.K, ok);
+        }
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int krow = k0 + 8 * bg + r;
+            const bool ok = krow < p.K;
+            rb[r] = load8<kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
+                                        n0 + 8 * bc, p.N, ok);
+        }
+    };
+    auto store_slice = [&](int buf) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = arow + 32 * i;
+            As[buf][row * CPR + (aq ^ swz(row))] = ra[i];
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int n = 8 * bc + j;
+            Bt[buf][n * CPR + (bg ^ swz(n))] = column8(rb, j);
+        }
+    };
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = (p.K + BK - 1) / BK;
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nk) load_slice((t + 1) * BK);
+#pragma unroll
+        for (int s = 0; s < BK / 16; ++s) {
+            // half-wave h supplies k = 16s + 8h .. +7 for both operands
+            const int q = 2 * s + h;
+            bf16x8 a[4], b[4];
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti) {
+                const int row = wm * 128 + ti * 32 + r32;
+                a[ti] = as_bf16x8(As[buf][row * CPR + (q ^ swz(row))]);
+            }
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                const int n = wn * 128 + tj * 32 + r32;
+                b[tj] = as_bf16x8(Bt[buf][n * CPR + (q ^ swz(n))]);
+            }
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 4; ++tj)
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
+                        a[ti], b[tj], acc[ti][tj], 0, 0, 0);
+        }
+        if (t + 1 < nk) store_slice(buf ^ 1);
+        __syncthreads();
+    }
+
+    // 32x32 accumulator layout: register r of lane l is row
+    // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the MFMA tile.
+#pragma unroll
+    for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 4; ++tj) {
+            const int col = n0 + wn * 128 + tj * 32 + r32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 128 + ti * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (kGuard && (row >= p.M || col >= p.N)) continue;
+                float* c = p.C + (int64_t)row * p.ldc + col;
+                *c = epilogue(acc[ti][tj][r], p.alpha, p.beta, c);
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_bf16(const GemmParams& p, hipStream_t s) {
+    const int tiles_n = (p.N + BN - 1) / BN;
+    const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool vec = rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2);
+    const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
+    const dim3 grid((unsigned)blocks), block(NT);
+    if (full)
+        hipLaunchKernelGGL((mfma_bf16_kernel<true, false>), grid, block, 0, s, p, tiles_n);
+    else if (vec)
+        hipLaunchKernelGGL((mfma_bf16_kernel<true, true>), grid, block, 0, s, p, tiles_n);
+    else
+        hipLaunchKernelGGL((mfma_bf16_kernel<false, true>), grid, block, 0, s, p, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace dgt

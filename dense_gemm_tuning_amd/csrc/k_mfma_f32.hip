@@ -1,0 +1,174 @@
+// k_mfma_f32.hip -- FP32 GEMM on the CDNA4 matrix cores.
+//
+// The pages' register-tiled kernel (dilfish.github.io 5.4: 128 x 128 block
+// tile, 8 x 8 outputs per thread, double buffering) is rebuilt around
+// wavefront-wide MFMA tiles: the register micro-tile of a lane becomes a
+// 64 x 64 tile per wavefront computed by 2 x 2 v_mfma_f32_32x32x2_f32
+// instructions, whose accumulators (64 fp32 per lane) stay in registers for
+// the whole K loop.  The pages' matrix-unit sections (dilfish.github.io 5.5,
+// qwbw.cn Level 2) use 16-bit inputs; on gfx950 the matrix cores also take
+// fp32 operands at the full fp32 rate, so SGEMM keeps fp32 inputs and
+// accumulation, with no TF32-style input truncation (dilfish.github.io 5.7
+// warns that TF32 is not lossless).
+//
+// Workgroup: 256 lanes = 4 wavefronts in a 2 x 2 grid over a 128 x 128 tile
+// of C; K advances in slices of 16.  Global -> LDS: each slice of A
+// (128 x 16) and B (16 x 128) is read with coalesced 128-bit loads into
+// registers one slice ahead and written to the other half of a double LDS
+// buffer (dilfish.github.io 5.4), one barrier per slice.
+//
+// Operand order inside a slice: the 32x32x2 instruction sums over two k
+// values, one per half-wavefront.  Half h of the wavefront feeds k = 8h + j
+// at step j (j = 0..7), so each lane reads its 8 A values as two 128-bit
+// LDS reads; any fixed assignment of k to steps is valid because every
+// product lands in the same sum.
+//
+// LDS layout: A row-major with the row pitch padded to 20 floats (so 8 lanes
+// reading 16 bytes from 8 consecutive rows hit 8 distinct bank groups), B
+// row-major with the pitch padded to 132 floats (the two half-wavefronts
+// read rows 8 apart and land on opposite halves of the 64 banks).  Ragged
+// shapes: zero-filled loads outside A and B and masked stores
+// (dilfish.github.io 5.7; elainafan.one masked tiled listing); the
+// specialisation for shapes that are multiples of the tile skips the checks.
+#include "gemm_common.hpp"
+
+namespace dgt {
+
+namespace {
+
+constexpr int BM = 128, BN = 128, BK = 16, NT = 256;
+constexpr int A_PITCH = BK + 4;    // floats
+constexpr int B_PITCH = BN + 4;    // floats
+
+// 16-byte chunk of 4 floats at [col, col+4) of one row, zero outside.
+template <bool kVec, bool kGuard>
+__device__ __forceinline__ float4 load4(const float* rowp, int col, int limit,
+                                        bool row_ok) {
+    if (!kGuard) return *reinterpret_cast<const float4*>(rowp + col);
+    if (!row_ok) return make_float4(0.f, 0.f, 0.f, 0.f);
+    if (kVec && col + 4 <= limit) return *reinterpret_cast<const float4*>(rowp + col);
+    float v[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) v[i] = (col + i < limit) ? rowp[col + i] : 0.0f;
+    return make_float4(v[0], v[1], v[2], v[3]);
+}
+
+template <bool kVec, bool kGuard>
+__global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles_n) {
+    __shared__ float As[2][BM * A_PITCH];
+    __shared__ float Bs[2][BK * B_PITCH];
+
+    const int tid = threadIdx.x;
+    const int lane = tid & 63, wave = tid >> 6;
+    const int wm = wave >> 1, wn = wave & 1;
+    const int h = lane >> 5, r32 = lane & 31;
+    const int m0 = (blockIdx.x / tiles_n) * BM;
+    const int n0 = (blockIdx.x % tiles_n) * BN;
+    const float* A = static_cast<const float*>(p.A);
+    const float* B = static_cast<const float*>(p.B);
+
+    // Per-lane global chunk coordinates (2 chunks of A, 2 of B per slice).
+    // A chunk f: row f/4, cols 4*(f%4); B chunk f: row f/32, cols 4*(f%32).
+    float4 ra[2], rb[2];
+    auto load_slice = [&](int k0) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int f = tid + NT * c;
+            const int row = m0 + (f >> 2), col = k0 + 4 * (f & 3);
+            const bool ok = row < p.M;
+            ra[c] = load4<kVec, kGuard>(A + (int64_t)(ok ? row : 0) * p.lda, col, p.K, ok);
+        }
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int f = tid + NT * c;
+            const int krow = k0 + (f >> 5), col = n0 + 4 * (f & 31);
+            const bool ok = krow < p.K;
+            rb[c] = load4<kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb, col, p.N, ok);
+        }
+    };
+    auto store_slice = [&](int buf) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int f = tid + NT * c;
+            *reinterpret_cast<float4*>(&As[buf][(f >> 2) * A_PITCH + 4 * (f & 3)]) = ra[c];
+            *reinterpret_cast<float4*>(&Bs[buf][(f >> 5) * B_PITCH + 4 * (f & 31)]) = rb[c];
+        }
+    };
+
+    floatx16 acc[2][2];
+#pragma unroll
+    for (int i = 0; i < 2; ++i)
+#pragma unroll
+        for (int j = 0; j < 2; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    const int nk = (p.K + BK - 1) / BK;
+    load_slice(0);
+    store_slice(0);
+    __syncthreads();
+    for (int t = 0; t < nk; ++t) {
+        const int buf = t & 1;
+        if (t + 1 < nk) load_slice((t + 1) * BK);
+
+        // A operands: rows wm*64 + ti*32 + r32, k = 8h .. 8h+7.
+        float a[2][8];
+#pragma unroll
+        for (int ti = 0; ti < 2; ++ti) {
+            const float* ap = &As[buf][(wm * 64 + ti * 32 + r32) * A_PITCH + 8 * h];
+            *reinterpret_cast<float4*>(&a[ti][0]) = *reinterpret_cast<const float4*>(ap);
+            *reinterpret_cast<float4*>(&a[ti][4]) = *reinterpret_cast<const float4*>(ap + 4);
+        }
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            float b[2];
+#pragma unroll
+            for (int tj = 0; tj < 2; ++tj)
+                b[tj] = Bs[buf][(8 * h + j) * B_PITCH + wn * 64 + tj * 32 + r32];
+#pragma unroll
+            for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 2; ++tj)
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        a[ti][j], b[tj], acc[ti][tj], 0, 0, 0);
+        }
+        if (t + 1 < nk) store_slice(buf ^ 1);
+        __syncthreads();
+    }
+
+    // Accumulator layout of a 32x32 MFMA tile: register r of lane l holds
+    // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
+#pragma unroll
+    for (int ti = 0; ti < 2; ++ti)
+#pragma unroll
+        for (int tj = 0; tj < 2; ++tj) {
+            const int col = n0 + wn * 64 + tj * 32 + r32;
+#pragma unroll
+            for (int r = 0; r < 16; ++r) {
+                const int row = m0 + wm * 64 + ti * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                if (kGuard && (row >= p.M || col >= p.N)) continue;
+                float* c = p.C + (int64_t)row * p.ldc + col;
+                *c = epilogue(acc[ti][tj][r], p.alpha, p.beta, c);
+            }
+        }
+}
+
+}  // namespace
+
+hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
+    const int tiles_n = (p.N + BN - 1) / BN;
+    const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool vec = rows_16b_aligned(p.A, p.lda, 4) && rows_16b_aligned(p.B, p.ldb, 4);
+    const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
+    const dim3 grid((unsigned)blocks), block(NT);
+    if (full)
+        hipLaunchKernelGGL((mfma_f32_kernel<true, false>), grid, block, 0, s, p, tiles_n);
+    else if (vec)
+        hipLaunchKernelGGL((mfma_f32_kernel<true, true>), grid, block, 0, s, p, tiles_n);
+    else
+        hipLaunchKernelGGL((mfma_f32_kernel<false, true>), grid, block, 0, s, p, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace dgt

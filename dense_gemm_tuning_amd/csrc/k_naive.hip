@@ -1,0 +1,83 @@
+// k_naive.hip -- baseline rung: one lane per output element, plus the
+// alpha == 0 / K == 0 scaling kernel.
+//
+// The naive mapping (dilfish.github.io section 5.2; chongfengling.github.io
+// section 2.1) gives every output C(i,j) its own lane, which walks k and does
+// two global loads and one FMA per step.  The column index, contiguous in
+// row-major memory, is bound to the lane index so that a wavefront reads one
+// contiguous run of B and one broadcast element of A per step
+// (chongfengling.github.io sections 2.2 and 2.4).  On gfx950 a wavefront is
+// 64 lanes, so the x-extent of the workgroup is 64, not 16 or 32.  Ragged
+// shapes are handled by the per-lane bounds check (chongfengling.github.io
+// section 2.1; elainafan.one, paragraph after the naive launch).  Arithmetic
+// intensity is 0.25 FLOP/B from the per-lane view (dilfish.github.io 5.2);
+// caches recover part of that, the layout does not.
+#include "gemm_common.hpp"
+
+namespace dgt {
+
+namespace {
+
+constexpr int kNaiveX = 64;  // one wavefront along the contiguous columns
+constexpr int kNaiveY = 4;   // four rows per workgroup (256 lanes)
+
+template <typename T>
+__global__ __launch_bounds__(kNaiveX * kNaiveY) void naive_kernel(GemmParams p,
+                                                                  int tiles_n) {
+    const int bn = blockIdx.x % tiles_n;
+    const int bm = blockIdx.x / tiles_n;
+    const int col = bn * kNaiveX + threadIdx.x;
+    const int row = bm * kNaiveY + threadIdx.y;
+    if (row >= p.M || col >= p.N) return;
+    const T* a = static_cast<const T*>(p.A) + (int64_t)row * p.lda;
+    const T* b = static_cast<const T*>(p.B) + col;
+    float acc = 0.0f;
+    for (int k = 0; k < p.K; ++k)
+        acc = fmaf(load_in(a + k), load_in(b + (int64_t)k * p.ldb), acc);
+    float* c = p.C + (int64_t)row * p.ldc + col;
+    *c = epilogue(acc, p.alpha, p.beta, c);
+}
+
+// C <- beta*C (A*B contributes nothing: alpha == 0 or K == 0); zeros when
+// beta == 0 without reading C.
+__global__ __launch_bounds__(256) void scale_kernel(float* C, int64_t ldc, int M,
+                                                    int N, float beta) {
+    const int64_t total = (int64_t)M * N;
+    for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
+         e += (int64_t)gridDim.x * blockDim.x) {
+        const int64_t i = e / N, j = e % N;
+        float* c = C + i * ldc + j;
+        *c = beta == 0.0f ? 0.0f : beta * (*c);
+    }
+}
+
+template <typename T>
+hipError_t launch_naive(const GemmParams& p, hipStream_t s) {
+    const int tiles_n = (p.N + kNaiveX - 1) / kNaiveX;
+    const int64_t tiles_m = (p.M + kNaiveY - 1) / kNaiveY;
+    const int64_t blocks = tiles_m * tiles_n;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    hipLaunchKernelGGL(naive_kernel<T>, dim3((unsigned)blocks),
+                       dim3(kNaiveX, kNaiveY), 0, s, p, tiles_n);
+    return hipGetLastError();
+}
+
+}  // namespace
+
+hipError_t launch_naive_f32(const GemmParams& p, hipStream_t s) {
+    return launch_naive<float>(p, s);
+}
+hipError_t launch_naive_bf16(const GemmParams& p, hipStream_t s) {
+    return launch_naive<uint16_t>(p, s);
+}
+
+hipError_t launch_scale(const GemmParams& p, hipStream_t s) {
+    const int64_t total = (int64_t)p.M * p.N;
+    int64_t blocks = (total + 255) / 256;
+    if (blocks > 65536) blocks = 65536;  // grid-stride loop covers the rest
+    hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
+                       p.C, p.ldc, p.M, p.N, p.beta);
+    return hipGetLastError();
+}
+
+}  // namespace dgt

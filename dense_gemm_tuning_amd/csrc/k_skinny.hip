@@ -1,0 +1,268 @@
+// k_skinny.hip -- the bandwidth-bound path for M <= 16 (decode-shaped GEMM).
+//
+// With a handful of rows of A, every element of B is used only M times:
+// the arithmetic intensity is about M FLOP per byte of 16-bit B (2M / 2) or
+// M/2 per byte of fp32 B, far below the ridge, so the time is the time to
+// stream B from HBM once (dilfish.github.io 5.1: GEMV is bandwidth-bound at
+// 0.5 FLOP/B and batching only scales it by the batch; qwbw.cn section 四:
+// at batch 1 the cost is loading the weights).  The kernel is built for
+// that: B is read exactly once, in 16-byte pieces whose lanes cover
+// contiguous row segments, with non-temporal hints (nothing else reuses it),
+// one K step ahead in registers; A (at most 16 rows) is re-read from cache;
+// no LDS staging of B at all.
+//
+// Compute still goes to the matrix cores, because the vector ALU would need
+// about 80% of its peak just for the FMAs at full HBM bandwidth.  The
+// operand freedom used: MFMA sums over k, so any assignment of k and of the
+// output columns to MFMA slots is valid if A and B agree and the store
+// inverts the column map.
+//
+//  * bf16: v_mfma_f32_16x16x32_bf16 with rows = the (up to 16) rows of A
+//    and columns = 16 columns of B.  Lane l (g = l/16, i = l%16) loads the
+//    8 x 8 block B[k0+8g .. +7][n0+8i .. +7] and transposes it in registers
+//    into eight k-contiguous column pieces; MFMA c (c = 0..7) takes column
+//    n0 + 8i + c from lane i, so one 32-deep K step covers 128 columns with
+//    8 MFMAs and a single 16-byte read of A per lane.
+//  * fp32: v_mfma_f32_16x16x4_f32 (one k per lane, no transpose).  Lane
+//    (g, i) loads B[k0+8g+t][n0+4i .. +3] for t = 0..7; slot t of the MFMA
+//    is k = k0 + 8g + t, so a lane's A operands are two 16-byte reads; one
+//    32-deep K step covers 64 columns with 32 MFMAs.
+//
+// Work split: a workgroup of 8 wavefronts owns one column strip (128 bf16
+// or 64 fp32 columns) over the whole of K; wavefront w takes the w-th
+// eighth of the K steps, and the eight partial tiles are summed in LDS in a
+// fixed order (deterministic, no atomics, no workspace).  Ragged shapes:
+// zero-filled loads, masked stores.
+#include "gemm_common.hpp"
+
+namespace dgt {
+
+namespace {
+
+constexpr int NT = 512;      // 8 wavefronts
+constexpr int NW = NT / 64;
+constexpr int KSTEP = 32;
+
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// 16-byte piece [col, col + 16/esz) of one row, zero outside; streamed.
+template <typename T, bool kVec, bool kGuard>
+__device__ __forceinline__ u32x4 load16(const T* rowp, int col, int limit, bool row_ok) {
+    constexpr int V = 16 / sizeof(T);
+    if (!kGuard || (row_ok && kVec && col + V <= limit))
+        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + col));
+    u32x4 out = {0u, 0u, 0u, 0u};
+    if (!row_ok) return out;
+    if constexpr (sizeof(T) == 4) {
+#pragma unroll
+        for (int v = 0; v < 4; ++v)
+            out[v] = (col + v < limit) ? __float_as_uint(reinterpret_cast<const float*>(rowp)[col + v]) : 0u;
+    } else {
+#pragma unroll
+        for (int v = 0; v < 4; ++v) {
+            const uint32_t lo = (col + 2 * v < limit) ? rowp[col + 2 * v] : 0u;
+            const uint32_t hi = (col + 2 * v + 1 < limit) ? rowp[col + 2 * v + 1] : 0u;
+            out[v] = lo | (hi << 16);
+        }
+    }
+    return out;
+}
+
+// A is small and shared by every workgroup: ordinary (cached) loads.
+template <typename T, bool kVec, bool kGuard>
+__device__ __forceinline__ u32x4 load16_cached(const T* rowp, int col, int limit, bool row_ok) {
+    constexpr int V = 16 / sizeof(T);
+    if (!kGuard || (row_ok && kVec && col + V <= limit))
+        return *reinterpret_cast<const u32x4*>(rowp + col);
+    return load16<T, kVec, true>(rowp, col, limit, row_ok);
+}
+
+// Column j of an 8 x 8 bf16 block (rows = k): dword e = rows 2e (low), 2e+1.
+__device__ __forceinline__ u32x4 column8(const u32x4 (&r)[8], int j) {
+    u32x4 o;
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+        const uint32_t lo = r[2 * e][j >> 1], hi = r[2 * e + 1][j >> 1];
+        o[e] = (j & 1) ? ((lo >> 16) | (hi & 0xffff0000u)) : ((lo & 0xffffu) | (hi << 16));
+    }
+    return o;
+}
+
+// Sum the NW partial tiles in a fixed order and apply the epilogue.
+template <int COLS>
+__device__ __forceinline__ void reduce_store(float (*red)[16][COLS + 4],
+                                             const GemmParams& p, int n0) {
+    __syncthreads();
+    for (int o = threadIdx.x; o < 16 * COLS; o += NT) {
+        const int m = o / COLS, nl = o % COLS, n = n0 + nl;
+        if (m >= p.M || n >= p.N) continue;
+        float s = 0.0f;
+#pragma unroll
+        for (int w = 0; w < NW; ++w) s += red[w][m][nl];
+        float* c = p.C + (int64_t)m * p.ldc + n;
+        *c = epilogue(s, p.alpha, p.beta, c);
+    }
+}
+
+// ---------------------------------------------------------------- bf16
+
+constexpr int BF_COLS = 128;
+
+template <bool kVec, bool kGuard>
+__global__ __launch_bounds__(NT, 1) void skinny_bf16_kernel(GemmParams p) {
+    __shared__ float red[NW][16][BF_COLS + 4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, i = lane & 15;
+    const int n0 = blockIdx.x * BF_COLS;
+    const int col = n0 + 8 * i;
+    const uint16_t* A = static_cast<const uint16_t*>(p.A);
+    const uint16_t* B = static_cast<const uint16_t*>(p.B);
+    const bool a_ok = i < p.M;
+    const uint16_t* arow = A + (int64_t)(a_ok ? i : 0) * p.lda;
+
+    const int nsteps = (p.K + KSTEP - 1) / KSTEP;
+    const int per = (nsteps + NW - 1) / NW;
+    const int s0 = wave * per;
+    const int s1 = min(s0 + per, nsteps);
+
+    floatx4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_b = [&](int step, u32x4 (&dst)[8]) {
+        const int kb = step * KSTEP + 8 * g;
+#pragma unroll
+        for (int r = 0; r < 8; ++r) {
+            const int krow = kb + r;
+            const bool ok = krow < p.K;
+            dst[r] = load16<uint16_t, kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
+                                                    col, p.N, ok);
+        }
+    };
+    auto compute = [&](int step, const u32x4 (&rb)[8]) {
+        const u32x4 a = load16_cached<uint16_t, kVec, kGuard>(arow, step * KSTEP + 8 * g,
+                                                              p.K, a_ok);
+        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
+#pragma unroll
+        for (int c = 0; c < 8; ++c)
+            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                av, __builtin_bit_cast(bf16x8, column8(rb, c)), acc[c], 0, 0, 0);
+    };
+
+    u32x4 b0[8], b1[8];
+    if (s0 < s1) load_b(s0, b0);
+    for (int s = s0; s < s1; s += 2) {
+        if (s + 1 < s1) load_b(s + 1, b1);
+        compute(s, b0);
+        if (s + 1 < s1) {
+            if (s + 2 < s1) load_b(s + 2, b0);
+            compute(s + 1, b1);
+        }
+    }
+
+    // 16x16 accumulator layout: register r of lane l is row 4*(l/16) + r,
+    // column l%16; MFMA c holds column n0 + 8*(l%16) + c.
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][4 * g + r][8 * i + c] = acc[c][r];
+    reduce_store<BF_COLS>(red, p, n0);
+}
+
+// ---------------------------------------------------------------- fp32
+
+constexpr int F_COLS = 64;
+
+template <bool kVec, bool kGuard>
+__global__ __launch_bounds__(NT, 1) void skinny_f32_kernel(GemmParams p) {
+    __shared__ float red[NW][16][F_COLS + 4];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, i = lane & 15;
+    const int n0 = blockIdx.x * F_COLS;
+    const int col = n0 + 4 * i;
+    const float* A = static_cast<const float*>(p.A);
+    const float* B = static_cast<const float*>(p.B);
+    const bool a_ok = i < p.M;
+    const float* arow = A + (int64_t)(a_ok ? i : 0) * p.lda;
+
+    const int nsteps = (p.K + KSTEP - 1) / KSTEP;
+    const int per = (nsteps + NW - 1) / NW;
+    const int s0 = wave * per;
+    const int s1 = min(s0 + per, nsteps);
+
+    floatx4 acc[4];
+#pragma unroll
+    for (int c = 0; c < 4; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    auto load_b = [&](int step, u32x4 (&dst)[8]) {
+        const int kb = step * KSTEP + 8 * g;
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const int krow = kb + t;
+            const bool ok = krow < p.K;
+            dst[t] = load16<float, kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
+                                                 col, p.N, ok);
+        }
+    };
+    auto compute = [&](int step, const u32x4 (&rb)[8]) {
+        const int ka = step * KSTEP + 8 * g;
+        const u32x4 a0 = load16_cached<float, kVec, kGuard>(arow, ka, p.K, a_ok);
+        const u32x4 a1 = load16_cached<float, kVec, kGuard>(arow, ka + 4, p.K, a_ok);
+#pragma unroll
+        for (int t = 0; t < 8; ++t) {
+            const float av = __uint_as_float(t < 4 ? a0[t] : a1[t - 4]);
+#pragma unroll
+            for (int c = 0; c < 4; ++c)
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
+                    av, __uint_as_float(rb[t][c]), acc[c], 0, 0, 0);
+        }
+    };
+
+    u32x4 b0[8], b1[8];
+    if (s0 < s1) load_b(s0, b0);
+    for (int s = s0; s < s1; s += 2) {
+        if (s + 1 < s1) load_b(s + 1, b1);
+        compute(s, b0);
+        if (s + 1 < s1) {
+            if (s + 2 < s1) load_b(s + 2, b0);
+            compute(s + 1, b1);
+        }
+    }
+
+    // MFMA c holds column n0 + 4*(l%16) + c.
+#pragma unroll
+    for (int c = 0; c < 4; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][4 * g + r][4 * i + c] = acc[c][r];
+    reduce_store<F_COLS>(red, p, n0);
+}
+
+}  // namespace
+
+hipError_t launch_skinny_bf16(const GemmParams& p, hipStream_t s) {
+    const int blocks = (p.N + BF_COLS - 1) / BF_COLS;
+    const bool vec = rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2);
+    const bool full = vec && p.N % BF_COLS == 0 && p.K % KSTEP == 0;
+    if (full)
+        hipLaunchKernelGGL((skinny_bf16_kernel<true, false>), dim3(blocks), dim3(NT), 0, s, p);
+    else if (vec)
+        hipLaunchKernelGGL((skinny_bf16_kernel<true, true>), dim3(blocks), dim3(NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((skinny_bf16_kernel<false, true>), dim3(blocks), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s) {
+    const int blocks = (p.N + F_COLS - 1) / F_COLS;
+    const bool vec = rows_16b_aligned(p.A, p.lda, 4) && rows_16b_aligned(p.B, p.ldb, 4);
+    const bool full = vec && p.N % F_COLS == 0 && p.K % KSTEP == 0;
+    if (full)
+        hipLaunchKernelGGL((skinny_f32_kernel<true, false>), dim3(blocks), dim3(NT), 0, s, p);
+    else if (vec)
+        hipLaunchKernelGGL((skinny_f32_kernel<true, true>), dim3(blocks), dim3(NT), 0, s, p);
+    else
+        hipLaunchKernelGGL((skinny_f32_kernel<false, true>), dim3(blocks), dim3(NT), 0, s, p);
+    return hipGetLastError();
+}
+
+}  // namespace dgt

@@ -1,0 +1,133 @@
+/*
+ * dgt_gemm.h -- C ABI of the MI355X (gfx950) dense GEMM library.
+ *
+ * Operation (every entry point): the BLAS GEMM form
+ *
+ *     C <- alpha * A * B + beta * C
+ *
+ * with C(i,j) = sum_k A(i,k) * B(k,j) (element formula: dilfish.github.io
+ * section 5.2; chongfengling.github.io section 1; elainafan.one
+ * "稠密矩阵乘法", where alpha and beta let one call both scale and
+ * accumulate).
+ *
+ * Layout: row-major with leading dimensions, the column index contiguous
+ * (chongfengling.github.io section 2.2; elainafan.one "行主序"):
+ *     A(i,k) = A[i*lda + k]   A is M x K,  lda >= max(1, K)
+ *     B(k,j) = B[k*ldb + j]   B is K x N,  ldb >= max(1, N)
+ *     C(i,j) = C[i*ldc + j]   C is M x N,  ldc >= max(1, N)
+ *
+ * Precision: gemm_f32 takes fp32 A and B; gemm_bf16 takes A and B as raw
+ * bf16 bit patterns (uint16_t, the upper half of an fp32 value: 8-bit
+ * exponent, 7-bit mantissa, dilfish.github.io section 5.5 table).  Both
+ * accumulate in fp32 on the matrix cores and read/write C in fp32.  The
+ * summation order is the kernel's own; results agree with an exact
+ * reference to fp32 accumulation accuracy, and bit for bit whenever every
+ * partial sum is exactly representable (e.g. small-integer inputs).
+ *
+ * Semantics of the edge cases (the pages leave them open; BLAS readings):
+ *   - beta == 0: C is write-only; NaN/Inf already in C never propagate.
+ *   - alpha == 0 or K == 0: A and B are not read; C <- beta*C (zeros when
+ *     beta == 0 too).
+ *   - M == 0 or N == 0: nothing is done; returns GEMM_OK.
+ *
+ * Memory and ownership: A, B and C are DEVICE pointers owned by the caller;
+ * they must stay valid until the work queued on `stream` has finished.  The
+ * library allocates nothing, frees nothing, keeps no per-call state and is
+ * safe to call from several host threads.  A misaligned pointer or leading
+ * dimension is accepted (fp32: 4-byte, bf16: 2-byte alignment); it only
+ * selects a slower load path, never a fault.
+ *
+ * Ordering: asynchronous.  Work is queued on `stream` (a hipStream_t cast
+ * to void*; NULL = the null stream) and the call returns without waiting.
+ *
+ * Errors: every entry point returns GEMM_OK (0) or a negative status; on an
+ * argument error nothing is queued.  The library never aborts or prints.
+ * Argument checks run on the host in this order: dimensions, leading
+ * dimensions, quick return for an empty C, null pointers, overlap of C with
+ * A or B, variant support.  gemm_status_string() names a status.
+ */
+#ifndef DGT_GEMM_H
+#define DGT_GEMM_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define DGT_GEMM_ABI_VERSION 1
+
+enum gemm_status {
+    GEMM_OK = 0,
+    GEMM_ERR_DIM = -1,          /* M, N or K negative                        */
+    GEMM_ERR_LD = -2,           /* lda < max(1,K), ldb < max(1,N) or
+                                   ldc < max(1,N)                            */
+    GEMM_ERR_NULL = -3,         /* NULL A/B (when read) or C with a
+                                   non-empty extent                          */
+    GEMM_ERR_OVERLAP = -4,      /* the byte range of C overlaps A's or B's   */
+    GEMM_ERR_VARIANT = -5,      /* unknown variant, or one that does not
+                                   support this shape / size                 */
+    GEMM_ERR_LAUNCH = -6        /* the HIP runtime rejected a kernel launch  */
+};
+
+/* Kernel ladder (for measurement and tests; GEMM_VARIANT_AUTO is what
+ * gemm_f32 / gemm_bf16 use).  Every variant computes the same operation
+ * and handles any shape that it accepts, ragged edges included. */
+enum gemm_variant {
+    GEMM_VARIANT_AUTO = 0,      /* MFMA tiles; skinny path when M <= 16       */
+    GEMM_VARIANT_NAIVE = 1,     /* one lane per output, K-loop of two global
+                                   loads and an FMA (dilfish.github.io 5.2;
+                                   chongfengling.github.io 2.1 and 2.4:
+                                   the contiguous column index on the
+                                   64-wide lane index)                        */
+    GEMM_VARIANT_LDS = 2,       /* LDS-staged 128x128 macro tiles, 128-bit
+                                   global loads, double-buffered, padded LDS
+                                   rows, 8x8 outputs per lane on the vector
+                                   ALU (dilfish.github.io 5.3 and 5.4)        */
+    GEMM_VARIANT_MFMA = 3,      /* LDS-staged macro tiles, double-buffered,
+                                   per-wavefront MFMA micro-tiles, masked
+                                   ragged edges (dilfish.github.io 5.4-5.5;
+                                   qwbw.cn section 三)                        */
+    GEMM_VARIANT_SKINNY = 4     /* M <= 16: streams B once from HBM, A held in
+                                   registers per step, K split over waves
+                                   and reduced in LDS (dilfish.github.io 5.1
+                                   GEMV row; qwbw.cn section 四)              */
+};
+
+/* C <- alpha*A*B + beta*C, fp32 inputs, fp32 accumulate/output. */
+int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
+             const float* B, int ldb, float beta, float* C, int ldc,
+             void* stream);
+
+/* C <- alpha*A*B + beta*C, bf16 inputs (raw bits), fp32 accumulate/output. */
+int gemm_bf16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
+              const uint16_t* B, int ldb, float beta, float* C, int ldc,
+              void* stream);
+
+/* Same as gemm_f32 / gemm_bf16 with an explicit ladder rung (enum
+ * gemm_variant).  GEMM_VARIANT_SKINNY requires M <= 16 and returns
+ * GEMM_ERR_VARIANT otherwise. */
+int gemm_f32_variant(int variant, int M, int N, int K, float alpha,
+                     const float* A, int lda, const float* B, int ldb,
+                     float beta, float* C, int ldc, void* stream);
+int gemm_bf16_variant(int variant, int M, int N, int K, float alpha,
+                      const uint16_t* A, int lda, const uint16_t* B, int ldb,
+                      float beta, float* C, int ldc, void* stream);
+
+/* The rung GEMM_VARIANT_AUTO picks for this call (dtype_is_bf16: 0 = fp32,
+ * 1 = bf16), or a negative status if the arguments are invalid.  Host only:
+ * touches no device and queues nothing. */
+int gemm_select_variant(int dtype_is_bf16, int M, int N, int K, int lda,
+                        int ldb, int ldc);
+
+/* Static string naming a status code (never NULL). */
+const char* gemm_status_string(int status);
+
+/* DGT_GEMM_ABI_VERSION of the built library. */
+int gemm_abi_version(void);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* DGT_GEMM_H */
