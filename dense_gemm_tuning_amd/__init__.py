@@ -123,6 +123,15 @@ def check(status: int) -> None:
         raise GemmError(status)
 
 
+def _ld(t) -> int:
+    """Row pitch of a 2-D tensor; for an empty or single-row operand the pitch
+    is never used (torch may report 0), so report a legal one."""
+    rows, cols = t.shape
+    if rows <= 1 or t.numel() == 0:
+        return max(t.stride(0), cols, 1)
+    return t.stride(0)
+
+
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
          stream=None) -> int:
     """C <- alpha*A*B + beta*C on torch tensors (row-major, unit column stride).
@@ -153,10 +162,7 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
         stream = torch.cuda.current_stream().cuda_stream
     elif hasattr(stream, "cuda_stream"):
         stream = stream.cuda_stream
-    # a single-row operand's row stride is never used; report a legal one
-    lda = A.stride(0) if M > 1 else max(A.stride(0), K, 1)
-    ldb = B.stride(0) if K > 1 else max(B.stride(0), N, 1)
-    ldc = C.stride(0) if M > 1 else max(C.stride(0), N, 1)
+    lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
             float(beta), C.data_ptr(), ldc, stream)
     bf16 = A.dtype == torch.bfloat16

@@ -127,7 +127,9 @@ def test_permutation_and_rank1(variant, dtype):
         if dtype == "bf16":
             A, B = gi.fp32_to_bf16_bits(A), gi.fp32_to_bf16_bits(B)
         st, C = run_gemm(variant, dtype, A, B, None, 1.0, 0.0)
-        want = (float(np.dot(v, w)) * np.outer(u, z)).astype(np.float32)
+        # + 0.0: an exact zero sum of products starting from +0 is +0, while
+        # the closed form's 0 * (negative) is -0
+        want = (float(np.dot(v, w)) * np.outer(u, z) + 0.0).astype(np.float32)
         assert_bit_exact(C, want, f"rank-1 {variant}/{dtype}")
 
 
