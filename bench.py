@@ -50,7 +50,7 @@ SECONDARY = ["f32_4096", "bf16_skinny_8x28672x8192"]
 
 # Kernel (source file) that dominates each workload's time, for the roofline.
 DOMINANT = {
-    "bf16_8192": ("mfma_bf16_kernel", "k_mfma_bf16.hip"),
+    "bf16_8192": ("mfma_bf16_dma_kernel", "k_mfma_bf16_dma.hip"),
     "f32_4096": ("mfma_f32_kernel", "k_mfma_f32.hip"),
     "bf16_skinny_8x28672x8192": ("skinny_bf16_kernel", "k_skinny.hip"),
 }

@@ -51,6 +51,8 @@ hipError_t launch_lds_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_lds_bf16(const GemmParams& p, hipStream_t s);
 hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_mfma_bf16(const GemmParams& p, hipStream_t s);
+bool mfma_bf16_dma_eligible(const GemmParams& p);
+hipError_t launch_mfma_bf16_dma(const GemmParams& p, hipStream_t s);
 hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_skinny_bf16(const GemmParams& p, hipStream_t s);
 

@@ -194,6 +194,7 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_kernel(GemmParams p, int tile
 }  // namespace
 
 hipError_t launch_mfma_bf16(const GemmParams& p, hipStream_t s) {
+    if (mfma_bf16_dma_eligible(p)) return launch_mfma_bf16_dma(p, s);
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
