@@ -151,6 +151,16 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
+    # timed region: K back-to-back launches between one pair of events
+    start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    start.record(stream)
+    for i in range(steps):
+        launch(i)
+    end.record(stream)
+    torch.cuda.synchronize()
+    total = start.elapsed_time(end)
+    # spread: a second pass with an event after every launch (the markers add
+    # a little time of their own, so this pass does not feed the average)
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
@@ -158,7 +168,6 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    total = ev[0].elapsed_time(ev[steps])
     res = {"ms_avg": total / steps, "ms_median": per[len(per) // 2],
            "ms_min": per[0], "ms_max": per[-1]}
     del dA, dB, dC

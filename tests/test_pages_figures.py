@@ -1,0 +1,60 @@
+"""The FLOP and byte model the bench reports against, pinned to numbers the
+pages print (tests/golden/pages_figures.json, each with its passage)."""
+
+import json
+import os
+
+import pytest
+
+import bench
+
+HERE = os.path.dirname(os.path.abspath(__file__))
+FIG = {f["id"]: f for f in json.load(open(os.path.join(HERE, "golden", "pages_figures.json")))["figures"]}
+
+
+def close(x, fig):
+    want, tol = fig["value"], fig["rel_tol"]
+    return abs(x - want) <= tol * abs(want) if tol else x == want
+
+
+def test_flop_count():
+    assert close(bench.gemm_flops(2048, 2048, 2048), FIG["flops_2048"])
+    assert bench.gemm_flops(2048, 2048, 2048) == 2 * 2048 ** 3
+
+
+def test_naive_and_tile_intensity():
+    assert close(bench.naive_lane_view_intensity(4096), FIG["naive_intensity"])
+    assert close(bench.tile_intensity(32), FIG["tile_intensity_T32"])
+    assert close(bench.tile_intensity(128), FIG["tile_intensity_T128"])
+
+
+def test_square_and_gemv_intensity():
+    n = 1024
+    ai = bench.arithmetic_intensity(bench.gemm_flops(n, n, n),
+                                    bench.algorithmic_bytes(n, n, n, 4, 0.0))
+    assert close(ai, FIG["square_1024_intensity"])
+    # matrix-vector product y = A x with A (M x K) fp32: one output column
+    M = K = 1 << 14
+    ai = bench.arithmetic_intensity(bench.gemm_flops(M, 1, K),
+                                    bench.algorithmic_bytes(M, 1, K, 4, 0.0))
+    assert close(ai, FIG["gemv_intensity"])
+
+
+def test_naive_counter_closed_form():
+    # two loads per k per warp of 32 lanes; each 32-lane request touches two
+    # 32-byte sectors in the 16 x 16 launch the page profiles
+    req = bench.naive_load_requests(2048, 2048, 2048, 32)
+    assert close(req, FIG["naive_requests_2048"])
+    assert close(2 * req, FIG["naive_sectors_2048"])
+
+
+def test_skinny_bytes_and_bf16_model():
+    # bytes the skinny workload must move: B dominates
+    by = bench.algorithmic_bytes(8, 28672, 8192, 2, 0.0)
+    assert by == 469762048 + 131072 + 917504
+
+
+@pytest.mark.parametrize("gpus", [2, 8])
+def test_bench_refuses_more_than_one_gpu(gpus, capsys):
+    assert bench.main(["--gpus", str(gpus)]) == 2
+    assert "one GPU" in capsys.readouterr().err
