@@ -40,16 +40,18 @@ namespace dgt {
 namespace {
 
 constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;
-constexpr int A_STAGE = BM * BK * 2;  // 16 KiB: 256 rows x 64 B
-constexpr int B_STAGE = BK * BN * 2;  // 16 KiB: 32 rows x 512 B
-constexpr int KALIGN = BK * NSTAGE;   // K multiple handled here
+constexpr int A_STAGE = BM * 2 * BK * 2;  // 32 KiB: 256 rows x 128 B (two slices)
+constexpr int B_STAGE = BK * BN * 2;      // 16 KiB: 32 rows x 512 B (one slice)
+constexpr int KALIGN = BK * NSTAGE;       // K multiple handled here
+constexpr int CPOL = 1;                   // sc0 on the copies
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-__device__ __forceinline__ int swz_a(int r) { return (r >> 2) & 3; }
+// A rows are 128 B = 8 chunks of 16 B; chunk q of row r sits at q ^ swz_a(r).
+__device__ __forceinline__ int swz_a(int r) { return (r ^ (r >> 3)) & 7; }
 
 // s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima (gfx9
 // encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in 6:4,
@@ -69,11 +71,10 @@ __device__ __forceinline__ void barrier() {
 
 __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int tiles_n) {
     // One LDS object per operand and stage, so that the compiler sees that a
-    // copy in flight into one stage does not alias reads of another.
+    // copy in flight into one stage does not alias reads of another.  A has
+    // two stages of two slices each, B four stages of one slice.
     __shared__ __attribute__((aligned(1024))) uint8_t sA0[A_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t sA1[A_STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t sA2[A_STAGE];
-    __shared__ __attribute__((aligned(1024))) uint8_t sA3[A_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t sB0[B_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t sB1[B_STAGE];
     __shared__ __attribute__((aligned(1024))) uint8_t sB2[B_STAGE];
@@ -86,46 +87,59 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
     const int n0 = (blockIdx.x % tiles_n) * BN;
     const uint16_t* A = static_cast<const uint16_t*>(p.A);
     const uint16_t* B = static_cast<const uint16_t*>(p.B);
-    const int nk = p.K / BK;
+    const int nk = p.K / BK;      // slices
+    const int npair = nk / 2;     // slice pairs
 
-    // Copy sources.  Wave w issues instructions j = 4w + i (i = 0..3) per
-    // operand: A instruction j fills rows 16j .. 16j+15 (4 lanes per row),
-    // B instruction j fills k-rows 2j and 2j+1 (32 lanes per row).
-    const uint16_t* asrc[4];
+    // Copy sources.  A: wave w issues instructions j = 8w + i (i = 0..7) per
+    // pair, instruction j filling rows 8j .. 8j+7 with 128 B each (8 lanes per
+    // row).  B: wave w issues j = 4w + i (i = 0..3) per slice, instruction j
+    // filling k-rows 2j and 2j+1 (32 lanes per row).
+    const uint16_t* asrc[8];
     const uint16_t* bsrc[4];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-        const int j = 4 * wave + i;
-        const int arow = 16 * j + (lane >> 2);
-        const int aq = (lane & 3) ^ swz_a(arow);
+    for (int i = 0; i < 8; ++i) {
+        const int arow = 8 * (8 * wave + i) + (lane >> 3);
+        const int aq = (lane & 7) ^ swz_a(arow);
         asrc[i] = A + (int64_t)(m0 + arow) * p.lda + 8 * aq;
-        const int brow = 2 * j + (lane >> 5);
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const int brow = 2 * (4 * wave + i) + (lane >> 5);
         const int bc = (lane & 31) ^ (4 * (brow & 3));
         bsrc[i] = B + (int64_t)brow * p.ldb + n0 + 8 * bc;
     }
     const int64_t b_slice = (int64_t)BK * p.ldb;
 
-    // Copy of one half of slice kt into stage (sa, sb): instructions
-    // i = 2*half, 2*half+1 of each operand.
-    auto issue_half = [&](uint8_t* sa, uint8_t* sb, int kt, int half) {
-        kt = kt < nk ? kt : nk - 1;  // past the end: re-read the last slice
+    // Half `half` (instructions 4*half .. 4*half+3) of A pair `pr` into sa.
+    auto copy_a = [&](uint8_t* sa, int pr, int half) {
+        pr = pr < npair ? pr : npair - 1;  // past the end: re-read the last pair
 #pragma unroll
-        for (int i = 2 * half; i < 2 * half + 2; ++i) {
-            const int j = 4 * wave + i;
-            __builtin_amdgcn_global_load_lds(asrc[i] + (int64_t)kt * BK,
-                                             (lds_void*)(sa + j * 1024), 16, 0, 0);
+        for (int i = 4 * half; i < 4 * half + 4; ++i)
+            __builtin_amdgcn_global_load_lds(asrc[i] + (int64_t)pr * (2 * BK),
+                                             (lds_void*)(sa + (8 * wave + i) * 1024), 16, 0,
+                                             CPOL);
+    };
+    // Half `half` (instructions 2*half, 2*half+1) of B slice kt into sb.
+    auto copy_b = [&](uint8_t* sb, int kt, int half) {
+        kt = kt < nk ? kt : nk - 1;        // past the end: re-read the last slice
+#pragma unroll
+        for (int i = 2 * half; i < 2 * half + 2; ++i)
             __builtin_amdgcn_global_load_lds(bsrc[i] + kt * b_slice,
-                                             (lds_void*)(sb + j * 1024), 16, 0, 0);
-        }
+                                             (lds_void*)(sb + (4 * wave + i) * 1024), 16, 0,
+                                             CPOL);
     };
 
-    // LDS read offsets.  A: row wm*128 + ti*32 + l%32, chunk 2s + h.
-    int a_off[4][2];
+    // LDS read offsets.  A: row wm*128 + ti*32 + l%32; slice-in-pair u, step s,
+    // half-wave h -> chunk 4u + 2s + h.
+    int a_off[4][2][2];
 #pragma unroll
     for (int ti = 0; ti < 4; ++ti) {
         const int row = wm * 128 + ti * 32 + (lane & 31);
 #pragma unroll
-        for (int s = 0; s < 2; ++s) a_off[ti][s] = row * 64 + (((2 * s + h) ^ swz_a(row)) << 4);
+        for (int u = 0; u < 2; ++u)
+#pragma unroll
+            for (int s = 0; s < 2; ++s)
+                a_off[ti][u][s] = row * 128 + (((4 * u + 2 * s + h) ^ swz_a(row)) << 4);
     }
     // B: source lane 4r+q of 16-lane group G reads k-row 16s + 8h + 4t + r,
     // columns wn*128 + tj*32 + 16*(G%2) + 4q .. +3; k & 3 == r.
@@ -147,11 +161,12 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    auto load_frags = [&](const uint8_t* sa, const uint8_t* sb, int s, bf16x8 (&a)[4],
-                          bf16x8 (&b)[4]) {
+    // Operands of step s of the slice held in (sa half u, sb).
+    auto load_frags = [&](const uint8_t* sa, int u, const uint8_t* sb, int s,
+                          bf16x8 (&a)[4], bf16x8 (&b)[4]) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
-            a[ti] = *reinterpret_cast<const bf16x8*>(sa + a_off[ti][s]);
+            a[ti] = *reinterpret_cast<const bf16x8*>(sa + a_off[ti][u][s]);
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             const uint8_t* base = sb + b_off[tj] + s * 8192;
@@ -162,10 +177,10 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
         }
     };
 
-    // 16 MFMAs on (a, b).  The 12 LDS reads and 4 copy instructions issued
-    // just before in program order are spread between them: per 4 MFMAs,
-    // 3 LDS reads and one copy, so the address unit never sees a burst that
-    // would hold the wave (and its MFMA issue) back.
+    // 16 MFMAs on (a, b).  The 12 LDS reads and the copies issued just before
+    // in program order are spread between them (3 LDS reads and one copy per
+    // 4 MFMAs), so the address unit never sees a burst that would hold the
+    // wave, and its MFMA issue, back.
     auto mfma_step = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -182,48 +197,58 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);
-            __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy (VMEM read)
+            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // copies (VMEM read)
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
     bf16x8 a0[4], b0[4], a1[4], b1[4];
 
-    // One K slice held in stage (sa, sb); the next slice is in (na, nb) and
-    // slice kt+3 goes to (fa, fb).  Slice u is copied in two halves: the
-    // first after the barrier of slice u-4 (its stage has just been retired),
-    // the second before the barrier of slice u-3; it is consumed after the
-    // barrier of slice u-1, about 2.5 slices later.  Between its second
-    // half and that barrier, 4 half-slices (16 copy instructions per wave)
-    // are issued, hence vmcnt(16).
-    auto slice = [&](uint8_t* sa, uint8_t* sb, uint8_t* na, uint8_t* nb, uint8_t* fa,
-                     uint8_t* fb, int kt) {
-        load_frags(sa, sb, 1, a1, b1);    // step 2 operands of this slice
-        issue_half(fa, fb, kt + 3, 1);
-        mfma_step(a0, b0);                // step 1 (operands read earlier)
-        WAIT_VMCNT_LGKM0(16);             // own copies of slice kt+1 landed and
-                                          // own reads of stage kt%4 returned
-        barrier();                        // ... for every wave; stage kt%4 retired
-        load_frags(na, nb, 0, a0, b0);    // step 1 operands of the next slice
-        issue_half(sa, sb, kt + NSTAGE, 0);
-        mfma_step(a1, b1);                // step 2
+    // Slice kt (its A in half u of sa, its B in sb); the next slice's A is in
+    // half nu of na, its B in nb.  Copies, per wave:
+    //   before the barrier: second half of B slice kt+3 into fb, and for even
+    //     kt the second half of A pair kt/2+1 into fa;
+    //   after the barrier: first half of B slice kt+4 into sb (just retired),
+    //     and for odd kt the first half of A pair (kt+3)/2 into fa (the pair
+    //     stage retired by this barrier).
+    // The barrier of slice kt publishes slice kt+1.  Counting the copies
+    // issued after the last one it needs gives 16 for even kt and 4 for odd kt
+    // (odd kt also needs the A pair finished in the previous region).
+    auto slice = [&](const uint8_t* sa, int u, uint8_t* sb, const uint8_t* na, int nu,
+                     const uint8_t* nb, uint8_t* fb, uint8_t* fa, int kt, bool even) {
+        load_frags(sa, u, sb, 1, a1, b1);  // step 2 operands of this slice
+        copy_b(fb, kt + 3, 1);
+        if (even) copy_a(fa, kt / 2 + 1, 1);
+        mfma_step(a0, b0);                 // step 1 (operands read earlier)
+        if (even) WAIT_VMCNT_LGKM0(16);    // own copies landed, own reads returned
+        else WAIT_VMCNT_LGKM0(4);
+        barrier();                         // ... for every wave
+        load_frags(na, nu, nb, 0, a0, b0); // step 1 operands of the next slice
+        copy_b(sb, kt + NSTAGE, 0);
+        if (!even) copy_a(fa, (kt + 3) / 2, 0);
+        mfma_step(a1, b1);                 // step 2
     };
 
-    issue_half(sA0, sB0, 0, 0);
-    issue_half(sA0, sB0, 0, 1);
-    issue_half(sA1, sB1, 1, 0);
-    issue_half(sA1, sB1, 1, 1);
-    issue_half(sA2, sB2, 2, 0);
-    issue_half(sA2, sB2, 2, 1);
-    issue_half(sA3, sB3, 3, 0);
-    WAIT_VMCNT(20);  // slice 0 landed; slices 1, 2 and half of 3 may be in flight
+    // Prologue: A pair 0, B slices 0..2, first halves of B slice 3 and A pair 1.
+    copy_a(sA0, 0, 0);
+    copy_a(sA0, 0, 1);
+    copy_b(sB0, 0, 0);
+    copy_b(sB0, 0, 1);
+    copy_b(sB1, 1, 0);
+    copy_b(sB1, 1, 1);
+    copy_b(sB2, 2, 0);
+    copy_b(sB2, 2, 1);
+    copy_b(sB3, 3, 0);
+    copy_a(sA1, 1, 0);
+    WAIT_VMCNT(14);  // A pair 0 and B slice 0 landed
     barrier();
-    load_frags(sA0, sB0, 0, a0, b0);
+    load_frags(sA0, 0, sB0, 0, a0, b0);
     for (int kt = 0; kt < nk; kt += NSTAGE) {
-        slice(sA0, sB0, sA1, sB1, sA3, sB3, kt);
-        slice(sA1, sB1, sA2, sB2, sA0, sB0, kt + 1);
-        slice(sA2, sB2, sA3, sB3, sA1, sB1, kt + 2);
-        slice(sA3, sB3, sA0, sB0, sA2, sB2, kt + 3);
+        // A pair kt/2 in sA0, pair kt/2+1 in sA1
+        slice(sA0, 0, sB0, sA0, 1, sB1, sB3, sA1, kt, true);
+        slice(sA0, 1, sB1, sA1, 0, sB2, sB0, sA0, kt + 1, false);
+        slice(sA1, 0, sB2, sA1, 1, sB3, sB1, sA0, kt + 2, true);
+        slice(sA1, 1, sB3, sA0, 0, sB0, sB2, sA1, kt + 3, false);
     }
     WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
 
