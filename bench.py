@@ -10,7 +10,8 @@ on.  TFLOP/s = 2MNK / time (chongfengling.github.io section 1 counts K
 multiplies and K adds per output; 2*2048^3 = 17.18e9 in its section 2.5).
 
 The same JSON line carries, under "also", the FP32 4096^3 case (against the
-fp32 matrix-core peak) and the skinny decode-shaped case M=8, N=28672,
+fp32 matrix-core peak), the FP16-input 8192^3 case (against the fp16 peak,
+equal to bf16's) and the skinny decode-shaped case M=8, N=28672,
 K=8192 (against HBM bandwidth: its time is the time to stream B once,
 dilfish.github.io 5.1 GEMV row), plus:
   * "roofline": the dominant kernel's algorithmic FLOP per launch over its
@@ -40,19 +41,20 @@ if ROOT not in sys.path:
 
 METRIC = "GEMM TFLOPS + % of MI355X roofline (FP32 4096^3, BF16 8192^3, skinny GB/s)"
 
-# Published MI355X peaks (dense, no sparsity): matrix cores bf16 2.5 PFLOP/s,
-# fp32 157.3 TFLOP/s; HBM3E 8 TB/s.
-PEAK_TFLOPS = {"bf16": 2500.0, "f32": 157.3}
+# Published MI355X peaks (dense, no sparsity): matrix cores bf16 and fp16
+# 2.5 PFLOP/s, fp32 157.3 TFLOP/s; HBM3E 8 TB/s.
+PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 PRIMARY = "bf16_8192"
-SECONDARY = ["f32_4096", "bf16_skinny_8x28672x8192"]
+SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192"]
 
 # Kernel (source file) that dominates each workload's time, for the roofline.
 DOMINANT = {
-    "bf16_8192": ("mfma_bf16_dma_kernel", "k_mfma_bf16_dma.hip"),
+    "bf16_8192": ("mfma16_dma_kernel<In::BF16>", "k_mfma_bf16_dma.hip"),
+    "f16_8192": ("mfma16_dma_kernel<In::F16>", "k_mfma_bf16_dma.hip"),
     "f32_4096": ("mfma_f32_kernel", "k_mfma_f32.hip"),
-    "bf16_skinny_8x28672x8192": ("skinny_bf16_kernel", "k_skinny.hip"),
+    "bf16_skinny_8x28672x8192": ("skinny16_kernel<In::BF16>", "k_skinny.hip"),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -123,8 +125,9 @@ def read_traffic(workload: str):
 
 def to_dev(torch, x, dtype):
     import numpy as np
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    if dtype in ("bf16", "f16"):
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+        return t.view(torch.bfloat16 if dtype == "bf16" else torch.float16)
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
@@ -140,7 +143,7 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
           else torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda"))
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    fn = dgt.gemm_bf16 if w.dtype == "bf16" else dgt.gemm_f32
+    fn = {"f32": dgt.gemm_f32, "bf16": dgt.gemm_bf16, "f16": dgt.gemm_f16}[w.dtype]
 
     def launch(i):
         st = fn(w.M, w.N, w.K, w.alpha, dA[i % copies].data_ptr(), w.K,
@@ -178,7 +181,7 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
 def roofline(w, ms_avg):
     kern, _ = DOMINANT[w.name]
     fl = gemm_flops(w.M, w.N, w.K)
-    by = algorithmic_bytes(w.M, w.N, w.K, 2 if w.dtype == "bf16" else 4, w.beta)
+    by = algorithmic_bytes(w.M, w.N, w.K, 4 if w.dtype == "f32" else 2, w.beta)
     traffic = read_traffic(w.name)
     if w.name.startswith("bf16_skinny"):
         ach = by / (ms_avg * 1e-3) / 1e9
@@ -296,7 +299,7 @@ def main(argv=None):
         "scaling": "weak",
         "vs_baseline": None,
         "dtype": w.dtype,
-        "data": "synthetic (seeded SplitMix64; bf16 N(0,1) / fp32 uniform[-1,1))",
+        "data": "synthetic (seeded SplitMix64; bf16/fp16 N(0,1) / fp32 uniform[-1,1))",
         "config": {"workload": head, "M": w.M, "N": w.N, "K": w.K,
                    "alpha": w.alpha, "beta": w.beta,
                    "inputs": w.dtype, "accumulate": "f32", "output": "f32"},

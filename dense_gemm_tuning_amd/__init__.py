@@ -40,8 +40,13 @@ VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
             "mfma": VARIANT_MFMA, "skinny": VARIANT_SKINNY}
 
 # Every symbol the header declares (the tests check the library exports them).
-EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f32_variant", "gemm_bf16_variant",
-           "gemm_select_variant", "gemm_status_string", "gemm_abi_version")
+EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",
+           "gemm_f16_variant", "gemm_select_variant", "gemm_status_string",
+           "gemm_abi_version")
+
+DTYPE_F32 = 0
+DTYPE_BF16 = 1
+DTYPE_F16 = 2
 
 _lib = None
 
@@ -63,11 +68,11 @@ def _load() -> ctypes.CDLL:
         lib = ctypes.CDLL(LIB_PATH)
         i, f, p = ctypes.c_int, ctypes.c_float, ctypes.c_void_p
         core = [i, i, i, f, p, i, p, i, f, p, i, p]
-        for name in ("gemm_f32", "gemm_bf16"):
+        for name in ("gemm_f32", "gemm_bf16", "gemm_f16"):
             fn = getattr(lib, name)
             fn.restype = i
             fn.argtypes = core
-        for name in ("gemm_f32_variant", "gemm_bf16_variant"):
+        for name in ("gemm_f32_variant", "gemm_bf16_variant", "gemm_f16_variant"):
             fn = getattr(lib, name)
             fn.restype = i
             fn.argtypes = [i, *core]
@@ -94,6 +99,10 @@ def gemm_bf16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
     return _load().gemm_bf16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
 
 
+def gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream=0) -> int:
+    return _load().gemm_f16(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
 def gemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                      stream=0) -> int:
     return _load().gemm_f32_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta,
@@ -106,8 +115,15 @@ def gemm_bf16_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                      C, ldc, stream)
 
 
-def gemm_select_variant(dtype_is_bf16, M, N, K, lda, ldb, ldc) -> int:
-    return _load().gemm_select_variant(int(bool(dtype_is_bf16)), M, N, K, lda, ldb, ldc)
+def gemm_f16_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                     stream=0) -> int:
+    return _load().gemm_f16_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta,
+                                    C, ldc, stream)
+
+
+def gemm_select_variant(dtype, M, N, K, lda, ldb, ldc) -> int:
+    """dtype: DTYPE_F32, DTYPE_BF16 or DTYPE_F16."""
+    return _load().gemm_select_variant(int(dtype), M, N, K, lda, ldb, ldc)
 
 
 def gemm_status_string(status: int) -> str:
@@ -136,7 +152,8 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
          stream=None) -> int:
     """C <- alpha*A*B + beta*C on torch tensors (row-major, unit column stride).
 
-    A and B are float32 or bfloat16 (bf16 bits are passed as-is), C float32.
+    A and B are float32, bfloat16 or float16 (16-bit bits are passed as-is),
+    C float32.
     Returns the status code; the work is queued on ``stream`` (default: torch's
     current stream) and not waited for.
     """
@@ -144,8 +161,8 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
 
     if isinstance(variant, str):
         variant = VARIANTS[variant]
-    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16):
-        raise TypeError("A and B must both be float32 or both bfloat16")
+    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise TypeError("A and B must both be float32, both bfloat16 or both float16")
     if C.dtype != torch.float32:
         raise TypeError("C must be float32")
     for t in (A, B, C):
@@ -165,7 +182,9 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
     lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
             float(beta), C.data_ptr(), ldc, stream)
-    bf16 = A.dtype == torch.bfloat16
+    auto_fn, var_fn = {torch.float32: (gemm_f32, gemm_f32_variant),
+                       torch.bfloat16: (gemm_bf16, gemm_bf16_variant),
+                       torch.float16: (gemm_f16, gemm_f16_variant)}[A.dtype]
     if variant == VARIANT_AUTO:
-        return (gemm_bf16 if bf16 else gemm_f32)(*args)
-    return (gemm_bf16_variant if bf16 else gemm_f32_variant)(variant, *args)
+        return auto_fn(*args)
+    return var_fn(variant, *args)

@@ -16,7 +16,7 @@ namespace {
 
 using dgt::GemmParams;
 
-enum class DType { F32, BF16 };
+enum class DType { F32, BF16, F16 };
 
 int elem_size(DType t) { return t == DType::F32 ? 4 : 2; }
 
@@ -77,19 +77,27 @@ int run(DType t, int variant, int M, int N, int K, float alpha, const void* A,
         e = dgt::launch_scale(p, s);
     } else {
         if (variant == GEMM_VARIANT_AUTO) variant = auto_variant(M);
-        const bool f32 = (t == DType::F32);
+        using dgt::In;
         switch (variant) {
             case GEMM_VARIANT_NAIVE:
-                e = f32 ? dgt::launch_naive_f32(p, s) : dgt::launch_naive_bf16(p, s);
+                e = t == DType::F32    ? dgt::launch_naive<In::F32>(p, s)
+                    : t == DType::BF16 ? dgt::launch_naive<In::BF16>(p, s)
+                                       : dgt::launch_naive<In::F16>(p, s);
                 break;
             case GEMM_VARIANT_LDS:
-                e = f32 ? dgt::launch_lds_f32(p, s) : dgt::launch_lds_bf16(p, s);
+                e = t == DType::F32    ? dgt::launch_lds<In::F32>(p, s)
+                    : t == DType::BF16 ? dgt::launch_lds<In::BF16>(p, s)
+                                       : dgt::launch_lds<In::F16>(p, s);
                 break;
             case GEMM_VARIANT_MFMA:
-                e = f32 ? dgt::launch_mfma_f32(p, s) : dgt::launch_mfma_bf16(p, s);
+                e = t == DType::F32    ? dgt::launch_mfma_f32(p, s)
+                    : t == DType::BF16 ? dgt::launch_mfma16<In::BF16>(p, s)
+                                       : dgt::launch_mfma16<In::F16>(p, s);
                 break;
             case GEMM_VARIANT_SKINNY:
-                e = f32 ? dgt::launch_skinny_f32(p, s) : dgt::launch_skinny_bf16(p, s);
+                e = t == DType::F32    ? dgt::launch_skinny_f32(p, s)
+                    : t == DType::BF16 ? dgt::launch_skinny16<In::BF16>(p, s)
+                                       : dgt::launch_skinny16<In::F16>(p, s);
                 break;
             default:
                 return GEMM_ERR_VARIANT;
@@ -115,6 +123,19 @@ int gemm_bf16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
                C, ldc, stream);
 }
 
+int gemm_f16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
+             const uint16_t* B, int ldb, float beta, float* C, int ldc, void* stream) {
+    return run(DType::F16, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
+               C, ldc, stream);
+}
+
+int gemm_f16_variant(int variant, int M, int N, int K, float alpha, const uint16_t* A,
+                     int lda, const uint16_t* B, int ldb, float beta, float* C, int ldc,
+                     void* stream) {
+    return run(DType::F16, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+               stream);
+}
+
 int gemm_f32_variant(int variant, int M, int N, int K, float alpha, const float* A,
                      int lda, const float* B, int ldb, float beta, float* C, int ldc,
                      void* stream) {
@@ -129,11 +150,10 @@ int gemm_bf16_variant(int variant, int M, int N, int K, float alpha,
                stream);
 }
 
-int gemm_select_variant(int dtype_is_bf16, int M, int N, int K, int lda, int ldb,
-                        int ldc) {
+int gemm_select_variant(int dtype, int M, int N, int K, int lda, int ldb, int ldc) {
+    if (dtype < GEMM_DTYPE_F32 || dtype > GEMM_DTYPE_F16) return GEMM_ERR_VARIANT;
     const int st = check_shape(M, N, K, lda, ldb, ldc);
     if (st != GEMM_OK) return st;
-    (void)dtype_is_bf16;
     return auto_variant(M);
 }
 

@@ -2,7 +2,8 @@
 //
 // All kernels compute C <- alpha*A*B + beta*C on row-major operands
 // (A(i,k) = A[i*lda+k], B(k,j) = B[k*ldb+j], C(i,j) = C[i*ldc+j]) with fp32
-// accumulation; inputs are fp32 or raw bf16 bits.  Offsets are 64-bit.
+// accumulation; inputs are fp32, or raw bf16 / IEEE binary16 bits.  Offsets
+// are 64-bit.
 #pragma once
 
 #include <hip/hip_runtime.h>
@@ -24,16 +25,56 @@ struct GemmParams {
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef _Float16 halfx8 __attribute__((ext_vector_type(8)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));  // 16 raw bytes
+
+// Input formats.  The 16-bit ones are passed as raw uint16_t bit patterns.
+enum class In { F32, BF16, F16 };
 
 // bf16 bits are the upper half of an fp32 value: widening is a shift.
 __device__ __forceinline__ float bf16_bits_to_f32(uint32_t h) {
     return __uint_as_float(h << 16);
 }
 
+template <In T> struct InFmt;
+template <> struct InFmt<In::F32> {
+    using S = float;
+    __device__ static float widen(float x) { return x; }
+};
+template <> struct InFmt<In::BF16> {
+    using S = uint16_t;
+    __device__ static float widen(uint16_t x) { return bf16_bits_to_f32(x); }
+};
+template <> struct InFmt<In::F16> {
+    using S = uint16_t;
+    __device__ static float widen(uint16_t x) { return (float)__builtin_bit_cast(_Float16, x); }
+};
+
 // Scalar input load widened to fp32.
-__device__ __forceinline__ float load_in(const float* p) { return *p; }
-__device__ __forceinline__ float load_in(const uint16_t* p) {
-    return bf16_bits_to_f32(*p);
+template <In T>
+__device__ __forceinline__ float load_in(const typename InFmt<T>::S* p) {
+    return InFmt<T>::widen(*p);
+}
+
+// Matrix-core products of 8 16-bit values per lane (raw 16-byte operands),
+// fp32 accumulate: 32x32x16 and 16x16x32 shapes.
+template <In T>
+__device__ __forceinline__ floatx16 mfma32x32x16(u32x4 a, u32x4 b, floatx16 c) {
+    if constexpr (T == In::BF16)
+        return __builtin_amdgcn_mfma_f32_32x32x16_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_32x32x16_f16(__builtin_bit_cast(halfx8, a),
+                                                      __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
+}
+template <In T>
+__device__ __forceinline__ floatx4 mfma16x16x32(u32x4 a, u32x4 b, floatx4 c) {
+    if constexpr (T == In::BF16)
+        return __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, a),
+                                                       __builtin_bit_cast(bf16x8, b), c, 0, 0, 0);
+    else
+        return __builtin_amdgcn_mfma_f32_16x16x32_f16(__builtin_bit_cast(halfx8, a),
+                                                      __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
 }
 
 // Epilogue of the BLAS form: alpha*acc + beta*c, where C is read only when
@@ -45,16 +86,14 @@ __device__ __forceinline__ float epilogue(float acc, float alpha, float beta,
 
 // Host-side launchers; each returns the hipError_t of its launch.
 hipError_t launch_scale(const GemmParams& p, hipStream_t s);
-hipError_t launch_naive_f32(const GemmParams& p, hipStream_t s);
-hipError_t launch_naive_bf16(const GemmParams& p, hipStream_t s);
-hipError_t launch_lds_f32(const GemmParams& p, hipStream_t s);
-hipError_t launch_lds_bf16(const GemmParams& p, hipStream_t s);
+template <In T> hipError_t launch_naive(const GemmParams& p, hipStream_t s);
+template <In T> hipError_t launch_lds(const GemmParams& p, hipStream_t s);
 hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s);
-hipError_t launch_mfma_bf16(const GemmParams& p, hipStream_t s);
-bool mfma_bf16_dma_eligible(const GemmParams& p);
-hipError_t launch_mfma_bf16_dma(const GemmParams& p, hipStream_t s);
+template <In T> hipError_t launch_mfma16(const GemmParams& p, hipStream_t s);
+bool mfma16_dma_eligible(const GemmParams& p);
+template <In T> hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s);
 hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s);
-hipError_t launch_skinny_bf16(const GemmParams& p, hipStream_t s);
+template <In T> hipError_t launch_skinny16(const GemmParams& p, hipStream_t s);
 
 // Largest M the skinny (decode) path accepts.
 constexpr int kSkinnyMaxM = 16;

@@ -30,31 +30,31 @@ namespace {
 
 constexpr int BM = 128, BN = 128, BK = 16, PAD = 4, NT = 256;
 
-template <typename T> struct Chunk;
-template <> struct Chunk<float> {
-    static constexpr int V = 4;  // elements per 16-byte chunk
+// A 16-byte chunk of inputs widened to fp32.
+template <In T> struct Chunk {
+    static constexpr int V = 8;  // 16-bit formats: 8 per chunk
+    __device__ static void unpack(const uint4& u, float* o) {
+        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            o[2 * i] = InFmt<T>::widen((uint16_t)(w[i] & 0xffffu));
+            o[2 * i + 1] = InFmt<T>::widen((uint16_t)(w[i] >> 16));
+        }
+    }
+};
+template <> struct Chunk<In::F32> {
+    static constexpr int V = 4;
     __device__ static void unpack(const uint4& u, float* o) {
         o[0] = __uint_as_float(u.x); o[1] = __uint_as_float(u.y);
         o[2] = __uint_as_float(u.z); o[3] = __uint_as_float(u.w);
     }
 };
-template <> struct Chunk<uint16_t> {
-    static constexpr int V = 8;
-    __device__ static void unpack(const uint4& u, float* o) {
-        const uint32_t w[4] = {u.x, u.y, u.z, u.w};
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            o[2 * i] = bf16_bits_to_f32(w[i] & 0xffffu);
-            o[2 * i + 1] = bf16_bits_to_f32(w[i] >> 16);
-        }
-    }
-};
 
 // Load the 16-byte chunk [col, col+V) of one row, zero-filling whatever lies
 // outside the row range or beyond `limit` columns.
-template <typename T, bool kVec>
-__device__ __forceinline__ void load_chunk(const T* rowp, int col, int limit,
-                                           bool row_ok, float* out) {
+template <In T, bool kVec>
+__device__ __forceinline__ void load_chunk(const typename InFmt<T>::S* rowp, int col,
+                                           int limit, bool row_ok, float* out) {
     constexpr int V = Chunk<T>::V;
     if (!row_ok) {
 #pragma unroll
@@ -66,12 +66,13 @@ __device__ __forceinline__ void load_chunk(const T* rowp, int col, int limit,
     } else {
 #pragma unroll
         for (int v = 0; v < V; ++v)
-            out[v] = (col + v < limit) ? load_in(rowp + col + v) : 0.0f;
+            out[v] = (col + v < limit) ? load_in<T>(rowp + col + v) : 0.0f;
     }
 }
 
-template <typename T, bool kVec>
+template <In T, bool kVec>
 __global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
+    using S = typename InFmt<T>::S;
     __shared__ float As[2][BK][BM + PAD];
     __shared__ float Bs[2][BK][BN + PAD];
     constexpr int V = Chunk<T>::V;
@@ -83,8 +84,8 @@ __global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
     const int tid = threadIdx.x;
     const int m0 = (blockIdx.x / tiles_n) * BM;
     const int n0 = (blockIdx.x % tiles_n) * BN;
-    const T* A = static_cast<const T*>(p.A);
-    const T* B = static_cast<const T*>(p.B);
+    const S* A = static_cast<const S*>(p.A);
+    const S* B = static_cast<const S*>(p.B);
 
     float ra[A_CH][V], rb[B_CH][V];
 
@@ -164,13 +165,15 @@ __global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
     }
 }
 
-template <typename T>
+}  // namespace
+
+template <In T>
 hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = rows_16b_aligned(p.A, p.lda, sizeof(T)) &&
-                     rows_16b_aligned(p.B, p.ldb, sizeof(T));
+    const bool vec = rows_16b_aligned(p.A, p.lda, sizeof(typename InFmt<T>::S)) &&
+                     rows_16b_aligned(p.B, p.ldb, sizeof(typename InFmt<T>::S));
     if (vec)
         hipLaunchKernelGGL((lds_kernel<T, true>), dim3((unsigned)blocks), dim3(NT),
                            0, s, p, tiles_n);
@@ -179,14 +182,8 @@ hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
                            0, s, p, tiles_n);
     return hipGetLastError();
 }
-
-}  // namespace
-
-hipError_t launch_lds_f32(const GemmParams& p, hipStream_t s) {
-    return launch_lds<float>(p, s);
-}
-hipError_t launch_lds_bf16(const GemmParams& p, hipStream_t s) {
-    return launch_lds<uint16_t>(p, s);
-}
+template hipError_t launch_lds<In::F32>(const GemmParams&, hipStream_t);
+template hipError_t launch_lds<In::BF16>(const GemmParams&, hipStream_t);
+template hipError_t launch_lds<In::F16>(const GemmParams&, hipStream_t);
 
 }  // namespace dgt

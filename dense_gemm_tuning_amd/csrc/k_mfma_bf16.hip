@@ -1,5 +1,7 @@
-// k_mfma_bf16.hip -- BF16-input / FP32-accumulate GEMM on the CDNA4 matrix
-// cores.
+// k_mfma_bf16.hip -- 16-bit-input (BF16 or FP16) / FP32-accumulate GEMM on
+// the CDNA4 matrix cores, register-staged (any shape, any alignment).  FP16
+// takes the same path with v_mfma_f32_32x32x16_f16 (the pages' matrix-unit
+// listings use half inputs: dilfish.github.io 5.5, qwbw.cn Level 2).
 //
 // The pages' matrix-unit rung (dilfish.github.io 5.5 WMMA listing; qwbw.cn
 // Level 2 and its double-buffering row) feeds 16-bit inputs to the matrix
@@ -79,12 +81,12 @@ __device__ __forceinline__ uint4 column8(const uint4 (&r)[8], int j) {
     return make_uint4(o[0], o[1], o[2], o[3]);
 }
 
-__device__ __forceinline__ bf16x8 as_bf16x8(const uint4& v) {
-    return __builtin_bit_cast(bf16x8, v);
+__device__ __forceinline__ u32x4 as_u32x4(const uint4& v) {
+    return u32x4{v.x, v.y, v.z, v.w};
 }
 
-template <bool kVec, bool kGuard>
-__global__ __launch_bounds__(NT, 1) void mfma_bf16_kernel(GemmParams p, int tiles_n) {
+template <In T, bool kVec, bool kGuard>
+__global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n) {
     __shared__ uint4 As[2][BM * CPR];
     __shared__ uint4 Bt[2][BN * CPR];
 
@@ -152,23 +154,22 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_kernel(GemmParams p, int tile
         for (int s = 0; s < BK / 16; ++s) {
             // half-wave h supplies k = 16s + 8h .. +7 for both operands
             const int q = 2 * s + h;
-            bf16x8 a[4], b[4];
+            u32x4 a[4], b[4];
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti) {
                 const int row = wm * 128 + ti * 32 + r32;
-                a[ti] = as_bf16x8(As[buf][row * CPR + (q ^ swz(row))]);
+                a[ti] = as_u32x4(As[buf][row * CPR + (q ^ swz(row))]);
             }
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj) {
                 const int n = wn * 128 + tj * 32 + r32;
-                b[tj] = as_bf16x8(Bt[buf][n * CPR + (q ^ swz(n))]);
+                b[tj] = as_u32x4(Bt[buf][n * CPR + (q ^ swz(n))]);
             }
 #pragma unroll
             for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
                 for (int tj = 0; tj < 4; ++tj)
-                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(
-                        a[ti], b[tj], acc[ti][tj], 0, 0, 0);
+                    acc[ti][tj] = mfma32x32x16<T>(a[ti], b[tj], acc[ti][tj]);
         }
         if (t + 1 < nk) store_slice(buf ^ 1);
         __syncthreads();
@@ -193,8 +194,9 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_kernel(GemmParams p, int tile
 
 }  // namespace
 
-hipError_t launch_mfma_bf16(const GemmParams& p, hipStream_t s) {
-    if (mfma_bf16_dma_eligible(p)) return launch_mfma_bf16_dma(p, s);
+template <In T>
+hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
+    if (mfma16_dma_eligible(p)) return launch_mfma16_dma<T>(p, s);
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -202,12 +204,14 @@ hipError_t launch_mfma_bf16(const GemmParams& p, hipStream_t s) {
     const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
     const dim3 grid((unsigned)blocks), block(NT);
     if (full)
-        hipLaunchKernelGGL((mfma_bf16_kernel<true, false>), grid, block, 0, s, p, tiles_n);
+        hipLaunchKernelGGL((mfma16_kernel<T, true, false>), grid, block, 0, s, p, tiles_n);
     else if (vec)
-        hipLaunchKernelGGL((mfma_bf16_kernel<true, true>), grid, block, 0, s, p, tiles_n);
+        hipLaunchKernelGGL((mfma16_kernel<T, true, true>), grid, block, 0, s, p, tiles_n);
     else
-        hipLaunchKernelGGL((mfma_bf16_kernel<false, true>), grid, block, 0, s, p, tiles_n);
+        hipLaunchKernelGGL((mfma16_kernel<T, false, true>), grid, block, 0, s, p, tiles_n);
     return hipGetLastError();
 }
+template hipError_t launch_mfma16<In::BF16>(const GemmParams&, hipStream_t);
+template hipError_t launch_mfma16<In::F16>(const GemmParams&, hipStream_t);
 
 }  // namespace dgt

@@ -1,4 +1,5 @@
-// k_mfma_bf16_dma.hip -- BF16-input / FP32-accumulate GEMM for whole tiles:
+// k_mfma_bf16_dma.hip -- 16-bit-input (BF16 or FP16) / FP32-accumulate GEMM
+// for whole tiles:
 // global -> LDS by DMA three K slices ahead, B transposed by the LDS read.
 //
 // Tiling as in the register-staged kernel (256 x 256 workgroup tile, 2 x 2
@@ -69,7 +70,8 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
-__global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int tiles_n) {
+template <In T>
+__global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_n) {
     // One LDS object per operand and stage, so that the compiler sees that a
     // copy in flight into one stage does not alias reads of another.  A has
     // two stages of two slices each, B four stages of one slice.
@@ -163,17 +165,17 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
 
     // Operands of step s of the slice held in (sa half u, sb).
     auto load_frags = [&](const uint8_t* sa, int u, const uint8_t* sb, int s,
-                          bf16x8 (&a)[4], bf16x8 (&b)[4]) {
+                          u32x4 (&a)[4], u32x4 (&b)[4]) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
-            a[ti] = *reinterpret_cast<const bf16x8*>(sa + a_off[ti][u][s]);
+            a[ti] = *reinterpret_cast<const u32x4*>(sa + a_off[ti][u][s]);
 #pragma unroll
         for (int tj = 0; tj < 4; ++tj) {
             const uint8_t* base = sb + b_off[tj] + s * 8192;
             const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base));
             const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base + 2048));
             const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
-            b[tj] = __builtin_bit_cast(bf16x8, v);
+            b[tj] = __builtin_bit_cast(u32x4, v);
         }
     };
 
@@ -181,13 +183,12 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
     // in program order are spread between them (3 LDS reads and one copy per
     // 4 MFMAs), so the address unit never sees a burst that would hold the
     // wave, and its MFMA issue, back.
-    auto mfma_step = [&](const bf16x8 (&a)[4], const bf16x8 (&b)[4]) {
+    auto mfma_step = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
             for (int tj = 0; tj < 4; ++tj)
-                acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x16_bf16(a[ti], b[tj], acc[ti][tj],
-                                                                     0, 0, 0);
+                acc[ti][tj] = mfma32x32x16<T>(a[ti], b[tj], acc[ti][tj]);
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
@@ -202,7 +203,7 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    bf16x8 a0[4], b0[4], a1[4], b1[4];
+    u32x4 a0[4], b0[4], a1[4], b1[4];
 
     // Slice kt (its A in half u of sa, its B in sb); the next slice's A is in
     // half nu of na, its B in nb.  Copies, per wave:
@@ -281,18 +282,21 @@ __global__ __launch_bounds__(NT, 1) void mfma_bf16_dma_kernel(GemmParams p, int 
 
 }  // namespace
 
-bool mfma_bf16_dma_eligible(const GemmParams& p) {
+bool mfma16_dma_eligible(const GemmParams& p) {
     return rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2) &&
            p.M % BM == 0 && p.N % BN == 0 && p.K % KALIGN == 0 && p.K > 0;
 }
 
-hipError_t launch_mfma_bf16_dma(const GemmParams& p, hipStream_t s) {
+template <In T>
+hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
     const int tiles_n = p.N / BN;
     const int64_t blocks = (int64_t)(p.M / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(mfma_bf16_dma_kernel, dim3((unsigned)blocks), dim3(NT), 0, s, p,
+    hipLaunchKernelGGL(mfma16_dma_kernel<T>, dim3((unsigned)blocks), dim3(NT), 0, s, p,
                        tiles_n);
     return hipGetLastError();
 }
+template hipError_t launch_mfma16_dma<In::BF16>(const GemmParams&, hipStream_t);
+template hipError_t launch_mfma16_dma<In::F16>(const GemmParams&, hipStream_t);
 
 }  // namespace dgt

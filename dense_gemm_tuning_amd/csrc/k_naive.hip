@@ -21,19 +21,20 @@ namespace {
 constexpr int kNaiveX = 64;  // one wavefront along the contiguous columns
 constexpr int kNaiveY = 4;   // four rows per workgroup (256 lanes)
 
-template <typename T>
+template <In T>
 __global__ __launch_bounds__(kNaiveX * kNaiveY) void naive_kernel(GemmParams p,
                                                                   int tiles_n) {
+    using S = typename InFmt<T>::S;
     const int bn = blockIdx.x % tiles_n;
     const int bm = blockIdx.x / tiles_n;
     const int col = bn * kNaiveX + threadIdx.x;
     const int row = bm * kNaiveY + threadIdx.y;
     if (row >= p.M || col >= p.N) return;
-    const T* a = static_cast<const T*>(p.A) + (int64_t)row * p.lda;
-    const T* b = static_cast<const T*>(p.B) + col;
+    const S* a = static_cast<const S*>(p.A) + (int64_t)row * p.lda;
+    const S* b = static_cast<const S*>(p.B) + col;
     float acc = 0.0f;
     for (int k = 0; k < p.K; ++k)
-        acc = fmaf(load_in(a + k), load_in(b + (int64_t)k * p.ldb), acc);
+        acc = fmaf(load_in<T>(a + k), load_in<T>(b + (int64_t)k * p.ldb), acc);
     float* c = p.C + (int64_t)row * p.ldc + col;
     *c = epilogue(acc, p.alpha, p.beta, c);
 }
@@ -51,7 +52,9 @@ __global__ __launch_bounds__(256) void scale_kernel(float* C, int64_t ldc, int M
     }
 }
 
-template <typename T>
+}  // namespace
+
+template <In T>
 hipError_t launch_naive(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + kNaiveX - 1) / kNaiveX;
     const int64_t tiles_m = (p.M + kNaiveY - 1) / kNaiveY;
@@ -61,15 +64,9 @@ hipError_t launch_naive(const GemmParams& p, hipStream_t s) {
                        dim3(kNaiveX, kNaiveY), 0, s, p, tiles_n);
     return hipGetLastError();
 }
-
-}  // namespace
-
-hipError_t launch_naive_f32(const GemmParams& p, hipStream_t s) {
-    return launch_naive<float>(p, s);
-}
-hipError_t launch_naive_bf16(const GemmParams& p, hipStream_t s) {
-    return launch_naive<uint16_t>(p, s);
-}
+template hipError_t launch_naive<In::F32>(const GemmParams&, hipStream_t);
+template hipError_t launch_naive<In::BF16>(const GemmParams&, hipStream_t);
+template hipError_t launch_naive<In::F16>(const GemmParams&, hipStream_t);
 
 hipError_t launch_scale(const GemmParams& p, hipStream_t s) {
     const int64_t total = (int64_t)p.M * p.N;

@@ -17,7 +17,7 @@
 // output columns to MFMA slots is valid if A and B agree and the store
 // inverts the column map.
 //
-//  * bf16: v_mfma_f32_16x16x32_bf16 with rows = the (up to 16) rows of A
+//  * bf16 / fp16: v_mfma_f32_16x16x32_{bf16,f16} with rows = the (up to 16) rows of A
 //    and columns = 16 columns of B.  Lane l (g = l/16, i = l%16) loads the
 //    8 x 8 block B[k0+8g .. +7][n0+8i .. +7] and transposes it in registers
 //    into eight k-contiguous column pieces; MFMA c (c = 0..7) takes column
@@ -42,8 +42,6 @@ namespace {
 constexpr int NT = 512;      // 8 wavefronts
 constexpr int NW = NT / 64;
 constexpr int KSTEP = 32;
-
-typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 // 16-byte piece [col, col + 16/esz) of one row, zero outside; streamed.
 template <typename T, bool kVec, bool kGuard>
@@ -108,8 +106,8 @@ __device__ __forceinline__ void reduce_store(float (*red)[16][COLS + 4],
 
 constexpr int BF_COLS = 128;
 
-template <bool kVec, bool kGuard>
-__global__ __launch_bounds__(NT, 1) void skinny_bf16_kernel(GemmParams p) {
+template <In T, bool kVec, bool kGuard>
+__global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
     __shared__ float red[NW][16][BF_COLS + 4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, i = lane & 15;
@@ -142,11 +140,8 @@ __global__ __launch_bounds__(NT, 1) void skinny_bf16_kernel(GemmParams p) {
     auto compute = [&](int step, const u32x4 (&rb)[8]) {
         const u32x4 a = load16_cached<uint16_t, kVec, kGuard>(arow, step * KSTEP + 8 * g,
                                                               p.K, a_ok);
-        const bf16x8 av = __builtin_bit_cast(bf16x8, a);
 #pragma unroll
-        for (int c = 0; c < 8; ++c)
-            acc[c] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
-                av, __builtin_bit_cast(bf16x8, column8(rb, c)), acc[c], 0, 0, 0);
+        for (int c = 0; c < 8; ++c) acc[c] = mfma16x16x32<T>(a, column8(rb, c), acc[c]);
     };
 
     u32x4 b0[8], b1[8];
@@ -239,18 +234,21 @@ __global__ __launch_bounds__(NT, 1) void skinny_f32_kernel(GemmParams p) {
 
 }  // namespace
 
-hipError_t launch_skinny_bf16(const GemmParams& p, hipStream_t s) {
+template <In T>
+hipError_t launch_skinny16(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + BF_COLS - 1) / BF_COLS;
     const bool vec = rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2);
     const bool full = vec && p.N % BF_COLS == 0 && p.K % KSTEP == 0;
     if (full)
-        hipLaunchKernelGGL((skinny_bf16_kernel<true, false>), dim3(blocks), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((skinny16_kernel<T, true, false>), dim3(blocks), dim3(NT), 0, s, p);
     else if (vec)
-        hipLaunchKernelGGL((skinny_bf16_kernel<true, true>), dim3(blocks), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((skinny16_kernel<T, true, true>), dim3(blocks), dim3(NT), 0, s, p);
     else
-        hipLaunchKernelGGL((skinny_bf16_kernel<false, true>), dim3(blocks), dim3(NT), 0, s, p);
+        hipLaunchKernelGGL((skinny16_kernel<T, false, true>), dim3(blocks), dim3(NT), 0, s, p);
     return hipGetLastError();
 }
+template hipError_t launch_skinny16<In::BF16>(const GemmParams&, hipStream_t);
+template hipError_t launch_skinny16<In::F16>(const GemmParams&, hipStream_t);
 
 hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + F_COLS - 1) / F_COLS;

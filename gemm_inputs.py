@@ -23,7 +23,9 @@ Distributions (row-major element order):
 
 Precision: fp32 inputs are the fp64 draw rounded to nearest-even fp32.  bf16
 inputs are that fp32 value rounded to nearest-even bf16 (the upper 16 bits,
-returned as raw ``uint16`` bit patterns).  The workloads never produce NaN.
+returned as raw ``uint16`` bit patterns); f16 inputs are that fp32 value
+rounded to nearest-even IEEE binary16 (numpy's conversion), also returned as
+raw ``uint16`` bits.  The workloads never produce NaN or infinity.
 
 Workloads: the pages tune a single operation, ``C = alpha*A*B + beta*C`` with
 row-major A (M x K), B (K x N), C (M x N) (elainafan.one, "稠密矩阵乘法" and
@@ -100,13 +102,13 @@ def draw(seed: int, rows: int, cols: int, dist: str, sigma: float = 1.0,
          dtype: str = "f32") -> np.ndarray:
     """Draw a packed row-major ``rows x cols`` matrix.
 
-    ``dtype`` is ``"f32"`` (returns float32) or ``"bf16"`` (returns uint16
-    bf16 bit patterns).  ``dist`` is ``"uniform"``, ``"int"`` or ``"normal"``.
+    ``dtype`` is ``"f32"`` (returns float32), ``"bf16"`` or ``"f16"`` (return
+    uint16 bit patterns).  ``dist`` is ``"uniform"``, ``"int"`` or ``"normal"``.
     """
     n = rows * cols
     if dtype == "f32":
         out = np.empty(n, dtype=np.float32)
-    elif dtype == "bf16":
+    elif dtype in ("bf16", "f16"):
         out = np.empty(n, dtype=np.uint16)
     else:
         raise ValueError(f"unknown dtype {dtype!r}")
@@ -127,14 +129,19 @@ def draw(seed: int, rows: int, cols: int, dist: str, sigma: float = 1.0,
             else:
                 raise ValueError(f"unknown distribution {dist!r}")
         v32 = v.astype(np.float32)  # round-to-nearest-even
-        out[s:s + cnt] = v32 if dtype == "f32" else fp32_to_bf16_bits(v32)
+        if dtype == "f32":
+            out[s:s + cnt] = v32
+        elif dtype == "bf16":
+            out[s:s + cnt] = fp32_to_bf16_bits(v32)
+        else:
+            out[s:s + cnt] = v32.astype(np.float16).view(np.uint16)
     return out.reshape(rows, cols)
 
 
 @dataclasses.dataclass(frozen=True)
 class Workload:
     name: str
-    dtype: str          # "f32" or "bf16" (input precision; C is always fp32)
+    dtype: str          # "f32", "bf16" or "f16" (input precision; C is always fp32)
     M: int
     N: int
     K: int
@@ -169,6 +176,8 @@ WORKLOADS = {
                          "uniform", seed_base=3000),
     "bf16_8192": Workload("bf16_8192", "bf16", 8192, 8192, 8192, 1.0, 0.0,
                           "normal", seed_base=4000),
+    "f16_8192": Workload("f16_8192", "f16", 8192, 8192, 8192, 1.0, 0.0, "normal",
+                         seed_base=6000),
     "bf16_skinny_8x28672x8192": Workload("bf16_skinny_8x28672x8192", "bf16",
                                          8, 28672, 8192, 1.0, 0.0, "normal",
                                          sigma=0.02, seed_base=5000),
@@ -187,5 +196,9 @@ def make_inputs(w: Workload):
 
 
 def as_fp32(x: np.ndarray, dtype: str) -> np.ndarray:
-    """The fp32 values an input array denotes (bf16 bits widened exactly)."""
-    return bf16_bits_to_fp32(x) if dtype == "bf16" else np.asarray(x, np.float32)
+    """The fp32 values an input array denotes (16-bit bits widened exactly)."""
+    if dtype == "bf16":
+        return bf16_bits_to_fp32(x)
+    if dtype == "f16":
+        return np.asarray(x, np.uint16).view(np.float16).astype(np.float32)
+    return np.asarray(x, np.float32)

@@ -18,8 +18,10 @@
  *
  * Precision: gemm_f32 takes fp32 A and B; gemm_bf16 takes A and B as raw
  * bf16 bit patterns (uint16_t, the upper half of an fp32 value: 8-bit
- * exponent, 7-bit mantissa, dilfish.github.io section 5.5 table).  Both
- * accumulate in fp32 on the matrix cores and read/write C in fp32.  The
+ * exponent, 7-bit mantissa); gemm_f16 takes raw IEEE binary16 bit patterns
+ * (5-bit exponent, 10-bit mantissa) -- the BF16 and FP16 rows of the
+ * dilfish.github.io section 5.5 precision table.  All accumulate in fp32 on
+ * the matrix cores and read/write C in fp32.  The
  * summation order is the kernel's own; results agree with an exact
  * reference to fp32 accumulation accuracy, and bit for bit whenever every
  * partial sum is exactly representable (e.g. small-integer inputs).
@@ -34,7 +36,7 @@
  * they must stay valid until the work queued on `stream` has finished.  The
  * library allocates nothing, frees nothing, keeps no per-call state and is
  * safe to call from several host threads.  A misaligned pointer or leading
- * dimension is accepted (fp32: 4-byte, bf16: 2-byte alignment); it only
+ * dimension is accepted (fp32: 4-byte, bf16/fp16: 2-byte alignment); it only
  * selects a slower load path, never a fault.
  *
  * Ordering: asynchronous.  Work is queued on `stream` (a hipStream_t cast
@@ -55,7 +57,10 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 1
+#define DGT_GEMM_ABI_VERSION 2
+
+/* Input formats (gemm_select_variant's dtype). */
+enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };
 
 enum gemm_status {
     GEMM_OK = 0,
@@ -71,7 +76,7 @@ enum gemm_status {
 };
 
 /* Kernel ladder (for measurement and tests; GEMM_VARIANT_AUTO is what
- * gemm_f32 / gemm_bf16 use).  Every variant computes the same operation
+ * gemm_f32 / gemm_bf16 / gemm_f16 use).  Every variant computes the same operation
  * and handles any shape that it accepts, ragged edges included. */
 enum gemm_variant {
     GEMM_VARIANT_AUTO = 0,      /* MFMA tiles; skinny path when M <= 16       */
@@ -104,7 +109,14 @@ int gemm_bf16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
               const uint16_t* B, int ldb, float beta, float* C, int ldc,
               void* stream);
 
-/* Same as gemm_f32 / gemm_bf16 with an explicit ladder rung (enum
+/* C <- alpha*A*B + beta*C, fp16 inputs (raw IEEE binary16 bits), fp32
+ * accumulate/output: the half-input / fp32-accumulate matrix-unit path of
+ * dilfish.github.io 5.5 (WMMA listing) and qwbw.cn Level 2. */
+int gemm_f16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
+             const uint16_t* B, int ldb, float beta, float* C, int ldc,
+             void* stream);
+
+/* Same as gemm_f32 / gemm_bf16 / gemm_f16 with an explicit ladder rung (enum
  * gemm_variant).  GEMM_VARIANT_SKINNY requires M <= 16 and returns
  * GEMM_ERR_VARIANT otherwise. */
 int gemm_f32_variant(int variant, int M, int N, int K, float alpha,
@@ -113,12 +125,15 @@ int gemm_f32_variant(int variant, int M, int N, int K, float alpha,
 int gemm_bf16_variant(int variant, int M, int N, int K, float alpha,
                       const uint16_t* A, int lda, const uint16_t* B, int ldb,
                       float beta, float* C, int ldc, void* stream);
+int gemm_f16_variant(int variant, int M, int N, int K, float alpha,
+                     const uint16_t* A, int lda, const uint16_t* B, int ldb,
+                     float beta, float* C, int ldc, void* stream);
 
-/* The rung GEMM_VARIANT_AUTO picks for this call (dtype_is_bf16: 0 = fp32,
- * 1 = bf16), or a negative status if the arguments are invalid.  Host only:
- * touches no device and queues nothing. */
-int gemm_select_variant(int dtype_is_bf16, int M, int N, int K, int lda,
-                        int ldb, int ldc);
+/* The rung GEMM_VARIANT_AUTO picks for this call (dtype: enum gemm_dtype),
+ * or a negative status if the arguments are invalid.  Host only: touches no
+ * device and queues nothing. */
+int gemm_select_variant(int dtype, int M, int N, int K, int lda, int ldb,
+                        int ldc);
 
 /* Static string naming a status code (never NULL). */
 const char* gemm_status_string(int status);

@@ -62,13 +62,14 @@ class Oracle:
                           ctypes.c_double, _d, _i64, _d, _i64]
         lib.oracle_widen_f32.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
         lib.oracle_widen_bf16.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
+        lib.oracle_widen_f16.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
         lib.oracle_round_f32.argtypes = [_d, _i64, ctypes.c_void_p]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
 
     def widen(self, x: np.ndarray, dtype: str) -> np.ndarray:
-        """Exact fp64 values of an input matrix (fp32 array or bf16 bits)."""
+        """Exact fp64 values of an input matrix (fp32 array, bf16 or f16 bits)."""
         x = np.ascontiguousarray(x)
         rows, cols = x.shape
         out = np.empty((rows, cols), dtype=np.float64)
@@ -78,6 +79,9 @@ class Oracle:
         elif dtype == "bf16":
             assert x.dtype == np.uint16
             self.lib.oracle_widen_bf16(x.ctypes.data, rows, cols, cols, _ptr(out))
+        elif dtype == "f16":
+            assert x.dtype == np.uint16
+            self.lib.oracle_widen_f16(x.ctypes.data, rows, cols, cols, _ptr(out))
         else:
             raise ValueError(dtype)
         return out
@@ -110,7 +114,7 @@ class Oracle:
 
     def gemm(self, A, B, C0, alpha: float, beta: float, dtype: str,
              order: str = "ikj") -> np.ndarray:
-        """Oracle result in fp64 for raw inputs (fp32 arrays or bf16 bits)."""
+        """Oracle result in fp64 for raw inputs (fp32 arrays, bf16 or f16 bits)."""
         A64 = self.widen(A, dtype)
         B64 = self.widen(B, dtype)
         C64 = self.widen(C0, "f32") if C0 is not None else None

@@ -21,8 +21,8 @@
  *       "行主序" and the matmul_cpu listing).
  *
  * Precision: every input is first widened EXACTLY to fp64 (fp32 values and
- * bf16 bit patterns are both exact in fp64), so the oracle consumes the
- * already-rounded inputs.  The sum runs over k in ascending order and
+ * bf16 and IEEE binary16 bit patterns are all exact in fp64), so the oracle
+ * consumes the already-rounded inputs.  The sum runs over k in ascending order and
  * accumulates in fp64.  Each product of two fp32 (24-bit significand) values
  * is exact in fp64 (48 <= 53 bits), so only the additions round.  The page's
  * own CPU loop (elainafan.one "CPU 实现") accumulates in float; the oracle
@@ -44,6 +44,7 @@
  * bit-identical (the page notes that loop order changes cache behaviour, not
  * the operations: elainafan.one, paragraph after the matmul_cpu listing).
  */
+#include <math.h>
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
@@ -75,6 +76,26 @@ void oracle_widen_bf16(const uint16_t* src, int64_t rows, int64_t cols,
     for (int64_t r = 0; r < rows; ++r)
         for (int64_t c = 0; c < cols; ++c)
             dst[r * cols + c] = bf16_bits_value(src[r * ld + c]);
+}
+
+/* IEEE 754 binary16 bit pattern -> fp64, from the format's definition:
+ * sign bit 15, biased exponent bits 14..10 (bias 15), fraction bits 9..0.
+ * Exponent 0: subnormal, fraction * 2^-24.  Exponent 31: infinity (fraction
+ * 0) or NaN.  Otherwise (1024 + fraction) * 2^(exponent - 25).  Exact. */
+static double f16_bits_value(uint16_t h) {
+    const int sign = h >> 15, e = (h >> 10) & 31, f = h & 1023;
+    double v;
+    if (e == 0) v = ldexp((double)f, -24);
+    else if (e == 31) v = f ? NAN : INFINITY;
+    else v = ldexp((double)(1024 + f), e - 25);
+    return sign ? -v : v;
+}
+
+void oracle_widen_f16(const uint16_t* src, int64_t rows, int64_t cols,
+                      int64_t ld, double* dst) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            dst[r * cols + c] = f16_bits_value(src[r * ld + c]);
 }
 
 /* ---- the definition ---------------------------------------------------- */

@@ -11,9 +11,9 @@
 
 A 16-bit-input matrix unit is expected to land 1e-4..1e-3 away from an fp32
 reference computed on the unrounded data (dilfish.github.io section 5.5); the
-oracle here consumes the already-rounded bf16 inputs, so only fp32
+oracle here consumes the already-rounded bf16 / fp16 inputs, so only fp32
 accumulation error remains (about 2**-24 * sqrt(K) relative) and the 1e-5
-gate applies to BF16 as well.
+gate applies to the 16-bit inputs as well.
 """
 
 import math

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 1
+    assert dgt.gemm_abi_version() == 2
     for code in range(0, -7, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
@@ -50,7 +50,7 @@ def test_abi_version_and_status_strings(lib):
 A_, B_, C_ = 0x100000, 0x200000, 0x300000
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16", "gemm_f16"])
 def test_argument_errors(lib, fn):
     f = getattr(dgt, fn)
     assert f(-1, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_DIM
@@ -68,7 +68,7 @@ def test_argument_errors(lib, fn):
     assert f(4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, B_ - 16, 4) == dgt.GEMM_ERR_OVERLAP
 
 
-@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16"])
+@pytest.mark.parametrize("fn", ["gemm_f32", "gemm_bf16", "gemm_f16"])
 def test_empty_c_is_a_no_op(lib, fn):
     f = getattr(dgt, fn)
     # quick return before any pointer check or launch
@@ -82,8 +82,10 @@ def test_variant_checks(lib):
     assert v(-1, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
     # the skinny rung takes at most 16 rows
     assert v(dgt.VARIANT_SKINNY, 17, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
-    assert dgt.gemm_bf16_variant(dgt.VARIANT_SKINNY, 17, 4, 4, 1.0, A_, 4, B_, 4, 0.0,
-                                 C_, 4) == dgt.GEMM_ERR_VARIANT
+    for fn in (dgt.gemm_bf16_variant, dgt.gemm_f16_variant):
+        assert fn(dgt.VARIANT_SKINNY, 17, 4, 4, 1.0, A_, 4, B_, 4, 0.0,
+                  C_, 4) == dgt.GEMM_ERR_VARIANT
+        assert fn(99, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
 
 
 def test_alpha_zero_does_not_need_a_or_b(lib):
@@ -95,12 +97,17 @@ def test_alpha_zero_does_not_need_a_or_b(lib):
 
 def test_auto_dispatch(lib):
     sel = dgt.gemm_select_variant
-    assert sel(1, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
-    assert sel(1, 16, 100, 100, 100, 100, 100) == dgt.VARIANT_SKINNY
-    assert sel(1, 17, 100, 100, 100, 100, 100) == dgt.VARIANT_MFMA
-    assert sel(0, 4096, 4096, 4096, 4096, 4096, 4096) == dgt.VARIANT_MFMA
-    assert sel(0, 4, 4, 4, 3, 4, 4) == dgt.GEMM_ERR_LD
-    assert sel(0, -4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_DIM
+    F32, BF16, F16 = dgt.DTYPE_F32, dgt.DTYPE_BF16, dgt.DTYPE_F16
+    assert sel(BF16, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
+    assert sel(F16, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
+    assert sel(BF16, 16, 100, 100, 100, 100, 100) == dgt.VARIANT_SKINNY
+    assert sel(BF16, 17, 100, 100, 100, 100, 100) == dgt.VARIANT_MFMA
+    assert sel(F16, 8192, 8192, 8192, 8192, 8192, 8192) == dgt.VARIANT_MFMA
+    assert sel(F32, 4096, 4096, 4096, 4096, 4096, 4096) == dgt.VARIANT_MFMA
+    assert sel(F32, 4, 4, 4, 3, 4, 4) == dgt.GEMM_ERR_LD
+    assert sel(F32, -4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_DIM
+    assert sel(3, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_VARIANT
+    assert sel(-1, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_VARIANT
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -170,6 +170,29 @@ def pin_bf16_inputs(o):
     assert np.array_equal(R, want), "bf16 integer product wrong"
 
 
+def pin_f16_inputs(o):
+    """f16 bits are IEEE 754 binary16 (dilfish.github.io 5.5 table: 5-bit
+    exponent, 10-bit mantissa).  Hand-decoded values, then every one of the
+    65536 patterns except the NaNs against numpy's own float16 conversion."""
+    hand = np.array([[0x3C00, 0xC000, 0x0001, 0x7BFF, 0x8400, 0x3555]], np.uint16)
+    # 0x3555: exponent 13, fraction 0x155 -> 1365/4096, the binary16 nearest 1/3
+    want = [1.0, -2.0, 2.0 ** -24, 65504.0, -2.0 ** -14, 1365 / 4096]
+    got = o.widen(hand, "f16")
+    assert got[0].tolist() == want, "f16 hand-decoded values wrong"
+    allbits = np.arange(65536, dtype=np.uint16)
+    ref = allbits.view(np.float16).astype(np.float64)
+    keep = ~np.isnan(ref)
+    got = o.widen(allbits.reshape(256, 256), "f16").reshape(-1)
+    assert np.array_equal(got[keep], ref[keep]), "f16 decoding disagrees with numpy"
+    assert np.all(np.isnan(got[~keep])), "f16 NaN patterns must decode to NaN"
+    # product through the GEMM: small integers are exact in binary16
+    A = gi.draw(73, 20, 30, "int", dtype="f16")
+    B = gi.draw(74, 30, 10, "int", dtype="f16")
+    R = o.gemm(A, B, None, 1.0, 0.0, "f16")
+    want = (A.view(np.float16).astype(np.float64) @ B.view(np.float16).astype(np.float64))
+    assert np.array_equal(R, want), "f16 integer product wrong"
+
+
 def pin_leading_dims_rectangular(o):
     """Non-square shapes keep rows and columns apart: row i of C depends on
     row i of A only, column j on column j of B only."""
@@ -186,7 +209,7 @@ def pin_leading_dims_rectangular(o):
 
 PINS = [pin_identity, pin_permutation, pin_rank1, pin_small_integers,
         pin_alpha_beta, pin_exact_rational, pin_library_float64, pin_bf16_inputs,
-        pin_leading_dims_rectangular]
+        pin_f16_inputs, pin_leading_dims_rectangular]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -239,6 +262,10 @@ MUTANTS = {
     "acc_not_reset": ("for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;",
                       "if (i == 0) for (int64_t j = 0; j < N; ++j) acc[j] = 0.0;"),
     "float_accumulator": ("acc[j] += a * brow[j];", "acc[j] = (float)(acc[j] + a * brow[j]);"),
+    "f16_bias": ("ldexp((double)(1024 + f), e - 25)", "ldexp((double)(1024 + f), e - 24)"),
+    "f16_subnormal": ("if (e == 0) v = ldexp((double)f, -24);",
+                      "if (e == 0) v = ldexp((double)(1024 + f), -25);"),
+    "f16_sign": ("return sign ? -v : v;", "return v;"),
 }
 
 
@@ -265,10 +292,13 @@ def test_pins_catch_planted_mistake(name, mutant_dir):
         f.write(head + sep + tail)
     lib = oracle.compile_source(path_c, os.path.join(str(mutant_dir), f"lib{name}.so"))
     mutant = oracle.Oracle(lib)
+    # stop at the first pin that objects: a mutant that indexes wrongly may
+    # read past its buffers, and later pins would only widen that read
     failed = []
     for pin in PINS:
         try:
             pin(mutant)
-        except AssertionError:
+        except (AssertionError, ValueError, OverflowError):
             failed.append(pin.__name__)
+            break
     assert failed, f"no pin catches the planted mistake {name!r}"

@@ -5,7 +5,8 @@ normwise relative error <= 1e-5 and max elementwise error
 <= 1e-4 * sqrt(K) * max(1,|alpha|) * sigma_A * sigma_B.
 
 Coverage: every rung (naive, LDS, MFMA, skinny) at sizes spanning several
-tiles plus a ragged tail; the five workload shapes in the configuration the
+tiles plus a ragged tail, for fp32, bf16 and fp16 inputs; the workload
+shapes in the configuration the
 bench times (AUTO), full-size ones on sampled rows the oracle computes one
 by one; ragged and degenerate shapes; padded leading dimensions and
 misaligned base pointers; beta == 0 with NaN in C; alpha == 0 and K == 0;
@@ -30,6 +31,8 @@ import dense_gemm_tuning_amd as dgt  # noqa: E402
 pytestmark = pytest.mark.gpu
 
 RUNGS = ["naive", "lds", "mfma", "skinny", "auto"]
+DTYPES = ["f32", "bf16", "f16"]
+TORCH_DTYPE = {"f32": None, "bf16": "bfloat16", "f16": "float16"}
 
 
 def say(*a):
@@ -49,10 +52,19 @@ def _gpu():
 
 
 def to_dev(x, dtype):
-    """numpy (fp32 or bf16 bits) -> torch device tensor of the library's type."""
-    if dtype == "bf16":
-        return torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda().view(torch.bfloat16)
+    """numpy (fp32, or bf16/f16 bits) -> torch device tensor of the library's type."""
+    if dtype in ("bf16", "f16"):
+        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
+        return t.view(getattr(torch, TORCH_DTYPE[dtype]))
     return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
+
+
+def bits16(x, dtype):
+    """fp32 values that are exact in the 16-bit format -> its raw bits."""
+    x = np.ascontiguousarray(x, np.float32)
+    if dtype == "bf16":
+        return gi.fp32_to_bf16_bits(x)
+    return x.astype(np.float16).view(np.uint16)
 
 
 def run_gemm(variant, dtype, A, B, C0, alpha, beta, M=None, stream=None):
@@ -84,7 +96,7 @@ SHAPES = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", RUNGS)
 def test_integer_inputs_bit_exact(variant, dtype):
     for idx, (M, N, K) in enumerate(SHAPES):
@@ -100,12 +112,12 @@ def test_integer_inputs_bit_exact(variant, dtype):
             assert_bit_exact(C, R, f"{variant}/{dtype} {M}x{N}x{K} a={alpha} b={beta}")
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", ["mfma", "lds", "skinny"])
 def test_permutation_and_rank1(variant, dtype):
     """Swapped rows/columns or transposed fragments cannot pass these."""
     rng = np.random.default_rng(7)
-    one = 1.0 if dtype == "f32" else gi.fp32_to_bf16_bits(np.float32([1.0]))[0]
+    one = 1.0 if dtype == "f32" else bits16([1.0], dtype)[0]
     for (M, N, K) in [(16, 300, 272), (256, 256, 256), (130, 70, 130)]:
         if not supports(variant, M):
             continue
@@ -124,8 +136,8 @@ def test_permutation_and_rank1(variant, dtype):
         w, z = rng.integers(-3, 4, K), rng.integers(-3, 4, N)
         A = np.outer(u, v).astype(np.float32)
         B = np.outer(w, z).astype(np.float32)
-        if dtype == "bf16":
-            A, B = gi.fp32_to_bf16_bits(A), gi.fp32_to_bf16_bits(B)
+        if dtype != "f32":
+            A, B = bits16(A, dtype), bits16(B, dtype)
         st, C = run_gemm(variant, dtype, A, B, None, 1.0, 0.0)
         # + 0.0: an exact zero sum of products starting from +0 is +0, while
         # the closed form's 0 * (negative) is -0
@@ -135,7 +147,7 @@ def test_permutation_and_rank1(variant, dtype):
 
 # ------------------------------------------------------ real-valued gates
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", RUNGS)
 def test_real_inputs_within_tolerance(variant, dtype):
     dist = "uniform" if dtype == "f32" else "normal"
@@ -193,7 +205,7 @@ def test_workload_integer_variants(name):
 
 # -------------------------------------------------------------- semantics
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", RUNGS)
 def test_alpha_zero_and_k_zero(variant, dtype):
     M, N = (16 if variant == "skinny" else 70), 90
@@ -211,7 +223,7 @@ def test_alpha_zero_and_k_zero(variant, dtype):
     assert st == 0 and np.all(C == 0.0)
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", RUNGS)
 def test_beta_zero_ignores_nan_in_c(variant, dtype):
     M, N, K = (8 if variant == "skinny" else 200), 300, 64
@@ -225,7 +237,7 @@ def test_beta_zero_ignores_nan_in_c(variant, dtype):
 def _strided(shape, ld, dtype, offset_elems, fill):
     """A device tensor view with row pitch ld and a base offset in elements."""
     rows, cols = shape
-    tdt = torch.float32 if dtype == "f32" else torch.bfloat16
+    tdt = torch.float32 if dtype == "f32" else getattr(torch, TORCH_DTYPE[dtype])
     base = torch.full((rows * ld + offset_elems + 8,), fill, dtype=tdt, device="cuda")
     return base, base[offset_elems:offset_elems + rows * ld].view(rows, ld)[:, :cols]
 
@@ -235,7 +247,7 @@ def _strided(shape, ld, dtype, offset_elems, fill):
 LAYOUTS = {"aligned_pad": (8, 0), "odd_pad": (3, 0), "misaligned": (8, 1)}
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", RUNGS)
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 def test_leading_dims_alignment_and_guard_band(variant, dtype, layout):
@@ -266,7 +278,7 @@ def test_leading_dims_alignment_and_guard_band(variant, dtype, layout):
     assert np.all(full[mask] == canary), "kernel wrote outside C"
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", ["mfma", "lds", "skinny"])
 def test_deterministic_and_stream(variant, dtype):
     M, N, K = (16 if variant == "skinny" else 384), 640, 1000
