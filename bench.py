@@ -11,9 +11,10 @@ multiplies and K adds per output; 2*2048^3 = 17.18e9 in its section 2.5).
 
 The same JSON line carries, under "also", the FP32 4096^3 case (against the
 fp32 matrix-core peak), the FP16-input 8192^3 case (against the fp16 peak,
-equal to bf16's) and the skinny decode-shaped case M=8, N=28672,
+equal to bf16's), the skinny decode-shaped case M=8, N=28672,
 K=8192 (against HBM bandwidth: its time is the time to stream B once,
-dilfish.github.io 5.1 GEMV row), plus:
+dilfish.github.io 5.1 GEMV row), and the BF16 square and skinny cases with
+a linear layer's operand storage (B stored N x K, A stored K x M), plus:
   * "roofline": the dominant kernel's algorithmic FLOP per launch over its
     measured launch time, against the published MI355X peak;
   * "cpu_baseline": the CPU oracle timed on a bounded row sample of the same
@@ -47,14 +48,28 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 PRIMARY = "bf16_8192"
-SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192"]
+SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
+             "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt"]
 
-# Kernel (source file) that dominates each workload's time, for the roofline.
+# Kernel that dominates each workload's time, for the roofline: a readable
+# name, its source file, and a pattern for the name rocprofv3 prints (the
+# template arguments: input format, then vector / guard flags where the
+# kernel has them, then trans_a, trans_b).
 DOMINANT = {
-    "bf16_8192": ("mfma16_dma_kernel<In::BF16>", "k_mfma_bf16_dma.hip"),
-    "f16_8192": ("mfma16_dma_kernel<In::F16>", "k_mfma_bf16_dma.hip"),
-    "f32_4096": ("mfma_f32_kernel", "k_mfma_f32.hip"),
-    "bf16_skinny_8x28672x8192": ("skinny16_kernel<In::BF16>", "k_skinny.hip"),
+    "bf16_8192": ("mfma16_dma_kernel<BF16, NN>", "k_mfma_bf16_dma.hip",
+                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
+    "f16_8192": ("mfma16_dma_kernel<F16, NN>", "k_mfma_bf16_dma.hip",
+                 r"mfma16_dma_kernel<\(dgt::In\)2, false, false>"),
+    "f32_4096": ("mfma_f32_kernel<NN>", "k_mfma_f32.hip",
+                 r"mfma_f32_kernel<true, false, false, false>"),
+    "bf16_skinny_8x28672x8192": ("skinny16_kernel<BF16, NN>", "k_skinny.hip",
+                                 r"skinny16_kernel<\(dgt::In\)1, true, false, false>"),
+    "bf16_8192_nt": ("mfma16_dma_kernel<BF16, NT>", "k_mfma_bf16_dma.hip",
+                     r"mfma16_dma_kernel<\(dgt::In\)1, false, true>"),
+    "bf16_8192_tn": ("mfma16_dma_kernel<BF16, TN>", "k_mfma_bf16_dma.hip",
+                     r"mfma16_dma_kernel<\(dgt::In\)1, true, false>"),
+    "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT>", "k_skinny.hip",
+                                    r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false>"),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -113,7 +128,7 @@ def read_traffic(workload: str):
     absent or taken on a different version of the kernel source."""
     if not os.path.exists(TRAFFIC_FILE):
         return None
-    kern, src = DOMINANT[workload]
+    kern, src, _ = DOMINANT[workload]
     want = source_digest(src)
     pat = re.compile(r"^traffic\s+workload=(\S+)\s+kernel=(\S+)\s+src=(\S+)\s+"
                      r"fetch_bytes=(\d+)\s+write_bytes=(\d+)", re.M)
@@ -143,11 +158,18 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
           else torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda"))
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
-    fn = {"f32": dgt.gemm_f32, "bf16": dgt.gemm_bf16, "f16": dgt.gemm_f16}[w.dtype]
+    lda, ldb = w.a_shape[1], w.b_shape[1]  # packed stored rows
+    if w.trans_a or w.trans_b:
+        code = {"f32": dgt.DTYPE_F32, "bf16": dgt.DTYPE_BF16, "f16": dgt.DTYPE_F16}[w.dtype]
+
+        def fn(*args):
+            return dgt.gemm_ex(code, w.trans_a, w.trans_b, dgt.VARIANT_AUTO, *args)
+    else:
+        fn = {"f32": dgt.gemm_f32, "bf16": dgt.gemm_bf16, "f16": dgt.gemm_f16}[w.dtype]
 
     def launch(i):
-        st = fn(w.M, w.N, w.K, w.alpha, dA[i % copies].data_ptr(), w.K,
-                dB[i % copies].data_ptr(), w.N, w.beta, dC.data_ptr(), w.N, sptr)
+        st = fn(w.M, w.N, w.K, w.alpha, dA[i % copies].data_ptr(), lda,
+                dB[i % copies].data_ptr(), ldb, w.beta, dC.data_ptr(), w.N, sptr)
         if st != 0:
             raise RuntimeError(dgt.gemm_status_string(st))
 
@@ -179,7 +201,7 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
 
 
 def roofline(w, ms_avg):
-    kern, _ = DOMINANT[w.name]
+    kern, _, _ = DOMINANT[w.name]
     fl = gemm_flops(w.M, w.N, w.K)
     by = algorithmic_bytes(w.M, w.N, w.K, 4 if w.dtype == "f32" else 2, w.beta)
     traffic = read_traffic(w.name)

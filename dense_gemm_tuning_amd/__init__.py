@@ -7,10 +7,11 @@ kernels behind it.  Pointers are device addresses passed as Python ints,
 returns the library's status code (0 = GEMM_OK); ``check`` turns a non-zero
 status into an exception.
 
-``gemm(A, B, C, alpha, beta, variant)`` is a convenience for torch tensors on
-the GPU: it reads shapes, leading dimensions (``stride(0)``) and
-``torch.cuda.current_stream()`` and calls ``gemm_f32`` / ``gemm_bf16`` (or the
-``_variant`` forms).  Torch is used for memory and streams only.
+``gemm(A, B, C, alpha, beta, variant, trans_a=..., trans_b=...)`` is a
+convenience for torch tensors on the GPU: it reads shapes, leading dimensions
+(``stride(0)``) and ``torch.cuda.current_stream()`` and calls ``gemm_f32`` /
+``gemm_bf16`` / ``gemm_f16`` (or ``gemm_ex`` for transposed or explicit-rung
+calls).  Torch is used for memory and streams only.
 
 There is no fallback: if the library has not been built, every call raises.
 """
@@ -30,6 +31,7 @@ GEMM_ERR_NULL = -3
 GEMM_ERR_OVERLAP = -4
 GEMM_ERR_VARIANT = -5
 GEMM_ERR_LAUNCH = -6
+GEMM_ERR_ARG = -7
 
 VARIANT_AUTO = 0
 VARIANT_NAIVE = 1
@@ -41,7 +43,7 @@ VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
 
 # Every symbol the header declares (the tests check the library exports them).
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",
-           "gemm_f16_variant", "gemm_select_variant", "gemm_status_string",
+           "gemm_f16_variant", "gemm_ex", "gemm_select_variant", "gemm_status_string",
            "gemm_abi_version")
 
 DTYPE_F32 = 0
@@ -76,8 +78,10 @@ def _load() -> ctypes.CDLL:
             fn = getattr(lib, name)
             fn.restype = i
             fn.argtypes = [i, *core]
+        lib.gemm_ex.restype = i
+        lib.gemm_ex.argtypes = [i, i, i, i, *core]
         lib.gemm_select_variant.restype = i
-        lib.gemm_select_variant.argtypes = [i] * 7
+        lib.gemm_select_variant.argtypes = [i] * 9
         lib.gemm_status_string.restype = ctypes.c_char_p
         lib.gemm_status_string.argtypes = [i]
         lib.gemm_abi_version.restype = i
@@ -121,9 +125,16 @@ def gemm_f16_variant(variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                                     C, ldc, stream)
 
 
-def gemm_select_variant(dtype, M, N, K, lda, ldb, ldc) -> int:
-    """dtype: DTYPE_F32, DTYPE_BF16 or DTYPE_F16."""
-    return _load().gemm_select_variant(int(dtype), M, N, K, lda, ldb, ldc)
+def gemm_ex(dtype, trans_a, trans_b, variant, M, N, K, alpha, A, lda, B, ldb, beta, C,
+            ldc, stream=0) -> int:
+    return _load().gemm_ex(int(dtype), int(trans_a), int(trans_b), int(variant), M, N, K,
+                           alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_select_variant(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc) -> int:
+    """dtype: DTYPE_F32, DTYPE_BF16 or DTYPE_F16; trans_a, trans_b: 0 or 1."""
+    return _load().gemm_select_variant(int(dtype), int(trans_a), int(trans_b), M, N, K,
+                                       lda, ldb, ldc)
 
 
 def gemm_status_string(status: int) -> str:
@@ -149,8 +160,10 @@ def _ld(t) -> int:
 
 
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
-         stream=None) -> int:
-    """C <- alpha*A*B + beta*C on torch tensors (row-major, unit column stride).
+         stream=None, trans_a: bool = False, trans_b: bool = False) -> int:
+    """C <- alpha*op(A)*op(B) + beta*C on torch tensors (row-major, unit column
+    stride).  op(X) is X, or X transposed when trans_x: then A is the stored
+    K x M tensor, B the stored N x K tensor.
 
     A and B are float32, bfloat16 or float16 (16-bit bits are passed as-is),
     C float32.
@@ -170,8 +183,8 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
             raise ValueError("operands must be 2-D row-major with unit column stride")
         if t.numel() > 0 and not t.is_cuda:
             raise ValueError("operands must be GPU tensors")
-    M, K = A.shape
-    K2, N = B.shape
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
                          f"C {tuple(C.shape)}")
@@ -182,9 +195,13 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
     lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
             float(beta), C.data_ptr(), ldc, stream)
-    auto_fn, var_fn = {torch.float32: (gemm_f32, gemm_f32_variant),
-                       torch.bfloat16: (gemm_bf16, gemm_bf16_variant),
-                       torch.float16: (gemm_f16, gemm_f16_variant)}[A.dtype]
+    dtype = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
+             torch.float16: DTYPE_F16}[A.dtype]
+    if trans_a or trans_b:
+        return gemm_ex(dtype, trans_a, trans_b, variant, *args)
+    auto_fn, var_fn = {DTYPE_F32: (gemm_f32, gemm_f32_variant),
+                       DTYPE_BF16: (gemm_bf16, gemm_bf16_variant),
+                       DTYPE_F16: (gemm_f16, gemm_f16_variant)}[dtype]
     if variant == VARIANT_AUTO:
         return auto_fn(*args)
     return var_fn(variant, *args)

@@ -20,10 +20,16 @@ enum class DType { F32, BF16, F16 };
 
 int elem_size(DType t) { return t == DType::F32 ? 4 : 2; }
 
-// Shape and leading-dimension checks (no pointers involved).
-int check_shape(int M, int N, int K, int lda, int ldb, int ldc) {
+bool valid_flag(int f) { return f == 0 || f == 1; }
+
+// Flag, shape and leading-dimension checks (no pointers involved).  A is
+// stored M x K (ta == 0) or K x M (ta == 1); B is stored K x N (tb == 0) or
+// N x K (tb == 1); ld is the stored row pitch.
+int check_shape(int ta, int tb, int M, int N, int K, int lda, int ldb, int ldc) {
+    if (!valid_flag(ta) || !valid_flag(tb)) return GEMM_ERR_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
-    if (lda < std::max(1, K) || ldb < std::max(1, N) || ldc < std::max(1, N))
+    if (lda < std::max(1, ta ? M : K) || ldb < std::max(1, tb ? K : N) ||
+        ldc < std::max(1, N))
         return GEMM_ERR_LD;
     return GEMM_OK;
 }
@@ -46,10 +52,10 @@ int auto_variant(int M) {
     return M <= dgt::kSkinnyMaxM ? GEMM_VARIANT_SKINNY : GEMM_VARIANT_MFMA;
 }
 
-int run(DType t, int variant, int M, int N, int K, float alpha, const void* A,
-        int lda, const void* B, int ldb, float beta, float* C, int ldc,
+int run(DType t, int ta, int tb, int variant, int M, int N, int K, float alpha,
+        const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
         void* stream) {
-    int st = check_shape(M, N, K, lda, ldb, ldc);
+    int st = check_shape(ta, tb, M, N, K, lda, ldb, ldc);
     if (st != GEMM_OK) return st;
     if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SKINNY)
         return GEMM_ERR_VARIANT;
@@ -59,8 +65,9 @@ int run(DType t, int variant, int M, int N, int K, float alpha, const void* A,
     if (reads_ab && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL;
     const int esz = elem_size(t);
     const uint64_t c_bytes = span_bytes(M, N, ldc, 4);
-    if (reads_ab && (overlaps(C, c_bytes, A, span_bytes(M, K, lda, esz)) ||
-                     overlaps(C, c_bytes, B, span_bytes(K, N, ldb, esz))))
+    const uint64_t a_bytes = ta ? span_bytes(K, M, lda, esz) : span_bytes(M, K, lda, esz);
+    const uint64_t b_bytes = tb ? span_bytes(N, K, ldb, esz) : span_bytes(K, N, ldb, esz);
+    if (reads_ab && (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes)))
         return GEMM_ERR_OVERLAP;
     if (variant == GEMM_VARIANT_SKINNY && M > dgt::kSkinnyMaxM) return GEMM_ERR_VARIANT;
 
@@ -70,6 +77,7 @@ int run(DType t, int variant, int M, int N, int K, float alpha, const void* A,
     p.A = A; p.lda = lda;
     p.B = B; p.ldb = ldb;
     p.C = C; p.ldc = ldc;
+    p.ta = ta; p.tb = tb;
     hipStream_t s = static_cast<hipStream_t>(stream);
 
     hipError_t e;
@@ -113,46 +121,58 @@ extern "C" {
 
 int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
              const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
-    return run(DType::F32, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
+    return run(DType::F32, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
                C, ldc, stream);
 }
 
 int gemm_bf16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
               const uint16_t* B, int ldb, float beta, float* C, int ldc, void* stream) {
-    return run(DType::BF16, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
+    return run(DType::BF16, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
                C, ldc, stream);
 }
 
 int gemm_f16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
              const uint16_t* B, int ldb, float beta, float* C, int ldc, void* stream) {
-    return run(DType::F16, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
+    return run(DType::F16, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
                C, ldc, stream);
 }
 
 int gemm_f16_variant(int variant, int M, int N, int K, float alpha, const uint16_t* A,
                      int lda, const uint16_t* B, int ldb, float beta, float* C, int ldc,
                      void* stream) {
-    return run(DType::F16, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run(DType::F16, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                stream);
 }
 
 int gemm_f32_variant(int variant, int M, int N, int K, float alpha, const float* A,
                      int lda, const float* B, int ldb, float beta, float* C, int ldc,
                      void* stream) {
-    return run(DType::F32, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run(DType::F32, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                stream);
 }
 
 int gemm_bf16_variant(int variant, int M, int N, int K, float alpha,
                       const uint16_t* A, int lda, const uint16_t* B, int ldb,
                       float beta, float* C, int ldc, void* stream) {
-    return run(DType::BF16, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run(DType::BF16, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                stream);
 }
 
-int gemm_select_variant(int dtype, int M, int N, int K, int lda, int ldb, int ldc) {
-    if (dtype < GEMM_DTYPE_F32 || dtype > GEMM_DTYPE_F16) return GEMM_ERR_VARIANT;
-    const int st = check_shape(M, N, K, lda, ldb, ldc);
+int gemm_ex(int dtype, int trans_a, int trans_b, int variant, int M, int N, int K,
+            float alpha, const void* A, int lda, const void* B, int ldb, float beta,
+            float* C, int ldc, void* stream) {
+    if (dtype < GEMM_DTYPE_F32 || dtype > GEMM_DTYPE_F16) return GEMM_ERR_ARG;
+    const DType t = dtype == GEMM_DTYPE_F32    ? DType::F32
+                    : dtype == GEMM_DTYPE_BF16 ? DType::BF16
+                                               : DType::F16;
+    return run(t, trans_a, trans_b, variant, M, N, K, alpha, A, lda, B, ldb, beta, C,
+               ldc, stream);
+}
+
+int gemm_select_variant(int dtype, int trans_a, int trans_b, int M, int N, int K,
+                        int lda, int ldb, int ldc) {
+    if (dtype < GEMM_DTYPE_F32 || dtype > GEMM_DTYPE_F16) return GEMM_ERR_ARG;
+    const int st = check_shape(trans_a, trans_b, M, N, K, lda, ldb, ldc);
     if (st != GEMM_OK) return st;
     return auto_variant(M);
 }
@@ -166,6 +186,7 @@ const char* gemm_status_string(int status) {
         case GEMM_ERR_OVERLAP: return "GEMM_ERR_OVERLAP: C overlaps A or B";
         case GEMM_ERR_VARIANT: return "GEMM_ERR_VARIANT: variant unknown or unsupported for this shape";
         case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: the HIP runtime rejected the launch";
+        case GEMM_ERR_ARG: return "GEMM_ERR_ARG: unknown dtype or transpose flag";
         default: return "unknown gemm status";
     }
 }

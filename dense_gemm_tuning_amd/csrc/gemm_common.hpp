@@ -1,13 +1,21 @@
 // gemm_common.hpp -- types and small device helpers shared by the kernels.
 //
-// All kernels compute C <- alpha*A*B + beta*C on row-major operands
-// (A(i,k) = A[i*lda+k], B(k,j) = B[k*ldb+j], C(i,j) = C[i*ldc+j]) with fp32
-// accumulation; inputs are fp32, or raw bf16 / IEEE binary16 bits.  Offsets
-// are 64-bit.
+// All kernels compute C <- alpha*op(A)*op(B) + beta*C on row-major storage
+// with fp32 accumulation; inputs are fp32, or raw bf16 / IEEE binary16 bits.
+// op(A)(i,k) = A[i*lda+k] (ta == 0) or A[k*lda+i] (ta == 1, A stored K x M);
+// op(B)(k,j) = B[k*ldb+j] (tb == 0) or B[j*ldb+k] (tb == 1, B stored N x K);
+// C(i,j) = C[i*ldc+j].  Offsets are 64-bit.
+//
+// The tiled kernels treat the two operands alike: what matters for staging
+// is whether an operand's stored rows run along k ("K-contiguous": A with
+// ta == 0, B with tb == 1) or along m / n ("MN-contiguous": A with ta == 1,
+// B with tb == 0), not whether it is A or B.
 #pragma once
 
 #include <hip/hip_runtime.h>
 #include <stdint.h>
+
+#include <type_traits>
 
 namespace dgt {
 
@@ -20,7 +28,18 @@ struct GemmParams {
     int64_t ldb;
     float* C;
     int64_t ldc;
+    int ta, tb;  // 1: the operand is stored transposed
 };
+
+// Calls fn(TA, TB) with std::bool_constant arguments matching p.ta, p.tb, so
+// that launchers can pick a kernel specialised for the operand layout.
+template <typename Fn>
+inline hipError_t with_layout(const GemmParams& p, Fn&& fn) {
+    using T = std::true_type;
+    using F = std::false_type;
+    if (p.ta) return p.tb ? fn(T{}, T{}) : fn(T{}, F{});
+    return p.tb ? fn(F{}, T{}) : fn(F{}, F{});
+}
 
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));

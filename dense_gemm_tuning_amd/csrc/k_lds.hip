@@ -16,11 +16,12 @@
 // read (the second barrier the pages insist on, dilfish.github.io 5.7 and
 // elainafan.one after the tiled listing, is the previous slice's barrier).
 //
-// LDS layout: A is stored transposed (k-major, As[k][m]) so that a lane's
-// 4 consecutive m are one 128-bit read; rows are padded by 4 floats (132
-// floats), which makes the transposing writes land on distinct banks
-// (dilfish.github.io 5.7 and qwbw.cn's "Pad" row on padding the second
-// dimension).  Ragged shapes: out-of-range loads are zero-filled and stores
+// LDS layout: both operands k-major (As[k][m], Bs[k][n]) so that a lane's
+// 4 consecutive m or n are one 128-bit read.  An operand whose stored rows
+// run along k (A, or B stored transposed) is written to LDS transposed; rows
+// are padded by 4 floats (132 floats), which makes those transposing writes
+// land on distinct banks (dilfish.github.io 5.7 and qwbw.cn's "Pad" row on
+// padding the second dimension).  Ragged shapes: out-of-range loads are zero-filled and stores
 // masked (dilfish.github.io 5.7; elainafan.one masked tiled listing).
 #include "gemm_common.hpp"
 
@@ -70,16 +71,54 @@ __device__ __forceinline__ void load_chunk(const typename InFmt<T>::S* rowp, int
     }
 }
 
-template <In T, bool kVec>
+// One operand's share of a K slice, fetched as 16-byte chunks along its
+// stored rows and parked in LDS as [k][mn] (both operands alike).  kKC: the
+// stored rows run along k (A untransposed, B transposed): the slice is 128
+// rows of 16 k, written to LDS transposed; otherwise the stored rows run
+// along m / n: the slice is 16 rows of 128, written as is.
+template <In T, bool kVec, bool kKC>
+struct OpSlice {
+    using S = typename InFmt<T>::S;
+    static constexpr int V = Chunk<T>::V;
+    static constexpr int CPR = kKC ? BK / V : BM / V;          // chunks per stored row
+    static constexpr int CH = (kKC ? BM : BK) * CPR / NT;      // chunks per lane
+    float r[CH][V];
+
+    // mn0: first m (or n) of the tile, mn_lim: M (or N).
+    __device__ void load(const S* X, int64_t ld, int mn0, int mn_lim, int k0, int K,
+                         int tid) {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int f = tid + NT * c, row = f / CPR, q = f % CPR;
+            if (kKC) {
+                const bool ok = mn0 + row < mn_lim;
+                load_chunk<T, kVec>(X + (int64_t)(ok ? mn0 + row : 0) * ld, k0 + q * V, K,
+                                    ok, r[c]);
+            } else {
+                const bool ok = k0 + row < K;
+                load_chunk<T, kVec>(X + (int64_t)(ok ? k0 + row : 0) * ld, mn0 + q * V,
+                                    mn_lim, ok, r[c]);
+            }
+        }
+    }
+    __device__ void store(float (*dst)[BM + PAD], int tid) const {
+#pragma unroll
+        for (int c = 0; c < CH; ++c) {
+            const int f = tid + NT * c, row = f / CPR, q = f % CPR;
+#pragma unroll
+            for (int v = 0; v < V; ++v) {
+                if (kKC) dst[q * V + v][row] = r[c][v];
+                else dst[row][q * V + v] = r[c][v];
+            }
+        }
+    }
+};
+
+template <In T, bool kVec, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
     using S = typename InFmt<T>::S;
     __shared__ float As[2][BK][BM + PAD];
     __shared__ float Bs[2][BK][BN + PAD];
-    constexpr int V = Chunk<T>::V;
-    constexpr int A_CPR = BK / V;            // chunks per row of the A slice
-    constexpr int A_CH = BM * A_CPR / NT;    // chunks per lane
-    constexpr int B_CPR = BN / V;
-    constexpr int B_CH = BK * B_CPR / NT;
 
     const int tid = threadIdx.x;
     const int m0 = (blockIdx.x / tiles_n) * BM;
@@ -87,39 +126,15 @@ __global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
     const S* A = static_cast<const S*>(p.A);
     const S* B = static_cast<const S*>(p.B);
 
-    float ra[A_CH][V], rb[B_CH][V];
-
+    OpSlice<T, kVec, !TA> ra;
+    OpSlice<T, kVec, TB> rb;
     auto load_slice = [&](int k0) {
-#pragma unroll
-        for (int c = 0; c < A_CH; ++c) {
-            const int f = tid + NT * c, r = f / A_CPR, q = f % A_CPR;
-            const int row = m0 + r;
-            const bool ok = row < p.M;
-            load_chunk<T, kVec>(A + (int64_t)(ok ? row : 0) * p.lda, k0 + q * V,
-                                p.K, ok, ra[c]);
-        }
-#pragma unroll
-        for (int c = 0; c < B_CH; ++c) {
-            const int f = tid + NT * c, r = f / B_CPR, q = f % B_CPR;
-            const int krow = k0 + r;
-            const bool ok = krow < p.K;
-            load_chunk<T, kVec>(B + (int64_t)(ok ? krow : 0) * p.ldb, n0 + q * V,
-                                p.N, ok, rb[c]);
-        }
+        ra.load(A, p.lda, m0, p.M, k0, p.K, tid);
+        rb.load(B, p.ldb, n0, p.N, k0, p.K, tid);
     };
     auto store_slice = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < A_CH; ++c) {
-            const int f = tid + NT * c, r = f / A_CPR, q = f % A_CPR;
-#pragma unroll
-            for (int v = 0; v < V; ++v) As[buf][q * V + v][r] = ra[c][v];
-        }
-#pragma unroll
-        for (int c = 0; c < B_CH; ++c) {
-            const int f = tid + NT * c, r = f / B_CPR, q = f % B_CPR;
-#pragma unroll
-            for (int v = 0; v < V; ++v) Bs[buf][r][q * V + v] = rb[c][v];
-        }
+        ra.store(As[buf], tid);
+        rb.store(Bs[buf], tid);
     };
 
     const int ty = tid / 16, tx = tid % 16;
@@ -174,13 +189,16 @@ hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = rows_16b_aligned(p.A, p.lda, sizeof(typename InFmt<T>::S)) &&
                      rows_16b_aligned(p.B, p.ldb, sizeof(typename InFmt<T>::S));
-    if (vec)
-        hipLaunchKernelGGL((lds_kernel<T, true>), dim3((unsigned)blocks), dim3(NT),
-                           0, s, p, tiles_n);
-    else
-        hipLaunchKernelGGL((lds_kernel<T, false>), dim3((unsigned)blocks), dim3(NT),
-                           0, s, p, tiles_n);
-    return hipGetLastError();
+    return with_layout(p, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (vec)
+            hipLaunchKernelGGL((lds_kernel<T, true, TA, TB>), dim3((unsigned)blocks),
+                               dim3(NT), 0, s, p, tiles_n);
+        else
+            hipLaunchKernelGGL((lds_kernel<T, false, TA, TB>), dim3((unsigned)blocks),
+                               dim3(NT), 0, s, p, tiles_n);
+        return hipGetLastError();
+    });
 }
 template hipError_t launch_lds<In::F32>(const GemmParams&, hipStream_t);
 template hipError_t launch_lds<In::BF16>(const GemmParams&, hipStream_t);

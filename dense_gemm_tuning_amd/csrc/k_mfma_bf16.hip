@@ -15,11 +15,13 @@
 // here).  The products of two bf16 values are exact in fp32.
 //
 // Operand layout.  The MFMA takes, per lane, 8 consecutive k of one row of
-// A and 8 consecutive k of one column of B.  A is row-major (k contiguous),
-// so its 16-byte chunks go to LDS unchanged.  B is row-major K x N (n
-// contiguous): each lane loads an 8 (k) x 8 (n) block as eight 16-byte row
-// pieces and transposes it in registers (byte permutes), then writes eight
-// 16-byte column pieces, so B sits in LDS as N x 64 with k contiguous.  The
+// A and 8 consecutive k of one column of B.  An operand stored with k
+// contiguous (A as M x K, or B stored transposed as N x K) has its 16-byte
+// chunks go to LDS unchanged.  One stored with m or n contiguous (B as
+// K x N, or A stored transposed as K x M): each lane loads an 8 (k) x 8
+// (mn) block as eight 16-byte row pieces and transposes it in registers
+// (byte permutes), then writes eight 16-byte column pieces, so both
+// operands sit in LDS as 256 x 64 with k contiguous.  The
 // pages warn that a fragment declared in the wrong major order still "looks
 // right" (dilfish.github.io 5.5); the tests check with permutation and
 // rank-1 inputs that rows and columns are not swapped.
@@ -85,7 +87,58 @@ __device__ __forceinline__ u32x4 as_u32x4(const uint4& v) {
     return u32x4{v.x, v.y, v.z, v.w};
 }
 
-template <In T, bool kVec, bool kGuard>
+// One operand's share of a 64-deep K slice, staged in LDS as 256 mn-rows of
+// 64 k (eight swizzled 16-byte chunks per row) whichever way it is stored.
+// kKC (stored rows run along k: A untransposed, B transposed): lane chunk i
+// is row (tid>>3) + 32*i, chunk tid&7, stored unchanged.  Otherwise (stored
+// rows run along m / n): the lane covers stored rows (k) 8*(tid>>5) .. +7
+// and columns (mn) 8*(tid&31) .. +7, transposed in registers on the store.
+template <bool kVec, bool kGuard, bool kKC>
+struct Op16 {
+    uint4 r[8];
+
+    // mn0: first m (or n) of the tile, mn_lim: M (or N).
+    __device__ void load(const uint16_t* X, int64_t ld, int mn0, int mn_lim, int k0, int K,
+                         int tid) {
+        if (kKC) {
+            const int q = tid & 7, row0 = tid >> 3;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = mn0 + row0 + 32 * i;
+                const bool ok = row < mn_lim;
+                r[i] = load8<kVec, kGuard>(X + (int64_t)(ok ? row : 0) * ld, k0 + 8 * q, K, ok);
+            }
+        } else {
+            const int c = tid & 31, g = tid >> 5;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int krow = k0 + 8 * g + i;
+                const bool ok = krow < K;
+                r[i] = load8<kVec, kGuard>(X + (int64_t)(ok ? krow : 0) * ld, mn0 + 8 * c,
+                                           mn_lim, ok);
+            }
+        }
+    }
+    __device__ void store(uint4* dst, int tid) const {
+        if (kKC) {
+            const int q = tid & 7, row0 = tid >> 3;
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const int row = row0 + 32 * i;
+                dst[row * CPR + (q ^ swz(row))] = r[i];
+            }
+        } else {
+            const int c = tid & 31, g = tid >> 5;
+#pragma unroll
+            for (int j = 0; j < 8; ++j) {
+                const int n = 8 * c + j;
+                dst[n * CPR + (g ^ swz(n))] = column8(r, j);
+            }
+        }
+    }
+};
+
+template <In T, bool kVec, bool kGuard, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n) {
     __shared__ uint4 As[2][BM * CPR];
     __shared__ uint4 Bt[2][BN * CPR];
@@ -99,40 +152,15 @@ __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n
     const uint16_t* A = static_cast<const uint16_t*>(p.A);
     const uint16_t* B = static_cast<const uint16_t*>(p.B);
 
-    // A: chunk i of this lane covers row (tid>>3) + 32*i, chunk q = tid&7.
-    // B: this lane covers rows 8*g .. 8*g+7 (g = tid>>5) of the slice and
-    //    columns 8*c .. 8*c+7 (c = tid&31).
-    const int aq = tid & 7, arow = tid >> 3;
-    const int bc = tid & 31, bg = tid >> 5;
-    uint4 ra[8], rb[8];
-
+    Op16<kVec, kGuard, !TA> ra;
+    Op16<kVec, kGuard, TB> rb;
     auto load_slice = [&](int k0) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = m0 + arow + 32 * i;
-            const bool ok = row < p.M;
-            ra[i] = load8<kVec, kGuard>(A + (int64_t)(ok ? row : 0) * p.lda,
-                                        k0 + 8 * aq, p.K, ok);
-        }
-#pragma unroll
-        for (int r = 0; r < 8; ++r) {
-            const int krow = k0 + 8 * bg + r;
-            const bool ok = krow < p.K;
-            rb[r] = load8<kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
-                                        n0 + 8 * bc, p.N, ok);
-        }
+        ra.load(A, p.lda, m0, p.M, k0, p.K, tid);
+        rb.load(B, p.ldb, n0, p.N, k0, p.K, tid);
     };
     auto store_slice = [&](int buf) {
-#pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = arow + 32 * i;
-            As[buf][row * CPR + (aq ^ swz(row))] = ra[i];
-        }
-#pragma unroll
-        for (int j = 0; j < 8; ++j) {
-            const int n = 8 * bc + j;
-            Bt[buf][n * CPR + (bg ^ swz(n))] = column8(rb, j);
-        }
+        ra.store(As[buf], tid);
+        rb.store(Bt[buf], tid);
     };
 
     floatx16 acc[4][4];
@@ -203,13 +231,19 @@ hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
     const bool vec = rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2);
     const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
     const dim3 grid((unsigned)blocks), block(NT);
-    if (full)
-        hipLaunchKernelGGL((mfma16_kernel<T, true, false>), grid, block, 0, s, p, tiles_n);
-    else if (vec)
-        hipLaunchKernelGGL((mfma16_kernel<T, true, true>), grid, block, 0, s, p, tiles_n);
-    else
-        hipLaunchKernelGGL((mfma16_kernel<T, false, true>), grid, block, 0, s, p, tiles_n);
-    return hipGetLastError();
+    return with_layout(p, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (full)
+            hipLaunchKernelGGL((mfma16_kernel<T, true, false, TA, TB>), grid, block, 0, s, p,
+                               tiles_n);
+        else if (vec)
+            hipLaunchKernelGGL((mfma16_kernel<T, true, true, TA, TB>), grid, block, 0, s, p,
+                               tiles_n);
+        else
+            hipLaunchKernelGGL((mfma16_kernel<T, false, true, TA, TB>), grid, block, 0, s, p,
+                               tiles_n);
+        return hipGetLastError();
+    });
 }
 template hipError_t launch_mfma16<In::BF16>(const GemmParams&, hipStream_t);
 template hipError_t launch_mfma16<In::F16>(const GemmParams&, hipStream_t);

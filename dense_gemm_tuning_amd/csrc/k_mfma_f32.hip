@@ -15,7 +15,10 @@
 // of C; K advances in slices of 16.  Global -> LDS: each slice of A
 // (128 x 16) and B (16 x 128) is read with coalesced 128-bit loads into
 // registers one slice ahead and written to the other half of a double LDS
-// buffer (dilfish.github.io 5.4), one barrier per slice.
+// buffer (dilfish.github.io 5.4), one barrier per slice.  Each operand is
+// staged by how it is stored: rows along k (A, or B stored N x K) go to LDS
+// as 128 rows of 16 k; rows along m / n (B, or A stored K x M) as 16 rows of
+// 128.  Transposed operands therefore cost no extra pass.
 //
 // Operand order inside a slice: the 32x32x2 instruction sums over two k
 // values, one per half-wavefront.  Half h of the wavefront feeds k = 8h + j
@@ -23,10 +26,10 @@
 // LDS reads; any fixed assignment of k to steps is valid because every
 // product lands in the same sum.
 //
-// LDS layout: A row-major with the row pitch padded to 20 floats (so 8 lanes
-// reading 16 bytes from 8 consecutive rows hit 8 distinct bank groups), B
-// row-major with the pitch padded to 132 floats (the two half-wavefronts
-// read rows 8 apart and land on opposite halves of the 64 banks).  Ragged
+// LDS layout: a k-contiguous operand has its row pitch padded to 20 floats
+// (so 8 lanes reading 16 bytes from 8 consecutive rows hit 8 distinct bank
+// groups), an m/n-contiguous one to 132 floats (the two half-wavefronts read
+// rows 8 apart and land on opposite halves of the 64 banks).  Ragged
 // shapes: zero-filled loads outside A and B and masked stores
 // (dilfish.github.io 5.7; elainafan.one masked tiled listing); the
 // specialisation for shapes that are multiples of the tile skips the checks.
@@ -37,8 +40,8 @@ namespace dgt {
 namespace {
 
 constexpr int BM = 128, BN = 128, BK = 16, NT = 256;
-constexpr int A_PITCH = BK + 4;    // floats
-constexpr int B_PITCH = BN + 4;    // floats
+constexpr int KC_PITCH = BK + 4;    // floats, rows along k
+constexpr int MN_PITCH = BN + 4;    // floats, rows along m or n
 
 // 16-byte chunk of 4 floats at [col, col+4) of one row, zero outside.
 template <bool kVec, bool kGuard>
@@ -53,10 +56,63 @@ __device__ __forceinline__ float4 load4(const float* rowp, int col, int limit,
     return make_float4(v[0], v[1], v[2], v[3]);
 }
 
-template <bool kVec, bool kGuard>
+// One operand's share of a K slice in LDS.  kKC (stored rows run along k:
+// A untransposed, B transposed): 128 mn-rows of 16 k, row pitch 20 floats,
+// and a lane reads its 8 k of one row as two 128-bit reads.  Otherwise
+// (stored rows run along m / n): 16 k-rows of 128, pitch 132, and a lane
+// reads one float per k.  Each lane moves two 16-byte chunks per slice.
+template <bool kVec, bool kGuard, bool kKC>
+struct OpF32 {
+    static constexpr int SIZE = kKC ? 128 * KC_PITCH : BK * MN_PITCH;  // floats per buffer
+    float4 r[2];
+
+    __device__ void load(const float* X, int64_t ld, int mn0, int mn_lim, int k0, int K,
+                         int tid) {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int f = tid + NT * c;
+            if (kKC) {  // chunk f: mn-row f/4, k 4*(f%4)
+                const int row = mn0 + (f >> 2), col = k0 + 4 * (f & 3);
+                const bool ok = row < mn_lim;
+                r[c] = load4<kVec, kGuard>(X + (int64_t)(ok ? row : 0) * ld, col, K, ok);
+            } else {    // chunk f: k-row f/32, mn 4*(f%32)
+                const int krow = k0 + (f >> 5), col = mn0 + 4 * (f & 31);
+                const bool ok = krow < K;
+                r[c] = load4<kVec, kGuard>(X + (int64_t)(ok ? krow : 0) * ld, col, mn_lim, ok);
+            }
+        }
+    }
+    __device__ void store(float* dst, int tid) const {
+#pragma unroll
+        for (int c = 0; c < 2; ++c) {
+            const int f = tid + NT * c;
+            float* d = kKC ? &dst[(f >> 2) * KC_PITCH + 4 * (f & 3)]
+                           : &dst[(f >> 5) * MN_PITCH + 4 * (f & 31)];
+            *reinterpret_cast<float4*>(d) = r[c];
+        }
+    }
+    // The operand of MFMA tile t (rows / columns w*64 + t*32 + l%32) for
+    // k = 8h + j: for kKC all eight j at once into v[t][0..7] ...
+    __device__ void read_all(const float* src, int w, int h, int r32, float (&v)[2][8]) const {
+#pragma unroll
+        for (int t = 0; t < 2; ++t) {
+            const float* a = &src[(w * 64 + t * 32 + r32) * KC_PITCH + 8 * h];
+            *reinterpret_cast<float4*>(&v[t][0]) = *reinterpret_cast<const float4*>(a);
+            *reinterpret_cast<float4*>(&v[t][4]) = *reinterpret_cast<const float4*>(a + 4);
+        }
+    }
+    // ... otherwise one j at a time.
+    __device__ float read_one(const float* src, int w, int h, int r32, int t, int j) const {
+        return src[(8 * h + j) * MN_PITCH + w * 64 + t * 32 + r32];
+    }
+};
+
+template <bool kVec, bool kGuard, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles_n) {
-    __shared__ float As[2][BM * A_PITCH];
-    __shared__ float Bs[2][BK * B_PITCH];
+    using OpA = OpF32<kVec, kGuard, !TA>;
+    using OpB = OpF32<kVec, kGuard, TB>;
+    __shared__ float As[2][OpA::SIZE];
+    __shared__ float Bs[2][OpB::SIZE];
 
     const int tid = threadIdx.x;
     const int lane = tid & 63, wave = tid >> 6;
@@ -67,32 +123,15 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
     const float* A = static_cast<const float*>(p.A);
     const float* B = static_cast<const float*>(p.B);
 
-    // Per-lane global chunk coordinates (2 chunks of A, 2 of B per slice).
-    // A chunk f: row f/4, cols 4*(f%4); B chunk f: row f/32, cols 4*(f%32).
-    float4 ra[2], rb[2];
+    OpA ra;
+    OpB rb;
     auto load_slice = [&](int k0) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int f = tid + NT * c;
-            const int row = m0 + (f >> 2), col = k0 + 4 * (f & 3);
-            const bool ok = row < p.M;
-            ra[c] = load4<kVec, kGuard>(A + (int64_t)(ok ? row : 0) * p.lda, col, p.K, ok);
-        }
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int f = tid + NT * c;
-            const int krow = k0 + (f >> 5), col = n0 + 4 * (f & 31);
-            const bool ok = krow < p.K;
-            rb[c] = load4<kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb, col, p.N, ok);
-        }
+        ra.load(A, p.lda, m0, p.M, k0, p.K, tid);
+        rb.load(B, p.ldb, n0, p.N, k0, p.K, tid);
     };
     auto store_slice = [&](int buf) {
-#pragma unroll
-        for (int c = 0; c < 2; ++c) {
-            const int f = tid + NT * c;
-            *reinterpret_cast<float4*>(&As[buf][(f >> 2) * A_PITCH + 4 * (f & 3)]) = ra[c];
-            *reinterpret_cast<float4*>(&Bs[buf][(f >> 5) * B_PITCH + 4 * (f & 31)]) = rb[c];
-        }
+        ra.store(As[buf], tid);
+        rb.store(Bs[buf], tid);
     };
 
     floatx16 acc[2][2];
@@ -111,26 +150,25 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
         const int buf = t & 1;
         if (t + 1 < nk) load_slice((t + 1) * BK);
 
-        // A operands: rows wm*64 + ti*32 + r32, k = 8h .. 8h+7.
-        float a[2][8];
-#pragma unroll
-        for (int ti = 0; ti < 2; ++ti) {
-            const float* ap = &As[buf][(wm * 64 + ti * 32 + r32) * A_PITCH + 8 * h];
-            *reinterpret_cast<float4*>(&a[ti][0]) = *reinterpret_cast<const float4*>(ap);
-            *reinterpret_cast<float4*>(&a[ti][4]) = *reinterpret_cast<const float4*>(ap + 4);
-        }
+        // Operands: A rows wm*64 + ti*32 + r32, B columns wn*64 + tj*32 + r32,
+        // k = 8h .. 8h+7 of the slice.
+        float a[2][8], b[2][8];
+        if constexpr (!TA) ra.read_all(As[buf], wm, h, r32, a);
+        if constexpr (TB) rb.read_all(Bs[buf], wn, h, r32, b);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float b[2];
+            float aj[2], bj[2];
 #pragma unroll
-            for (int tj = 0; tj < 2; ++tj)
-                b[tj] = Bs[buf][(8 * h + j) * B_PITCH + wn * 64 + tj * 32 + r32];
+            for (int x = 0; x < 2; ++x) {
+                aj[x] = TA ? ra.read_one(As[buf], wm, h, r32, x, j) : a[x][j];
+                bj[x] = TB ? b[x][j] : rb.read_one(Bs[buf], wn, h, r32, x, j);
+            }
 #pragma unroll
             for (int ti = 0; ti < 2; ++ti)
 #pragma unroll
                 for (int tj = 0; tj < 2; ++tj)
                     acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
-                        a[ti][j], b[tj], acc[ti][tj], 0, 0, 0);
+                        aj[ti], bj[tj], acc[ti][tj], 0, 0, 0);
         }
         if (t + 1 < nk) store_slice(buf ^ 1);
         __syncthreads();
@@ -162,13 +200,19 @@ hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
     const bool vec = rows_16b_aligned(p.A, p.lda, 4) && rows_16b_aligned(p.B, p.ldb, 4);
     const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
     const dim3 grid((unsigned)blocks), block(NT);
-    if (full)
-        hipLaunchKernelGGL((mfma_f32_kernel<true, false>), grid, block, 0, s, p, tiles_n);
-    else if (vec)
-        hipLaunchKernelGGL((mfma_f32_kernel<true, true>), grid, block, 0, s, p, tiles_n);
-    else
-        hipLaunchKernelGGL((mfma_f32_kernel<false, true>), grid, block, 0, s, p, tiles_n);
-    return hipGetLastError();
+    return with_layout(p, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (full)
+            hipLaunchKernelGGL((mfma_f32_kernel<true, false, TA, TB>), grid, block, 0, s, p,
+                               tiles_n);
+        else if (vec)
+            hipLaunchKernelGGL((mfma_f32_kernel<true, true, TA, TB>), grid, block, 0, s, p,
+                               tiles_n);
+        else
+            hipLaunchKernelGGL((mfma_f32_kernel<false, true, TA, TB>), grid, block, 0, s, p,
+                               tiles_n);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace dgt

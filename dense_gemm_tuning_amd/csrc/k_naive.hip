@@ -11,7 +11,9 @@
 // shapes are handled by the per-lane bounds check (chongfengling.github.io
 // section 2.1; elainafan.one, paragraph after the naive launch).  Arithmetic
 // intensity is 0.25 FLOP/B from the per-lane view (dilfish.github.io 5.2);
-// caches recover part of that, the layout does not.
+// caches recover part of that, the layout does not.  Transposed operands
+// only change the stride along k; with B stored N x K the wavefront's B
+// reads are strided (this rung does not restage them).
 #include "gemm_common.hpp"
 
 namespace dgt {
@@ -30,11 +32,14 @@ __global__ __launch_bounds__(kNaiveX * kNaiveY) void naive_kernel(GemmParams p,
     const int col = bn * kNaiveX + threadIdx.x;
     const int row = bm * kNaiveY + threadIdx.y;
     if (row >= p.M || col >= p.N) return;
-    const S* a = static_cast<const S*>(p.A) + (int64_t)row * p.lda;
-    const S* b = static_cast<const S*>(p.B) + col;
+    // op(A)(row, k) and op(B)(k, col) walk k with a stride of 1 or ld,
+    // depending on how each operand is stored.
+    const S* a = static_cast<const S*>(p.A) + (p.ta ? (int64_t)row : (int64_t)row * p.lda);
+    const S* b = static_cast<const S*>(p.B) + (p.tb ? (int64_t)col * p.ldb : (int64_t)col);
+    const int64_t sa = p.ta ? p.lda : 1, sb = p.tb ? 1 : p.ldb;
     float acc = 0.0f;
     for (int k = 0; k < p.K; ++k)
-        acc = fmaf(load_in<T>(a + k), load_in<T>(b + (int64_t)k * p.ldb), acc);
+        acc = fmaf(load_in<T>(a + k * sa), load_in<T>(b + k * sb), acc);
     float* c = p.C + (int64_t)row * p.ldc + col;
     *c = epilogue(acc, p.alpha, p.beta, c);
 }

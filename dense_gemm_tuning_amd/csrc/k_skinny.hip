@@ -28,6 +28,12 @@
 //    is k = k0 + 8g + t, so a lane's A operands are two 16-byte reads; one
 //    32-deep K step covers 64 columns with 32 MFMAs.
 //
+// Transposed operands: with B stored N x K (a linear layer's [out, in]
+// weight) a lane's 16-byte load already holds 8 (or 4) consecutive k of one
+// column, so no register transpose is needed (16-bit inputs: a kernel of
+// its own, below); A stored K x M is read element by element (it is tiny
+// and cached).
+//
 // Work split: a workgroup of 8 wavefronts owns one column strip (128 bf16
 // or 64 fp32 columns) over the whole of K; wavefront w takes the w-th
 // eighth of the K steps, and the eight partial tiles are summed in LDS in a
@@ -106,7 +112,28 @@ __device__ __forceinline__ void reduce_store(float (*red)[16][COLS + 4],
 
 constexpr int BF_COLS = 128;
 
-template <In T, bool kVec, bool kGuard>
+// 8 consecutive k (from ka) of row i of op(A) as one MFMA operand.  arow is
+// row i of A (stored M x K), or column i of A stored K x M, read element by
+// element with stride lda (A is tiny and cached).
+template <bool kVec, bool kGuard, bool TA>
+__device__ __forceinline__ u32x4 load_a16(const uint16_t* arow, int ka, const GemmParams& p,
+                                          bool a_ok) {
+    if constexpr (TA) {
+        u32x4 a;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+            const int k0 = ka + 2 * e, k1 = k0 + 1;
+            const uint32_t lo = (!kGuard || k0 < p.K) ? arow[(int64_t)k0 * p.lda] : 0u;
+            const uint32_t hi = (!kGuard || k1 < p.K) ? arow[(int64_t)k1 * p.lda] : 0u;
+            a[e] = lo | (hi << 16);
+        }
+        return a;
+    } else {
+        return load16_cached<uint16_t, kVec, kGuard>(arow, ka, p.K, a_ok);
+    }
+}
+
+template <In T, bool kVec, bool kGuard, bool TA>
 __global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
     __shared__ float red[NW][16][BF_COLS + 4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -116,7 +143,9 @@ __global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
     const uint16_t* A = static_cast<const uint16_t*>(p.A);
     const uint16_t* B = static_cast<const uint16_t*>(p.B);
     const bool a_ok = i < p.M;
-    const uint16_t* arow = A + (int64_t)(a_ok ? i : 0) * p.lda;
+    // Row i of op(A): a stored row (k contiguous), or column i of A stored
+    // K x M (stride lda).  Rows past M use row 0 and are never stored.
+    const uint16_t* arow = A + (TA ? (int64_t)(a_ok ? i : 0) : (int64_t)(a_ok ? i : 0) * p.lda);
 
     const int nsteps = (p.K + KSTEP - 1) / KSTEP;
     const int per = (nsteps + NW - 1) / NW;
@@ -127,6 +156,8 @@ __global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // dst[r] = stored row k = kb + r, columns col .. col+7; the MFMA operand
+    // is a column of that block.
     auto load_b = [&](int step, u32x4 (&dst)[8]) {
         const int kb = step * KSTEP + 8 * g;
 #pragma unroll
@@ -138,8 +169,7 @@ __global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
         }
     };
     auto compute = [&](int step, const u32x4 (&rb)[8]) {
-        const u32x4 a = load16_cached<uint16_t, kVec, kGuard>(arow, step * KSTEP + 8 * g,
-                                                              p.K, a_ok);
+        const u32x4 a = load_a16<kVec, kGuard, TA>(arow, step * KSTEP + 8 * g, p, a_ok);
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = mfma16x16x32<T>(a, column8(rb, c), acc[c]);
     };
@@ -164,11 +194,136 @@ __global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
     reduce_store<BF_COLS>(red, p, n0);
 }
 
+// ------------------------------------------- 16-bit, B stored N x K
+
+// B stored N x K (a linear layer's [out, in] weight): every column of op(B)
+// is a stored row with k contiguous.  The MFMA lane layout would let one
+// load instruction fetch only 64 B from each of 16 rows, which halves the
+// rate the memory side delivers; instead each instruction fetches 256 B from
+// each of 4 rows (16 lanes per row, as the K x N layout does), the wave
+// parks the piece in a private LDS region, and reads the MFMA operands back
+// from there.  A group is 32 columns (stored rows) x 128 k = 8 KiB, eight
+// load instructions; a 128-deep step is four groups (the workgroup's 128
+// columns).  LDS rows are 256 B with chunk c of row r at c ^ (r & 15), so
+// both the writes (16 lanes of one row) and the operand reads (16 rows, one
+// chunk) touch 16 distinct 16-byte bank groups.
+constexpr int BT_KSTEP = 128;
+constexpr int BT_GROUP_ROWS = 32;
+constexpr int BT_STAGE = BT_GROUP_ROWS * 256;  // bytes per wave
+
+template <In T, bool kVec, bool kGuard, bool TA>
+__global__ __launch_bounds__(NT, 1) void skinny16_bt_kernel(GemmParams p) {
+    __shared__ float red[NW][16][BF_COLS + 4];
+    __shared__ __attribute__((aligned(16))) uint8_t stage_all[NW][BT_STAGE];
+    const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
+    const int g = lane >> 4, i = lane & 15;
+    const int n0 = blockIdx.x * BF_COLS;
+    const uint16_t* A = static_cast<const uint16_t*>(p.A);
+    const uint16_t* B = static_cast<const uint16_t*>(p.B);
+    const bool a_ok = i < p.M;
+    const uint16_t* arow = A + (TA ? (int64_t)(a_ok ? i : 0) : (int64_t)(a_ok ? i : 0) * p.lda);
+    uint8_t* stage = stage_all[wave];
+
+    const int nsteps = (p.K + BT_KSTEP - 1) / BT_KSTEP;
+    const int per = (nsteps + NW - 1) / NW;
+    const int s0 = wave * per;
+    const int s1 = min(s0 + per, nsteps);
+
+    floatx4 acc[8];
+#pragma unroll
+    for (int c = 0; c < 8; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
+
+    // Group cp of step s: instruction j fetches local rows 4j .. 4j+3; lane
+    // l takes local row 4j + l/16, chunk l%16 (k = 128s + 8*(l%16)).
+    auto load_group = [&](int s, int cp, u32x4 (&r)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int row = n0 + BT_GROUP_ROWS * cp + 4 * j + g;
+            const bool ok = row < p.N;
+            r[j] = load16<uint16_t, kVec, kGuard>(B + (int64_t)(ok ? row : 0) * p.ldb,
+                                                  s * BT_KSTEP + 8 * i, p.K, ok);
+        }
+    };
+    auto park = [&](const u32x4 (&r)[8]) {
+#pragma unroll
+        for (int j = 0; j < 8; ++j) {
+            const int lr = 4 * j + g;
+            *reinterpret_cast<u32x4*>(stage + lr * 256 + ((i ^ (lr & 15)) << 4)) = r[j];
+        }
+    };
+    // MFMA block b of the group (local rows 16b + i), quarter u (chunk 4u + g).
+    auto compute = [&](auto cpc, const u32x4 (&a)[4]) {
+        constexpr int cp = decltype(cpc)::value;
+#pragma unroll
+        for (int b = 0; b < 2; ++b)
+#pragma unroll
+            for (int u = 0; u < 4; ++u) {
+                const u32x4 bop = *reinterpret_cast<const u32x4*>(
+                    stage + (16 * b + i) * 256 + (((4 * u + g) ^ i) << 4));
+                acc[2 * cp + b] = mfma16x16x32<T>(a[u], bop, acc[2 * cp + b]);
+            }
+    };
+    auto load_a = [&](int s, u32x4 (&a)[4]) {
+#pragma unroll
+        for (int u = 0; u < 4; ++u)
+            a[u] = load_a16<kVec, kGuard, TA>(arow, s * BT_KSTEP + 32 * u + 8 * g, p, a_ok);
+    };
+
+    // Two groups in flight.  The loop body has no branch: on the last
+    // iteration the prefetch re-reads the current step (never used), so the
+    // loads stay in flight across the back edge.  LDS operations of one wave
+    // complete in order, so parking a group after the previous group's
+    // operand reads needs no wait.
+    u32x4 r0[8], r1[8], a0[4], a1[4];
+    if (s0 < s1) {
+        load_a(s0, a0);
+        load_group(s0, 0, r0);
+    }
+    // Each phase issues the next group's loads, then parks and consumes the
+    // group loaded one phase earlier; the scheduling barriers keep the
+    // compiler from gathering several phases' loads into one burst or from
+    // sinking them below the waits of the park.
+    for (int s = s0; s < s1; ++s) {
+        const int sn = s + 1 < s1 ? s + 1 : s;
+        load_group(s, 1, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        park(r0);
+        compute(std::integral_constant<int, 0>{}, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(s, 2, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        park(r1);
+        compute(std::integral_constant<int, 1>{}, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_group(s, 3, r1);
+        __builtin_amdgcn_sched_barrier(0);
+        park(r0);
+        compute(std::integral_constant<int, 2>{}, a0);
+        __builtin_amdgcn_sched_barrier(0);
+        load_a(sn, a1);
+        load_group(sn, 0, r0);
+        __builtin_amdgcn_sched_barrier(0);
+        park(r1);
+        compute(std::integral_constant<int, 3>{}, a0);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int u = 0; u < 4; ++u) a0[u] = a1[u];
+    }
+
+    // 16x16 accumulator layout: register r of lane l is row 4*(l/16) + r,
+    // column l%16; accumulator c holds columns n0 + 16c .. +15.
+#pragma unroll
+    for (int c = 0; c < 8; ++c)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) red[wave][4 * g + r][16 * c + i] = acc[c][r];
+    reduce_store<BF_COLS>(red, p, n0);
+}
+
 // ---------------------------------------------------------------- fp32
 
 constexpr int F_COLS = 64;
 
-template <bool kVec, bool kGuard>
+template <bool kVec, bool kGuard, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 1) void skinny_f32_kernel(GemmParams p) {
     __shared__ float red[NW][16][F_COLS + 4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -178,7 +333,7 @@ __global__ __launch_bounds__(NT, 1) void skinny_f32_kernel(GemmParams p) {
     const float* A = static_cast<const float*>(p.A);
     const float* B = static_cast<const float*>(p.B);
     const bool a_ok = i < p.M;
-    const float* arow = A + (int64_t)(a_ok ? i : 0) * p.lda;
+    const float* arow = A + (TA ? (int64_t)(a_ok ? i : 0) : (int64_t)(a_ok ? i : 0) * p.lda);
 
     const int nsteps = (p.K + KSTEP - 1) / KSTEP;
     const int per = (nsteps + NW - 1) / NW;
@@ -189,27 +344,49 @@ __global__ __launch_bounds__(NT, 1) void skinny_f32_kernel(GemmParams p) {
 #pragma unroll
     for (int c = 0; c < 4; ++c) acc[c] = floatx4{0.f, 0.f, 0.f, 0.f};
 
+    // B as K x N: dst[t] = stored row k = kb + t, columns col .. col+3.  B
+    // stored N x K: dst[2c + x] = stored row n = col + c, k = kb + 4x .. +3.
     auto load_b = [&](int step, u32x4 (&dst)[8]) {
         const int kb = step * KSTEP + 8 * g;
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const int krow = kb + t;
-            const bool ok = krow < p.K;
-            dst[t] = load16<float, kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
-                                                 col, p.N, ok);
+            if constexpr (TB) {
+                const int n = col + (t >> 1);
+                const bool ok = n < p.N;
+                dst[t] = load16<float, kVec, kGuard>(B + (int64_t)(ok ? n : 0) * p.ldb,
+                                                     kb + 4 * (t & 1), p.K, ok);
+            } else {
+                const int krow = kb + t;
+                const bool ok = krow < p.K;
+                dst[t] = load16<float, kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
+                                                     col, p.N, ok);
+            }
         }
     };
     auto compute = [&](int step, const u32x4 (&rb)[8]) {
         const int ka = step * KSTEP + 8 * g;
-        const u32x4 a0 = load16_cached<float, kVec, kGuard>(arow, ka, p.K, a_ok);
-        const u32x4 a1 = load16_cached<float, kVec, kGuard>(arow, ka + 4, p.K, a_ok);
+        float av[8];
+        if constexpr (TA) {
+#pragma unroll
+            for (int t = 0; t < 8; ++t)
+                av[t] = (!kGuard || ka + t < p.K) ? arow[(int64_t)(ka + t) * p.lda] : 0.0f;
+        } else {
+            const u32x4 a0 = load16_cached<float, kVec, kGuard>(arow, ka, p.K, a_ok);
+            const u32x4 a1 = load16_cached<float, kVec, kGuard>(arow, ka + 4, p.K, a_ok);
+#pragma unroll
+            for (int t = 0; t < 4; ++t) {
+                av[t] = __uint_as_float(a0[t]);
+                av[t + 4] = __uint_as_float(a1[t]);
+            }
+        }
 #pragma unroll
         for (int t = 0; t < 8; ++t) {
-            const float av = __uint_as_float(t < 4 ? a0[t] : a1[t - 4]);
 #pragma unroll
-            for (int c = 0; c < 4; ++c)
-                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(
-                    av, __uint_as_float(rb[t][c]), acc[c], 0, 0, 0);
+            for (int c = 0; c < 4; ++c) {
+                const uint32_t bv = TB ? rb[2 * c + (t >> 2)][t & 3] : rb[t][c];
+                acc[c] = __builtin_amdgcn_mfma_f32_16x16x4f32(av[t], __uint_as_float(bv),
+                                                              acc[c], 0, 0, 0);
+            }
         }
     };
 
@@ -238,14 +415,28 @@ template <In T>
 hipError_t launch_skinny16(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + BF_COLS - 1) / BF_COLS;
     const bool vec = rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2);
-    const bool full = vec && p.N % BF_COLS == 0 && p.K % KSTEP == 0;
-    if (full)
-        hipLaunchKernelGGL((skinny16_kernel<T, true, false>), dim3(blocks), dim3(NT), 0, s, p);
-    else if (vec)
-        hipLaunchKernelGGL((skinny16_kernel<T, true, true>), dim3(blocks), dim3(NT), 0, s, p);
-    else
-        hipLaunchKernelGGL((skinny16_kernel<T, false, true>), dim3(blocks), dim3(NT), 0, s, p);
-    return hipGetLastError();
+    const int kstep = p.tb ? BT_KSTEP : KSTEP;
+    const bool full = vec && p.N % BF_COLS == 0 && p.K % kstep == 0;
+    return with_layout(p, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        const dim3 grid(blocks), block(NT);
+        if constexpr (TB) {
+            if (full)
+                hipLaunchKernelGGL((skinny16_bt_kernel<T, true, false, TA>), grid, block, 0, s, p);
+            else if (vec)
+                hipLaunchKernelGGL((skinny16_bt_kernel<T, true, true, TA>), grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny16_bt_kernel<T, false, true, TA>), grid, block, 0, s, p);
+        } else {
+            if (full)
+                hipLaunchKernelGGL((skinny16_kernel<T, true, false, TA>), grid, block, 0, s, p);
+            else if (vec)
+                hipLaunchKernelGGL((skinny16_kernel<T, true, true, TA>), grid, block, 0, s, p);
+            else
+                hipLaunchKernelGGL((skinny16_kernel<T, false, true, TA>), grid, block, 0, s, p);
+        }
+        return hipGetLastError();
+    });
 }
 template hipError_t launch_skinny16<In::BF16>(const GemmParams&, hipStream_t);
 template hipError_t launch_skinny16<In::F16>(const GemmParams&, hipStream_t);
@@ -254,13 +445,19 @@ hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + F_COLS - 1) / F_COLS;
     const bool vec = rows_16b_aligned(p.A, p.lda, 4) && rows_16b_aligned(p.B, p.ldb, 4);
     const bool full = vec && p.N % F_COLS == 0 && p.K % KSTEP == 0;
-    if (full)
-        hipLaunchKernelGGL((skinny_f32_kernel<true, false>), dim3(blocks), dim3(NT), 0, s, p);
-    else if (vec)
-        hipLaunchKernelGGL((skinny_f32_kernel<true, true>), dim3(blocks), dim3(NT), 0, s, p);
-    else
-        hipLaunchKernelGGL((skinny_f32_kernel<false, true>), dim3(blocks), dim3(NT), 0, s, p);
-    return hipGetLastError();
+    return with_layout(p, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (full)
+            hipLaunchKernelGGL((skinny_f32_kernel<true, false, TA, TB>), dim3(blocks), dim3(NT),
+                               0, s, p);
+        else if (vec)
+            hipLaunchKernelGGL((skinny_f32_kernel<true, true, TA, TB>), dim3(blocks), dim3(NT),
+                               0, s, p);
+        else
+            hipLaunchKernelGGL((skinny_f32_kernel<false, true, TA, TB>), dim3(blocks), dim3(NT),
+                               0, s, p);
+        return hipGetLastError();
+    });
 }
 
 }  // namespace dgt

@@ -29,12 +29,13 @@ raw ``uint16`` bits.  The workloads never produce NaN or infinity.
 
 Workloads: the pages tune a single operation, ``C = alpha*A*B + beta*C`` with
 row-major A (M x K), B (K x N), C (M x N) (elainafan.one, "稠密矩阵乘法" and
-"行主序").  ``WORKLOADS`` lists the five shapes the library is checked and
+"行主序").  ``WORKLOADS`` lists the shapes the library is checked and
 measured on: a small square case, a ragged one that exercises edge masking
-and the beta path, the FP32 4096^3 and BF16 8192^3 square cases the pages'
-tuning ladders target (qwbw.cn, section 三 table at 4096^3), and a skinny
+and the beta path, the FP32 4096^3 and BF16/FP16 8192^3 square cases the
+pages' tuning ladders target (qwbw.cn, section 三 table at 4096^3), a skinny
 decode-style case whose time is weight loading (dilfish.github.io, section
-5.1 table, GEMV row).
+5.1 table, GEMV row), and the BF16 square and skinny cases again with the
+operands stored the way a linear layer keeps them.
 """
 
 from __future__ import annotations
@@ -150,6 +151,18 @@ class Workload:
     dist: str           # "uniform", "int" or "normal"
     sigma: float = 1.0
     seed_base: int = 0
+    trans_a: bool = False   # A stored K x M (op(A) = A^T)
+    trans_b: bool = False   # B stored N x K (op(B) = B^T)
+
+    @property
+    def a_shape(self):
+        """Stored shape of A."""
+        return (self.K, self.M) if self.trans_a else (self.M, self.K)
+
+    @property
+    def b_shape(self):
+        """Stored shape of B."""
+        return (self.N, self.K) if self.trans_b else (self.K, self.N)
 
     @property
     def flops(self) -> int:
@@ -181,14 +194,25 @@ WORKLOADS = {
     "bf16_skinny_8x28672x8192": Workload("bf16_skinny_8x28672x8192", "bf16",
                                          8, 28672, 8192, 1.0, 0.0, "normal",
                                          sigma=0.02, seed_base=5000),
+    # The linear-layer storage (input [batch, in], weight [out, in]): the
+    # forward product X W^T has B stored N x K, the weight gradient G^T X has
+    # A stored K x M (elainafan.one "全连接层").
+    "bf16_8192_nt": Workload("bf16_8192_nt", "bf16", 8192, 8192, 8192, 1.0, 0.0,
+                             "normal", seed_base=7000, trans_b=True),
+    "bf16_8192_tn": Workload("bf16_8192_tn", "bf16", 8192, 8192, 8192, 1.0, 0.0,
+                             "normal", seed_base=8000, trans_a=True),
+    "bf16_skinny_8x28672x8192_nt": Workload("bf16_skinny_8x28672x8192_nt", "bf16",
+                                            8, 28672, 8192, 1.0, 0.0, "normal",
+                                            sigma=0.02, seed_base=9000, trans_b=True),
 }
 
 
 def make_inputs(w: Workload):
-    """Return ``(A, B, C0)`` for workload ``w`` (C0 is None when beta == 0)."""
+    """Return ``(A, B, C0)`` for workload ``w`` (C0 is None when beta == 0).
+    A and B have their stored shapes (``w.a_shape``, ``w.b_shape``)."""
     sa, sb, sc = w.seeds()
-    A = draw(sa, w.M, w.K, w.dist, w.sigma, w.dtype)
-    B = draw(sb, w.K, w.N, w.dist, w.sigma, w.dtype)
+    A = draw(sa, *w.a_shape, w.dist, w.sigma, w.dtype)
+    B = draw(sb, *w.b_shape, w.dist, w.sigma, w.dtype)
     C0 = None
     if w.beta != 0.0:
         C0 = draw(sc, w.M, w.N, w.dist, w.sigma, "f32")

@@ -3,18 +3,26 @@
  *
  * Operation (every entry point): the BLAS GEMM form
  *
- *     C <- alpha * A * B + beta * C
+ *     C <- alpha * op(A) * op(B) + beta * C
  *
- * with C(i,j) = sum_k A(i,k) * B(k,j) (element formula: dilfish.github.io
- * section 5.2; chongfengling.github.io section 1; elainafan.one
- * "稠密矩阵乘法", where alpha and beta let one call both scale and
- * accumulate).
+ * with C(i,j) = sum_k op(A)(i,k) * op(B)(k,j) (element formula:
+ * dilfish.github.io section 5.2; chongfengling.github.io section 1;
+ * elainafan.one "稠密矩阵乘法", where alpha and beta let one call both scale
+ * and accumulate).  op(X) is X, or X transposed when gemm_ex is asked for it
+ * (every other entry point: no transposes).
  *
  * Layout: row-major with leading dimensions, the column index contiguous
  * (chongfengling.github.io section 2.2; elainafan.one "行主序"):
- *     A(i,k) = A[i*lda + k]   A is M x K,  lda >= max(1, K)
- *     B(k,j) = B[k*ldb + j]   B is K x N,  ldb >= max(1, N)
- *     C(i,j) = C[i*ldc + j]   C is M x N,  ldc >= max(1, N)
+ *     op(A)(i,k) = A[i*lda + k]  trans_a = 0: A stored M x K, lda >= max(1, K)
+ *     op(A)(i,k) = A[k*lda + i]  trans_a = 1: A stored K x M, lda >= max(1, M)
+ *     op(B)(k,j) = B[k*ldb + j]  trans_b = 0: B stored K x N, ldb >= max(1, N)
+ *     op(B)(k,j) = B[j*ldb + k]  trans_b = 1: B stored N x K, ldb >= max(1, K)
+ *     C(i,j)     = C[i*ldc + j]  C is M x N,                  ldc >= max(1, N)
+ * The transposed forms are the operands of a linear layer stored as in
+ * elainafan.one "全连接层" (input X [batch, in], weight W [out, in], output
+ * gradient G [batch, out]): the forward pass X*W^T is trans_b = 1, the
+ * weight gradient G^T*X is trans_a = 1, the input gradient G*W needs
+ * neither.  A column-major caller passes its storage with the flags set.
  *
  * Precision: gemm_f32 takes fp32 A and B; gemm_bf16 takes A and B as raw
  * bf16 bit patterns (uint16_t, the upper half of an fp32 value: 8-bit
@@ -44,9 +52,10 @@
  *
  * Errors: every entry point returns GEMM_OK (0) or a negative status; on an
  * argument error nothing is queued.  The library never aborts or prints.
- * Argument checks run on the host in this order: dimensions, leading
- * dimensions, quick return for an empty C, null pointers, overlap of C with
- * A or B, variant support.  gemm_status_string() names a status.
+ * Argument checks run on the host in this order: dtype and transpose flags,
+ * dimensions, leading dimensions, variant id, quick return for an empty C,
+ * null pointers, overlap of C with A or B, variant support for the shape.
+ * gemm_status_string() names a status.
  */
 #ifndef DGT_GEMM_H
 #define DGT_GEMM_H
@@ -57,9 +66,9 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 2
+#define DGT_GEMM_ABI_VERSION 3
 
-/* Input formats (gemm_select_variant's dtype). */
+/* Input formats (the dtype argument of gemm_ex and gemm_select_variant). */
 enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };
 
 enum gemm_status {
@@ -72,7 +81,9 @@ enum gemm_status {
     GEMM_ERR_OVERLAP = -4,      /* the byte range of C overlaps A's or B's   */
     GEMM_ERR_VARIANT = -5,      /* unknown variant, or one that does not
                                    support this shape / size                 */
-    GEMM_ERR_LAUNCH = -6        /* the HIP runtime rejected a kernel launch  */
+    GEMM_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch  */
+    GEMM_ERR_ARG = -7           /* dtype not a gemm_dtype, or a transpose
+                                   flag other than 0 or 1                    */
 };
 
 /* Kernel ladder (for measurement and tests; GEMM_VARIANT_AUTO is what
@@ -129,11 +140,22 @@ int gemm_f16_variant(int variant, int M, int N, int K, float alpha,
                      const uint16_t* A, int lda, const uint16_t* B, int ldb,
                      float beta, float* C, int ldc, void* stream);
 
-/* The rung GEMM_VARIANT_AUTO picks for this call (dtype: enum gemm_dtype),
- * or a negative status if the arguments are invalid.  Host only: touches no
- * device and queues nothing. */
-int gemm_select_variant(int dtype, int M, int N, int K, int lda, int ldb,
-                        int ldc);
+/* General form: C <- alpha*op(A)*op(B) + beta*C with the input format
+ * `dtype` (enum gemm_dtype; A and B point to float for GEMM_DTYPE_F32, to
+ * raw uint16_t bits otherwise), transpose flags trans_a / trans_b (0 or 1,
+ * storage as in the layout table above) and a ladder rung `variant` (enum
+ * gemm_variant; every rung takes every layout).  The untransposed call is
+ * the same operation as gemm_f32 / gemm_bf16 / gemm_f16 (_variant), with the
+ * same kernels. */
+int gemm_ex(int dtype, int trans_a, int trans_b, int variant, int M, int N,
+            int K, float alpha, const void* A, int lda, const void* B, int ldb,
+            float beta, float* C, int ldc, void* stream);
+
+/* The rung GEMM_VARIANT_AUTO picks for this call (dtype: enum gemm_dtype;
+ * trans_a, trans_b as for gemm_ex), or a negative status if the arguments
+ * are invalid.  Host only: touches no device and queues nothing. */
+int gemm_select_variant(int dtype, int trans_a, int trans_b, int M, int N,
+                        int K, int lda, int ldb, int ldc);
 
 /* Static string naming a status code (never NULL). */
 const char* gemm_status_string(int status);

@@ -9,7 +9,8 @@ The arithmetic lives in ``gemm_oracle.c`` (built with gcc into
 the oracle computes and which passage each part follows is stated at the top
 of the C file.  The tests pin it against identity and permutation matrices,
 rank-1 closed forms, small-integer matrices (exact), the alpha/beta readings,
-exact rational arithmetic on sampled elements, and numpy's float64 matmul.
+exact rational arithmetic on sampled elements, numpy's float64 matmul, and
+the linear-layer products with transposed operands.
 """
 
 from __future__ import annotations
@@ -64,6 +65,8 @@ class Oracle:
         lib.oracle_widen_bf16.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
         lib.oracle_widen_f16.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
         lib.oracle_round_f32.argtypes = [_d, _i64, ctypes.c_void_p]
+        lib.oracle_op.restype = None
+        lib.oracle_op.argtypes = [_d, _i64, _i64, _i64, ctypes.c_int, _d]
         lib.oracle_num_threads.restype = ctypes.c_int
         lib.oracle_set_num_threads.argtypes = [ctypes.c_int]
         self.lib = lib
@@ -112,11 +115,22 @@ class Oracle:
            float(beta), cptr, max(N, 1), _ptr(R), max(N, 1))
         return R
 
+    def op(self, X64: np.ndarray, trans: bool) -> np.ndarray:
+        """op(X) of a stored fp64 matrix: X, or its transpose when trans."""
+        X64 = np.ascontiguousarray(X64, dtype=np.float64)
+        srows, scols = X64.shape
+        rows, cols = (scols, srows) if trans else (srows, scols)
+        out = np.empty((rows, cols), dtype=np.float64)
+        self.lib.oracle_op(_ptr(X64), rows, cols, max(scols, 1), int(bool(trans)), _ptr(out))
+        return out
+
     def gemm(self, A, B, C0, alpha: float, beta: float, dtype: str,
-             order: str = "ikj") -> np.ndarray:
-        """Oracle result in fp64 for raw inputs (fp32 arrays, bf16 or f16 bits)."""
-        A64 = self.widen(A, dtype)
-        B64 = self.widen(B, dtype)
+             order: str = "ikj", trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
+        """Oracle result in fp64 for raw inputs (fp32 arrays, bf16 or f16 bits).
+
+        A and B are given as stored: K x M when trans_a, N x K when trans_b."""
+        A64 = self.op(self.widen(A, dtype), trans_a)
+        B64 = self.op(self.widen(B, dtype), trans_b)
         C64 = self.widen(C0, "f32") if C0 is not None else None
         return self.gemm64(A64, B64, C64, alpha, beta, order)
 
@@ -155,8 +169,8 @@ def gemm64(A64, B64, C0_64, alpha, beta, order="ikj"):
     return default().gemm64(A64, B64, C0_64, alpha, beta, order)
 
 
-def gemm(A, B, C0, alpha, beta, dtype, order="ikj"):
-    return default().gemm(A, B, C0, alpha, beta, dtype, order)
+def gemm(A, B, C0, alpha, beta, dtype, order="ikj", trans_a=False, trans_b=False):
+    return default().gemm(A, B, C0, alpha, beta, dtype, order, trans_a, trans_b)
 
 
 def round_f32(R64):

@@ -19,6 +19,14 @@
  *   Row-major storage: X(r,c) = X[r*ld + c] with the column index
  *       contiguous (chongfengling.github.io section 2.2; elainafan.one
  *       "行主序" and the matmul_cpu listing).
+ *   Transposed operands: C <- alpha * op(A)*op(B) + beta * C, where op(X) is
+ *       X or its transpose, op(X)(r,c) = X(c,r).  A linear layer keeps its
+ *       input X as [batch, in] and its weight W as [out, in], and both of
+ *       its backward products are GEMMs (elainafan.one "全连接层"); with
+ *       that storage the forward product is X * W^T, the weight gradient
+ *       G^T * X and the input gradient G * W.  The page's formulas are lost
+ *       in the extraction; these are the products its shapes admit.
+ *       oracle_op forms op(X) explicitly before the product.
  *
  * Precision: every input is first widened EXACTLY to fp64 (fp32 values and
  * bf16 and IEEE binary16 bit patterns are all exact in fp64), so the oracle
@@ -52,6 +60,18 @@
 #ifdef _OPENMP
 #include <omp.h>
 #endif
+
+/* ---- op(X): the operand as used by the product ------------------------ */
+
+/* out (rows x cols, packed) = op(X), where X is stored row-major with leading
+ * dimension ld: X itself (rows x cols stored) when trans == 0, or the
+ * transpose of X (X stored cols x rows) when trans == 1. */
+void oracle_op(const double* X, int64_t rows, int64_t cols, int64_t ld, int trans,
+               double* out) {
+    for (int64_t r = 0; r < rows; ++r)
+        for (int64_t c = 0; c < cols; ++c)
+            out[r * cols + c] = trans ? X[c * ld + r] : X[r * ld + c];
+}
 
 /* ---- exact widening of the inputs to fp64 ------------------------------ */
 

@@ -39,8 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 2
-    for code in range(0, -7, -1):
+    assert dgt.gemm_abi_version() == 3
+    for code in range(0, -8, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
     assert dgt.gemm_status_string(12345) == "unknown gemm status"
@@ -98,16 +98,58 @@ def test_alpha_zero_does_not_need_a_or_b(lib):
 def test_auto_dispatch(lib):
     sel = dgt.gemm_select_variant
     F32, BF16, F16 = dgt.DTYPE_F32, dgt.DTYPE_BF16, dgt.DTYPE_F16
-    assert sel(BF16, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
-    assert sel(F16, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
-    assert sel(BF16, 16, 100, 100, 100, 100, 100) == dgt.VARIANT_SKINNY
-    assert sel(BF16, 17, 100, 100, 100, 100, 100) == dgt.VARIANT_MFMA
-    assert sel(F16, 8192, 8192, 8192, 8192, 8192, 8192) == dgt.VARIANT_MFMA
-    assert sel(F32, 4096, 4096, 4096, 4096, 4096, 4096) == dgt.VARIANT_MFMA
-    assert sel(F32, 4, 4, 4, 3, 4, 4) == dgt.GEMM_ERR_LD
-    assert sel(F32, -4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_DIM
-    assert sel(3, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_VARIANT
-    assert sel(-1, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_VARIANT
+    assert sel(BF16, 0, 0, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
+    assert sel(BF16, 0, 1, 8, 28672, 8192, 8192, 8192, 28672) == dgt.VARIANT_SKINNY
+    assert sel(F16, 0, 0, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
+    assert sel(BF16, 0, 0, 16, 100, 100, 100, 100, 100) == dgt.VARIANT_SKINNY
+    assert sel(BF16, 0, 0, 17, 100, 100, 100, 100, 100) == dgt.VARIANT_MFMA
+    assert sel(F16, 1, 1, 8192, 8192, 8192, 8192, 8192, 8192) == dgt.VARIANT_MFMA
+    assert sel(F32, 0, 0, 4096, 4096, 4096, 4096, 4096, 4096) == dgt.VARIANT_MFMA
+    assert sel(F32, 0, 0, 4, 4, 4, 3, 4, 4) == dgt.GEMM_ERR_LD
+    assert sel(F32, 0, 0, -4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_DIM
+    assert sel(3, 0, 0, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_ARG
+    assert sel(-1, 0, 0, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_ARG
+    assert sel(F32, 2, 0, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_ARG
+    assert sel(F32, 0, -1, 4, 4, 4, 4, 4, 4) == dgt.GEMM_ERR_ARG
+
+
+@pytest.mark.parametrize("dtype", [0, 1, 2])
+def test_transposed_leading_dimensions(lib, dtype):
+    """Stored shapes: A is K x M when trans_a (lda >= M), B is N x K when
+    trans_b (ldb >= K); C is always M x N."""
+    ex = dgt.gemm_ex
+    M, N, K = 6, 10, 4
+    for ta, tb in [(0, 0), (0, 1), (1, 0), (1, 1)]:
+        lda = M if ta else K
+        ldb = K if tb else N
+        assert ex(dtype, ta, tb, 0, M, N, K, 1.0, A_, lda - 1, B_, ldb, 0.0, C_, N) == \
+            dgt.GEMM_ERR_LD, (ta, tb)
+        assert ex(dtype, ta, tb, 0, M, N, K, 1.0, A_, lda, B_, ldb - 1, 0.0, C_, N) == \
+            dgt.GEMM_ERR_LD, (ta, tb)
+        assert ex(dtype, ta, tb, 0, M, N, K, 1.0, A_, lda, B_, ldb, 0.0, C_, N - 1) == \
+            dgt.GEMM_ERR_LD, (ta, tb)
+        # legal pitches reach the pointer checks (NULL C stops before a launch)
+        assert ex(dtype, ta, tb, 0, M, N, K, 1.0, A_, lda, B_, ldb, 0.0, 0, N) == \
+            dgt.GEMM_ERR_NULL, (ta, tb)
+    # bad flags and dtype are rejected first
+    assert ex(dtype, 2, 0, 0, M, N, K, 1.0, A_, K, B_, N, 0.0, C_, N) == dgt.GEMM_ERR_ARG
+    assert ex(dtype, 0, 3, 0, -1, N, K, 1.0, A_, K, B_, N, 0.0, C_, N) == dgt.GEMM_ERR_ARG
+    assert ex(7, 0, 0, 0, M, N, K, 1.0, A_, K, B_, N, 0.0, C_, N) == dgt.GEMM_ERR_ARG
+    assert ex(dtype, 0, 0, 9, M, N, K, 1.0, A_, K, B_, N, 0.0, C_, N) == dgt.GEMM_ERR_VARIANT
+    assert ex(dtype, 1, 1, dgt.VARIANT_SKINNY, 17, N, K, 1.0, A_, 17, B_, K, 0.0, C_, N) == \
+        dgt.GEMM_ERR_VARIANT
+
+
+def test_transposed_overlap_uses_stored_extent(lib):
+    """A stored K x M spans (K-1)*lda + M elements, not (M-1)*lda + K."""
+    ex = dgt.gemm_ex
+    M, N, K = 2, 4, 64           # A^T stored 64 x 2 with lda 2: 128 floats = 512 B
+    a = 0x100000
+    c_inside = a + 4 * 100       # inside the stored K x M extent, outside an M x K one
+    assert ex(0, 1, 0, 0, M, N, K, 1.0, a, M, B_, N, 0.0, c_inside, N) == dgt.GEMM_ERR_OVERLAP
+    b = 0x200000                 # B^T stored 4 x 64 (ldb 64): 256 floats
+    c_in_b = b + 4 * 200
+    assert ex(0, 0, 1, 0, M, N, K, 1.0, A_, K, b, K, 0.0, c_in_b, N) == dgt.GEMM_ERR_OVERLAP
 
 
 def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):

@@ -85,3 +85,29 @@ def test_workload_table():
     assert r.with_ints().dist == "int" and r.with_ints().seed_base != r.seed_base
     A, B, C0 = gi.make_inputs(w["f32_256"])
     assert A.shape == (256, 256) and C0 is None
+
+
+def test_f16_draw_rounding():
+    # binary16 keeps 10 fraction bits (dilfish.github.io 5.5 table, FP16 row);
+    # the generator rounds fp32 -> binary16 to nearest even
+    x = gi.draw(9, 64, 64, "normal", dtype="f16")
+    assert x.dtype == np.uint16
+    v = gi.as_fp32(x, "f16")
+    assert np.all(np.isfinite(v))
+    assert np.array_equal(v.astype(np.float16).view(np.uint16), x)
+    ref = gi.draw(9, 64, 64, "normal", dtype="f32")
+    assert np.all(np.abs(v - ref) <= np.abs(ref) * 2.0**-11 + 2.0**-25)
+
+
+def test_transposed_workloads_store_operands_transposed():
+    w = gi.WORKLOADS["bf16_8192_nt"]
+    assert (w.trans_a, w.trans_b) == (False, True)
+    assert w.a_shape == (8192, 8192) and w.b_shape == (8192, 8192)
+    s = gi.WORKLOADS["bf16_skinny_8x28672x8192_nt"]
+    assert s.a_shape == (8, 8192) and s.b_shape == (28672, 8192)
+    small = s.scaled(N=300, K=200)
+    A, B, C0 = gi.make_inputs(small)
+    assert A.shape == (8, 200) and B.shape == (300, 200)
+    t = gi.WORKLOADS["bf16_8192_tn"].scaled(M=40, N=30, K=20)
+    A, B, _ = gi.make_inputs(t)
+    assert A.shape == (20, 40) and B.shape == (20, 30)

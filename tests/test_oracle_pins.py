@@ -10,6 +10,8 @@ Where the pins come from:
 * the operation: C(i,j) = sum_k A(i,k) B(k,j), generalised to
   alpha*A*B + beta*C (elainafan.one "稠密矩阵乘法"; dilfish.github.io 5.2);
 * row-major storage (chongfengling.github.io 2.2; elainafan.one "行主序");
+* transposed operands: op(X) = X^T, and the three products of a linear layer
+  stored as X [batch, in], W [out, in] (elainafan.one "全连接层");
 * identity / permutation / rank-1 algebra, exact small-integer arithmetic,
   numpy's float64 matmul as an independent library routine, and exact
   rational arithmetic (``fractions.Fraction``) with the textbook fp64
@@ -207,9 +209,67 @@ def pin_leading_dims_rectangular(o):
     assert np.array_equal(R, want), "single-entry product lands in the wrong place"
 
 
+def pin_transposed_permutation(o):
+    """A stored as P with trans_a gives op(A) = P^T: (P^T B)[p[i], :] = B[i, :].
+    B stored as Q with trans_b gives op(B) = Q^T: (A Q^T)[:, q[j]] = A[:, j].
+    Square operands, so a mistake in op() cannot read outside them."""
+    n = 23
+    p = np.random.default_rng(13).permutation(n)
+    P = np.zeros((n, n), np.float32)
+    P[np.arange(n), p] = 1.0
+    B = _rng_f32(91, n, n)
+    R = o.gemm(P, B, None, 1.0, 0.0, "f32", trans_a=True)
+    assert np.array_equal(R[p], B.astype(np.float64)), "op(A) = P^T does not undo P"
+    q = np.random.default_rng(14).permutation(n)
+    Q = np.zeros((n, n), np.float32)
+    Q[q, np.arange(n)] = 1.0
+    A = _rng_f32(92, n, n)
+    R = o.gemm(A, Q, None, 1.0, 0.0, "f32", trans_b=True)
+    # Q^T[j, q[j]] = 1, so column q[j] of A Q^T is column j of A
+    assert np.array_equal(R[:, q], A.astype(np.float64)), "op(B) = Q^T wrong"
+
+
+def pin_transposed_rank1(o):
+    """Stored A = v u^T (K x M) with trans_a, stored B = z w^T (N x K) with
+    trans_b: op(A) op(B) = (v.w) u z^T, exactly; non-square on purpose."""
+    M, K, N = 17, 23, 29
+    r = np.random.default_rng(15)
+    u, v = r.integers(-3, 4, M), r.integers(-3, 4, K)
+    w, z = r.integers(-3, 4, K), r.integers(-3, 4, N)
+    A_s = np.outer(v, u).astype(np.float32)
+    B_s = np.outer(z, w).astype(np.float32)
+    C0 = r.integers(-5, 6, (M, N)).astype(np.float32)
+    want = 1.5 * int(np.dot(v, w)) * np.outer(u, z).astype(np.float64) + 0.5 * C0
+    for ta, tb, A, B in [(True, True, A_s, B_s), (True, False, A_s, B_s.T.copy()),
+                         (False, True, A_s.T.copy(), B_s)]:
+        R = o.gemm(A, B, C0, 1.5, 0.5, "f32", trans_a=ta, trans_b=tb)
+        assert np.array_equal(R, want), f"rank-1 with trans_a={ta}, trans_b={tb} wrong"
+
+
+def pin_linear_layer_products(o):
+    """The three products of a linear layer stored as X [batch, in], W [out,
+    in], G [batch, out] (elainafan.one "全连接层"): X W^T, G^T X and G W, on
+    small integers, equal numpy's float64 matmul of the explicit transposes."""
+    batch, d_in, d_out = 12, 40, 24
+    X = _ints(101, batch, d_in)
+    W = _ints(102, d_out, d_in)
+    G = _ints(103, batch, d_out)
+    x, w, g = (t.astype(np.float64) for t in (X, W, G))
+    Y = o.gemm(X, W, None, 1.0, 0.0, "f32", trans_b=True)
+    assert np.array_equal(Y, x @ w.T), "forward X W^T wrong"
+    dW = o.gemm(G, X, None, 1.0, 0.0, "f32", trans_a=True)
+    assert np.array_equal(dW, g.T @ x), "weight gradient G^T X wrong"
+    dX = o.gemm(G, W, None, 1.0, 0.0, "f32")
+    assert np.array_equal(dX, g @ w), "input gradient G W wrong"
+    # both flags: X stored transposed ([in, batch]) with W as is, op() = X, W^T
+    Y2 = o.gemm(X.T.copy(), W, None, 1.0, 0.0, "f32", trans_a=True, trans_b=True)
+    assert np.array_equal(Y2, x @ w.T), "trans_a and trans_b together wrong"
+
+
 PINS = [pin_identity, pin_permutation, pin_rank1, pin_small_integers,
         pin_alpha_beta, pin_exact_rational, pin_library_float64, pin_bf16_inputs,
-        pin_f16_inputs, pin_leading_dims_rectangular]
+        pin_f16_inputs, pin_leading_dims_rectangular, pin_transposed_permutation,
+        pin_transposed_rank1, pin_linear_layer_products]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -266,6 +326,8 @@ MUTANTS = {
     "f16_subnormal": ("if (e == 0) v = ldexp((double)f, -24);",
                       "if (e == 0) v = ldexp((double)(1024 + f), -25);"),
     "f16_sign": ("return sign ? -v : v;", "return v;"),
+    "op_ignores_trans": ("out[r * cols + c] = trans ? X[c * ld + r] : X[r * ld + c];",
+                         "out[r * cols + c] = X[r * ld + c];"),
 }
 
 

@@ -15,15 +15,13 @@ permutation and rank-1 inputs that expose swapped fragment layouts
 (dilfish.github.io 5.5 warns these "look right").
 """
 
-import math
-import sys
-
 import numpy as np
 import pytest
 
 import gemm_inputs as gi
 import oracle
 from gates import assert_bit_exact, assert_close
+from gpu_util import TORCH_DTYPE, bits16, run_gemm, say, to_dev
 
 torch = pytest.importorskip("torch")
 import dense_gemm_tuning_amd as dgt  # noqa: E402
@@ -32,12 +30,6 @@ pytestmark = pytest.mark.gpu
 
 RUNGS = ["naive", "lds", "mfma", "skinny", "auto"]
 DTYPES = ["f32", "bf16", "f16"]
-TORCH_DTYPE = {"f32": None, "bf16": "bfloat16", "f16": "float16"}
-
-
-def say(*a):
-    print(*a, flush=True)
-    sys.stdout.flush()
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -49,34 +41,6 @@ def _gpu():
     torch.cuda.set_device(0)
     yield
     torch.cuda.synchronize()
-
-
-def to_dev(x, dtype):
-    """numpy (fp32, or bf16/f16 bits) -> torch device tensor of the library's type."""
-    if dtype in ("bf16", "f16"):
-        t = torch.from_numpy(np.ascontiguousarray(x).view(np.int16)).cuda()
-        return t.view(getattr(torch, TORCH_DTYPE[dtype]))
-    return torch.from_numpy(np.ascontiguousarray(x, dtype=np.float32)).cuda()
-
-
-def bits16(x, dtype):
-    """fp32 values that are exact in the 16-bit format -> its raw bits."""
-    x = np.ascontiguousarray(x, np.float32)
-    if dtype == "bf16":
-        return gi.fp32_to_bf16_bits(x)
-    return x.astype(np.float16).view(np.uint16)
-
-
-def run_gemm(variant, dtype, A, B, C0, alpha, beta, M=None, stream=None):
-    """Copy operands to the GPU, run one call, return (status, C as numpy)."""
-    M, K = A.shape
-    N = B.shape[1]
-    dA, dB = to_dev(A, dtype), to_dev(B, dtype)
-    dC = (torch.from_numpy(np.ascontiguousarray(C0, np.float32)).cuda() if C0 is not None
-          else torch.full((M, N), float("nan"), device="cuda"))
-    st = dgt.gemm(dA, dB, dC, alpha, beta, variant=variant, stream=stream)
-    torch.cuda.synchronize()
-    return st, dC.cpu().numpy()
 
 
 def supports(variant, M):
@@ -178,28 +142,33 @@ def test_workload_configs(name):
     say(f"workload {name}: generating inputs")
     A, B, C0 = gi.make_inputs(w)
     say(f"workload {name}: running AUTO on the GPU")
-    st, C = run_gemm("auto", w.dtype, A, B, C0, w.alpha, w.beta)
+    st, C = run_gemm("auto", w.dtype, A, B, C0, w.alpha, w.beta, trans_a=w.trans_a,
+                     trans_b=w.trans_b)
     assert st == 0
     big = w.M * w.N * w.K > 4e9
     rows = _sample_rows(w.M) if big else list(range(w.M))
     say(f"workload {name}: oracle on {len(rows)} rows")
-    Ar = A[rows]
+    Ar = A[:, rows] if w.trans_a else A[rows]  # rows of op(A)
     C0r = C0[rows] if C0 is not None else None
-    R = oracle.gemm(Ar, B, C0r, w.alpha, w.beta, w.dtype)
+    R = oracle.gemm(Ar, B, C0r, w.alpha, w.beta, w.dtype, trans_a=w.trans_a,
+                    trans_b=w.trans_b)
     assert_close(C[rows], R, w.K, w.alpha, w.sigma, w.sigma, what=name)
     assert np.all(np.isfinite(C))
 
 
-@pytest.mark.parametrize("name", ["f32_256", "f32_1000_ragged", "bf16_skinny_8x28672x8192"])
+@pytest.mark.parametrize("name", ["f32_256", "f32_1000_ragged", "bf16_skinny_8x28672x8192",
+                                  "bf16_skinny_8x28672x8192_nt"])
 def test_workload_integer_variants(name):
     w = gi.WORKLOADS[name].with_ints()
     if w.M * w.N * w.K > 4e9:
         w = w.scaled(N=4096 + 96)  # same M and K, fewer columns (ragged tail)
     A, B, C0 = gi.make_inputs(w)
     say(f"integer workload {w.name} {w.M}x{w.N}x{w.K}")
-    st, C = run_gemm("auto", w.dtype, A, B, C0, w.alpha, w.beta)
+    st, C = run_gemm("auto", w.dtype, A, B, C0, w.alpha, w.beta, trans_a=w.trans_a,
+                     trans_b=w.trans_b)
     assert st == 0
-    R = oracle.round_f32(oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype))
+    R = oracle.round_f32(oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype,
+                                     trans_a=w.trans_a, trans_b=w.trans_b))
     assert_bit_exact(C, R, w.name)
 
 
