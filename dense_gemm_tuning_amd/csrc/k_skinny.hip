@@ -168,21 +168,46 @@ __global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
                                                     col, p.N, ok);
         }
     };
-    auto compute = [&](int step, const u32x4 (&rb)[8]) {
-        const u32x4 a = load_a16<kVec, kGuard, TA>(arow, step * KSTEP + 8 * g, p, a_ok);
+    auto load_a = [&](int step) {
+        return load_a16<kVec, kGuard, TA>(arow, step * KSTEP + 8 * g, p, a_ok);
+    };
+    auto compute = [&](const u32x4& a, const u32x4 (&rb)[8]) {
 #pragma unroll
         for (int c = 0; c < 8; ++c) acc[c] = mfma16x16x32<T>(a, column8(rb, c), acc[c]);
     };
 
-    u32x4 b0[8], b1[8];
-    if (s0 < s1) load_b(s0, b0);
-    for (int s = s0; s < s1; s += 2) {
-        if (s + 1 < s1) load_b(s + 1, b1);
-        compute(s, b0);
-        if (s + 1 < s1) {
-            if (s + 2 < s1) load_b(s + 2, b0);
-            compute(s + 1, b1);
-        }
+    // Two steps in flight: each phase issues the next step's loads (A with
+    // B, so that waiting for A never drains the B prefetch), then consumes
+    // the step loaded one phase earlier.  The scheduling barriers keep the
+    // phases in this order; unrolled by two so that the buffers alternate
+    // without a branch in the loop body.
+    u32x4 b0[8], b1[8], a0, a1;
+    int s = s0;
+    if (s < s1) {
+        a0 = load_a(s);
+        load_b(s, b0);
+    }
+    for (; s + 2 < s1; s += 2) {
+        a1 = load_a(s + 1);
+        load_b(s + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        a0 = load_a(s + 2);
+        load_b(s + 2, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(a1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+    }
+    if (s + 1 < s1) {
+        a1 = load_a(s + 1);
+        load_b(s + 1, b1);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(a0, b0);
+        __builtin_amdgcn_sched_barrier(0);
+        compute(a1, b1);
+    } else if (s < s1) {
+        compute(a0, b0);
     }
 
     // 16x16 accumulator layout: register r of lane l is row 4*(l/16) + r,
@@ -269,22 +294,17 @@ __global__ __launch_bounds__(NT, 1) void skinny16_bt_kernel(GemmParams p) {
             a[u] = load_a16<kVec, kGuard, TA>(arow, s * BT_KSTEP + 32 * u + 8 * g, p, a_ok);
     };
 
-    // Two groups in flight.  The loop body has no branch: on the last
-    // iteration the prefetch re-reads the current step (never used), so the
+    // Two groups in flight.  Each phase issues the next group's loads, then
+    // parks and consumes the group loaded one phase earlier; the scheduling
+    // barriers keep the compiler from gathering several phases' loads into
+    // one burst or from sinking them below the waits of the park.  The last
+    // step is peeled (no prefetch), so the loop body has no branch and the
     // loads stay in flight across the back edge.  LDS operations of one wave
     // complete in order, so parking a group after the previous group's
     // operand reads needs no wait.
     u32x4 r0[8], r1[8], a0[4], a1[4];
-    if (s0 < s1) {
-        load_a(s0, a0);
-        load_group(s0, 0, r0);
-    }
-    // Each phase issues the next group's loads, then parks and consumes the
-    // group loaded one phase earlier; the scheduling barriers keep the
-    // compiler from gathering several phases' loads into one burst or from
-    // sinking them below the waits of the park.
-    for (int s = s0; s < s1; ++s) {
-        const int sn = s + 1 < s1 ? s + 1 : s;
+    auto step = [&](int s, auto prefetch) {
+        constexpr bool kPrefetch = decltype(prefetch)::value;
         load_group(s, 1, r1);
         __builtin_amdgcn_sched_barrier(0);
         park(r0);
@@ -300,14 +320,24 @@ __global__ __launch_bounds__(NT, 1) void skinny16_bt_kernel(GemmParams p) {
         park(r0);
         compute(std::integral_constant<int, 2>{}, a0);
         __builtin_amdgcn_sched_barrier(0);
-        load_a(sn, a1);
-        load_group(sn, 0, r0);
+        if constexpr (kPrefetch) {
+            load_a(s + 1, a1);
+            load_group(s + 1, 0, r0);
+        }
         __builtin_amdgcn_sched_barrier(0);
         park(r1);
         compute(std::integral_constant<int, 3>{}, a0);
         __builtin_amdgcn_sched_barrier(0);
+        if constexpr (kPrefetch) {
 #pragma unroll
-        for (int u = 0; u < 4; ++u) a0[u] = a1[u];
+            for (int u = 0; u < 4; ++u) a0[u] = a1[u];
+        }
+    };
+    if (s0 < s1) {
+        load_a(s0, a0);
+        load_group(s0, 0, r0);
+        for (int s = s0; s + 1 < s1; ++s) step(s, std::true_type{});
+        step(s1 - 1, std::false_type{});
     }
 
     // 16x16 accumulator layout: register r of lane l is row 4*(l/16) + r,
