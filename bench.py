@@ -13,8 +13,10 @@ The same JSON line carries, under "also", the FP32 4096^3 case (against the
 fp32 matrix-core peak), the FP16-input 8192^3 case (against the fp16 peak,
 equal to bf16's), the skinny decode-shaped case M=8, N=28672,
 K=8192 (against HBM bandwidth: its time is the time to stream B once,
-dilfish.github.io 5.1 GEMV row), and the BF16 square and skinny cases with
-a linear layer's operand storage (B stored N x K, A stored K x M), plus:
+dilfish.github.io 5.1 GEMV row), the BF16 square and skinny cases with a
+linear layer's operand storage (B stored N x K, A stored K x M), that
+layer's forward with its bias fused, and a strided batch of 16 x 2048^3,
+plus:
   * "roofline": the dominant kernel's algorithmic FLOP per launch over its
     measured launch time, against the published MI355X peak;
   * "cpu_baseline": the CPU oracle timed on a bounded row sample of the same
@@ -49,7 +51,8 @@ HBM_PEAK_GBS = 8000.0
 
 PRIMARY = "bf16_8192"
 SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
-             "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt"]
+             "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
+             "bf16_bmm_16x2048"]
 
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
@@ -70,6 +73,10 @@ DOMINANT = {
                      r"mfma16_dma_kernel<\(dgt::In\)1, true, false>"),
     "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT>", "k_skinny.hip",
                                     r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false>"),
+    "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
+                                 r"mfma16_dma_kernel<\(dgt::In\)1, false, true>"),
+    "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
+                         r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -152,16 +159,23 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
     t0 = time.perf_counter()
     A, B, C0 = gi.make_inputs(w)
     log(f"[{w.name}] inputs generated in {time.perf_counter() - t0:.1f} s")
+    bias = gi.make_bias(w)
     dA = [to_dev(torch, A, w.dtype) for _ in range(copies)]
     dB = [to_dev(torch, B, w.dtype) for _ in range(copies)]
     dC = (torch.from_numpy(C0).cuda() if C0 is not None
-          else torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda"))
+          else torch.zeros((w.batch, w.M, w.N), dtype=torch.float32, device="cuda"))
+    dbias = torch.from_numpy(bias).cuda() if bias is not None else None
     stream = torch.cuda.current_stream()
     sptr = stream.cuda_stream
     lda, ldb = w.a_shape[1], w.b_shape[1]  # packed stored rows
-    if w.trans_a or w.trans_b:
-        code = {"f32": dgt.DTYPE_F32, "bf16": dgt.DTYPE_BF16, "f16": dgt.DTYPE_F16}[w.dtype]
-
+    code = {"f32": dgt.DTYPE_F32, "bf16": dgt.DTYPE_BF16, "f16": dgt.DTYPE_F16}[w.dtype]
+    if w.batch > 1 or bias is not None:
+        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s):
+            return dgt.gemm_strided_batched(
+                code, w.trans_a, w.trans_b, dgt.VARIANT_AUTO, M, N, K, alpha,
+                A, lda, w.a_shape[0] * lda, B, ldb, w.b_shape[0] * ldb, beta, C, ldc, M * N,
+                dbias.data_ptr() if dbias is not None else 0, N, w.batch, s)
+    elif w.trans_a or w.trans_b:
         def fn(*args):
             return dgt.gemm_ex(code, w.trans_a, w.trans_b, dgt.VARIANT_AUTO, *args)
     else:
@@ -202,8 +216,10 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
 
 def roofline(w, ms_avg):
     kern, _, _ = DOMINANT[w.name]
-    fl = gemm_flops(w.M, w.N, w.K)
-    by = algorithmic_bytes(w.M, w.N, w.K, 4 if w.dtype == "f32" else 2, w.beta)
+    fl = gemm_flops(w.M, w.N, w.K) * w.batch
+    by = algorithmic_bytes(w.M, w.N, w.K, 4 if w.dtype == "f32" else 2, w.beta) * w.batch
+    if w.bias:
+        by += w.N * 4 * w.batch
     traffic = read_traffic(w.name)
     if w.name.startswith("bf16_skinny"):
         ach = by / (ms_avg * 1e-3) / 1e9
@@ -286,7 +302,7 @@ def main(argv=None):
         log(f"[{name}] {w.M}x{w.N}x{w.K} {w.dtype}: warmup {args.warmup}, steps {args.steps}")
         res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies)
         res["roofline"] = roofline(w, res["ms_avg"])
-        res["tflops"] = gemm_flops(w.M, w.N, w.K) / (res["ms_avg"] * 1e-3) / 1e12
+        res["tflops"] = gemm_flops(w.M, w.N, w.K) * w.batch / (res["ms_avg"] * 1e-3) / 1e12
         log(f"[{name}] {res['ms_avg']:.4f} ms  {res['tflops']:.1f} TFLOP/s  "
             f"roofline frac {res['roofline']['frac']:.3f}")
         results[name] = (w, res, inputs)
@@ -303,7 +319,8 @@ def main(argv=None):
     for name in names[1:]:
         w2, r2, _ = results[name]
         entry = {"workload": name, "M": w2.M, "N": w2.N, "K": w2.K, "dtype": w2.dtype,
-                 "ms_per_step": round(r2["ms_avg"], 5),
+                 "trans_a": w2.trans_a, "trans_b": w2.trans_b, "batch": w2.batch,
+                 "bias": w2.bias, "ms_per_step": round(r2["ms_avg"], 5),
                  "tflops": round(r2["tflops"], 2), "roofline": r2["roofline"]}
         if name.startswith("bf16_skinny"):
             entry["gbs"] = r2["roofline"]["achieved"]

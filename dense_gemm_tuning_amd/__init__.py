@@ -43,8 +43,8 @@ VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
 
 # Every symbol the header declares (the tests check the library exports them).
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",
-           "gemm_f16_variant", "gemm_ex", "gemm_select_variant", "gemm_status_string",
-           "gemm_abi_version")
+           "gemm_f16_variant", "gemm_ex", "gemm_strided_batched", "gemm_select_variant",
+           "gemm_status_string", "gemm_abi_version")
 
 DTYPE_F32 = 0
 DTYPE_BF16 = 1
@@ -80,6 +80,10 @@ def _load() -> ctypes.CDLL:
             fn.argtypes = [i, *core]
         lib.gemm_ex.restype = i
         lib.gemm_ex.argtypes = [i, i, i, i, *core]
+        i64 = ctypes.c_int64
+        lib.gemm_strided_batched.restype = i
+        lib.gemm_strided_batched.argtypes = [i, i, i, i, i, i, i, f, p, i, i64, p, i, i64, f,
+                                             p, i, i64, p, i64, i, p]
         lib.gemm_select_variant.restype = i
         lib.gemm_select_variant.argtypes = [i] * 9
         lib.gemm_status_string.restype = ctypes.c_char_p
@@ -129,6 +133,15 @@ def gemm_ex(dtype, trans_a, trans_b, variant, M, N, K, alpha, A, lda, B, ldb, be
             ldc, stream=0) -> int:
     return _load().gemm_ex(int(dtype), int(trans_a), int(trans_b), int(variant), M, N, K,
                            alpha, A, lda, B, ldb, beta, C, ldc, stream)
+
+
+def gemm_strided_batched(dtype, trans_a, trans_b, variant, M, N, K, alpha, A, lda, stride_a,
+                         B, ldb, stride_b, beta, C, ldc, stride_c, bias, stride_bias, batch,
+                         stream=0) -> int:
+    return _load().gemm_strided_batched(int(dtype), int(trans_a), int(trans_b), int(variant),
+                                        M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b,
+                                        beta, C, ldc, stride_c, bias, stride_bias, batch,
+                                        stream)
 
 
 def gemm_select_variant(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc) -> int:
@@ -205,3 +218,64 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
     if variant == VARIANT_AUTO:
         return auto_fn(*args)
     return var_fn(variant, *args)
+
+
+def gemm_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, bias=None,
+                 variant=VARIANT_AUTO, stream=None, trans_a: bool = False,
+                 trans_b: bool = False) -> int:
+    """C[z] <- alpha*op(A[z])*op(B[z]) + beta*C[z] + bias[z] on torch tensors.
+
+    A, B and C are 3-D (batch first; a batch stride of 0, e.g. from
+    ``expand``, shares one matrix) or 2-D for an operand shared by every
+    problem; each matrix is row-major with unit column stride.  bias is None,
+    a 1-D tensor of N floats (shared) or a 2-D [batch, N] tensor.  Returns
+    the status code of gemm_strided_batched.
+    """
+    import torch
+
+    if isinstance(variant, str):
+        variant = VARIANTS[variant]
+    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise TypeError("A and B must both be float32, both bfloat16 or both float16")
+    if C.dtype != torch.float32 or C.dim() != 3:
+        raise TypeError("C must be a 3-D float32 tensor")
+    batch = C.shape[0]
+
+    def mat(t, name):
+        if t.dim() == 2:
+            return t, 0
+        if t.dim() != 3 or t.shape[0] not in (batch, 1):
+            raise ValueError(f"{name} must be 2-D or [batch, rows, cols]")
+        return t[0] if t.shape[0] == 1 else t, (0 if t.shape[0] == 1 else t.stride(0))
+
+    def pitch(t):
+        m = t if t.dim() == 2 else t[0]
+        if m.numel() > 0 and m.stride(1) != 1:
+            raise ValueError("matrices must be row-major with unit column stride")
+        return _ld(m)
+
+    A2, sa = mat(A, "A")
+    B2, sb = mat(B, "B")
+    a_rows, a_cols = A2.shape[-2:]
+    b_rows, b_cols = B2.shape[-2:]
+    M, K = (a_cols, a_rows) if trans_a else (a_rows, a_cols)
+    K2, N = (b_cols, b_rows) if trans_b else (b_rows, b_cols)
+    if K2 != K or tuple(C.shape[1:]) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"C {tuple(C.shape)}")
+    bias_ptr, sbias = 0, 0
+    if bias is not None:
+        if bias.dtype != torch.float32 or bias.shape[-1] != N or bias.stride(-1) != 1:
+            raise ValueError("bias must be float32 [N] or [batch, N] with unit stride")
+        bias_ptr = bias.data_ptr()
+        sbias = bias.stride(0) if bias.dim() == 2 else 0
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    dtype = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
+             torch.float16: DTYPE_F16}[A.dtype]
+    return gemm_strided_batched(dtype, trans_a, trans_b, variant, M, N, K, float(alpha),
+                                A2.data_ptr(), pitch(A2), sa, B2.data_ptr(), pitch(B2), sb,
+                                float(beta), C.data_ptr(), pitch(C), C.stride(0),
+                                bias_ptr, sbias, batch, stream)

@@ -40,79 +40,148 @@ uint64_t span_bytes(int rows, int cols, int ld, int esz) {
     return ((uint64_t)(rows - 1) * (uint64_t)ld + (uint64_t)cols) * (uint64_t)esz;
 }
 
-bool overlaps(const void* a, uint64_t na, const void* b, uint64_t nb) {
-    if (na == 0 || nb == 0) return false;
-    const uintptr_t x = reinterpret_cast<uintptr_t>(a), y = reinterpret_cast<uintptr_t>(b);
-    return x < y + nb && y < x + na;
-}
-
 // The rung AUTO resolves to; the alpha == 0 / K == 0 case is handled before.
 // Both input types have a skinny kernel, so the choice depends on M only.
 int auto_variant(int M) {
     return M <= dgt::kSkinnyMaxM ? GEMM_VARIANT_SKINNY : GEMM_VARIANT_MFMA;
 }
 
-int run(DType t, int ta, int tb, int variant, int M, int N, int K, float alpha,
-        const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
-        void* stream) {
-    int st = check_shape(ta, tb, M, N, K, lda, ldb, ldc);
+// One call of the library: the operation, the batch and the stream.
+struct Call {
+    DType t;
+    int ta, tb, variant;
+    int M, N, K;
+    float alpha, beta;
+    const void* A;
+    int lda;
+    int64_t stride_a;  // elements
+    const void* B;
+    int ldb;
+    int64_t stride_b;  // elements
+    float* C;
+    int ldc;
+    int64_t stride_c;  // floats
+    const float* bias;
+    int64_t stride_bias;  // floats
+    int batch;
+    void* stream;
+};
+
+// [lo, hi) byte range covered by `batch` problems of `span` bytes, `stride`
+// bytes apart (empty when span == 0).
+struct Range {
+    uintptr_t lo, hi;
+};
+Range batch_range(const void* base, uint64_t span, int64_t stride_bytes, int batch) {
+    const uintptr_t b = reinterpret_cast<uintptr_t>(base);
+    if (span == 0 || batch <= 0) return {b, b};
+    return {b, b + (uint64_t)(batch - 1) * (uint64_t)stride_bytes + span};
+}
+bool overlaps(const Range& x, const Range& y) {
+    return x.lo < x.hi && y.lo < y.hi && x.lo < y.hi && y.lo < x.hi;
+}
+
+// Largest gridDim.y of one launch; longer batches take several launches.
+constexpr int kMaxBatchPerLaunch = 65535;
+
+hipError_t dispatch(DType t, int variant, const GemmParams& p, bool reads_ab, hipStream_t s) {
+    using dgt::In;
+    if (!reads_ab) return dgt::launch_scale(p, s);
+    switch (variant) {
+        case GEMM_VARIANT_NAIVE:
+            return t == DType::F32    ? dgt::launch_naive<In::F32>(p, s)
+                   : t == DType::BF16 ? dgt::launch_naive<In::BF16>(p, s)
+                                      : dgt::launch_naive<In::F16>(p, s);
+        case GEMM_VARIANT_LDS:
+            return t == DType::F32    ? dgt::launch_lds<In::F32>(p, s)
+                   : t == DType::BF16 ? dgt::launch_lds<In::BF16>(p, s)
+                                      : dgt::launch_lds<In::F16>(p, s);
+        case GEMM_VARIANT_MFMA:
+            return t == DType::F32    ? dgt::launch_mfma_f32(p, s)
+                   : t == DType::BF16 ? dgt::launch_mfma16<In::BF16>(p, s)
+                                      : dgt::launch_mfma16<In::F16>(p, s);
+        case GEMM_VARIANT_SKINNY:
+            return t == DType::F32    ? dgt::launch_skinny_f32(p, s)
+                   : t == DType::BF16 ? dgt::launch_skinny16<In::BF16>(p, s)
+                                      : dgt::launch_skinny16<In::F16>(p, s);
+        default:
+            return hipErrorInvalidConfiguration;
+    }
+}
+
+// Strides beyond this (in elements) cannot describe device memory; rejecting
+// them keeps the range arithmetic below from overflowing.
+constexpr int64_t kMaxStride = int64_t(1) << 48;
+
+bool valid_stride(int64_t s) { return s >= 0 && s < kMaxStride; }
+
+int run(const Call& c) {
+    if (c.batch < 0 || !valid_stride(c.stride_a) || !valid_stride(c.stride_b) ||
+        !valid_stride(c.stride_c) || !valid_stride(c.stride_bias))
+        return GEMM_ERR_ARG;
+    int st = check_shape(c.ta, c.tb, c.M, c.N, c.K, c.lda, c.ldb, c.ldc);
     if (st != GEMM_OK) return st;
-    if (variant < GEMM_VARIANT_AUTO || variant > GEMM_VARIANT_SKINNY)
+    if (c.variant < GEMM_VARIANT_AUTO || c.variant > GEMM_VARIANT_SKINNY)
         return GEMM_ERR_VARIANT;
-    if (M == 0 || N == 0) return GEMM_OK;  // empty C: nothing to do
-    const bool reads_ab = (alpha != 0.0f) && (K > 0);
-    if (C == nullptr) return GEMM_ERR_NULL;
-    if (reads_ab && (A == nullptr || B == nullptr)) return GEMM_ERR_NULL;
-    const int esz = elem_size(t);
-    const uint64_t c_bytes = span_bytes(M, N, ldc, 4);
-    const uint64_t a_bytes = ta ? span_bytes(K, M, lda, esz) : span_bytes(M, K, lda, esz);
-    const uint64_t b_bytes = tb ? span_bytes(N, K, ldb, esz) : span_bytes(K, N, ldb, esz);
-    if (reads_ab && (overlaps(C, c_bytes, A, a_bytes) || overlaps(C, c_bytes, B, b_bytes)))
+    if (c.M == 0 || c.N == 0 || c.batch == 0) return GEMM_OK;  // empty C: nothing to do
+    const bool reads_ab = (c.alpha != 0.0f) && (c.K > 0);
+    if (c.C == nullptr) return GEMM_ERR_NULL;
+    if (reads_ab && (c.A == nullptr || c.B == nullptr)) return GEMM_ERR_NULL;
+    const int esz = elem_size(c.t);
+    const uint64_t c_span = span_bytes(c.M, c.N, c.ldc, 4);
+    // the problems of a batch must not write over each other
+    if (c.batch > 1 && (uint64_t)c.stride_c * 4 < c_span) return GEMM_ERR_OVERLAP;
+    const Range rc = batch_range(c.C, c_span, c.stride_c * 4, c.batch);
+    if (reads_ab) {
+        const uint64_t a_span =
+            c.ta ? span_bytes(c.K, c.M, c.lda, esz) : span_bytes(c.M, c.K, c.lda, esz);
+        const uint64_t b_span =
+            c.tb ? span_bytes(c.N, c.K, c.ldb, esz) : span_bytes(c.K, c.N, c.ldb, esz);
+        if (overlaps(rc, batch_range(c.A, a_span, c.stride_a * esz, c.batch)) ||
+            overlaps(rc, batch_range(c.B, b_span, c.stride_b * esz, c.batch)))
+            return GEMM_ERR_OVERLAP;
+    }
+    if (c.bias && overlaps(rc, batch_range(c.bias, (uint64_t)c.N * 4, c.stride_bias * 4, c.batch)))
         return GEMM_ERR_OVERLAP;
-    if (variant == GEMM_VARIANT_SKINNY && M > dgt::kSkinnyMaxM) return GEMM_ERR_VARIANT;
+    int variant = c.variant;
+    if (variant == GEMM_VARIANT_SKINNY && c.M > dgt::kSkinnyMaxM) return GEMM_ERR_VARIANT;
+    if (variant == GEMM_VARIANT_AUTO) variant = auto_variant(c.M);
 
     GemmParams p;
-    p.M = M; p.N = N; p.K = K;
-    p.alpha = alpha; p.beta = beta;
-    p.A = A; p.lda = lda;
-    p.B = B; p.ldb = ldb;
-    p.C = C; p.ldc = ldc;
-    p.ta = ta; p.tb = tb;
-    hipStream_t s = static_cast<hipStream_t>(stream);
+    p.M = c.M; p.N = c.N; p.K = c.K;
+    p.alpha = c.alpha; p.beta = c.beta;
+    p.A = c.A; p.lda = c.lda;
+    p.B = c.B; p.ldb = c.ldb;
+    p.C = c.C; p.ldc = c.ldc;
+    p.ta = c.ta; p.tb = c.tb;
+    p.stride_a = c.stride_a * esz;
+    p.stride_b = c.stride_b * esz;
+    p.stride_c = c.stride_c;
+    p.stride_bias = c.stride_bias;
+    p.bias = c.bias;
+    hipStream_t s = static_cast<hipStream_t>(c.stream);
 
-    hipError_t e;
-    if (!reads_ab) {
-        e = dgt::launch_scale(p, s);
-    } else {
-        if (variant == GEMM_VARIANT_AUTO) variant = auto_variant(M);
-        using dgt::In;
-        switch (variant) {
-            case GEMM_VARIANT_NAIVE:
-                e = t == DType::F32    ? dgt::launch_naive<In::F32>(p, s)
-                    : t == DType::BF16 ? dgt::launch_naive<In::BF16>(p, s)
-                                       : dgt::launch_naive<In::F16>(p, s);
-                break;
-            case GEMM_VARIANT_LDS:
-                e = t == DType::F32    ? dgt::launch_lds<In::F32>(p, s)
-                    : t == DType::BF16 ? dgt::launch_lds<In::BF16>(p, s)
-                                       : dgt::launch_lds<In::F16>(p, s);
-                break;
-            case GEMM_VARIANT_MFMA:
-                e = t == DType::F32    ? dgt::launch_mfma_f32(p, s)
-                    : t == DType::BF16 ? dgt::launch_mfma16<In::BF16>(p, s)
-                                       : dgt::launch_mfma16<In::F16>(p, s);
-                break;
-            case GEMM_VARIANT_SKINNY:
-                e = t == DType::F32    ? dgt::launch_skinny_f32(p, s)
-                    : t == DType::BF16 ? dgt::launch_skinny16<In::BF16>(p, s)
-                                       : dgt::launch_skinny16<In::F16>(p, s);
-                break;
-            default:
-                return GEMM_ERR_VARIANT;
-        }
+    for (int z0 = 0; z0 < c.batch; z0 += kMaxBatchPerLaunch) {
+        GemmParams q = p;
+        q.batch = std::min(kMaxBatchPerLaunch, c.batch - z0);
+        q.A = static_cast<const char*>(p.A) + (int64_t)z0 * p.stride_a;
+        q.B = static_cast<const char*>(p.B) + (int64_t)z0 * p.stride_b;
+        q.C = p.C + (int64_t)z0 * p.stride_c;
+        if (p.bias) q.bias = p.bias + (int64_t)z0 * p.stride_bias;
+        const hipError_t e = dispatch(c.t, variant, q, reads_ab, s);
+        if (e == hipErrorInvalidConfiguration) return GEMM_ERR_VARIANT;
+        if (e != hipSuccess) return GEMM_ERR_LAUNCH;
     }
-    if (e == hipErrorInvalidConfiguration) return GEMM_ERR_VARIANT;
-    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+    return GEMM_OK;
+}
+
+// The single-problem entry points.
+int run1(DType t, int ta, int tb, int variant, int M, int N, int K, float alpha,
+         const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
+         void* stream) {
+    Call c{t, ta, tb, variant, M, N, K, alpha, beta, A, lda, 0, B, ldb, 0, C, ldc, 0,
+           nullptr, 0, 1, stream};
+    return run(c);
 }
 
 }  // namespace
@@ -121,40 +190,40 @@ extern "C" {
 
 int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
              const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
-    return run(DType::F32, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
+    return run1(DType::F32, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
                C, ldc, stream);
 }
 
 int gemm_bf16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
               const uint16_t* B, int ldb, float beta, float* C, int ldc, void* stream) {
-    return run(DType::BF16, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
+    return run1(DType::BF16, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
                C, ldc, stream);
 }
 
 int gemm_f16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
              const uint16_t* B, int ldb, float beta, float* C, int ldc, void* stream) {
-    return run(DType::F16, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
+    return run1(DType::F16, 0, 0, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb, beta,
                C, ldc, stream);
 }
 
 int gemm_f16_variant(int variant, int M, int N, int K, float alpha, const uint16_t* A,
                      int lda, const uint16_t* B, int ldb, float beta, float* C, int ldc,
                      void* stream) {
-    return run(DType::F16, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run1(DType::F16, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                stream);
 }
 
 int gemm_f32_variant(int variant, int M, int N, int K, float alpha, const float* A,
                      int lda, const float* B, int ldb, float beta, float* C, int ldc,
                      void* stream) {
-    return run(DType::F32, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run1(DType::F32, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                stream);
 }
 
 int gemm_bf16_variant(int variant, int M, int N, int K, float alpha,
                       const uint16_t* A, int lda, const uint16_t* B, int ldb,
                       float beta, float* C, int ldc, void* stream) {
-    return run(DType::BF16, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+    return run1(DType::BF16, 0, 0, variant, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
                stream);
 }
 
@@ -165,8 +234,23 @@ int gemm_ex(int dtype, int trans_a, int trans_b, int variant, int M, int N, int 
     const DType t = dtype == GEMM_DTYPE_F32    ? DType::F32
                     : dtype == GEMM_DTYPE_BF16 ? DType::BF16
                                                : DType::F16;
-    return run(t, trans_a, trans_b, variant, M, N, K, alpha, A, lda, B, ldb, beta, C,
-               ldc, stream);
+    return run1(t, trans_a, trans_b, variant, M, N, K, alpha, A, lda, B, ldb, beta, C,
+                ldc, stream);
+}
+
+int gemm_strided_batched(int dtype, int trans_a, int trans_b, int variant, int M, int N,
+                         int K, float alpha, const void* A, int lda, int64_t stride_a,
+                         const void* B, int ldb, int64_t stride_b, float beta, float* C,
+                         int ldc, int64_t stride_c, const float* bias, int64_t stride_bias,
+                         int batch, void* stream) {
+    if (dtype < GEMM_DTYPE_F32 || dtype > GEMM_DTYPE_F16) return GEMM_ERR_ARG;
+    if (!valid_flag(trans_a) || !valid_flag(trans_b)) return GEMM_ERR_ARG;
+    const DType t = dtype == GEMM_DTYPE_F32    ? DType::F32
+                    : dtype == GEMM_DTYPE_BF16 ? DType::BF16
+                                               : DType::F16;
+    Call c{t, trans_a, trans_b, variant, M, N, K, alpha, beta, A, lda, stride_a, B, ldb,
+           stride_b, C, ldc, stride_c, bias, stride_bias, batch, stream};
+    return run(c);
 }
 
 int gemm_select_variant(int dtype, int trans_a, int trans_b, int M, int N, int K,

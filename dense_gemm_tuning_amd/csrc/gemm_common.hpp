@@ -29,7 +29,23 @@ struct GemmParams {
     float* C;
     int64_t ldc;
     int ta, tb;  // 1: the operand is stored transposed
+    // Strided batch: problem z of a launch (blockIdx.y, z < batch) reads
+    // A + z*stride_a bytes and B + z*stride_b bytes, writes C + z*stride_c
+    // floats and adds bias + z*stride_bias floats.  bias (N floats per
+    // problem, broadcast over the rows of C) is optional: nullptr = none.
+    int64_t stride_a, stride_b, stride_c, stride_bias;
+    const float* bias;
+    int batch;
 };
+
+// Point p at problem blockIdx.y of a strided batch.
+__device__ __forceinline__ void select_problem(GemmParams& p) {
+    const int64_t z = blockIdx.y;
+    p.A = static_cast<const char*>(p.A) + z * p.stride_a;
+    p.B = static_cast<const char*>(p.B) + z * p.stride_b;
+    p.C += z * p.stride_c;
+    if (p.bias) p.bias += z * p.stride_bias;
+}
 
 // Calls fn(TA, TB) with std::bool_constant arguments matching p.ta, p.tb, so
 // that launchers can pick a kernel specialised for the operand layout.
@@ -96,11 +112,13 @@ __device__ __forceinline__ floatx4 mfma16x16x32(u32x4 a, u32x4 b, floatx4 c) {
                                                       __builtin_bit_cast(halfx8, b), c, 0, 0, 0);
 }
 
-// Epilogue of the BLAS form: alpha*acc + beta*c, where C is read only when
-// beta != 0 (so NaN/Inf in a write-only C never propagate).
-__device__ __forceinline__ float epilogue(float acc, float alpha, float beta,
-                                          const float* c) {
-    return beta == 0.0f ? alpha * acc : alpha * acc + beta * (*c);
+// Epilogue of the BLAS form plus the optional bias of a linear layer:
+// (alpha*acc + beta*c) + bias[col], where C is read only when beta != 0 (so
+// NaN/Inf in a write-only C never propagate).
+__device__ __forceinline__ float epilogue(float acc, const GemmParams& p, const float* c,
+                                          int col) {
+    const float r = p.beta == 0.0f ? p.alpha * acc : p.alpha * acc + p.beta * (*c);
+    return p.bias ? r + p.bias[col] : r;
 }
 
 // Host-side launchers; each returns the hipError_t of its launch.
@@ -123,6 +141,13 @@ constexpr int kSkinnyMaxM = 16;
 inline bool rows_16b_aligned(const void* base, int64_t ld, int elem_size) {
     return (reinterpret_cast<uintptr_t>(base) % 16 == 0) &&
            ((ld * elem_size) % 16 == 0);
+}
+
+// The same for A and B of every problem of a batch (batch strides are in
+// bytes and must keep the alignment too).
+inline bool operands_16b_aligned(const GemmParams& p, int elem_size) {
+    return rows_16b_aligned(p.A, p.lda, elem_size) && rows_16b_aligned(p.B, p.ldb, elem_size) &&
+           p.stride_a % 16 == 0 && p.stride_b % 16 == 0;
 }
 
 }  // namespace dgt

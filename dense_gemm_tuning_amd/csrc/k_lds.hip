@@ -117,6 +117,7 @@ struct OpSlice {
 template <In T, bool kVec, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
     using S = typename InFmt<T>::S;
+    select_problem(p);
     __shared__ float As[2][BK][BM + PAD];
     __shared__ float Bs[2][BK][BN + PAD];
 
@@ -175,7 +176,7 @@ __global__ __launch_bounds__(NT, 2) void lds_kernel(GemmParams p, int tiles_n) {
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
             const int col = n0 + (j < 4 ? tx * 4 + j : 64 + tx * 4 + (j - 4));
-            if (col < p.N) crow[col] = epilogue(acc[i][j], p.alpha, p.beta, crow + col);
+            if (col < p.N) crow[col] = epilogue(acc[i][j], p, crow + col, col);
         }
     }
 }
@@ -187,15 +188,14 @@ hipError_t launch_lds(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = rows_16b_aligned(p.A, p.lda, sizeof(typename InFmt<T>::S)) &&
-                     rows_16b_aligned(p.B, p.ldb, sizeof(typename InFmt<T>::S));
+    const bool vec = operands_16b_aligned(p, sizeof(typename InFmt<T>::S));
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (vec)
-            hipLaunchKernelGGL((lds_kernel<T, true, TA, TB>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((lds_kernel<T, true, TA, TB>), dim3((unsigned)blocks, p.batch),
                                dim3(NT), 0, s, p, tiles_n);
         else
-            hipLaunchKernelGGL((lds_kernel<T, false, TA, TB>), dim3((unsigned)blocks),
+            hipLaunchKernelGGL((lds_kernel<T, false, TA, TB>), dim3((unsigned)blocks, p.batch),
                                dim3(NT), 0, s, p, tiles_n);
         return hipGetLastError();
     });

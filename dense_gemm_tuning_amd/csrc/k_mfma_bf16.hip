@@ -140,6 +140,7 @@ struct Op16 {
 
 template <In T, bool kVec, bool kGuard, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n) {
+    select_problem(p);
     __shared__ uint4 As[2][BM * CPR];
     __shared__ uint4 Bt[2][BN * CPR];
 
@@ -215,7 +216,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n
                 const int row = m0 + wm * 128 + ti * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (kGuard && (row >= p.M || col >= p.N)) continue;
                 float* c = p.C + (int64_t)row * p.ldc + col;
-                *c = epilogue(acc[ti][tj][r], p.alpha, p.beta, c);
+                *c = epilogue(acc[ti][tj][r], p, c, col);
             }
         }
 }
@@ -228,9 +229,9 @@ hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2);
+    const bool vec = operands_16b_aligned(p, 2);
     const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
-    const dim3 grid((unsigned)blocks), block(NT);
+    const dim3 grid((unsigned)blocks, p.batch), block(NT);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (full)

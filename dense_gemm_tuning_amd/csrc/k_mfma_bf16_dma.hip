@@ -211,6 +211,7 @@ constexpr int prologue_after() {
 // K-contiguous when TB.
 template <In T, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_n) {
+    select_problem(p);
     constexpr bool AK = !TA, BKc = TB;
     using OpA = typename std::conditional<AK, KcOperand, MnOperand>::type;
     using OpB = typename std::conditional<BKc, KcOperand, MnOperand>::type;
@@ -338,9 +339,15 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
     // 32x32 accumulator layout: register r of lane l is row
     // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the MFMA tile.  C is read
-    // only when beta != 0.
-    float* cbase = p.C + (int64_t)(m0 + wm * 128 + 4 * h) * p.ldc + n0 + wn * 128 + (lane & 31);
+    // only when beta != 0.  A lane's four bias values (one per column tile)
+    // are read once; without a bias it adds -0.0, which leaves every value,
+    // signed zeros included, unchanged.
+    const int col0 = n0 + wn * 128 + (lane & 31);
+    float* cbase = p.C + (int64_t)(m0 + wm * 128 + 4 * h) * p.ldc + col0;
     const float alpha = p.alpha, beta = p.beta;
+    float bias[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) bias[tj] = p.bias ? p.bias[col0 + tj * 32] : -0.0f;
     if (beta == 0.0f) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -349,7 +356,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
-                        alpha * acc[ti][tj][r];
+                        alpha * acc[ti][tj][r] + bias[tj];
     } else {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -358,7 +365,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 #pragma unroll
                 for (int r = 0; r < 16; ++r) {
                     float* c = cbase + (int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32;
-                    *c = alpha * acc[ti][tj][r] + beta * (*c);
+                    *c = (alpha * acc[ti][tj][r] + beta * (*c)) + bias[tj];
                 }
     }
 }
@@ -366,8 +373,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 }  // namespace
 
 bool mfma16_dma_eligible(const GemmParams& p) {
-    return rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2) &&
-           p.M % BM == 0 && p.N % BN == 0 && p.K % KALIGN == 0 && p.K > 0;
+    return operands_16b_aligned(p, 2) && p.M % BM == 0 && p.N % BN == 0 && p.K % KALIGN == 0 && p.K > 0;
 }
 
 template <In T>
@@ -377,8 +383,8 @@ hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-        hipLaunchKernelGGL((mfma16_dma_kernel<T, TA, TB>), dim3((unsigned)blocks), dim3(NT), 0,
-                           s, p, tiles_n);
+        hipLaunchKernelGGL((mfma16_dma_kernel<T, TA, TB>), dim3((unsigned)blocks, p.batch),
+                           dim3(NT), 0, s, p, tiles_n);
         return hipGetLastError();
     });
 }

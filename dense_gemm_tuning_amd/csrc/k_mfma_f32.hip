@@ -109,6 +109,7 @@ struct OpF32 {
 
 template <bool kVec, bool kGuard, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles_n) {
+    select_problem(p);
     using OpA = OpF32<kVec, kGuard, !TA>;
     using OpB = OpF32<kVec, kGuard, TB>;
     __shared__ float As[2][OpA::SIZE];
@@ -186,7 +187,7 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
                 const int row = m0 + wm * 64 + ti * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (kGuard && (row >= p.M || col >= p.N)) continue;
                 float* c = p.C + (int64_t)row * p.ldc + col;
-                *c = epilogue(acc[ti][tj][r], p.alpha, p.beta, c);
+                *c = epilogue(acc[ti][tj][r], p, c, col);
             }
         }
 }
@@ -197,9 +198,9 @@ hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = rows_16b_aligned(p.A, p.lda, 4) && rows_16b_aligned(p.B, p.ldb, 4);
+    const bool vec = operands_16b_aligned(p, 4);
     const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
-    const dim3 grid((unsigned)blocks), block(NT);
+    const dim3 grid((unsigned)blocks, p.batch), block(NT);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (full)

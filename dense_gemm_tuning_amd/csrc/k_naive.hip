@@ -27,6 +27,7 @@ template <In T>
 __global__ __launch_bounds__(kNaiveX * kNaiveY) void naive_kernel(GemmParams p,
                                                                   int tiles_n) {
     using S = typename InFmt<T>::S;
+    select_problem(p);
     const int bn = blockIdx.x % tiles_n;
     const int bm = blockIdx.x / tiles_n;
     const int col = bn * kNaiveX + threadIdx.x;
@@ -41,19 +42,20 @@ __global__ __launch_bounds__(kNaiveX * kNaiveY) void naive_kernel(GemmParams p,
     for (int k = 0; k < p.K; ++k)
         acc = fmaf(load_in<T>(a + k * sa), load_in<T>(b + k * sb), acc);
     float* c = p.C + (int64_t)row * p.ldc + col;
-    *c = epilogue(acc, p.alpha, p.beta, c);
+    *c = epilogue(acc, p, c, col);
 }
 
-// C <- beta*C (A*B contributes nothing: alpha == 0 or K == 0); zeros when
-// beta == 0 without reading C.
-__global__ __launch_bounds__(256) void scale_kernel(float* C, int64_t ldc, int M,
-                                                    int N, float beta) {
-    const int64_t total = (int64_t)M * N;
+// C <- beta*C (+ bias) when A*B contributes nothing (alpha == 0 or K == 0);
+// beta == 0 writes zeros (or the bias) without reading C.
+__global__ __launch_bounds__(256) void scale_kernel(GemmParams p) {
+    select_problem(p);
+    const int64_t total = (int64_t)p.M * p.N;
     for (int64_t e = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; e < total;
          e += (int64_t)gridDim.x * blockDim.x) {
-        const int64_t i = e / N, j = e % N;
-        float* c = C + i * ldc + j;
-        *c = beta == 0.0f ? 0.0f : beta * (*c);
+        const int64_t i = e / p.N, j = e % p.N;
+        float* c = p.C + i * p.ldc + j;
+        const float r = p.beta == 0.0f ? 0.0f : p.beta * (*c);
+        *c = p.bias ? r + p.bias[j] : r;
     }
 }
 
@@ -65,7 +67,7 @@ hipError_t launch_naive(const GemmParams& p, hipStream_t s) {
     const int64_t tiles_m = (p.M + kNaiveY - 1) / kNaiveY;
     const int64_t blocks = tiles_m * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    hipLaunchKernelGGL(naive_kernel<T>, dim3((unsigned)blocks),
+    hipLaunchKernelGGL(naive_kernel<T>, dim3((unsigned)blocks, p.batch),
                        dim3(kNaiveX, kNaiveY), 0, s, p, tiles_n);
     return hipGetLastError();
 }
@@ -77,8 +79,7 @@ hipError_t launch_scale(const GemmParams& p, hipStream_t s) {
     const int64_t total = (int64_t)p.M * p.N;
     int64_t blocks = (total + 255) / 256;
     if (blocks > 65536) blocks = 65536;  // grid-stride loop covers the rest
-    hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks), dim3(256), 0, s,
-                       p.C, p.ldc, p.M, p.N, p.beta);
+    hipLaunchKernelGGL(scale_kernel, dim3((unsigned)blocks, p.batch), dim3(256), 0, s, p);
     return hipGetLastError();
 }
 

@@ -104,7 +104,7 @@ __device__ __forceinline__ void reduce_store(float (*red)[16][COLS + 4],
 #pragma unroll
         for (int w = 0; w < NW; ++w) s += red[w][m][nl];
         float* c = p.C + (int64_t)m * p.ldc + n;
-        *c = epilogue(s, p.alpha, p.beta, c);
+        *c = epilogue(s, p, c, n);
     }
 }
 
@@ -135,6 +135,7 @@ __device__ __forceinline__ u32x4 load_a16(const uint16_t* arow, int ka, const Ge
 
 template <In T, bool kVec, bool kGuard, bool TA>
 __global__ __launch_bounds__(NT, 1) void skinny16_kernel(GemmParams p) {
+    select_problem(p);
     __shared__ float red[NW][16][BF_COLS + 4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, i = lane & 15;
@@ -238,6 +239,7 @@ constexpr int BT_STAGE = BT_GROUP_ROWS * 256;  // bytes per wave
 
 template <In T, bool kVec, bool kGuard, bool TA>
 __global__ __launch_bounds__(NT, 1) void skinny16_bt_kernel(GemmParams p) {
+    select_problem(p);
     __shared__ float red[NW][16][BF_COLS + 4];
     __shared__ __attribute__((aligned(16))) uint8_t stage_all[NW][BT_STAGE];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
@@ -355,6 +357,7 @@ constexpr int F_COLS = 64;
 
 template <bool kVec, bool kGuard, bool TA, bool TB>
 __global__ __launch_bounds__(NT, 1) void skinny_f32_kernel(GemmParams p) {
+    select_problem(p);
     __shared__ float red[NW][16][F_COLS + 4];
     const int lane = threadIdx.x & 63, wave = threadIdx.x >> 6;
     const int g = lane >> 4, i = lane & 15;
@@ -444,12 +447,12 @@ __global__ __launch_bounds__(NT, 1) void skinny_f32_kernel(GemmParams p) {
 template <In T>
 hipError_t launch_skinny16(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + BF_COLS - 1) / BF_COLS;
-    const bool vec = rows_16b_aligned(p.A, p.lda, 2) && rows_16b_aligned(p.B, p.ldb, 2);
+    const bool vec = operands_16b_aligned(p, 2);
     const int kstep = p.tb ? BT_KSTEP : KSTEP;
     const bool full = vec && p.N % BF_COLS == 0 && p.K % kstep == 0;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
-        const dim3 grid(blocks), block(NT);
+        const dim3 grid(blocks, p.batch), block(NT);
         if constexpr (TB) {
             if (full)
                 hipLaunchKernelGGL((skinny16_bt_kernel<T, true, false, TA>), grid, block, 0, s, p);
@@ -473,18 +476,18 @@ template hipError_t launch_skinny16<In::F16>(const GemmParams&, hipStream_t);
 
 hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + F_COLS - 1) / F_COLS;
-    const bool vec = rows_16b_aligned(p.A, p.lda, 4) && rows_16b_aligned(p.B, p.ldb, 4);
+    const bool vec = operands_16b_aligned(p, 4);
     const bool full = vec && p.N % F_COLS == 0 && p.K % KSTEP == 0;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (full)
-            hipLaunchKernelGGL((skinny_f32_kernel<true, false, TA, TB>), dim3(blocks), dim3(NT),
+            hipLaunchKernelGGL((skinny_f32_kernel<true, false, TA, TB>), dim3(blocks, p.batch), dim3(NT),
                                0, s, p);
         else if (vec)
-            hipLaunchKernelGGL((skinny_f32_kernel<true, true, TA, TB>), dim3(blocks), dim3(NT),
+            hipLaunchKernelGGL((skinny_f32_kernel<true, true, TA, TB>), dim3(blocks, p.batch), dim3(NT),
                                0, s, p);
         else
-            hipLaunchKernelGGL((skinny_f32_kernel<false, true, TA, TB>), dim3(blocks), dim3(NT),
+            hipLaunchKernelGGL((skinny_f32_kernel<false, true, TA, TB>), dim3(blocks, p.batch), dim3(NT),
                                0, s, p);
         return hipGetLastError();
     });

@@ -34,8 +34,9 @@ measured on: a small square case, a ragged one that exercises edge masking
 and the beta path, the FP32 4096^3 and BF16/FP16 8192^3 square cases the
 pages' tuning ladders target (qwbw.cn, section 三 table at 4096^3), a skinny
 decode-style case whose time is weight loading (dilfish.github.io, section
-5.1 table, GEMV row), and the BF16 square and skinny cases again with the
-operands stored the way a linear layer keeps them.
+5.1 table, GEMV row), the BF16 square and skinny cases again with the
+operands stored the way a linear layer keeps them, that layer's forward with
+its bias, and a strided batch of independent products.
 """
 
 from __future__ import annotations
@@ -153,6 +154,8 @@ class Workload:
     seed_base: int = 0
     trans_a: bool = False   # A stored K x M (op(A) = A^T)
     trans_b: bool = False   # B stored N x K (op(B) = B^T)
+    batch: int = 1          # independent problems, stacked on a leading axis
+    bias: bool = False      # a bias row of N floats per problem
 
     @property
     def a_shape(self):
@@ -166,7 +169,7 @@ class Workload:
 
     @property
     def flops(self) -> int:
-        return 2 * self.M * self.N * self.K
+        return 2 * self.M * self.N * self.K * self.batch
 
     def seeds(self):
         return self.seed_base + 1, self.seed_base + 2, self.seed_base + 3
@@ -204,19 +207,41 @@ WORKLOADS = {
     "bf16_skinny_8x28672x8192_nt": Workload("bf16_skinny_8x28672x8192_nt", "bf16",
                                             8, 28672, 8192, 1.0, 0.0, "normal",
                                             sigma=0.02, seed_base=9000, trans_b=True),
+    # The linear layer's forward with its bias fused into the epilogue, and a
+    # strided batch of independent products.
+    "bf16_linear_bias_8192_nt": Workload("bf16_linear_bias_8192_nt", "bf16", 8192, 8192, 8192,
+                                         1.0, 0.0, "normal", seed_base=10000, trans_b=True,
+                                         bias=True),
+    "bf16_bmm_16x2048": Workload("bf16_bmm_16x2048", "bf16", 2048, 2048, 2048, 1.0, 0.0,
+                                 "normal", seed_base=11000, batch=16),
 }
+
+
+def _stack(seed, batch, rows, cols, dist, sigma, dtype):
+    """``batch`` matrices drawn as one stream (problem z is rows z*rows ..)."""
+    x = draw(seed, batch * rows, cols, dist, sigma, dtype)
+    return x if batch == 1 else x.reshape(batch, rows, cols)
 
 
 def make_inputs(w: Workload):
     """Return ``(A, B, C0)`` for workload ``w`` (C0 is None when beta == 0).
-    A and B have their stored shapes (``w.a_shape``, ``w.b_shape``)."""
+    A and B have their stored shapes (``w.a_shape``, ``w.b_shape``), with a
+    leading batch axis when ``w.batch > 1``."""
     sa, sb, sc = w.seeds()
-    A = draw(sa, *w.a_shape, w.dist, w.sigma, w.dtype)
-    B = draw(sb, *w.b_shape, w.dist, w.sigma, w.dtype)
+    A = _stack(sa, w.batch, *w.a_shape, w.dist, w.sigma, w.dtype)
+    B = _stack(sb, w.batch, *w.b_shape, w.dist, w.sigma, w.dtype)
     C0 = None
     if w.beta != 0.0:
-        C0 = draw(sc, w.M, w.N, w.dist, w.sigma, "f32")
+        C0 = _stack(sc, w.batch, w.M, w.N, w.dist, w.sigma, "f32")
     return A, B, C0
+
+
+def make_bias(w: Workload):
+    """The bias rows of workload ``w``, fp32 [batch, N] (uniform on [-1, 1)),
+    or None."""
+    if not w.bias:
+        return None
+    return draw(w.seed_base + 4, w.batch, w.N, "uniform", 1.0, "f32")
 
 
 def as_fp32(x: np.ndarray, dtype: str) -> np.ndarray:

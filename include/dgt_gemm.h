@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 3
+#define DGT_GEMM_ABI_VERSION 4
 
 /* Input formats (the dtype argument of gemm_ex and gemm_select_variant). */
 enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };
@@ -78,12 +78,15 @@ enum gemm_status {
                                    ldc < max(1,N)                            */
     GEMM_ERR_NULL = -3,         /* NULL A/B (when read) or C with a
                                    non-empty extent                          */
-    GEMM_ERR_OVERLAP = -4,      /* the byte range of C overlaps A's or B's   */
+    GEMM_ERR_OVERLAP = -4,      /* the byte range of C overlaps A's, B's or
+                                   the bias's, or two problems of a batch
+                                   share C elements                          */
     GEMM_ERR_VARIANT = -5,      /* unknown variant, or one that does not
                                    support this shape / size                 */
     GEMM_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch  */
-    GEMM_ERR_ARG = -7           /* dtype not a gemm_dtype, or a transpose
-                                   flag other than 0 or 1                    */
+    GEMM_ERR_ARG = -7           /* dtype not a gemm_dtype, a transpose flag
+                                   other than 0 or 1, a negative batch, or a
+                                   stride outside [0, 2^48)                  */
 };
 
 /* Kernel ladder (for measurement and tests; GEMM_VARIANT_AUTO is what
@@ -150,6 +153,30 @@ int gemm_f16_variant(int variant, int M, int N, int K, float alpha,
 int gemm_ex(int dtype, int trans_a, int trans_b, int variant, int M, int N,
             int K, float alpha, const void* A, int lda, const void* B, int ldb,
             float beta, float* C, int ldc, void* stream);
+
+/* Strided batch with the bias of a linear layer: for z = 0 .. batch-1,
+ *
+ *   C_z <- alpha * op(A_z) * op(B_z) + beta * C_z + 1 * bias_z^T
+ *
+ * where X_z = X + z * stride_x (strides in ELEMENTS of the operand: A and B
+ * in their input format, C and bias in floats; 0 repeats one operand for
+ * every problem, e.g. a shared weight), and bias_z is a row of N floats
+ * added to every row of C_z (elainafan.one "全连接层": the linear layer
+ * computes X*W^T + b; its input keeps a batch dimension).  bias may be NULL
+ * (no bias); it is added after the BLAS form, unscaled, also when
+ * alpha == 0 or K == 0.  Every other argument is as for gemm_ex.
+ * Requirements: batch >= 0 (0 does nothing), strides in [0, 2^48), the
+ * problems' C ranges disjoint (stride_c * 4 bytes at least the span of one
+ * C when batch > 1), C disjoint from every A, B and bias range.  Any batch
+ * size is accepted; the library splits it into launches of at most 65535
+ * problems, queued in order on `stream`. */
+int gemm_strided_batched(int dtype, int trans_a, int trans_b, int variant,
+                         int M, int N, int K, float alpha,
+                         const void* A, int lda, int64_t stride_a,
+                         const void* B, int ldb, int64_t stride_b,
+                         float beta, float* C, int ldc, int64_t stride_c,
+                         const float* bias, int64_t stride_bias, int batch,
+                         void* stream);
 
 /* The rung GEMM_VARIANT_AUTO picks for this call (dtype: enum gemm_dtype;
  * trans_a, trans_b as for gemm_ex), or a negative status if the arguments

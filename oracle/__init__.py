@@ -60,7 +60,7 @@ class Oracle:
             f = getattr(lib, name)
             f.restype = None
             f.argtypes = [_i64, _i64, _i64, ctypes.c_double, _d, _i64, _d, _i64,
-                          ctypes.c_double, _d, _i64, _d, _i64]
+                          ctypes.c_double, _d, _i64, _d, _d, _i64]
         lib.oracle_widen_f32.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
         lib.oracle_widen_bf16.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
         lib.oracle_widen_f16.argtypes = [ctypes.c_void_p, _i64, _i64, _i64, _d]
@@ -90,8 +90,9 @@ class Oracle:
         return out
 
     def gemm64(self, A64, B64, C0_64, alpha: float, beta: float,
-               order: str = "ikj") -> np.ndarray:
-        """alpha*A*B + beta*C0 in fp64 on already-widened operands.
+               order: str = "ikj", bias=None) -> np.ndarray:
+        """alpha*A*B + beta*C0 (+ bias on every row) in fp64 on already-widened
+        operands.
 
         ``C0_64`` may be given even when ``beta == 0``; the oracle must then
         ignore it (that reading is pinned by a test with a NaN-filled C0).
@@ -110,9 +111,14 @@ class Oracle:
             if beta != 0.0:
                 raise ValueError("beta != 0 needs C0")
             cptr = _d()
+        bptr = _d()
+        if bias is not None:
+            bias = np.ascontiguousarray(bias, dtype=np.float64)
+            assert bias.shape == (N,)
+            bptr = _ptr(bias)
         fn = self.lib.oracle_gemm if order == "ikj" else self.lib.oracle_gemm_ijk
         fn(M, N, K, float(alpha), _ptr(A64), max(K, 1), _ptr(B64), max(N, 1),
-           float(beta), cptr, max(N, 1), _ptr(R), max(N, 1))
+           float(beta), cptr, max(N, 1), bptr, _ptr(R), max(N, 1))
         return R
 
     def op(self, X64: np.ndarray, trans: bool) -> np.ndarray:
@@ -125,14 +131,29 @@ class Oracle:
         return out
 
     def gemm(self, A, B, C0, alpha: float, beta: float, dtype: str,
-             order: str = "ikj", trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
+             order: str = "ikj", trans_a: bool = False, trans_b: bool = False,
+             bias=None) -> np.ndarray:
         """Oracle result in fp64 for raw inputs (fp32 arrays, bf16 or f16 bits).
 
-        A and B are given as stored: K x M when trans_a, N x K when trans_b."""
+        A and B are given as stored: K x M when trans_a, N x K when trans_b;
+        bias is None or N fp32 values added to every row."""
         A64 = self.op(self.widen(A, dtype), trans_a)
         B64 = self.op(self.widen(B, dtype), trans_b)
         C64 = self.widen(C0, "f32") if C0 is not None else None
-        return self.gemm64(A64, B64, C64, alpha, beta, order)
+        b64 = None if bias is None else self.widen(np.asarray(bias, np.float32)[None, :], "f32")[0]
+        return self.gemm64(A64, B64, C64, alpha, beta, order, b64)
+
+    def gemm_batched(self, As, Bs, C0s, alpha: float, beta: float, dtype: str,
+                     trans_a: bool = False, trans_b: bool = False, biases=None) -> np.ndarray:
+        """A batch of independent problems, one after another: As, Bs (stored
+        shapes), C0s and biases are sequences (or 3-D / 2-D arrays) of the
+        same length; C0s and biases may be None.  Returns [batch, M, N]."""
+        out = []
+        for z in range(len(As)):
+            out.append(self.gemm(As[z], Bs[z], None if C0s is None else C0s[z], alpha, beta,
+                                 dtype, trans_a=trans_a, trans_b=trans_b,
+                                 bias=None if biases is None else biases[z]))
+        return np.stack(out) if out else np.zeros((0, 0, 0))
 
     def round_f32(self, R64: np.ndarray) -> np.ndarray:
         """fp64 -> fp32, nearest-even."""
@@ -169,8 +190,12 @@ def gemm64(A64, B64, C0_64, alpha, beta, order="ikj"):
     return default().gemm64(A64, B64, C0_64, alpha, beta, order)
 
 
-def gemm(A, B, C0, alpha, beta, dtype, order="ikj", trans_a=False, trans_b=False):
-    return default().gemm(A, B, C0, alpha, beta, dtype, order, trans_a, trans_b)
+def gemm(A, B, C0, alpha, beta, dtype, order="ikj", trans_a=False, trans_b=False, bias=None):
+    return default().gemm(A, B, C0, alpha, beta, dtype, order, trans_a, trans_b, bias)
+
+
+def gemm_batched(As, Bs, C0s, alpha, beta, dtype, trans_a=False, trans_b=False, biases=None):
+    return default().gemm_batched(As, Bs, C0s, alpha, beta, dtype, trans_a, trans_b, biases)
 
 
 def round_f32(R64):

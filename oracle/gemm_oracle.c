@@ -27,6 +27,11 @@
  *       G^T * X and the input gradient G * W.  The page's formulas are lost
  *       in the extraction; these are the products its shapes admit.
  *       oracle_op forms op(X) explicitly before the product.
+ *   Bias: the linear layer adds its bias vector b to every output row
+ *       (elainafan.one "全连接层": X * W^T + b), so with a bias
+ *       C(i,j) <- alpha * (op(A) op(B))(i,j) + beta * C(i,j) + b(j): added
+ *       after the BLAS form, unscaled.  A batch of problems is a loop over
+ *       independent problems (in the Python wrapper).
  *
  * Precision: every input is first widened EXACTLY to fp64 (fp32 values and
  * bf16 and IEEE binary16 bit patterns are all exact in fp64), so the oracle
@@ -129,18 +134,24 @@ static double combine(double alpha, double acc, double beta, const double* c0) {
     return r;
 }
 
+/* The linear layer's bias: b(j) added to every row after the BLAS form
+ * (bias == NULL: none). */
+static double add_bias(double r, const double* bias, int64_t j) {
+    return bias ? r + bias[j] : r;
+}
+
 /* Literal triple loop: for each (i, j), acc = sum over ascending k. */
 void oracle_gemm_ijk(int64_t M, int64_t N, int64_t K, double alpha,
                      const double* A, int64_t lda, const double* B, int64_t ldb,
-                     double beta, const double* C0, int64_t ldc0,
+                     double beta, const double* C0, int64_t ldc0, const double* bias,
                      double* R, int64_t ldr) {
     for (int64_t i = 0; i < M; ++i) {
         for (int64_t j = 0; j < N; ++j) {
             double acc = 0.0;
             for (int64_t k = 0; k < K; ++k)
                 acc += A[i * lda + k] * B[k * ldb + j];
-            R[i * ldr + j] = combine(alpha, acc, beta,
-                                     C0 ? &C0[i * ldc0 + j] : NULL);
+            R[i * ldr + j] = add_bias(combine(alpha, acc, beta,
+                                              C0 ? &C0[i * ldc0 + j] : NULL), bias, j);
         }
     }
 }
@@ -150,7 +161,7 @@ void oracle_gemm_ijk(int64_t M, int64_t N, int64_t K, double alpha,
  * and are shared among threads; no sum is ever split across threads. */
 void oracle_gemm(int64_t M, int64_t N, int64_t K, double alpha,
                  const double* A, int64_t lda, const double* B, int64_t ldb,
-                 double beta, const double* C0, int64_t ldc0,
+                 double beta, const double* C0, int64_t ldc0, const double* bias,
                  double* R, int64_t ldr) {
 #pragma omp parallel
     {
@@ -164,8 +175,8 @@ void oracle_gemm(int64_t M, int64_t N, int64_t K, double alpha,
                 for (int64_t j = 0; j < N; ++j) acc[j] += a * brow[j];
             }
             for (int64_t j = 0; j < N; ++j)
-                R[i * ldr + j] = combine(alpha, acc[j], beta,
-                                         C0 ? &C0[i * ldc0 + j] : NULL);
+                R[i * ldr + j] = add_bias(combine(alpha, acc[j], beta,
+                                                  C0 ? &C0[i * ldc0 + j] : NULL), bias, j);
         }
         free(acc);
     }

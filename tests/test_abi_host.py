@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 3
+    assert dgt.gemm_abi_version() == 4
     for code in range(0, -8, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
@@ -157,3 +157,45 @@ def test_binding_fails_loudly_without_library(monkeypatch, tmp_path):
     monkeypatch.setattr(dgt, "LIB_PATH", str(tmp_path / "missing.so"))
     with pytest.raises(RuntimeError, match="not built"):
         dgt.gemm_abi_version()
+
+
+def test_strided_batched_argument_checks(lib):
+    sb = dgt.gemm_strided_batched
+    M, N, K = 4, 8, 16
+    # (dtype, ta, tb, variant, M, N, K, alpha, A, lda, sa, B, ldb, sb, beta, C, ldc, sc,
+    #  bias, sbias, batch)
+    base = dict(dtype=0, ta=0, tb=0, variant=0, M=M, N=N, K=K, alpha=1.0, A=A_, lda=K, sa=M * K,
+                B=B_, ldb=N, sb=K * N, beta=0.0, C=C_, ldc=N, sc=M * N, bias=0, sbias=0, batch=3)
+
+    def call(**kw):
+        a = dict(base, **kw)
+        return sb(a["dtype"], a["ta"], a["tb"], a["variant"], a["M"], a["N"], a["K"], a["alpha"],
+                  a["A"], a["lda"], a["sa"], a["B"], a["ldb"], a["sb"], a["beta"], a["C"],
+                  a["ldc"], a["sc"], a["bias"], a["sbias"], a["batch"])
+
+    # valid arguments reach the pointer checks (NULL C stops before a launch)
+    assert call(C=0) == dgt.GEMM_ERR_NULL
+    assert call(batch=-1) == dgt.GEMM_ERR_ARG
+    assert call(sa=-1) == dgt.GEMM_ERR_ARG
+    assert call(sc=1 << 48) == dgt.GEMM_ERR_ARG
+    assert call(sbias=-4) == dgt.GEMM_ERR_ARG
+    assert call(dtype=5) == dgt.GEMM_ERR_ARG
+    assert call(tb=2) == dgt.GEMM_ERR_ARG
+    assert call(lda=K - 1) == dgt.GEMM_ERR_LD
+    assert call(variant=7) == dgt.GEMM_ERR_VARIANT
+    # empty batch or empty C: nothing to do, no pointer needed
+    assert call(batch=0, A=0, B=0, C=0) == dgt.GEMM_OK
+    assert call(M=0, A=0, B=0, C=0) == dgt.GEMM_OK
+    # problems of one batch writing the same C elements
+    assert call(sc=M * N - 1) == dgt.GEMM_ERR_OVERLAP
+    assert call(sc=0) == dgt.GEMM_ERR_OVERLAP
+    assert call(sc=0, batch=1, C=0) == dgt.GEMM_ERR_NULL   # one problem: stride unused
+    # C reaching into the last A of the batch (A spans 3 problems of M*K floats)
+    assert call(C=A_ + 4 * (2 * M * K + 5)) == dgt.GEMM_ERR_OVERLAP
+    # C overlapping the bias of a later problem
+    bias = 0x400000
+    assert call(bias=bias, sbias=N, C=bias + 4 * (2 * N + 1)) == dgt.GEMM_ERR_OVERLAP
+    # A and B may overlap each other and repeat: only C's writes matter
+    assert call(B=A_, sb=0, C=0) == dgt.GEMM_ERR_NULL
+    # skinny rung still limited to M <= 16
+    assert call(variant=dgt.VARIANT_SKINNY, M=17, sc=17 * N) == dgt.GEMM_ERR_VARIANT

@@ -11,7 +11,8 @@ Where the pins come from:
   alpha*A*B + beta*C (elainafan.one "稠密矩阵乘法"; dilfish.github.io 5.2);
 * row-major storage (chongfengling.github.io 2.2; elainafan.one "行主序");
 * transposed operands: op(X) = X^T, and the three products of a linear layer
-  stored as X [batch, in], W [out, in] (elainafan.one "全连接层");
+  stored as X [batch, in], W [out, in], and its bias added to every row
+  (elainafan.one "全连接层"); batches against numpy's batched matmul;
 * identity / permutation / rank-1 algebra, exact small-integer arithmetic,
   numpy's float64 matmul as an independent library routine, and exact
   rational arithmetic (``fractions.Fraction``) with the textbook fp64
@@ -266,10 +267,45 @@ def pin_linear_layer_products(o):
     assert np.array_equal(Y2, x @ w.T), "trans_a and trans_b together wrong"
 
 
+def pin_linear_bias(o):
+    """F.linear's bias (elainafan.one "全连接层": X W^T + b): b is added to
+    every row after the BLAS form, unscaled; numpy's float64 matmul plus a
+    broadcast add on small integers is exact."""
+    batch, d_in, d_out = 12, 40, 24
+    X, W = _ints(111, batch, d_in), _ints(112, d_out, d_in)
+    b = _ints(113, 1, d_out)[0]
+    C0 = _ints(114, batch, d_out)
+    x, w, c0, bb = (t.astype(np.float64) for t in (X, W, C0, b))
+    Y = o.gemm(X, W, C0, 1.5, 0.5, "f32", trans_b=True, bias=b)
+    assert np.array_equal(Y, 1.5 * (x @ w.T) + 0.5 * c0 + bb[None, :]), "bias epilogue wrong"
+    Y = o.gemm(X, W, None, 0.0, 0.0, "f32", trans_b=True, bias=b)
+    assert np.array_equal(Y, np.broadcast_to(bb, (batch, d_out))), "alpha = 0: C must be the bias"
+    Z = o.gemm(np.zeros((batch, 0), np.float32), np.zeros((d_out, 0), np.float32), C0, 1.0,
+               -2.0, "f32", trans_b=True, bias=b)
+    assert np.array_equal(Z, -2.0 * c0 + bb[None, :]), "K = 0: C must be beta*C0 + bias"
+
+
+def pin_batched(o):
+    """A batch is independent problems: numpy's batched matmul (np.matmul on
+    3-D stacks) of the same stacks, with a shared and a per-problem operand."""
+    nb, M, N, K = 3, 7, 9, 11
+    A3 = np.stack([_ints(120 + z, M, K) for z in range(nb)])
+    B = _ints(125, K, N)                                   # shared by every problem
+    B3t = np.stack([_ints(130 + z, N, K) for z in range(nb)])  # stored transposed
+    C03 = np.stack([_ints(135 + z, M, N) for z in range(nb)])
+    bias = np.stack([_ints(140 + z, 1, N)[0] for z in range(nb)])
+    a3, b, c03, bs = (t.astype(np.float64) for t in (A3, B, C03, bias))
+    R = o.gemm_batched(A3, [B] * nb, C03, 2.0, -1.0, "f32", biases=bias)
+    assert np.array_equal(R, 2.0 * np.matmul(a3, b) - c03 + bs[:, None, :]), "batch wrong"
+    R = o.gemm_batched(A3, B3t, None, 1.0, 0.0, "f32", trans_b=True)
+    want = np.matmul(a3, B3t.astype(np.float64).transpose(0, 2, 1))
+    assert np.array_equal(R, want), "batch with stored-transposed B wrong"
+
+
 PINS = [pin_identity, pin_permutation, pin_rank1, pin_small_integers,
         pin_alpha_beta, pin_exact_rational, pin_library_float64, pin_bf16_inputs,
         pin_f16_inputs, pin_leading_dims_rectangular, pin_transposed_permutation,
-        pin_transposed_rank1, pin_linear_layer_products]
+        pin_transposed_rank1, pin_linear_layer_products, pin_linear_bias, pin_batched]
 
 
 @pytest.mark.parametrize("pin", PINS, ids=lambda f: f.__name__)
@@ -328,6 +364,9 @@ MUTANTS = {
     "f16_sign": ("return sign ? -v : v;", "return v;"),
     "op_ignores_trans": ("out[r * cols + c] = trans ? X[c * ld + r] : X[r * ld + c];",
                          "out[r * cols + c] = X[r * ld + c];"),
+    "bias_dropped": ("return bias ? r + bias[j] : r;", "return r;"),
+    "bias_one_column": ("return bias ? r + bias[j] : r;", "return bias ? r + bias[0] : r;"),
+    "bias_subtracted": ("return bias ? r + bias[j] : r;", "return bias ? r - bias[j] : r;"),
 }
 
 

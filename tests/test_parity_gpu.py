@@ -141,19 +141,38 @@ def test_workload_configs(name):
     w = gi.WORKLOADS[name]
     say(f"workload {name}: generating inputs")
     A, B, C0 = gi.make_inputs(w)
+    bias = gi.make_bias(w)
     say(f"workload {name}: running AUTO on the GPU")
-    st, C = run_gemm("auto", w.dtype, A, B, C0, w.alpha, w.beta, trans_a=w.trans_a,
-                     trans_b=w.trans_b)
+    if w.batch > 1 or bias is not None:
+        # the strided-batch entry point, as the bench times it
+        A3 = A if w.batch > 1 else A[None]
+        B3 = B if w.batch > 1 else B[None]
+        dC = (torch.from_numpy(np.ascontiguousarray(C0, np.float32).reshape(w.batch, w.M, w.N))
+              .cuda() if C0 is not None else torch.zeros((w.batch, w.M, w.N), device="cuda"))
+        dbias = None if bias is None else torch.from_numpy(bias).cuda()
+        st = dgt.gemm_batched(to_dev(A3, w.dtype), to_dev(B3, w.dtype), dC, w.alpha, w.beta,
+                              bias=dbias, trans_a=w.trans_a, trans_b=w.trans_b)
+        torch.cuda.synchronize()
+        C3 = dC.cpu().numpy()
+        del dC
+        problems = [0, w.batch - 1] if w.batch > 1 else [0]
+    else:
+        st, C = run_gemm("auto", w.dtype, A, B, C0, w.alpha, w.beta, trans_a=w.trans_a,
+                         trans_b=w.trans_b)
+        A3, B3, C3, problems = A[None], B[None], C[None], [0]
     assert st == 0
     big = w.M * w.N * w.K > 4e9
     rows = _sample_rows(w.M) if big else list(range(w.M))
-    say(f"workload {name}: oracle on {len(rows)} rows")
-    Ar = A[:, rows] if w.trans_a else A[rows]  # rows of op(A)
-    C0r = C0[rows] if C0 is not None else None
-    R = oracle.gemm(Ar, B, C0r, w.alpha, w.beta, w.dtype, trans_a=w.trans_a,
-                    trans_b=w.trans_b)
-    assert_close(C[rows], R, w.K, w.alpha, w.sigma, w.sigma, what=name)
-    assert np.all(np.isfinite(C))
+    for z in problems:
+        say(f"workload {name}: oracle on {len(rows)} rows of problem {z}")
+        Ar = A3[z][:, rows] if w.trans_a else A3[z][rows]  # rows of op(A)
+        C0r = None
+        if C0 is not None:
+            C0r = np.asarray(C0, np.float32).reshape(w.batch, w.M, w.N)[z][rows]
+        R = oracle.gemm(Ar, B3[z], C0r, w.alpha, w.beta, w.dtype, trans_a=w.trans_a,
+                        trans_b=w.trans_b, bias=None if bias is None else bias[z])
+        assert_close(C3[z][rows], R, w.K, w.alpha, w.sigma, w.sigma, what=f"{name}[{z}]")
+    assert np.all(np.isfinite(C3))
 
 
 @pytest.mark.parametrize("name", ["f32_256", "f32_1000_ragged", "bf16_skinny_8x28672x8192",
