@@ -4,9 +4,11 @@
 One step = one GEMM call C = alpha*A*B + beta*C on the headline workload
 (BF16 inputs, FP32 accumulate/output, M = N = K = 8192), inputs already
 resident in HBM.  W untimed warm-up calls (the pages ask for warm-up before
-quoting numbers: dilfish.github.io 5.7), then K timed calls bracketed by
-device synchronisation, timed with HIP events on the stream the kernels run
-on.  TFLOP/s = 2MNK / time (chongfengling.github.io section 1 counts K
+quoting numbers: dilfish.github.io 5.7; here they also let the power-managed
+clock settle, which takes some 40-80 calls of the 8192^3 GEMM after the GPU
+has idled while the next inputs were generated), then K timed calls
+bracketed by device synchronisation, timed with HIP events on the stream the
+kernels run on.  TFLOP/s = 2MNK / time (chongfengling.github.io section 1 counts K
 multiplies and K adds per output; 2*2048^3 = 17.18e9 in its section 2.5).
 
 The same JSON line carries, under "also", the FP32 4096^3 case (against the
@@ -267,8 +269,11 @@ def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    # The power-managed clock overshoots and then settles over the first
+    # ~40-80 launches of an 8192^3 GEMM after the GPU has idled (per-launch
+    # times 0.82, 1.1, ..., 0.81 ms); 100 untimed launches reach steady state.
+    ap.add_argument("--warmup", type=int, default=100)
     ap.add_argument("--only", default=None, help="time a single workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--copy-calibration", action="store_true")

@@ -210,8 +210,10 @@ constexpr int prologue_after() {
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
 template <In T, bool TA, bool TB>
-__global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_n) {
-    select_problem(p);
+__global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_n,
+                                                          int grouped) {
+    const TileIdx tile = xcd_tile(p.M / BM, tiles_n, grouped != 0);
+    select_problem(p, tile.z);
     constexpr bool AK = !TA, BKc = TB;
     using OpA = typename std::conditional<AK, KcOperand, MnOperand>::type;
     using OpB = typename std::conditional<BKc, KcOperand, MnOperand>::type;
@@ -230,8 +232,8 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-    const int m0 = (blockIdx.x / tiles_n) * BM;
-    const int n0 = (blockIdx.x % tiles_n) * BN;
+    const int m0 = tile.bm * BM;
+    const int n0 = tile.bn * BN;
     const int nk = p.K / BK;  // slices
 
     OpA opa;
@@ -383,8 +385,10 @@ hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        // linear order only for one problem with both operands k-contiguous
+        const int grouped = !(p.batch == 1 && !TA && TB);
         hipLaunchKernelGGL((mfma16_dma_kernel<T, TA, TB>), dim3((unsigned)blocks, p.batch),
-                           dim3(NT), 0, s, p, tiles_n);
+                           dim3(NT), 0, s, p, tiles_n, grouped);
         return hipGetLastError();
     });
 }
