@@ -54,7 +54,7 @@ HBM_PEAK_GBS = 8000.0
 PRIMARY = "bf16_8192"
 SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
              "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
-             "bf16_bmm_16x2048"]
+             "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt"]
 
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
@@ -67,16 +67,19 @@ DOMINANT = {
                  r"mfma16_dma_kernel<\(dgt::In\)2, false, false>"),
     "f32_4096": ("mfma_f32_kernel<NN>", "k_mfma_f32.hip",
                  r"mfma_f32_kernel<true, false, false, false>"),
-    "bf16_skinny_8x28672x8192": ("skinny16_kernel<BF16, NN>", "k_skinny.hip",
-                                 r"skinny16_kernel<\(dgt::In\)1, true, false, false>"),
+    "bf16_skinny_8x28672x8192": ("skinny16_kernel<BF16, NN, 1 row block>", "k_skinny16.hip",
+                                 r"skinny16_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_8192_nt": ("mfma16_dma_kernel<BF16, NT>", "k_mfma_bf16_dma.hip",
                      r"mfma16_dma_kernel<\(dgt::In\)1, false, true>"),
     "bf16_8192_tn": ("mfma16_dma_kernel<BF16, TN>", "k_mfma_bf16_dma.hip",
                      r"mfma16_dma_kernel<\(dgt::In\)1, true, false>"),
-    "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT>", "k_skinny.hip",
-                                    r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false>"),
+    "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 1 row block>", "k_skinny16.hip",
+                                    r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
                                  r"mfma16_dma_kernel<\(dgt::In\)1, false, true>"),
+    "bf16_decode_64x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 4 row blocks>",
+                                     "k_skinny16.hip",
+                                     r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 4>"),
     "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
                          r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
 }
@@ -126,7 +129,8 @@ def naive_load_requests(M: int, N: int, K: int, wave: int) -> int:
 
 def source_digest(fname: str) -> str:
     h = hashlib.sha256()
-    for f in (fname, "gemm_common.hpp"):
+    extra = ("skinny_common.hpp",) if fname.startswith("k_skinny") else ()
+    for f in (fname, "gemm_common.hpp", *extra):
         with open(os.path.join(ROOT, "dense_gemm_tuning_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -216,6 +220,13 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
     return res, (A, B, C0)
 
 
+def streams_b(w) -> bool:
+    """Shapes the skinny path runs (M <= 64): bound by streaming B from HBM
+    once, so their roofline is HBM bandwidth; the bench alternates two copies
+    of B so the 256 MB Infinity Cache cannot serve it."""
+    return w.M <= 64
+
+
 def roofline(w, ms_avg):
     kern, _, _ = DOMINANT[w.name]
     fl = gemm_flops(w.M, w.N, w.K) * w.batch
@@ -223,7 +234,7 @@ def roofline(w, ms_avg):
     if w.bias:
         by += w.N * 4 * w.batch
     traffic = read_traffic(w.name)
-    if w.name.startswith("bf16_skinny"):
+    if streams_b(w):
         ach = by / (ms_avg * 1e-3) / 1e9
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS,
                 "unit": "GB/s", "frac": round(ach / HBM_PEAK_GBS, 4),
@@ -303,7 +314,7 @@ def main(argv=None):
     results = {}
     for name in names:
         w = gi.WORKLOADS[name]
-        copies = 2 if name.startswith("bf16_skinny") else 1  # B > 256 MB cache
+        copies = 2 if streams_b(w) else 1  # B > 256 MB cache
         log(f"[{name}] {w.M}x{w.N}x{w.K} {w.dtype}: warmup {args.warmup}, steps {args.steps}")
         res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies)
         res["roofline"] = roofline(w, res["ms_avg"])
@@ -327,7 +338,7 @@ def main(argv=None):
                  "trans_a": w2.trans_a, "trans_b": w2.trans_b, "batch": w2.batch,
                  "bias": w2.bias, "ms_per_step": round(r2["ms_avg"], 5),
                  "tflops": round(r2["tflops"], 2), "roofline": r2["roofline"]}
-        if name.startswith("bf16_skinny"):
+        if streams_b(w2):
             entry["gbs"] = r2["roofline"]["achieved"]
         also.append(entry)
 

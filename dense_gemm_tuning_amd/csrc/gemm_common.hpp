@@ -173,8 +173,8 @@ template <In T> hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s)
 hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s);
 template <In T> hipError_t launch_skinny16(const GemmParams& p, hipStream_t s);
 
-// Largest M the skinny (decode) path accepts.
-constexpr int kSkinnyMaxM = 16;
+// Largest M the skinny (decode) path accepts: four blocks of 16 rows.
+constexpr int kSkinnyMaxM = 64;
 
 // True when every row start of a row-major operand is 16-byte aligned, so
 // 128-bit loads are legal at any chunk whose column is a multiple of

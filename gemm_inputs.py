@@ -214,6 +214,11 @@ WORKLOADS = {
                                          bias=True),
     "bf16_bmm_16x2048": Workload("bf16_bmm_16x2048", "bf16", 2048, 2048, 2048, 1.0, 0.0,
                                  "normal", seed_base=11000, batch=16),
+    # A mid-size decode batch (64 rows) against the same [out, in] weight:
+    # still bound by streaming the weight once (64 FLOP per byte of it).
+    "bf16_decode_64x28672x8192_nt": Workload("bf16_decode_64x28672x8192_nt", "bf16", 64, 28672,
+                                             8192, 1.0, 0.0, "normal", sigma=0.02,
+                                             seed_base=12000, trans_b=True),
 }
 
 

@@ -93,7 +93,7 @@ enum gemm_status {
  * gemm_f32 / gemm_bf16 / gemm_f16 use).  Every variant computes the same operation
  * and handles any shape that it accepts, ragged edges included. */
 enum gemm_variant {
-    GEMM_VARIANT_AUTO = 0,      /* MFMA tiles; skinny path when M <= 16       */
+    GEMM_VARIANT_AUTO = 0,      /* MFMA tiles; skinny path when M <= 64       */
     GEMM_VARIANT_NAIVE = 1,     /* one lane per output, K-loop of two global
                                    loads and an FMA (dilfish.github.io 5.2;
                                    chongfengling.github.io 2.1 and 2.4:
@@ -107,10 +107,11 @@ enum gemm_variant {
                                    per-wavefront MFMA micro-tiles, masked
                                    ragged edges (dilfish.github.io 5.4-5.5;
                                    qwbw.cn section 三)                        */
-    GEMM_VARIANT_SKINNY = 4     /* M <= 16: streams B once from HBM, A held in
-                                   registers per step, K split over waves
-                                   and reduced in LDS (dilfish.github.io 5.1
-                                   GEMV row; qwbw.cn section 四)              */
+    GEMM_VARIANT_SKINNY = 4     /* M <= 64: streams B once from HBM, A held in
+                                   registers per step (up to four 16-row
+                                   blocks), K split over waves and reduced
+                                   in LDS (dilfish.github.io 5.1 GEMV row and
+                                   batching; qwbw.cn section 四)              */
 };
 
 /* C <- alpha*A*B + beta*C, fp32 inputs, fp32 accumulate/output. */
@@ -131,7 +132,7 @@ int gemm_f16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
              void* stream);
 
 /* Same as gemm_f32 / gemm_bf16 / gemm_f16 with an explicit ladder rung (enum
- * gemm_variant).  GEMM_VARIANT_SKINNY requires M <= 16 and returns
+ * gemm_variant).  GEMM_VARIANT_SKINNY requires M <= 64 and returns
  * GEMM_ERR_VARIANT otherwise. */
 int gemm_f32_variant(int variant, int M, int N, int K, float alpha,
                      const float* A, int lda, const float* B, int ldb,

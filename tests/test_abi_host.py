@@ -80,10 +80,10 @@ def test_variant_checks(lib):
     v = dgt.gemm_f32_variant
     assert v(99, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
     assert v(-1, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
-    # the skinny rung takes at most 16 rows
-    assert v(dgt.VARIANT_SKINNY, 17, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
+    # the skinny rung takes at most 64 rows
+    assert v(dgt.VARIANT_SKINNY, 65, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
     for fn in (dgt.gemm_bf16_variant, dgt.gemm_f16_variant):
-        assert fn(dgt.VARIANT_SKINNY, 17, 4, 4, 1.0, A_, 4, B_, 4, 0.0,
+        assert fn(dgt.VARIANT_SKINNY, 65, 4, 4, 1.0, A_, 4, B_, 4, 0.0,
                   C_, 4) == dgt.GEMM_ERR_VARIANT
         assert fn(99, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
 
@@ -102,7 +102,8 @@ def test_auto_dispatch(lib):
     assert sel(BF16, 0, 1, 8, 28672, 8192, 8192, 8192, 28672) == dgt.VARIANT_SKINNY
     assert sel(F16, 0, 0, 8, 28672, 8192, 8192, 28672, 28672) == dgt.VARIANT_SKINNY
     assert sel(BF16, 0, 0, 16, 100, 100, 100, 100, 100) == dgt.VARIANT_SKINNY
-    assert sel(BF16, 0, 0, 17, 100, 100, 100, 100, 100) == dgt.VARIANT_MFMA
+    assert sel(BF16, 0, 0, 64, 100, 100, 100, 100, 100) == dgt.VARIANT_SKINNY
+    assert sel(BF16, 0, 0, 65, 100, 100, 100, 100, 100) == dgt.VARIANT_MFMA
     assert sel(F16, 1, 1, 8192, 8192, 8192, 8192, 8192, 8192) == dgt.VARIANT_MFMA
     assert sel(F32, 0, 0, 4096, 4096, 4096, 4096, 4096, 4096) == dgt.VARIANT_MFMA
     assert sel(F32, 0, 0, 4, 4, 4, 3, 4, 4) == dgt.GEMM_ERR_LD
@@ -136,7 +137,7 @@ def test_transposed_leading_dimensions(lib, dtype):
     assert ex(dtype, 0, 3, 0, -1, N, K, 1.0, A_, K, B_, N, 0.0, C_, N) == dgt.GEMM_ERR_ARG
     assert ex(7, 0, 0, 0, M, N, K, 1.0, A_, K, B_, N, 0.0, C_, N) == dgt.GEMM_ERR_ARG
     assert ex(dtype, 0, 0, 9, M, N, K, 1.0, A_, K, B_, N, 0.0, C_, N) == dgt.GEMM_ERR_VARIANT
-    assert ex(dtype, 1, 1, dgt.VARIANT_SKINNY, 17, N, K, 1.0, A_, 17, B_, K, 0.0, C_, N) == \
+    assert ex(dtype, 1, 1, dgt.VARIANT_SKINNY, 65, N, K, 1.0, A_, 65, B_, K, 0.0, C_, N) == \
         dgt.GEMM_ERR_VARIANT
 
 
@@ -197,5 +198,5 @@ def test_strided_batched_argument_checks(lib):
     assert call(bias=bias, sbias=N, C=bias + 4 * (2 * N + 1)) == dgt.GEMM_ERR_OVERLAP
     # A and B may overlap each other and repeat: only C's writes matter
     assert call(B=A_, sb=0, C=0) == dgt.GEMM_ERR_NULL
-    # skinny rung still limited to M <= 16
-    assert call(variant=dgt.VARIANT_SKINNY, M=17, sc=17 * N) == dgt.GEMM_ERR_VARIANT
+    # skinny rung still limited to M <= 64
+    assert call(variant=dgt.VARIANT_SKINNY, M=65, sc=65 * N) == dgt.GEMM_ERR_VARIANT

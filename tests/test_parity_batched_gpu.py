@@ -58,7 +58,7 @@ def dev3(x, dtype):
 def test_batched_integer_bit_exact(variant, dtype, layout, bias_mode):
     ta, tb = LAYOUTS[layout]
     nb = 3
-    shapes = ([(8, 300, 256), (13, 128, 64)] if variant == "skinny"
+    shapes = ([(8, 300, 256), (13, 128, 64), (36, 256, 256)] if variant == "skinny"
               else [(65, 129, 127), (256, 256, 256)])
     for idx, (M, N, K) in enumerate(shapes):
         say(f"batched {variant} {dtype} {layout} bias={bias_mode} {nb}x{M}x{N}x{K}")

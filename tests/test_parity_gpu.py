@@ -44,7 +44,7 @@ def _gpu():
 
 
 def supports(variant, M):
-    return not (variant == "skinny" and M > 16)
+    return not (variant == "skinny" and M > 64)
 
 
 def ints(seed, r, c, dtype):
@@ -82,7 +82,7 @@ def test_permutation_and_rank1(variant, dtype):
     """Swapped rows/columns or transposed fragments cannot pass these."""
     rng = np.random.default_rng(7)
     one = 1.0 if dtype == "f32" else bits16([1.0], dtype)[0]
-    for (M, N, K) in [(16, 300, 272), (256, 256, 256), (130, 70, 130)]:
+    for (M, N, K) in [(16, 300, 272), (256, 256, 256), (130, 70, 130), (48, 300, 272)]:
         if not supports(variant, M):
             continue
         say(f"perm/rank1 {variant} {dtype} {M}x{N}x{K}")
@@ -116,7 +116,8 @@ def test_permutation_and_rank1(variant, dtype):
 def test_real_inputs_within_tolerance(variant, dtype):
     dist = "uniform" if dtype == "f32" else "normal"
     for (M, N, K, alpha, beta) in [(300, 520, 777, 1.0, 0.0), (16, 1000, 1000, 1.5, 0.5),
-                                   (513, 257, 1030, -0.5, 2.0)]:
+                                   (513, 257, 1030, -0.5, 2.0), (40, 700, 1000, -1.0, 1.0),
+                                   (64, 384, 2048, 1.0, 0.0)]:
         if not supports(variant, M):
             continue
         say(f"real parity {variant} {dtype} {M}x{N}x{K}")
@@ -290,6 +291,6 @@ def test_status_codes_on_gpu():
     A = torch.zeros((4, 4), device="cuda")
     C = torch.zeros((4, 4), device="cuda")
     assert dgt.gemm(A, A, C, variant="skinny") == 0
-    big = torch.zeros((17, 4), device="cuda")
-    assert dgt.gemm(big, A, torch.zeros((17, 4), device="cuda"), variant="skinny") == dgt.GEMM_ERR_VARIANT
+    big = torch.zeros((65, 4), device="cuda")
+    assert dgt.gemm(big, A, torch.zeros((65, 4), device="cuda"), variant="skinny") == dgt.GEMM_ERR_VARIANT
     assert dgt.gemm(A, A, A) == dgt.GEMM_ERR_OVERLAP

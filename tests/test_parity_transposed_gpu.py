@@ -34,7 +34,8 @@ LAYOUTS = {"nt": (False, True), "tn": (True, False), "tt": (True, True)}
 
 SHAPES = [(1, 1, 1), (15, 17, 16), (17, 65, 65), (65, 129, 127), (128, 256, 256),
           (300, 260, 520), (256, 512, 384), (512, 256, 256)]
-SKINNY_SHAPES = [(1, 1, 1), (15, 17, 16), (8, 200, 300), (16, 384, 256), (5, 1000, 129)]
+SKINNY_SHAPES = [(1, 1, 1), (15, 17, 16), (8, 200, 300), (16, 384, 256), (5, 1000, 129),
+                 (17, 130, 96), (33, 384, 256), (48, 257, 300), (64, 512, 512)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -83,7 +84,7 @@ def test_integer_inputs_bit_exact(variant, dtype, layout):
 def test_real_inputs_within_tolerance(variant, dtype, layout):
     ta, tb = LAYOUTS[layout]
     dist = "uniform" if dtype == "f32" else "normal"
-    cases = ([(16, 1000, 1000, 1.5, 0.5)] if variant == "skinny"
+    cases = ([(16, 1000, 1000, 1.5, 0.5), (50, 640, 1024, 1.0, 0.0)] if variant == "skinny"
              else [(300, 520, 777, 1.0, 0.0), (512, 512, 1024, -0.5, 2.0)])
     for (M, N, K, alpha, beta) in cases:
         say(f"real parity {variant} {dtype} {layout} {M}x{N}x{K}")
@@ -105,7 +106,7 @@ def test_selection_matrices(variant, dtype, layout):
     op(B) = column selection T (T[q[j], j] = 1): C = columns q of op(A)."""
     ta, tb = LAYOUTS[layout]
     rng = np.random.default_rng(17)
-    shapes = ([(16, 300, 272)] if variant == "skinny"
+    shapes = ([(16, 300, 272), (64, 256, 384)] if variant == "skinny"
               else [(256, 256, 256), (130, 70, 130), (512, 256, 384)])
     dist = "uniform" if dtype == "f32" else "normal"
     for (M, N, K) in shapes:
