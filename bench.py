@@ -54,7 +54,8 @@ HBM_PEAK_GBS = 8000.0
 PRIMARY = "bf16_8192"
 SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
              "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
-             "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt"]
+             "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt", "f32_1000_splitk",
+             "bf16_splitk_1024x1024x16384"]
 
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
@@ -80,6 +81,11 @@ DOMINANT = {
     "bf16_decode_64x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 4 row blocks>",
                                      "k_skinny16.hip",
                                      r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 4>"),
+    "f32_1000_splitk": ("mfma_f32_kernel<NN, guarded> x 8 K slices + reduce (per call)",
+                        "k_mfma_f32.hip", r"mfma_f32_kernel<true, true, false, false>"),
+    "bf16_splitk_1024x1024x16384": ("mfma16_dma_kernel<BF16, NN> x 16 K slices + reduce "
+                                    "(per call)", "k_mfma_bf16_dma.hip",
+                                    r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
     "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
                          r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
 }
@@ -175,7 +181,14 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
     sptr = stream.cuda_stream
     lda, ldb = w.a_shape[1], w.b_shape[1]  # packed stored rows
     code = {"f32": dgt.DTYPE_F32, "bf16": dgt.DTYPE_BF16, "f16": dgt.DTYPE_F16}[w.dtype]
-    if w.batch > 1 or bias is not None:
+    if w.splits != 1:
+        need = dgt.gemm_splitk_workspace_size(code, w.M, w.N, w.K, w.splits)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")  # outside the timing
+
+        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s):
+            return dgt.gemm_splitk(code, w.trans_a, w.trans_b, M, N, K, alpha, A, lda, B, ldb,
+                                   beta, C, ldc, w.splits, ws.data_ptr(), need, s)
+    elif w.batch > 1 or bias is not None:
         def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s):
             return dgt.gemm_strided_batched(
                 code, w.trans_a, w.trans_b, dgt.VARIANT_AUTO, M, N, K, alpha,

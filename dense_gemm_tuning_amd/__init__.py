@@ -32,6 +32,7 @@ GEMM_ERR_OVERLAP = -4
 GEMM_ERR_VARIANT = -5
 GEMM_ERR_LAUNCH = -6
 GEMM_ERR_ARG = -7
+GEMM_ERR_WORKSPACE = -8
 
 VARIANT_AUTO = 0
 VARIANT_NAIVE = 1
@@ -43,7 +44,8 @@ VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
 
 # Every symbol the header declares (the tests check the library exports them).
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",
-           "gemm_f16_variant", "gemm_ex", "gemm_strided_batched", "gemm_select_variant",
+           "gemm_f16_variant", "gemm_ex", "gemm_strided_batched", "gemm_splitk",
+           "gemm_splitk_slices", "gemm_splitk_workspace_size", "gemm_select_variant",
            "gemm_status_string", "gemm_abi_version")
 
 DTYPE_F32 = 0
@@ -81,6 +83,12 @@ def _load() -> ctypes.CDLL:
         lib.gemm_ex.restype = i
         lib.gemm_ex.argtypes = [i, i, i, i, *core]
         i64 = ctypes.c_int64
+        lib.gemm_splitk.restype = i
+        lib.gemm_splitk.argtypes = [i, i, i, *core[:11], i, p, i64, p]
+        lib.gemm_splitk_slices.restype = i
+        lib.gemm_splitk_slices.argtypes = [i, i, i, i, i]
+        lib.gemm_splitk_workspace_size.restype = i64
+        lib.gemm_splitk_workspace_size.argtypes = [i, i, i, i, i]
         lib.gemm_strided_batched.restype = i
         lib.gemm_strided_batched.argtypes = [i, i, i, i, i, i, i, f, p, i, i64, p, i, i64, f,
                                              p, i, i64, p, i64, i, p]
@@ -142,6 +150,21 @@ def gemm_strided_batched(dtype, trans_a, trans_b, variant, M, N, K, alpha, A, ld
                                         M, N, K, alpha, A, lda, stride_a, B, ldb, stride_b,
                                         beta, C, ldc, stride_c, bias, stride_bias, batch,
                                         stream)
+
+
+def gemm_splitk(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                workspace, workspace_bytes, stream=0) -> int:
+    return _load().gemm_splitk(int(dtype), int(trans_a), int(trans_b), M, N, K, alpha, A, lda,
+                               B, ldb, beta, C, ldc, int(splits), workspace,
+                               int(workspace_bytes), stream)
+
+
+def gemm_splitk_slices(dtype, M, N, K, splits) -> int:
+    return _load().gemm_splitk_slices(int(dtype), M, N, K, int(splits))
+
+
+def gemm_splitk_workspace_size(dtype, M, N, K, splits) -> int:
+    return _load().gemm_splitk_workspace_size(int(dtype), M, N, K, int(splits))
 
 
 def gemm_select_variant(dtype, trans_a, trans_b, M, N, K, lda, ldb, ldc) -> int:
@@ -279,3 +302,39 @@ def gemm_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, bias=None,
                                 A2.data_ptr(), pitch(A2), sa, B2.data_ptr(), pitch(B2), sb,
                                 float(beta), C.data_ptr(), pitch(C), C.stride(0),
                                 bias_ptr, sbias, batch, stream)
+
+
+def gemm_split(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0,
+               workspace=None, stream=None, trans_a: bool = False,
+               trans_b: bool = False) -> int:
+    """Split-K form of ``gemm`` on torch tensors (gemm_splitk).  ``workspace``
+    is a device tensor of at least gemm_splitk_workspace_size bytes; when None
+    one is allocated here with torch (the library itself allocates nothing).
+    Returns the status code."""
+    import torch
+
+    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise TypeError("A and B must both be float32, both bfloat16 or both float16")
+    if C.dtype != torch.float32:
+        raise TypeError("C must be float32")
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"C {tuple(C.shape)}")
+    dtype = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
+             torch.float16: DTYPE_F16}[A.dtype]
+    need = gemm_splitk_workspace_size(dtype, M, N, K, splits)
+    if need < 0:
+        return need
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=C.device)
+    ws_ptr = workspace.data_ptr() if workspace is not None else 0
+    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
+    if stream is None:
+        stream = torch.cuda.current_stream().cuda_stream
+    elif hasattr(stream, "cuda_stream"):
+        stream = stream.cuda_stream
+    return gemm_splitk(dtype, trans_a, trans_b, M, N, K, float(alpha), A.data_ptr(), _ld(A),
+                       B.data_ptr(), _ld(B), float(beta), C.data_ptr(), _ld(C), splits,
+                       ws_ptr, ws_bytes, stream)

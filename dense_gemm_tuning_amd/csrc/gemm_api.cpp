@@ -184,9 +184,127 @@ int run1(DType t, int ta, int tb, int variant, int M, int N, int K, float alpha,
     return run(c);
 }
 
+// ------------------------------------------------------------- split-K
+
+// K slices: kc columns of op(A) / rows of op(B) each (a multiple of 128, so
+// every slice keeps the whole-tile kernels' K granularity and 16-byte
+// alignment), the last one shorter when K is not a multiple.
+struct SplitPlan {
+    int splits, kc;
+};
+
+// Workgroup slots of the kernel AUTO picks, and its output tiles.
+void tile_budget(DType t, int M, int N, int64_t& tiles, int64_t& slots) {
+    if (M <= dgt::kSkinnyMaxM) {  // skinny: a column strip per workgroup
+        const int cols = t == DType::F32 ? 64 : 128;
+        tiles = (N + cols - 1) / cols;
+        slots = 256;
+    } else if (t == DType::F32) {  // 128 x 128 tiles, two workgroups per CU
+        tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
+        slots = 512;
+    } else {  // 256 x 256 tiles, one workgroup per CU
+        tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
+        slots = 256;
+    }
+}
+
+constexpr int kSliceAlign = 128;   // K granularity of a slice
+constexpr int kMinSliceK = 128;    // no slice shorter than this when chosen automatically
+constexpr int kMaxSplits = 64;
+
+SplitPlan plan_splitk(DType t, int M, int N, int K, int requested) {
+    if (K <= 0 || requested == 1) return {1, K};
+    int want = requested;
+    if (want == 0) {  // enough slices to fill the workgroup slots
+        int64_t tiles, slots;
+        tile_budget(t, M, N, tiles, slots);
+        const int64_t fill = tiles > 0 ? slots / tiles : 1;
+        const int64_t most = (K + kMinSliceK - 1) / kMinSliceK;  // slices of kMinSliceK
+        want = (int)std::max<int64_t>(1, std::min<int64_t>(fill, most));
+    }
+    want = std::min(want, kMaxSplits);
+    if (want <= 1) return {1, K};
+    int kc = (K + want - 1) / want;
+    kc = (kc + kSliceAlign - 1) / kSliceAlign * kSliceAlign;
+    const int splits = (K + kc - 1) / kc;
+    if (splits <= 1) return {1, K};
+    return {splits, kc};
+}
+
+bool dtype_of(int dtype, DType& t) {
+    if (dtype < GEMM_DTYPE_F32 || dtype > GEMM_DTYPE_F16) return false;
+    t = dtype == GEMM_DTYPE_F32 ? DType::F32 : dtype == GEMM_DTYPE_BF16 ? DType::BF16 : DType::F16;
+    return true;
+}
+
 }  // namespace
 
 extern "C" {
+
+int gemm_splitk_slices(int dtype, int M, int N, int K, int splits) {
+    DType t;
+    if (!dtype_of(dtype, t) || splits < 0) return GEMM_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    return plan_splitk(t, M, N, K, splits).splits;
+}
+
+int64_t gemm_splitk_workspace_size(int dtype, int M, int N, int K, int splits) {
+    const int s = gemm_splitk_slices(dtype, M, N, K, splits);
+    if (s < 0) return s;
+    return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
+
+int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
+                int splits, void* workspace, int64_t workspace_bytes, void* stream) {
+    DType t;
+    if (!dtype_of(dtype, t) || splits < 0 || workspace_bytes < 0) return GEMM_ERR_ARG;
+    int st = check_shape(trans_a, trans_b, M, N, K, lda, ldb, ldc);
+    if (st != GEMM_OK) return st;
+    const SplitPlan plan = plan_splitk(t, M, N, K, splits);
+    const bool reads_ab = alpha != 0.0f && K > 0;
+    if (plan.splits == 1 || !reads_ab || M == 0 || N == 0)
+        return run1(t, trans_a, trans_b, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb,
+                    beta, C, ldc, stream);
+    if (C == nullptr || A == nullptr || B == nullptr) return GEMM_ERR_NULL;
+    const int64_t ws_need = (int64_t)plan.splits * M * N * 4;
+    if (workspace == nullptr || workspace_bytes < ws_need) return GEMM_ERR_WORKSPACE;
+    float* W = static_cast<float*>(workspace);
+    const int esz = elem_size(t);
+    const Range rw = batch_range(W, (uint64_t)ws_need, 0, 1);
+    const Range rc = batch_range(C, span_bytes(M, N, ldc, 4), 0, 1);
+    const uint64_t a_span = trans_a ? span_bytes(K, M, lda, esz) : span_bytes(M, K, lda, esz);
+    const uint64_t b_span = trans_b ? span_bytes(N, K, ldb, esz) : span_bytes(K, N, ldb, esz);
+    if (overlaps(rw, rc) || overlaps(rw, batch_range(A, a_span, 0, 1)) ||
+        overlaps(rw, batch_range(B, b_span, 0, 1)))
+        return GEMM_ERR_OVERLAP;
+
+    // Phase 1: slice z covers k in [z*kc, z*kc + K_z): a strided batch of the
+    // equal slices, then the shorter last one, each into W + z*M*N.
+    const int64_t sa = trans_a ? (int64_t)plan.kc * lda : plan.kc;   // elements
+    const int64_t sb = trans_b ? plan.kc : (int64_t)plan.kc * ldb;
+    const int last_k = K - (plan.splits - 1) * plan.kc;
+    const int full = last_k == plan.kc ? plan.splits : plan.splits - 1;
+    Call c{t, trans_a, trans_b, GEMM_VARIANT_AUTO, M, N, plan.kc, 1.0f, 0.0f, A, lda, sa, B,
+           ldb, sb, W, N, (int64_t)M * N, nullptr, 0, full, stream};
+    st = run(c);
+    if (st != GEMM_OK) return st;
+    if (full < plan.splits) {
+        Call l = c;
+        l.K = last_k;
+        l.A = static_cast<const char*>(A) + (int64_t)full * sa * esz;
+        l.B = static_cast<const char*>(B) + (int64_t)full * sb * esz;
+        l.C = W + (int64_t)full * M * N;
+        l.batch = 1;
+        st = run(l);
+        if (st != GEMM_OK) return st;
+    }
+    // Phase 2: C <- alpha * sum_z W_z + beta * C, in slice order.
+    const hipError_t e = dgt::launch_splitk_reduce(W, plan.splits, M, N, alpha, beta, C, ldc,
+                                                   static_cast<hipStream_t>(stream));
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 
 int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
              const float* B, int ldb, float beta, float* C, int ldc, void* stream) {
@@ -270,7 +388,8 @@ const char* gemm_status_string(int status) {
         case GEMM_ERR_OVERLAP: return "GEMM_ERR_OVERLAP: C overlaps A or B";
         case GEMM_ERR_VARIANT: return "GEMM_ERR_VARIANT: variant unknown or unsupported for this shape";
         case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: the HIP runtime rejected the launch";
-        case GEMM_ERR_ARG: return "GEMM_ERR_ARG: unknown dtype or transpose flag";
+        case GEMM_ERR_ARG: return "GEMM_ERR_ARG: unknown dtype or transpose flag, negative batch, splits or size, or stride out of range";
+        case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: workspace missing or smaller than gemm_splitk_workspace_size";
         default: return "unknown gemm status";
     }
 }

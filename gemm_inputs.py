@@ -156,6 +156,7 @@ class Workload:
     trans_b: bool = False   # B stored N x K (op(B) = B^T)
     batch: int = 1          # independent problems, stacked on a leading axis
     bias: bool = False      # a bias row of N floats per problem
+    splits: int = 1         # split-K request (1: none, 0: automatic)
 
     @property
     def a_shape(self):
@@ -219,6 +220,12 @@ WORKLOADS = {
     "bf16_decode_64x28672x8192_nt": Workload("bf16_decode_64x28672x8192_nt", "bf16", 64, 28672,
                                              8192, 1.0, 0.0, "normal", sigma=0.02,
                                              seed_base=12000, trans_b=True),
+    # Too few output tiles to fill the GPU: split-K (automatic slice count).
+    "f32_1000_splitk": Workload("f32_1000_splitk", "f32", 1000, 1000, 1000, 1.5, 0.5,
+                                "uniform", seed_base=13000, splits=0),
+    "bf16_splitk_1024x1024x16384": Workload("bf16_splitk_1024x1024x16384", "bf16", 1024, 1024,
+                                            16384, 1.0, 0.0, "normal", seed_base=14000,
+                                            splits=0),
 }
 
 

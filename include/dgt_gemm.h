@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 4
+#define DGT_GEMM_ABI_VERSION 5
 
 /* Input formats (the dtype argument of gemm_ex and gemm_select_variant). */
 enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };
@@ -84,9 +84,12 @@ enum gemm_status {
     GEMM_ERR_VARIANT = -5,      /* unknown variant, or one that does not
                                    support this shape / size                 */
     GEMM_ERR_LAUNCH = -6,       /* the HIP runtime rejected a kernel launch  */
-    GEMM_ERR_ARG = -7           /* dtype not a gemm_dtype, a transpose flag
-                                   other than 0 or 1, a negative batch, or a
-                                   stride outside [0, 2^48)                  */
+    GEMM_ERR_ARG = -7,          /* dtype not a gemm_dtype, a transpose flag
+                                   other than 0 or 1, a negative batch,
+                                   splits or workspace size, or a stride
+                                   outside [0, 2^48)                         */
+    GEMM_ERR_WORKSPACE = -8     /* gemm_splitk: workspace NULL or smaller
+                                   than gemm_splitk_workspace_size           */
 };
 
 /* Kernel ladder (for measurement and tests; GEMM_VARIANT_AUTO is what
@@ -178,6 +181,38 @@ int gemm_strided_batched(int dtype, int trans_a, int trans_b, int variant,
                          float beta, float* C, int ldc, int64_t stride_c,
                          const float* bias, int64_t stride_bias, int batch,
                          void* stream);
+
+/* Split-K, for shapes with too few output tiles to fill the GPU (e.g. a
+ * small M x N with a long K).  Same operation and arguments as gemm_ex with
+ * GEMM_VARIANT_AUTO, computed in two phases queued on `stream`: the K range
+ * is cut into slices (whole multiples of 128 except the last), each slice's
+ * product is written to the caller's `workspace` as fp32 partials (M x N
+ * per slice), and a second kernel sums the slices in a fixed order and
+ * applies alpha and beta -- deterministic, no atomics, nothing allocated.
+ * The pages do not describe split-K; they note that a launch whose blocks
+ * are partly idle leaves compute unused (elainafan.one "朴素 CUDA 实现",
+ * after the launch code), and this is the case where the whole grid is too
+ * small: the reduction dimension supplies the missing parallelism.
+ * `splits` = 0 picks the number of slices that fills the GPU's workgroup
+ * slots (each slice at least 128 deep); a positive value is a request (at
+ * most 64; rounding of the slice length may give fewer).  With one slice
+ * the call is gemm_ex and needs no workspace.  The workspace (device
+ * memory, 16-byte aligned, at least gemm_splitk_workspace_size bytes) must
+ * not overlap A, B or C and must stay untouched until the work on `stream`
+ * has finished; its contents on return are unspecified. */
+int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K,
+                float alpha, const void* A, int lda, const void* B, int ldb,
+                float beta, float* C, int ldc, int splits, void* workspace,
+                int64_t workspace_bytes, void* stream);
+
+/* Number of K slices gemm_splitk uses for this shape and request (>= 1), or
+ * a negative status.  Host only. */
+int gemm_splitk_slices(int dtype, int M, int N, int K, int splits);
+
+/* Bytes of workspace gemm_splitk needs for this shape and request: slices x
+ * M x N x 4, or 0 with one slice; a negative status for bad arguments.
+ * Host only. */
+int64_t gemm_splitk_workspace_size(int dtype, int M, int N, int K, int splits);
 
 /* The rung GEMM_VARIANT_AUTO picks for this call (dtype: enum gemm_dtype;
  * trans_a, trans_b as for gemm_ex), or a negative status if the arguments

@@ -39,8 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 4
-    for code in range(0, -8, -1):
+    assert dgt.gemm_abi_version() == 5
+    for code in range(0, -9, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
     assert dgt.gemm_status_string(12345) == "unknown gemm status"
@@ -200,3 +200,57 @@ def test_strided_batched_argument_checks(lib):
     assert call(B=A_, sb=0, C=0) == dgt.GEMM_ERR_NULL
     # skinny rung still limited to M <= 64
     assert call(variant=dgt.VARIANT_SKINNY, M=65, sc=65 * N) == dgt.GEMM_ERR_VARIANT
+
+
+def test_splitk_planning(lib):
+    sl, ws = dgt.gemm_splitk_slices, dgt.gemm_splitk_workspace_size
+    F32, BF16 = dgt.DTYPE_F32, dgt.DTYPE_BF16
+    # 1000^3 fp32: 64 tiles of 128 x 128 for 512 workgroup slots -> 8 slices
+    # of 128 (the last 104 deep)
+    assert sl(F32, 1000, 1000, 1000, 0) == 8
+    assert ws(F32, 1000, 1000, 1000, 0) == 8 * 1000 * 1000 * 4
+    # 1024 x 1024 bf16 with K = 16384: 16 tiles of 256 x 256 -> 16 slices
+    assert sl(BF16, 1024, 1024, 16384, 0) == 16
+    # enough tiles already, or K too short to split: one slice, no workspace
+    assert sl(BF16, 8192, 8192, 8192, 0) == 1 and ws(BF16, 8192, 8192, 8192, 0) == 0
+    assert sl(F32, 1000, 1000, 128, 0) == 1       # one 128-deep slice covers K
+    # requests: slice length rounds up to a multiple of 128
+    assert sl(F32, 100, 100, 1000, 3) == 3       # 3 x 384 >= 1000
+    assert sl(F32, 100, 100, 1000, 7) == 4       # ceil(1000/7) = 143 rounds up to 256: 4 slices
+    assert sl(F32, 100, 100, 300, 5) == 3        # 128-deep slices: 128, 128, 44
+    assert sl(F32, 100, 100, 1000, 1) == 1
+    assert 32 < sl(F32, 100, 100, 100000, 1000) <= 64  # capped at 64 (rounding: 61)
+    assert sl(F32, 100, 100, 1000, -1) == dgt.GEMM_ERR_ARG
+    assert sl(9, 100, 100, 1000, 0) == dgt.GEMM_ERR_ARG
+    assert sl(F32, -1, 100, 1000, 0) == dgt.GEMM_ERR_DIM
+
+
+def test_splitk_argument_checks(lib):
+    f = dgt.gemm_splitk
+    M, N, K = 64, 64, 4096
+    need = dgt.gemm_splitk_workspace_size(0, M, N, K, 4)
+    assert need == 4 * M * N * 4
+    W = 0x800000
+    args = lambda **kw: dict(dict(dtype=0, ta=0, tb=0, M=M, N=N, K=K, alpha=1.0, A=A_, lda=K,
+                                  B=B_, ldb=N, beta=0.0, C=C_, ldc=N, splits=4, ws=W,
+                                  wsb=need), **kw)
+
+    def call(**kw):
+        a = args(**kw)
+        return f(a["dtype"], a["ta"], a["tb"], a["M"], a["N"], a["K"], a["alpha"], a["A"],
+                 a["lda"], a["B"], a["ldb"], a["beta"], a["C"], a["ldc"], a["splits"], a["ws"],
+                 a["wsb"])
+
+    assert call(splits=-1) == dgt.GEMM_ERR_ARG
+    assert call(wsb=-1) == dgt.GEMM_ERR_ARG
+    assert call(dtype=3) == dgt.GEMM_ERR_ARG
+    assert call(lda=K - 1) == dgt.GEMM_ERR_LD
+    assert call(ws=0) == dgt.GEMM_ERR_WORKSPACE
+    assert call(wsb=need - 4) == dgt.GEMM_ERR_WORKSPACE
+    assert call(C=0) == dgt.GEMM_ERR_NULL
+    assert call(ws=C_ + 64) == dgt.GEMM_ERR_OVERLAP           # workspace overlaps C
+    assert call(ws=A_ - 64) == dgt.GEMM_ERR_OVERLAP           # ... or A
+    # one slice is plain gemm_ex: no workspace needed (stops at the NULL C)
+    assert call(splits=1, ws=0, wsb=0, C=0) == dgt.GEMM_ERR_NULL
+    # empty C: nothing to do
+    assert call(M=0, A=0, B=0, C=0, ws=0) == dgt.GEMM_OK

@@ -144,7 +144,15 @@ def test_workload_configs(name):
     A, B, C0 = gi.make_inputs(w)
     bias = gi.make_bias(w)
     say(f"workload {name}: running AUTO on the GPU")
-    if w.batch > 1 or bias is not None:
+    if w.splits != 1:
+        # split-K, as the bench times it
+        dC = (torch.from_numpy(np.ascontiguousarray(C0, np.float32)).cuda() if C0 is not None
+              else torch.zeros((w.M, w.N), device="cuda"))
+        st = dgt.gemm_split(to_dev(A, w.dtype), to_dev(B, w.dtype), dC, w.alpha, w.beta,
+                            splits=w.splits, trans_a=w.trans_a, trans_b=w.trans_b)
+        torch.cuda.synchronize()
+        A3, B3, C3, problems = A[None], B[None], dC.cpu().numpy()[None], [0]
+    elif w.batch > 1 or bias is not None:
         # the strided-batch entry point, as the bench times it
         A3 = A if w.batch > 1 else A[None]
         B3 = B if w.batch > 1 else B[None]
