@@ -7,10 +7,14 @@
 // qwbw.cn Level 2), with a deeper software pipeline than the pages' double
 // buffer (dilfish.github.io 5.4; qwbw.cn's double-buffering row):
 //
-//  * K advances in slices of 32.  Copies use global_load_lds_dwordx4: lane
-//    l's 16 bytes land at LDS base + 16*l, so one instruction fills 1 KiB and
-//    no operand byte passes through a VGPR; a swizzle is applied by the
-//    choice of which global chunk each lane fetches.
+//  * K advances in slices of 32.  Copies use buffer_load_dwordx4 ... lds:
+//    lane l's 16 bytes land at LDS base + 16*l, so one instruction fills
+//    1 KiB and no operand byte passes through a VGPR; a swizzle is applied by
+//    the choice of which global chunk each lane fetches.  Each wave addresses
+//    its rows through a buffer descriptor (wave-uniform base, 32-bit lane
+//    offsets, range-checked by the hardware); against the same copies as
+//    global_load_lds the L2 requests return sooner and the kernel is ~2%
+//    faster.
 //  * An operand is staged by how it is stored, not by whether it is A or B.
 //    K-contiguous (A as M x K, B transposed as N x K): two LDS stages of two
 //    slices each, 256 rows of 128 B (chunk q of row r at q ^ ((r ^ r>>3) & 7)),
@@ -25,9 +29,9 @@
 //    5.5).  Either way 64 KiB per operand, 128 KiB of the 160 KiB LDS.
 //  * Copies start as soon as a stage is retired, 1.25 to 2.5 slices (1200 to
 //    2500 MFMA cycles) before the data is needed, which covers L2-miss
-//    latency to the memory side.  Each wave's copies are spread one or two
-//    per 4 MFMAs; issued in a burst they queue at the address unit and hold
-//    back the wave's MFMA issue.  Copies past the last slice re-read the last
+//    latency to the memory side.  Each wave's copies are spread one per two
+//    MFMAs; issued in bursts they queue at the address unit and in L1 and
+//    hold back the wave's MFMA issue.  Copies past the last slice re-read the last
 //    slice (never consumed) so every step waits on the same count.
 //  * Per slice each wavefront issues 32 MFMAs in two 16-deep steps; the LDS
 //    reads of the next step are interleaved with them.  The workgroup
@@ -36,7 +40,9 @@
 //    first operands of slice t+1 are read while step 2 of slice t computes.
 //
 // Used for shapes that are whole tiles (M, N multiples of 256, K of 128) with
-// 16-byte aligned rows; the register-staged kernel handles everything else.
+// 16-byte aligned rows and row pitches below 2^24 elements (so that 64 rows
+// of lane offsets fit 32 bits); the register-staged kernel handles
+// everything else.
 #include "gemm_common.hpp"
 
 namespace dgt {
@@ -48,6 +54,8 @@ constexpr int KC_STAGE = 256 * 2 * BK * 2;  // 32 KiB: 256 rows x 128 B (two sli
 constexpr int MN_STAGE = BK * 256 * 2;      // 16 KiB: 32 k-rows x 512 B (one slice)
 constexpr int KALIGN = BK * NSTAGE;         // K multiple handled here
 constexpr int CPOL = 1;                     // sc0 on the copies
+constexpr int RSRC_W3 = 0x00020000;         // buffer descriptor word 3 (raw 32-bit data)
+constexpr int64_t kMaxPitch = int64_t(1) << 24;  // row pitch limit of the buffer offsets
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
@@ -88,10 +96,13 @@ __device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, 
 // A K-contiguous operand: stage = a pair of slices, 256 rows x 128 B.  Wave w
 // issues copy instructions j = 8w + i (i = 0..7) per pair, instruction j
 // filling rows 8j .. 8j+7 (8 lanes per row).  A pair takes 8 instructions per
-// wave, issued as two halves of 4.
+// wave, issued as two halves of 4.  The wave's descriptor covers its 64 rows;
+// pair pr adds 128*pr bytes through the scalar offset.
 struct KcOperand {
-    const uint16_t* src[8];
-    int off[4][2][2];  // LDS read offset: tile t, slice-in-pair u, step s
+    const uint16_t* base;  // row 64*wave of the tile (wave-uniform)
+    uint32_t voff[8];      // lane byte offsets from base, per instruction
+    uint32_t bytes;        // descriptor range: 64 rows
+    int off[4][2][2];      // LDS read offset: tile t, slice-in-pair u, step s
     int npair;
 
     // mn0: first row (m or n) of the workgroup tile; w: this wave's half of
@@ -102,8 +113,10 @@ struct KcOperand {
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * (8 * wave + i) + (lane >> 3);
             const int q = (lane & 7) ^ swz_kc(row);
-            src[i] = X + (int64_t)(mn0 + row) * ld + 8 * q;
+            voff[i] = (uint32_t)(((int64_t)(row - 64 * wave) * ld + 8 * q) * 2);
         }
+        base = X + (int64_t)(mn0 + 64 * wave) * ld;
+        bytes = (uint32_t)(64 * ld * 2);
         // rows w*128 + t*32 + l%32; half-wave h reads chunk 4u + 2s + h
         const int h = lane >> 5;
 #pragma unroll
@@ -120,11 +133,12 @@ struct KcOperand {
     // Half `half` of pair pr into stage st (past the end: the last pair).
     __device__ void copy(uint8_t* st, int pr, int half, int wave) const {
         pr = pr < npair ? pr : npair - 1;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, RSRC_W3);
 #pragma unroll
         for (int i = 4 * half; i < 4 * half + 4; ++i)
-            __builtin_amdgcn_global_load_lds(src[i] + (int64_t)pr * (2 * BK),
-                                             (lds_void*)(st + (8 * wave + i) * 1024), 16, 0,
-                                             CPOL);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
+                                                     voff[i], (uint32_t)pr * (2 * BK * 2), 0, CPOL);
     }
     // Operands of step s of the slice in half u of stage st.
     __device__ void frags(const uint8_t* st, int u, int s, u32x4 (&f)[4]) const {
@@ -138,7 +152,9 @@ struct KcOperand {
 // issues j = 4w + i (i = 0..3) per slice, instruction j filling k-rows 2j
 // and 2j+1 (32 lanes per row), as two halves of 2.
 struct MnOperand {
-    const uint16_t* src[4];
+    const uint16_t* base;  // k-row 8*wave of slice 0, first column of the tile
+    uint32_t voff[4];      // lane byte offsets from base, per instruction
+    uint32_t bytes;        // descriptor range: 8 k-rows
     int off[4];
     int64_t slice;
     int nk;
@@ -149,8 +165,10 @@ struct MnOperand {
         for (int i = 0; i < 4; ++i) {
             const int krow = 2 * (4 * wave + i) + (lane >> 5);
             const int c = (lane & 31) ^ (4 * (krow & 3));
-            src[i] = X + (int64_t)krow * ld + mn0 + 8 * c;
+            voff[i] = (uint32_t)(((int64_t)(krow - 8 * wave) * ld + 8 * c) * 2);
         }
+        base = X + (int64_t)(8 * wave) * ld + mn0;
+        bytes = (uint32_t)(8 * ld * 2);
         // Source lane 4r+q of 16-lane group G reads k-row 16s + 8h + 4t + r,
         // columns w*128 + tile*32 + 16*(G%2) + 4q .. +3 (t = which of the two
         // reads); k & 3 == r.
@@ -166,11 +184,12 @@ struct MnOperand {
     // Half `half` of slice kt into stage st (past the end: the last slice).
     __device__ void copy(uint8_t* st, int kt, int half, int wave) const {
         kt = kt < nk ? kt : nk - 1;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, bytes, RSRC_W3);
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
-            __builtin_amdgcn_global_load_lds(src[i] + kt * slice,
-                                             (lds_void*)(st + (4 * wave + i) * 1024), 16, 0,
-                                             CPOL);
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16,
+                                                     voff[i], 0, 0, CPOL);
     }
     __device__ void frags(const uint8_t* st, int s, u32x4 (&f)[4]) const {
 #pragma unroll
@@ -262,8 +281,8 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
     // 16 MFMAs on (a, b).  The LDS reads and the copies issued just before
     // in program order are spread between them (per 4 MFMAs: 2 to 4 LDS
-    // reads and up to 2 copies), so the address unit never sees a burst that
-    // would hold the wave, and its MFMA issue, back.
+    // reads; a copy after every second MFMA), so the address unit never sees
+    // a burst that would hold the wave, and its MFMA issue, back.
     constexpr int DS_PER = (OpA::kReads + OpB::kReads) / 4;
     auto mfma_step = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
 #pragma unroll
@@ -277,8 +296,8 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
             for (int m = 0; m < 4; ++m) {
                 __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
                 if (m < DS_PER) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                if (m & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // copy
             }
-            __builtin_amdgcn_sched_group_barrier(0x020, 2, 0);  // copies (VMEM read)
         }
         __builtin_amdgcn_sched_barrier(0);
     };
@@ -375,7 +394,8 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 }  // namespace
 
 bool mfma16_dma_eligible(const GemmParams& p) {
-    return operands_16b_aligned(p, 2) && p.M % BM == 0 && p.N % BN == 0 && p.K % KALIGN == 0 && p.K > 0;
+    return operands_16b_aligned(p, 2) && p.M % BM == 0 && p.N % BN == 0 && p.K % KALIGN == 0 &&
+           p.K > 0 && p.lda < kMaxPitch && p.ldb < kMaxPitch;
 }
 
 template <In T>
