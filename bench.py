@@ -82,9 +82,9 @@ DOMINANT = {
                                      "k_skinny16.hip",
                                      r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 4>"),
     "f32_1000_splitk": ("mfma_f32_kernel<NN, guarded> x 8 K slices + reduce (per call)",
-                        "k_mfma_f32.hip", r"mfma_f32_kernel<true, true, false, false>"),
+                        "k_mfma_f32.hip+k_splitk.hip", r"mfma_f32_kernel<true, true, false, false>"),
     "bf16_splitk_1024x1024x16384": ("mfma16_dma_kernel<BF16, NN> x 16 K slices + reduce "
-                                    "(per call)", "k_mfma_bf16_dma.hip",
+                                    "(per call)", "k_mfma_bf16_dma.hip+k_splitk.hip",
                                     r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
     "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
                          r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
@@ -134,9 +134,12 @@ def naive_load_requests(M: int, N: int, K: int, wave: int) -> int:
 # ------------------------------------------------------------ measurement
 
 def source_digest(fname: str) -> str:
+    """Digest of the kernel sources a workload runs: one file, or several
+    joined by '+', with the headers they include."""
     h = hashlib.sha256()
-    extra = ("skinny_common.hpp",) if fname.startswith("k_skinny") else ()
-    for f in (fname, "gemm_common.hpp", *extra):
+    files = fname.split("+")
+    extra = ("skinny_common.hpp",) if any(f.startswith("k_skinny") for f in files) else ()
+    for f in (*files, "gemm_common.hpp", *extra):
         with open(os.path.join(ROOT, "dense_gemm_tuning_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
@@ -149,7 +152,7 @@ def read_traffic(workload: str):
         return None
     kern, src, _ = DOMINANT[workload]
     want = source_digest(src)
-    pat = re.compile(r"^traffic\s+workload=(\S+)\s+kernel=(\S+)\s+src=(\S+)\s+"
+    pat = re.compile(r"^traffic\s+workload=(\S+)\s+kernel=(.+?)\s+src=(\S+)\s+"
                      r"fetch_bytes=(\d+)\s+write_bytes=(\d+)", re.M)
     for m in pat.finditer(open(TRAFFIC_FILE).read()):
         if m.group(1) == workload and m.group(3) == want:

@@ -58,3 +58,21 @@ def test_skinny_bytes_and_bf16_model():
 def test_bench_refuses_more_than_one_gpu(gpus, capsys):
     assert bench.main(["--gpus", str(gpus)]) == 2
     assert "one GPU" in capsys.readouterr().err
+
+
+def test_traffic_lines_parse_kernel_names_with_spaces(tmp_path, monkeypatch):
+    """The committed counter summary names kernels such as
+    'mfma16_dma_kernel<BF16, NN>'; a line is used only when its source digest
+    matches the current kernel source."""
+    w = "bf16_8192"
+    kern, src, _ = bench.DOMINANT[w]
+    assert " " in kern
+    dig = bench.source_digest(src)
+    f = tmp_path / "hbm.md"
+    f.write_text(f"traffic workload={w} kernel={kern} src={dig} fetch_bytes=1000 write_bytes=24\n"
+                 f"traffic workload=f32_4096 kernel=x src=0000 fetch_bytes=5 write_bytes=5\n")
+    monkeypatch.setattr(bench, "TRAFFIC_FILE", str(f))
+    assert bench.read_traffic(w) == 1024
+    assert bench.read_traffic("f32_4096") is None  # stale digest
+    f.write_text(f"traffic workload={w} kernel={kern} src=ffff fetch_bytes=1000 write_bytes=24\n")
+    assert bench.read_traffic(w) is None
