@@ -55,7 +55,8 @@ PRIMARY = "bf16_8192"
 SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
              "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
              "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt", "f32_1000_splitk",
-             "bf16_splitk_1024x1024x16384"]
+             "bf16_splitk_1024x1024x16384", "bf16_skinny_shard_8x3584x8192",
+             "bf16_shard_8192x1024x8192"]
 
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
@@ -86,6 +87,12 @@ DOMINANT = {
     "bf16_splitk_1024x1024x16384": ("mfma16_dma_kernel<BF16, NN> x 16 K slices + reduce "
                                     "(per call)", "k_mfma_bf16_dma.hip+k_splitk.hip",
                                     r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
+    "bf16_skinny_shard_8x3584x8192": ("skinny16_kernel<BF16, NN, 1 row block> x 8 K slices + "
+                                      "reduce (per call)", "k_skinny16.hip+k_splitk.hip",
+                                      r"skinny16_kernel<\(dgt::In\)1, true, false, false, 1>"),
+    "bf16_shard_8192x1024x8192": ("mfma16_dma_kernel<BF16, NN> x 2 K slices + reduce (per call)",
+                                  "k_mfma_bf16_dma.hip+k_splitk.hip",
+                                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
     "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
                          r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
 }
@@ -238,9 +245,22 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
 
 def streams_b(w) -> bool:
     """Shapes the skinny path runs (M <= 64): bound by streaming B from HBM
-    once, so their roofline is HBM bandwidth; the bench alternates two copies
-    of B so the 256 MB Infinity Cache cannot serve it."""
+    once, so their roofline is HBM bandwidth."""
     return w.M <= 64
+
+
+INFINITY_CACHE_BYTES = 256 << 20
+
+
+def input_copies(w) -> int:
+    """Copies of the inputs the bench rotates through: for shapes that stream
+    B, enough that the copies together are at least twice the 256 MB
+    Infinity Cache, so no launch finds its B there (2 for a 448 MiB B, 10 for
+    a 56 MiB one); one otherwise."""
+    if not streams_b(w):
+        return 1
+    b_bytes = w.K * w.N * (4 if w.dtype == "f32" else 2) * w.batch
+    return max(2, -(-2 * INFINITY_CACHE_BYTES // b_bytes))
 
 
 def roofline(w, ms_avg):
@@ -330,7 +350,7 @@ def main(argv=None):
     results = {}
     for name in names:
         w = gi.WORKLOADS[name]
-        copies = 2 if streams_b(w) else 1  # B > 256 MB cache
+        copies = input_copies(w)
         log(f"[{name}] {w.M}x{w.N}x{w.K} {w.dtype}: warmup {args.warmup}, steps {args.steps}")
         res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies)
         res["roofline"] = roofline(w, res["ms_avg"])

@@ -226,6 +226,15 @@ WORKLOADS = {
     "bf16_splitk_1024x1024x16384": Workload("bf16_splitk_1024x1024x16384", "bf16", 1024, 1024,
                                             16384, 1.0, 0.0, "normal", seed_base=14000,
                                             splits=0),
+    # One GPU's share when the two headline BF16 products are split by
+    # columns of B / C over 8 GPUs: 8 x 8192 x 3584 (skinny, 58.7 MB of B) and
+    # 8192 x 1024 x 8192.  Each has too few column strips / tiles to fill the
+    # GPU on its own, so both run split-K (automatic slice count).
+    "bf16_skinny_shard_8x3584x8192": Workload("bf16_skinny_shard_8x3584x8192", "bf16", 8, 3584,
+                                              8192, 1.0, 0.0, "normal", sigma=0.02,
+                                              seed_base=15000, splits=0),
+    "bf16_shard_8192x1024x8192": Workload("bf16_shard_8192x1024x8192", "bf16", 8192, 1024, 8192,
+                                          1.0, 0.0, "normal", seed_base=16000, splits=0),
 }
 
 

@@ -27,9 +27,11 @@ pytestmark = pytest.mark.gpu
 LAYOUTS = {"nn": (False, False), "nt": (False, True), "tn": (True, False)}
 CODE = {"f32": 0, "bf16": 1, "f16": 2}
 # (M, N, K, splits): automatic (the 1000^3 shape gets 8 slices), requests,
-# K not a multiple of the slice, slices on the skinny path and on whole tiles
+# K not a multiple of the slice, slices on the skinny path and on whole tiles,
+# and one GPU's share of the skinny shape under an 8-way column split
+# (8 x 3584 x 8192, 8 automatic slices)
 CASES = [(1000, 1000, 1000, 0), (300, 260, 1000, 3), (64, 64, 4096, 4), (1, 1, 300, 2),
-         (256, 256, 2048, 0), (130, 70, 700, 5)]
+         (256, 256, 2048, 0), (130, 70, 700, 5), (8, 3584, 8192, 0)]
 
 
 @pytest.fixture(scope="module", autouse=True)
