@@ -178,6 +178,12 @@ template <In T> hipError_t launch_skinny16(const GemmParams& p, hipStream_t s);
 // Largest M the skinny (decode) path accepts: four blocks of 16 rows.
 constexpr int kSkinnyMaxM = 64;
 
+// Buffer descriptors for the global -> LDS copies (buffer_load ... lds):
+// word 3 of a raw 32-bit-data descriptor, and the row pitch (elements) below
+// which a workgroup's rows of lane offsets fit the 32-bit buffer offset.
+constexpr int kBufferRsrcW3 = 0x00020000;
+constexpr int64_t kMaxBufferPitch = int64_t(1) << 24;
+
 // True when every row start of a row-major operand is 16-byte aligned, so
 // 128-bit loads are legal at any chunk whose column is a multiple of
 // 16 / elem_size.

@@ -54,8 +54,6 @@ constexpr int KC_STAGE = 256 * 2 * BK * 2;  // 32 KiB: 256 rows x 128 B (two sli
 constexpr int MN_STAGE = BK * 256 * 2;      // 16 KiB: 32 k-rows x 512 B (one slice)
 constexpr int KALIGN = BK * NSTAGE;         // K multiple handled here
 constexpr int CPOL = 1;                     // sc0 on the copies
-constexpr int RSRC_W3 = 0x00020000;         // buffer descriptor word 3 (raw 32-bit data)
-constexpr int64_t kMaxPitch = int64_t(1) << 24;  // row pitch limit of the buffer offsets
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
@@ -134,7 +132,7 @@ struct KcOperand {
     __device__ void copy(uint8_t* st, int pr, int half, int wave) const {
         pr = pr < npair ? pr : npair - 1;
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, RSRC_W3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufferRsrcW3);
 #pragma unroll
         for (int i = 4 * half; i < 4 * half + 4; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
@@ -185,7 +183,7 @@ struct MnOperand {
     __device__ void copy(uint8_t* st, int kt, int half, int wave) const {
         kt = kt < nk ? kt : nk - 1;
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, bytes, RSRC_W3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, bytes, kBufferRsrcW3);
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16,
@@ -395,7 +393,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
 bool mfma16_dma_eligible(const GemmParams& p) {
     return operands_16b_aligned(p, 2) && p.M % BM == 0 && p.N % BN == 0 && p.K % KALIGN == 0 &&
-           p.K > 0 && p.lda < kMaxPitch && p.ldb < kMaxPitch;
+           p.K > 0 && p.lda < kMaxBufferPitch && p.ldb < kMaxBufferPitch;
 }
 
 template <In T>

@@ -34,8 +34,12 @@ LAYOUTS = {"nt": (False, True), "tn": (True, False), "tt": (True, True)}
 
 SHAPES = [(1, 1, 1), (15, 17, 16), (17, 65, 65), (65, 129, 127), (128, 256, 256),
           (300, 260, 520), (256, 512, 384), (512, 256, 256)]
+# Skinny shapes with B stored N x K and several row blocks: a last column
+# strip with 44 rows (N = 300) or one (N = 129), and K = 128, a single K step,
+# which leaves all but one wave of the workgroup without a step.
 SKINNY_SHAPES = [(1, 1, 1), (15, 17, 16), (8, 200, 300), (16, 384, 256), (5, 1000, 129),
-                 (17, 130, 96), (33, 384, 256), (48, 257, 300), (64, 512, 512)]
+                 (17, 130, 96), (33, 384, 256), (48, 257, 300), (64, 512, 512),
+                 (40, 300, 512), (20, 1000, 128), (64, 129, 256)]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -148,11 +152,15 @@ def _strided(rows, cols, ld, dtype, offset, fill):
 @pytest.mark.parametrize("variant", RUNGS)
 @pytest.mark.parametrize("pad,offset", [(8, 0), (3, 0), (8, 1)],
                          ids=["aligned_pad", "odd_pad", "misaligned"])
-def test_padded_and_misaligned_storage(variant, dtype, layout, pad, offset):
+@pytest.mark.parametrize("skinny_m", [13, 40])
+def test_padded_and_misaligned_storage(variant, dtype, layout, pad, offset, skinny_m):
     """Padded pitches of the stored operands, optionally misaligned bases; C's
-    padding and the elements past its end must stay untouched."""
+    padding and the elements past its end must stay untouched.  The skinny
+    rung runs with one row block (8 waves) and with three (4 waves)."""
     ta, tb = LAYOUTS[layout]
-    M, N, K = (13 if variant == "skinny" else 256), 256, 256
+    if variant != "skinny" and skinny_m != 13:
+        pytest.skip("row count only varies for the skinny rung")
+    M, N, K = (skinny_m if variant == "skinny" else 256), 256, 256
     sa, sb = stored(M, N, K, ta, tb)
     A = gi.draw(61, *sa, "int", dtype=dtype)
     B = gi.draw(62, *sb, "int", dtype=dtype)
