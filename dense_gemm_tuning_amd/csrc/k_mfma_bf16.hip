@@ -224,8 +224,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n
 }  // namespace
 
 template <In T>
-hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
-    if (mfma16_dma_eligible(p)) return launch_mfma16_dma<T>(p, s);
+hipError_t launch_mfma16_regs(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -246,6 +245,34 @@ hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
         return hipGetLastError();
     });
 }
+// The DMA kernel takes any M and N but K in multiples of its 32-deep
+// slice.  For another K above 32 it computes the largest such multiple and
+// the register-staged kernel then adds the remaining k (fewer than 32) onto
+// C with beta = 1, together with the bias: the same C = alpha*A*B + beta*C
+// (+ bias) in two sums, for one more pass over C.
+template <In T>
+hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
+    if (mfma16_dma_eligible(p)) return launch_mfma16_dma<T>(p, s);
+    constexpr int kDmaStep = 32;
+    if (p.K > kDmaStep) {
+        GemmParams q = p;
+        q.K = p.K / kDmaStep * kDmaStep;
+        q.bias = nullptr;
+        if (mfma16_dma_eligible(q)) {
+            const hipError_t e = launch_mfma16_dma<T>(q, s);
+            if (e != hipSuccess) return e;
+            GemmParams r = p;
+            const int64_t k0 = q.K;
+            r.K = p.K - q.K;
+            r.A = static_cast<const uint16_t*>(p.A) + (p.ta ? k0 * p.lda : k0);
+            r.B = static_cast<const uint16_t*>(p.B) + (p.tb ? k0 : k0 * p.ldb);
+            r.beta = 1.0f;
+            return launch_mfma16_regs<T>(r, s);
+        }
+    }
+    return launch_mfma16_regs<T>(p, s);
+}
+
 template hipError_t launch_mfma16<In::BF16>(const GemmParams&, hipStream_t);
 template hipError_t launch_mfma16<In::F16>(const GemmParams&, hipStream_t);
 

@@ -39,10 +39,15 @@
 //    has waited for its own copies) and retires slice t's stage, so the
 //    first operands of slice t+1 are read while step 2 of slice t computes.
 //
-// Used for shapes that are whole tiles (M, N multiples of 256, K of 128) with
-// 16-byte aligned rows and row pitches below 2^24 elements (so that 64 rows
-// of lane offsets fit 32 bits); the register-staged kernel handles
-// everything else.
+// Used for K a multiple of 32 with 16-byte aligned rows and row pitches
+// below 2^24 elements (so that 64 rows of lane offsets fit 32 bits), any M
+// and N: on edge tiles the copy descriptors' ranges stop at the operands'
+// last elements and the epilogue stores only the valid part (a K that is
+// not a multiple of 32 cannot be clipped that way: k past K within a row
+// would feed stored outputs).  The K loop runs in groups of four slices; in
+// the last group, slices past K keep their copies, reads and barriers (so
+// every wait count holds) but their MFMAs multiply zeroed fragments.  The register-staged kernel
+// handles the other shapes.
 #include "gemm_common.hpp"
 
 namespace dgt {
@@ -52,7 +57,7 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;
 constexpr int KC_STAGE = 256 * 2 * BK * 2;  // 32 KiB: 256 rows x 128 B (two slices)
 constexpr int MN_STAGE = BK * 256 * 2;      // 16 KiB: 32 k-rows x 512 B (one slice)
-constexpr int KALIGN = BK * NSTAGE;         // K multiple handled here
+constexpr int KALIGN = BK;                  // K multiple handled here
 constexpr int CPOL = 1;                     // sc0 on the copies
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
@@ -104,9 +109,15 @@ struct KcOperand {
     int npair;
 
     // mn0: first row (m or n) of the workgroup tile; w: this wave's half of
-    // it (wm or wn).
+    // it (wm or wn); mn_lim: rows of the operand (M or N), K its row length.
+    // The descriptor range ends at the wave's last element (k = K - 1 of its
+    // last row, or of row mn_lim - 1 on an edge tile), so rows past mn_lim
+    // and the k past K of a final half pair are never read from memory (they
+    // return zeros; they only feed outputs that are not stored, or slices
+    // that are not computed).
+    template <bool kEdge>
     __device__ void init(const uint16_t* X, int64_t ld, int mn0, int w, int wave, int lane,
-                         int nk) {
+                         int nk, int mn_lim, int K) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * (8 * wave + i) + (lane >> 3);
@@ -114,7 +125,9 @@ struct KcOperand {
             voff[i] = (uint32_t)(((int64_t)(row - 64 * wave) * ld + 8 * q) * 2);
         }
         base = X + (int64_t)(mn0 + 64 * wave) * ld;
-        bytes = (uint32_t)(64 * ld * 2);
+        int rows = 64;
+        if constexpr (kEdge) rows = min(64, mn_lim - (mn0 + 64 * wave));
+        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + K) * 2);
         // rows w*128 + t*32 + l%32; half-wave h reads chunk 4u + 2s + h
         const int h = lane >> 5;
 #pragma unroll
@@ -126,17 +139,32 @@ struct KcOperand {
                 for (int s = 0; s < 2; ++s)
                     off[t][u][s] = row * 128 + (((4 * u + 2 * s + h) ^ swz_kc(row)) << 4);
         }
-        npair = nk / 2;
+        npair = (nk + 1) / 2;  // an odd slice count ends with half a pair
     }
     // Half `half` of pair pr into stage st (past the end: the last pair).
+    // With a K tail (kTail) the descriptor starts at the pair, so the whole
+    // offset of every lane is range-checked (the scalar offset is not) and
+    // the k past K of a final half pair is never read; pair and range are
+    // wave-uniform, which readfirstlane tells the compiler.  Otherwise every
+    // k read is below K and the pair's offset goes in the scalar offset.
+    template <bool kEdge = false, bool kTail = false>
     __device__ void copy(uint8_t* st, int pr, int half, int wave) const {
         pr = pr < npair ? pr : npair - 1;
+        const uint8_t* from = reinterpret_cast<const uint8_t*>(base);
+        uint32_t range = bytes, soff = (uint32_t)pr * (2 * BK * 2);
+        if constexpr (kTail) {
+            pr = __builtin_amdgcn_readfirstlane(pr);
+            const uint32_t skip = (uint32_t)pr * (2 * BK * 2);
+            range = __builtin_amdgcn_readfirstlane(bytes > skip ? bytes - skip : 0u);
+            from += skip;
+            soff = 0;
+        }
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufferRsrcW3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)from, 0, range, kBufferRsrcW3);
 #pragma unroll
         for (int i = 4 * half; i < 4 * half + 4; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
-                                                     voff[i], (uint32_t)pr * (2 * BK * 2), 0, CPOL);
+                                                     voff[i], soff, 0, CPOL);
     }
     // Operands of step s of the slice in half u of stage st.
     __device__ void frags(const uint8_t* st, int u, int s, u32x4 (&f)[4]) const {
@@ -156,9 +184,17 @@ struct MnOperand {
     int off[4];
     int64_t slice;
     int nk;
+    int64_t ld_;
+    int rows_left0;        // k-rows from this wave's first one to the end
+    int cols;              // valid columns of the tile (edge tiles)
 
+    // mn_lim, K: columns and rows of the stored operand.  On an edge tile the
+    // range of slice kt's descriptor stops at the operand's last element;
+    // columns past mn_lim in earlier rows are read (they belong to the next
+    // row) but only feed outputs the epilogue does not store.
+    template <bool kEdge>
     __device__ void init(const uint16_t* X, int64_t ld, int mn0, int w, int wave, int lane,
-                         int nk_) {
+                         int nk_, int mn_lim, int K) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int krow = 2 * (4 * wave + i) + (lane >> 5);
@@ -167,6 +203,9 @@ struct MnOperand {
         }
         base = X + (int64_t)(8 * wave) * ld + mn0;
         bytes = (uint32_t)(8 * ld * 2);
+        ld_ = ld;
+        rows_left0 = K - 8 * wave;
+        cols = kEdge ? mn_lim - mn0 : 0;
         // Source lane 4r+q of 16-lane group G reads k-row 16s + 8h + 4t + r,
         // columns w*128 + tile*32 + 16*(G%2) + 4q .. +3 (t = which of the two
         // reads); k & 3 == r.
@@ -180,10 +219,16 @@ struct MnOperand {
         nk = nk_;
     }
     // Half `half` of slice kt into stage st (past the end: the last slice).
+    template <bool kEdge = false, bool kTail = false>
     __device__ void copy(uint8_t* st, int kt, int half, int wave) const {
         kt = kt < nk ? kt : nk - 1;
+        uint32_t range = bytes;
+        if constexpr (kEdge) {
+            const int64_t end = (int64_t)(rows_left0 - BK * kt - 1) * ld_ + cols;  // elements
+            if (end < 8 * ld_) range = (uint32_t)(end * 2);
+        }
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, bytes, kBufferRsrcW3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, range, kBufferRsrcW3);
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16,
@@ -226,10 +271,14 @@ constexpr int prologue_after() {
 
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
-template <In T, bool TA, bool TB>
-__global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_n,
-                                                          int grouped) {
-    const TileIdx tile = xcd_tile(p.M / BM, tiles_n, grouped != 0);
+// kEdge: M or N not a multiple of the tile (edge tiles read through
+// clipped descriptor ranges and store only their valid part).  kTail: the
+// slice count is not a multiple of four (in the last group the slices past
+// K multiply zeroed fragments).
+template <In T, bool TA, bool TB, bool kEdge, bool kTail>
+__global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_m,
+                                                          int tiles_n, int grouped) {
+    const TileIdx tile = xcd_tile(tiles_m, tiles_n, grouped != 0);
     select_problem(p, tile.z);
     constexpr bool AK = !TA, BKc = TB;
     using OpA = typename std::conditional<AK, KcOperand, MnOperand>::type;
@@ -255,8 +304,10 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
     OpA opa;
     OpB opb;
-    opa.init(static_cast<const uint16_t*>(p.A), p.lda, m0, wm, wave, lane, nk);
-    opb.init(static_cast<const uint16_t*>(p.B), p.ldb, n0, wn, wave, lane, nk);
+    opa.template init<kEdge>(static_cast<const uint16_t*>(p.A), p.lda, m0, wm, wave, lane, nk,
+                             p.M, p.K);
+    opb.template init<kEdge>(static_cast<const uint16_t*>(p.B), p.ldb, n0, wn, wave, lane, nk,
+                             p.N, p.K);
 
     floatx16 acc[4][4];
 #pragma unroll
@@ -302,6 +353,21 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
     u32x4 a0[4], b0[4], a1[4], b1[4];
 
+    // Slices past K (the last group when the slice count is not a multiple
+    // of four) multiply zero fragments: both operands are masked to zero by
+    // a wave-uniform mask, without a branch that would split the schedule,
+    // and 0 * 0 adds exactly nothing whatever the stale stage holds.
+    auto gate = [&](int kt, u32x4 (&a)[4], u32x4 (&b)[4]) {
+        const uint32_t keep = __builtin_amdgcn_readfirstlane(kt < nk ? 0xffffffffu : 0u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) {
+                a[t][e] &= keep;
+                b[t][e] &= keep;
+            }
+    };
+
     // Slice kt at position J of its group of four.  Copies, per wave:
     //   before the barrier: MN-contiguous operands the second half of slice
     //     kt+3 (into stage (J+3)%4); for even J, K-contiguous operands the
@@ -315,36 +381,38 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
         constexpr int J = decltype(Jc)::value;
         constexpr bool kEven = J % 2 == 0;
         frags(Jc, 1, a1, b1);  // step 2 operands of this slice
-        if constexpr (!AK) opa.copy(pick<(J + 3) % 4>(sA0, sA1, sA2, sA3), kt + 3, 1, wave);
-        if constexpr (!BKc) opb.copy(pick<(J + 3) % 4>(sB0, sB1, sB2, sB3), kt + 3, 1, wave);
-        if constexpr (kEven && AK) opa.copy(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
-        if constexpr (kEven && BKc) opb.copy(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
+        if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<(J + 3) % 4>(sA0, sA1, sA2, sA3), kt + 3, 1, wave);
+        if constexpr (!BKc) opb.template copy<kEdge, kTail>(pick<(J + 3) % 4>(sB0, sB1, sB2, sB3), kt + 3, 1, wave);
+        if constexpr (kEven && AK) opa.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
+        if constexpr (kEven && BKc) opb.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
+        if constexpr (kTail) gate(kt, a0, b0);
         mfma_step(a0, b0);  // step 1 (operands read earlier)
         WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>()));  // own copies landed, reads returned
         barrier();                                           // ... for every wave
         frags(std::integral_constant<int, (J + 1) % 4>{}, 0, a0, b0);  // next slice, step 1
-        if constexpr (!AK) opa.copy(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
-        if constexpr (!BKc) opb.copy(pick<J>(sB0, sB1, sB2, sB3), kt + NSTAGE, 0, wave);
-        if constexpr (!kEven && AK) opa.copy(pick<((J + 3) / 2) % 2>(sA0, sA1, sA2, sA3), (kt + 3) / 2, 0, wave);
-        if constexpr (!kEven && BKc) opb.copy(pick<((J + 3) / 2) % 2>(sB0, sB1, sB2, sB3), (kt + 3) / 2, 0, wave);
+        if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
+        if constexpr (!BKc) opb.template copy<kEdge, kTail>(pick<J>(sB0, sB1, sB2, sB3), kt + NSTAGE, 0, wave);
+        if constexpr (!kEven && AK) opa.template copy<kEdge, kTail>(pick<((J + 3) / 2) % 2>(sA0, sA1, sA2, sA3), (kt + 3) / 2, 0, wave);
+        if constexpr (!kEven && BKc) opb.template copy<kEdge, kTail>(pick<((J + 3) / 2) % 2>(sB0, sB1, sB2, sB3), (kt + 3) / 2, 0, wave);
+        if constexpr (kTail) gate(kt, a1, b1);
         mfma_step(a1, b1);  // step 2
     };
 
     // Prologue: K-contiguous operands pair 0; MN-contiguous ones slices 0..2
     // and the first half of slice 3; then K-contiguous ones the first half of
     // pair 1.
-    if constexpr (AK) { opa.copy(sA0, 0, 0, wave); opa.copy(sA0, 0, 1, wave); }
-    if constexpr (BKc) { opb.copy(sB0, 0, 0, wave); opb.copy(sB0, 0, 1, wave); }
-    if constexpr (!AK) { opa.copy(sA0, 0, 0, wave); opa.copy(sA0, 0, 1, wave); }
-    if constexpr (!BKc) { opb.copy(sB0, 0, 0, wave); opb.copy(sB0, 0, 1, wave); }
-    if constexpr (!AK) { opa.copy(sA1, 1, 0, wave); opa.copy(sA1, 1, 1, wave); }
-    if constexpr (!BKc) { opb.copy(sB1, 1, 0, wave); opb.copy(sB1, 1, 1, wave); }
-    if constexpr (!AK) { opa.copy(sA2, 2, 0, wave); opa.copy(sA2, 2, 1, wave); }
-    if constexpr (!BKc) { opb.copy(sB2, 2, 0, wave); opb.copy(sB2, 2, 1, wave); }
-    if constexpr (!AK) opa.copy(sA3, 3, 0, wave);
-    if constexpr (!BKc) opb.copy(sB3, 3, 0, wave);
-    if constexpr (AK) opa.copy(sA1, 1, 0, wave);
-    if constexpr (BKc) opb.copy(sB1, 1, 0, wave);
+    if constexpr (AK) { opa.template copy<kEdge, kTail>(sA0, 0, 0, wave); opa.template copy<kEdge, kTail>(sA0, 0, 1, wave); }
+    if constexpr (BKc) { opb.template copy<kEdge, kTail>(sB0, 0, 0, wave); opb.template copy<kEdge, kTail>(sB0, 0, 1, wave); }
+    if constexpr (!AK) { opa.template copy<kEdge, kTail>(sA0, 0, 0, wave); opa.template copy<kEdge, kTail>(sA0, 0, 1, wave); }
+    if constexpr (!BKc) { opb.template copy<kEdge, kTail>(sB0, 0, 0, wave); opb.template copy<kEdge, kTail>(sB0, 0, 1, wave); }
+    if constexpr (!AK) { opa.template copy<kEdge, kTail>(sA1, 1, 0, wave); opa.template copy<kEdge, kTail>(sA1, 1, 1, wave); }
+    if constexpr (!BKc) { opb.template copy<kEdge, kTail>(sB1, 1, 0, wave); opb.template copy<kEdge, kTail>(sB1, 1, 1, wave); }
+    if constexpr (!AK) { opa.template copy<kEdge, kTail>(sA2, 2, 0, wave); opa.template copy<kEdge, kTail>(sA2, 2, 1, wave); }
+    if constexpr (!BKc) { opb.template copy<kEdge, kTail>(sB2, 2, 0, wave); opb.template copy<kEdge, kTail>(sB2, 2, 1, wave); }
+    if constexpr (!AK) opa.template copy<kEdge, kTail>(sA3, 3, 0, wave);
+    if constexpr (!BKc) opb.template copy<kEdge, kTail>(sB3, 3, 0, wave);
+    if constexpr (AK) opa.template copy<kEdge, kTail>(sA1, 1, 0, wave);
+    if constexpr (BKc) opb.template copy<kEdge, kTail>(sB1, 1, 0, wave);
     WAIT_VMCNT((prologue_after<AK, BKc>()));  // slice 0 of both operands landed
     barrier();
     frags(std::integral_constant<int, 0>{}, 0, a0, b0);
@@ -358,7 +426,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
     // 32x32 accumulator layout: register r of lane l is row
     // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the MFMA tile.  C is read
-    // only when beta != 0.  A lane's four bias values (one per column tile)
+    // only when beta != 0, an MFMA tile at a time.  A lane's four bias values (one per column tile)
     // are read once; without a bias it adds -0.0, which leaves every value,
     // signed zeros included, unchanged.
     const int col0 = n0 + wn * 128 + (lane & 31);
@@ -366,7 +434,13 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     const float alpha = p.alpha, beta = p.beta;
     float bias[4];
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) bias[tj] = p.bias ? p.bias[col0 + tj * 32] : -0.0f;
+    for (int tj = 0; tj < 4; ++tj)
+        bias[tj] = p.bias && (!kEdge || col0 + tj * 32 < p.N) ? p.bias[col0 + tj * 32] : -0.0f;
+    // on edge tiles only rows < M and columns < N are stored
+    const int row0 = m0 + wm * 128 + 4 * h;
+    auto ok = [&](int ti, int tj, int r) {
+        return !kEdge || (row0 + ti * 32 + 8 * (r >> 2) + (r & 3) < p.M && col0 + tj * 32 < p.N);
+    };
     if (beta == 0.0f) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -374,39 +448,60 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
             for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
-                        alpha * acc[ti][tj][r] + bias[tj];
+                    if (ok(ti, tj, r))
+                        cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
+                            alpha * acc[ti][tj][r] + bias[tj];
     } else {
+        // C is read one 32 x 32 MFMA tile (16 values a lane) at a time
+        // before those values are stored, so the reads of a tile overlap.
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < 4; ++tj) {
+                float cv[16];
 #pragma unroll
-                for (int r = 0; r < 16; ++r) {
-                    float* c = cbase + (int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32;
-                    *c = (alpha * acc[ti][tj][r] + beta * (*c)) + bias[tj];
-                }
+                for (int r = 0; r < 16; ++r)
+                    cv[r] = ok(ti, tj, r)
+                                ? cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32]
+                                : 0.0f;
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    if (ok(ti, tj, r))
+                        cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
+                            (alpha * acc[ti][tj][r] + beta * cv[r]) + bias[tj];
+            }
     }
 }
 
 }  // namespace
 
+// Any M and N (edge tiles are clipped), K a multiple of KALIGN, 16-byte
+// aligned rows, and pitches within the 32-bit buffer offsets.
 bool mfma16_dma_eligible(const GemmParams& p) {
-    return operands_16b_aligned(p, 2) && p.M % BM == 0 && p.N % BN == 0 && p.K % KALIGN == 0 &&
-           p.K > 0 && p.lda < kMaxBufferPitch && p.ldb < kMaxBufferPitch;
+    return operands_16b_aligned(p, 2) && p.M > 0 && p.N > 0 && p.K % KALIGN == 0 && p.K > 0 &&
+           p.lda < kMaxBufferPitch && p.ldb < kMaxBufferPitch;
 }
 
 template <In T>
 hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
-    const int tiles_n = p.N / BN;
-    const int64_t blocks = (int64_t)(p.M / BM) * tiles_n;
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+    const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool edge = p.M % BM != 0 || p.N % BN != 0;
+    const bool tail = (p.K / BK) % NSTAGE != 0;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         // linear order only for one problem with both operands k-contiguous
         const int grouped = !(p.batch == 1 && !TA && TB);
-        hipLaunchKernelGGL((mfma16_dma_kernel<T, TA, TB>), dim3((unsigned)blocks, p.batch),
-                           dim3(NT), 0, s, p, tiles_n, grouped);
+        const dim3 grid((unsigned)blocks, p.batch);
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(NT), 0, s, p, tiles_m, tiles_n, grouped);
+        };
+        // a K tail takes the edge-tile instance whatever M and N (its guards
+        // then always pass); built without edges it spills registers
+        if (tail) go(mfma16_dma_kernel<T, TA, TB, true, true>);
+        else if (edge) go(mfma16_dma_kernel<T, TA, TB, true, false>);
+        else go(mfma16_dma_kernel<T, TA, TB, false, false>);
         return hipGetLastError();
     });
 }
