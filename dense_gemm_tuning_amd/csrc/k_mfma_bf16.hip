@@ -245,31 +245,11 @@ hipError_t launch_mfma16_regs(const GemmParams& p, hipStream_t s) {
         return hipGetLastError();
     });
 }
-// The DMA kernel takes any M and N but K in multiples of its 32-deep
-// slice.  For another K above 32 it computes the largest such multiple and
-// the register-staged kernel then adds the remaining k (fewer than 32) onto
-// C with beta = 1, together with the bias: the same C = alpha*A*B + beta*C
-// (+ bias) in two sums, for one more pass over C.
+// Operands with 16-byte aligned rows take the DMA kernel (any M, N and K);
+// the register-staged kernel takes the others.
 template <In T>
 hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
     if (mfma16_dma_eligible(p)) return launch_mfma16_dma<T>(p, s);
-    constexpr int kDmaStep = 32;
-    if (p.K > kDmaStep) {
-        GemmParams q = p;
-        q.K = p.K / kDmaStep * kDmaStep;
-        q.bias = nullptr;
-        if (mfma16_dma_eligible(q)) {
-            const hipError_t e = launch_mfma16_dma<T>(q, s);
-            if (e != hipSuccess) return e;
-            GemmParams r = p;
-            const int64_t k0 = q.K;
-            r.K = p.K - q.K;
-            r.A = static_cast<const uint16_t*>(p.A) + (p.ta ? k0 * p.lda : k0);
-            r.B = static_cast<const uint16_t*>(p.B) + (p.tb ? k0 : k0 * p.ldb);
-            r.beta = 1.0f;
-            return launch_mfma16_regs<T>(r, s);
-        }
-    }
     return launch_mfma16_regs<T>(p, s);
 }
 

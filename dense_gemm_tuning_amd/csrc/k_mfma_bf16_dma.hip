@@ -39,15 +39,16 @@
 //    has waited for its own copies) and retires slice t's stage, so the
 //    first operands of slice t+1 are read while step 2 of slice t computes.
 //
-// Used for K a multiple of 32 with 16-byte aligned rows and row pitches
-// below 2^24 elements (so that 64 rows of lane offsets fit 32 bits), any M
-// and N: on edge tiles the copy descriptors' ranges stop at the operands'
-// last elements and the epilogue stores only the valid part (a K that is
-// not a multiple of 32 cannot be clipped that way: k past K within a row
-// would feed stored outputs).  The K loop runs in groups of four slices; in
-// the last group, slices past K keep their copies, reads and barriers (so
-// every wait count holds) but their MFMAs multiply zeroed fragments.  The register-staged kernel
-// handles the other shapes.
+// Used for any M, N and K with 16-byte aligned rows and row pitches below
+// 2^24 elements (so that 64 rows of lane offsets fit 32 bits).  On edge
+// tiles the copy descriptors' ranges stop at the operands' last elements and
+// the epilogue stores only the valid part.  When K is not a multiple of 128
+// the K loop runs in groups of four 32-deep slices and the last group (1 to
+// 4 slices) after it as ordinary slices (each keeps its copies, waits and
+// barrier, so every wait count holds); in a partial last slice the
+// k-contiguous fragments are masked past K, and m/n-contiguous rows past K
+// read as zeros through the descriptor range.  The register-staged kernel
+// handles unaligned operands.
 #include "gemm_common.hpp"
 
 namespace dgt {
@@ -57,13 +58,20 @@ namespace {
 constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;
 constexpr int KC_STAGE = 256 * 2 * BK * 2;  // 32 KiB: 256 rows x 128 B (two slices)
 constexpr int MN_STAGE = BK * 256 * 2;      // 16 KiB: 32 k-rows x 512 B (one slice)
-constexpr int KALIGN = BK;                  // K multiple handled here
 constexpr int CPOL = 1;                     // sc0 on the copies
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
 typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
+
+// A copy descriptor's range ends at an operand's last element rounded up to
+// a whole 16-byte chunk: the hardware returns zeros for a 16-byte load that
+// reaches past the range, even for its bytes inside it.  The rounding never
+// reads another page (a 16-byte aligned chunk lies within one), and what it
+// reads past the element only feeds outputs that are not stored or k that
+// are masked.
+__device__ __forceinline__ int round8(int n) { return (n + 7) & ~7; }
 
 // K-contiguous rows are 128 B = 8 chunks of 16 B; chunk q of row r sits at
 // q ^ swz_kc(r).
@@ -127,7 +135,7 @@ struct KcOperand {
         base = X + (int64_t)(mn0 + 64 * wave) * ld;
         int rows = 64;
         if constexpr (kEdge) rows = min(64, mn_lim - (mn0 + 64 * wave));
-        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + K) * 2);
+        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round8(K)) * 2);
         // rows w*128 + t*32 + l%32; half-wave h reads chunk 4u + 2s + h
         const int h = lane >> 5;
 #pragma unroll
@@ -205,7 +213,7 @@ struct MnOperand {
         bytes = (uint32_t)(8 * ld * 2);
         ld_ = ld;
         rows_left0 = K - 8 * wave;
-        cols = kEdge ? mn_lim - mn0 : 0;
+        cols = kEdge ? round8(mn_lim - mn0) : 0;
         // Source lane 4r+q of 16-lane group G reads k-row 16s + 8h + 4t + r,
         // columns w*128 + tile*32 + 16*(G%2) + 4q .. +3 (t = which of the two
         // reads); k & 3 == r.
@@ -225,7 +233,7 @@ struct MnOperand {
         uint32_t range = bytes;
         if constexpr (kEdge) {
             const int64_t end = (int64_t)(rows_left0 - BK * kt - 1) * ld_ + cols;  // elements
-            if (end < 8 * ld_) range = (uint32_t)(end * 2);
+            if (end < 8 * ld_) range = end <= 0 ? 0u : (uint32_t)(end * 2);
         }
         const __amdgpu_buffer_rsrc_t rs =
             __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, range, kBufferRsrcW3);
@@ -272,9 +280,9 @@ constexpr int prologue_after() {
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
 // kEdge: M or N not a multiple of the tile (edge tiles read through
-// clipped descriptor ranges and store only their valid part).  kTail: the
-// slice count is not a multiple of four (in the last group the slices past
-// K multiply zeroed fragments).
+// clipped descriptor ranges and store only their valid part).  kTail: K is
+// not a multiple of 128 (a last group of 1 to 4 slices after the loop, the
+// last slice possibly partial).
 template <In T, bool TA, bool TB, bool kEdge, bool kTail>
 __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_m,
                                                           int tiles_n, int grouped) {
@@ -300,7 +308,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
     const int m0 = tile.bm * BM;
     const int n0 = tile.bn * BN;
-    const int nk = p.K / BK;  // slices
+    const int nk = (p.K + BK - 1) / BK;  // slices (the last one partial when K % 32 != 0)
 
     OpA opa;
     OpB opb;
@@ -353,20 +361,6 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
     u32x4 a0[4], b0[4], a1[4], b1[4];
 
-    // Slices past K (the last group when the slice count is not a multiple
-    // of four) multiply zero fragments: both operands are masked to zero by
-    // a wave-uniform mask, without a branch that would split the schedule,
-    // and 0 * 0 adds exactly nothing whatever the stale stage holds.
-    auto gate = [&](int kt, u32x4 (&a)[4], u32x4 (&b)[4]) {
-        const uint32_t keep = __builtin_amdgcn_readfirstlane(kt < nk ? 0xffffffffu : 0u);
-#pragma unroll
-        for (int t = 0; t < 4; ++t)
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                a[t][e] &= keep;
-                b[t][e] &= keep;
-            }
-    };
 
     // Slice kt at position J of its group of four.  Copies, per wave:
     //   before the barrier: MN-contiguous operands the second half of slice
@@ -377,15 +371,37 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     //     the first half of pair (kt+3)/2 into the pair stage retired by this
     //     barrier.
     // The barrier of slice kt publishes slice kt+1.
-    auto slice = [&](auto Jc, int kt) {
+    // In a partial last slice (K % 32 != 0), k-contiguous fragments hold
+    // whatever follows k = K - 1 in the row; they are masked to zero element
+    // by element (a lane's fragment of step s holds k = 32kt + 16s + 8h ..
+    // +7).  m/n-contiguous operands need no mask: their rows past K lie past
+    // the copy descriptor's range and read as zeros.
+    auto mask_k = [&](int kt, int s, u32x4 (&f)[4]) {
+        const int valid = p.K - (BK * kt + 16 * s + 8 * h);  // elements of the 8 still below K
+        uint32_t m[4];
+#pragma unroll
+        for (int e = 0; e < 4; ++e)
+            m[e] = (2 * e < valid ? 0x0000ffffu : 0u) | (2 * e + 1 < valid ? 0xffff0000u : 0u);
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) f[t][e] &= m[e];
+    };
+    auto slice = [&](auto Jc, int kt, auto maskc) {
         constexpr int J = decltype(Jc)::value;
         constexpr bool kEven = J % 2 == 0;
+        constexpr bool kMask = decltype(maskc)::value;
         frags(Jc, 1, a1, b1);  // step 2 operands of this slice
+        if constexpr (kMask) {
+            if (kt == nk - 1 && p.K % BK != 0) {
+                if constexpr (AK) { mask_k(kt, 0, a0); mask_k(kt, 1, a1); }
+                if constexpr (BKc) { mask_k(kt, 0, b0); mask_k(kt, 1, b1); }
+            }
+        }
         if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<(J + 3) % 4>(sA0, sA1, sA2, sA3), kt + 3, 1, wave);
         if constexpr (!BKc) opb.template copy<kEdge, kTail>(pick<(J + 3) % 4>(sB0, sB1, sB2, sB3), kt + 3, 1, wave);
         if constexpr (kEven && AK) opa.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
         if constexpr (kEven && BKc) opb.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
-        if constexpr (kTail) gate(kt, a0, b0);
         mfma_step(a0, b0);  // step 1 (operands read earlier)
         WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>()));  // own copies landed, reads returned
         barrier();                                           // ... for every wave
@@ -394,7 +410,6 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
         if constexpr (!BKc) opb.template copy<kEdge, kTail>(pick<J>(sB0, sB1, sB2, sB3), kt + NSTAGE, 0, wave);
         if constexpr (!kEven && AK) opa.template copy<kEdge, kTail>(pick<((J + 3) / 2) % 2>(sA0, sA1, sA2, sA3), (kt + 3) / 2, 0, wave);
         if constexpr (!kEven && BKc) opb.template copy<kEdge, kTail>(pick<((J + 3) / 2) % 2>(sB0, sB1, sB2, sB3), (kt + 3) / 2, 0, wave);
-        if constexpr (kTail) gate(kt, a1, b1);
         mfma_step(a1, b1);  // step 2
     };
 
@@ -416,11 +431,22 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     WAIT_VMCNT((prologue_after<AK, BKc>()));  // slice 0 of both operands landed
     barrier();
     frags(std::integral_constant<int, 0>{}, 0, a0, b0);
-    for (int kt = 0; kt < nk; kt += NSTAGE) {
-        slice(std::integral_constant<int, 0>{}, kt);
-        slice(std::integral_constant<int, 1>{}, kt + 1);
-        slice(std::integral_constant<int, 2>{}, kt + 2);
-        slice(std::integral_constant<int, 3>{}, kt + 3);
+    using NoMask = std::false_type;
+    int kt = 0;
+    // with a K tail the last group (1 to 4 slices, the last possibly
+    // partial) runs after the loop
+    for (; kt + NSTAGE < nk + (kTail ? 0 : 1); kt += NSTAGE) {
+        slice(std::integral_constant<int, 0>{}, kt, NoMask{});
+        slice(std::integral_constant<int, 1>{}, kt + 1, NoMask{});
+        slice(std::integral_constant<int, 2>{}, kt + 2, NoMask{});
+        slice(std::integral_constant<int, 3>{}, kt + 3, NoMask{});
+    }
+    if constexpr (kTail) {
+        const int rest = nk - kt;
+        slice(std::integral_constant<int, 0>{}, kt, std::true_type{});
+        if (rest >= 2) slice(std::integral_constant<int, 1>{}, kt + 1, std::true_type{});
+        if (rest >= 3) slice(std::integral_constant<int, 2>{}, kt + 2, std::true_type{});
+        if (rest >= 4) slice(std::integral_constant<int, 3>{}, kt + 3, std::true_type{});
     }
     WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
 
@@ -475,10 +501,10 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
 
 }  // namespace
 
-// Any M and N (edge tiles are clipped), K a multiple of KALIGN, 16-byte
+// Any M, N and K (edge tiles and a K tail are clipped or masked), 16-byte
 // aligned rows, and pitches within the 32-bit buffer offsets.
 bool mfma16_dma_eligible(const GemmParams& p) {
-    return operands_16b_aligned(p, 2) && p.M > 0 && p.N > 0 && p.K % KALIGN == 0 && p.K > 0 &&
+    return operands_16b_aligned(p, 2) && p.M > 0 && p.N > 0 && p.K > 0 &&
            p.lda < kMaxBufferPitch && p.ldb < kMaxBufferPitch;
 }
 
@@ -488,7 +514,7 @@ hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool edge = p.M % BM != 0 || p.N % BN != 0;
-    const bool tail = (p.K / BK) % NSTAGE != 0;
+    const bool tail = p.K % (BK * NSTAGE) != 0;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         // linear order only for one problem with both operands k-contiguous

@@ -3,17 +3,18 @@ tiles, against the CPU oracle, through the C ABI.
 
 M and N that are not multiples of 256 run the global->LDS DMA kernel with
 edge tiles: the copy descriptors' ranges stop at each operand's last
-element and the epilogue stores only rows < M and columns < N.  A K that is
-a multiple of 32 but not of 128 runs there too, its last group of slices
-skipping the MFMAs past K (including half a k-contiguous pair); any other K
-is computed as two sums, the largest multiple of 32 by the DMA kernel and
-the remaining k by the register-staged kernel, which accumulates onto C
-with beta = 1 and adds the bias.  Covered, for every
-stored layout: integer inputs bit-exact, a guard band around a padded C
-(nothing outside C is written), alpha / beta applied once across the two
-sums, the bias added once, beta = 0 never reading a NaN-filled C, real
+element and the epilogue stores only rows < M and columns < N.  Any K runs
+there too: when K is not a multiple of 128 the last group of 1 to 4 slices
+runs after the main loop, and in a partial last slice the k-contiguous
+fragments are masked past K element by element while m/n-contiguous rows
+past K read as zeros through the copy range.  Covered, for every stored
+layout: integer inputs bit-exact (K = 5 .. 1096, with and without a partial
+slice, with half a k-contiguous pair, and with K not a multiple of 8 on
+padded storage), a guard band around a padded C (nothing outside C is
+written), the bias added once, beta = 0 never reading a NaN-filled C, real
 inputs within the gates, a large ragged shape on sampled rows, and
-run-to-run determinism.
+run-to-run determinism.  Shapes whose stored rows are not 16-byte aligned
+take the register-staged kernel.
 """
 
 import numpy as np
@@ -32,12 +33,11 @@ pytestmark = pytest.mark.gpu
 LAYOUTS = {"nn": (False, False), "nt": (False, True), "tn": (True, False), "tt": (True, True)}
 
 # (M, N, K): edge tiles with K a multiple of 128, including eight rows and
-# eight columns; K a multiple of 32 only (one launch; 32, 96 and 224 slices
-# of 32 leave 1, 3 and 3 slices in the last group, 32 and 224 end in half a
-# pair); then K with a remainder (two sums, the remainder as small as 8).
-# Stored row lengths are multiples of 8 elements (16-byte rows, which the
-# DMA kernel needs); (300, 260, 520) is not, and takes the register-staged
-# kernel throughout.
+# eight columns; K a multiple of 32 only (32, 96 and 224: one, three and
+# seven slices, ending in half a k-contiguous pair when odd); K with a
+# partial last slice (200, 1000, 136, 1096: 8 of 32 k valid).  Stored row
+# lengths are multiples of 8 elements (16-byte rows, which the DMA kernel
+# needs); (300, 260, 520) is not, and takes the register-staged kernel.
 EDGE = [(296, 264, 512), (264, 1000, 256), (1000, 296, 384), (8, 704, 128), (520, 8, 256)]
 RAGGED_K = [(256, 256, 32), (512, 512, 96), (296, 264, 224), (512, 512, 200),
             (296, 264, 1000), (256, 384, 136), (72, 4096, 1096), (300, 260, 520)]
@@ -78,6 +78,37 @@ def test_edge_and_ragged_k_integer_bit_exact(dtype, layout):
 
 
 @pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_k_not_multiple_of_8_on_padded_storage(layout):
+    """Pitches padded to multiples of 8 elements keep 16-byte rows, so K that
+    is not a multiple of 8 still runs the DMA kernel: the last slice's
+    fragments are masked element by element (K = 5 and 77 fit in one or
+    three slices)."""
+    ta, tb = LAYOUTS[layout]
+    for idx, (M, N, K) in enumerate([(296, 264, 1001), (264, 520, 999), (300, 256, 77),
+                                     (256, 300, 5)]):
+        sa, sb = stored(M, N, K, ta, tb)
+        A = gi.draw(2300 + idx, *sa, "int", dtype="bf16")
+        B = gi.draw(2400 + idx, *sb, "int", dtype="bf16")
+        C0 = gi.draw(2500 + idx, M, N, "int")
+
+        def padded(X):
+            rows, cols = X.shape
+            ld = (cols + 7) // 8 * 8 + 8
+            t = torch.zeros((rows, ld), dtype=torch.bfloat16, device="cuda")
+            t[:, :cols] = to_dev(X, "bf16")
+            return t[:, :cols]
+
+        dA, dB = padded(A), padded(B)
+        dC = torch.from_numpy(C0).cuda()
+        say(f"padded K {layout} {M}x{N}x{K}")
+        st = dgt.gemm(dA, dB, dC, 1.5, 0.5, trans_a=ta, trans_b=tb)
+        torch.cuda.synchronize()
+        assert st == 0, dgt.gemm_status_string(st)
+        R = oracle.round_f32(oracle.gemm(A, B, C0, 1.5, 0.5, "bf16", trans_a=ta, trans_b=tb))
+        assert_bit_exact(dC.cpu().numpy(), R, f"padded K {layout} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", list(LAYOUTS))
 def test_edge_guard_band(layout):
     """C padded (ldc > N) inside a canary-filled buffer: an edge tile stores
     only its valid part, so the padding and the elements after C keep the
@@ -107,8 +138,8 @@ def test_edge_guard_band(layout):
 
 @pytest.mark.parametrize("layout", ["nn", "nt"])
 def test_ragged_k_bias_added_once(layout):
-    """The bias goes with the second sum only: added exactly once, for one
-    problem and for a strided batch whose problems take the same split."""
+    """With a partial last slice the bias is still added once, by the
+    epilogue, for every problem of a strided batch."""
     ta, tb = LAYOUTS[layout]
     M, N, K, batch = 296, 264, 1000, 3
     sa, sb = stored(M, N, K, ta, tb)
@@ -141,7 +172,8 @@ def test_edge_real_inputs(dtype):
 
 def test_large_ragged_sampled_rows_and_determinism():
     """8000^3: edge tiles in M and N and 250 slices of 32 (the last group
-    has two); sampled rows against the oracle, and two runs bit for bit."""
+    runs after the loop); sampled rows against the oracle, and two runs bit
+    for bit."""
     M = N = K = 8000
     A = gi.draw(2200, M, K, "normal", dtype="bf16")
     B = gi.draw(2201, K, N, "normal", dtype="bf16")
