@@ -61,24 +61,25 @@ SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
 # template arguments: input format, then vector / guard flags where the
-# kernel has them, then trans_a, trans_b).
+# kernel has them, then trans_a, trans_b; the DMA kernel's end with its
+# edge-tile and K-tail flags, false for whole tiles).
 DOMINANT = {
     "bf16_8192": ("mfma16_dma_kernel<BF16, NN>", "k_mfma_bf16_dma.hip",
-                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
+                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
     "f16_8192": ("mfma16_dma_kernel<F16, NN>", "k_mfma_bf16_dma.hip",
-                 r"mfma16_dma_kernel<\(dgt::In\)2, false, false>"),
+                 r"mfma16_dma_kernel<\(dgt::In\)2, false, false, false, false>"),
     "f32_4096": ("mfma_f32_kernel<NN>", "k_mfma_f32.hip",
                  r"mfma_f32_kernel<true, false, false, false>"),
     "bf16_skinny_8x28672x8192": ("skinny16_kernel<BF16, NN, 1 row block>", "k_skinny16.hip",
                                  r"skinny16_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_8192_nt": ("mfma16_dma_kernel<BF16, NT>", "k_mfma_bf16_dma.hip",
-                     r"mfma16_dma_kernel<\(dgt::In\)1, false, true>"),
+                     r"mfma16_dma_kernel<\(dgt::In\)1, false, true, false, false>"),
     "bf16_8192_tn": ("mfma16_dma_kernel<BF16, TN>", "k_mfma_bf16_dma.hip",
-                     r"mfma16_dma_kernel<\(dgt::In\)1, true, false>"),
+                     r"mfma16_dma_kernel<\(dgt::In\)1, true, false, false, false>"),
     "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 1 row block>", "k_skinny16.hip",
                                     r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
-                                 r"mfma16_dma_kernel<\(dgt::In\)1, false, true>"),
+                                 r"mfma16_dma_kernel<\(dgt::In\)1, false, true, false, false>"),
     "bf16_decode_64x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 4 row blocks>",
                                      "k_skinny16.hip",
                                      r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 4>"),
@@ -86,15 +87,15 @@ DOMINANT = {
                         "k_mfma_f32.hip+k_splitk.hip", r"mfma_f32_kernel<true, true, false, false>"),
     "bf16_splitk_1024x1024x16384": ("mfma16_dma_kernel<BF16, NN> x 16 K slices + reduce "
                                     "(per call)", "k_mfma_bf16_dma.hip+k_splitk.hip",
-                                    r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
+                                    r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
     "bf16_skinny_shard_8x3584x8192": ("skinny16_kernel<BF16, NN, 1 row block> x 8 K slices + "
                                       "reduce (per call)", "k_skinny16.hip+k_splitk.hip",
                                       r"skinny16_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_shard_8192x1024x8192": ("mfma16_dma_kernel<BF16, NN> x 2 K slices + reduce (per call)",
                                   "k_mfma_bf16_dma.hip+k_splitk.hip",
-                                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
+                                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
     "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
-                         r"mfma16_dma_kernel<\(dgt::In\)1, false, false>"),
+                         r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
