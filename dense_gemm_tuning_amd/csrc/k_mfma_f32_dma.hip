@@ -1,0 +1,415 @@
+// k_mfma_f32_dma.hip -- FP32 GEMM on whole 256 x 256 tiles: global -> LDS by
+// DMA up to three K slices ahead, one wavefront per SIMD.
+//
+// The pages' register-tiled SGEMM (dilfish.github.io 5.4: block tile, a
+// per-thread register tile, double buffering) becomes, on the matrix cores,
+// a 128 x 128 tile of C per wavefront held in accumulation registers
+// (4 x 4 v_mfma_f32_32x32x2_f32 tiles, 256 fp32 per lane) and a 2 x 2 grid
+// of wavefronts per workgroup.  It is the 16-bit DMA kernel's structure with
+// fp32 elements: the byte geometry of its LDS stages is the same, so are its
+// copy counts per slice, waits and barrier placement.
+//
+//  * K advances in slices of 16.  Copies use buffer_load_dwordx4 ... lds:
+//    lane l's 16 bytes land at LDS base + 16*l; a swizzle is applied by the
+//    choice of which global chunk each lane fetches.  Each wave addresses its
+//    rows through a buffer descriptor (wave-uniform base, 32-bit lane
+//    offsets).
+//  * K-contiguous operand (A as M x K, B transposed as N x K): two LDS stages
+//    of two slices each, 256 rows of 128 B (32 floats; chunk q of row r at
+//    q ^ ((r ^ r>>3) & 7)).  A lane reads its 4 k of a half slice with one
+//    16-byte LDS read.
+//  * MN-contiguous operand (B as K x N, A transposed as K x M): four stages
+//    of one slice, 16 k-rows of 1024 B; chunk c of k-row k at c ^ 8((k>>3)&1),
+//    so the two half-wavefronts, which read k-rows 8 apart, use opposite
+//    halves of the LDS banks.  A lane reads one float per k (no transposing
+//    LDS read exists for 32-bit data).
+//  * The 32x32x2 instruction sums over two k, one per half-wavefront: half
+//    h feeds k = 8h + 4s + j at sub-step j of half slice s, so a lane's 4 k of
+//    a k-contiguous operand are adjacent; every product still lands in the
+//    same sum.
+//  * Per slice each wavefront issues 128 MFMAs in two half slices of 64; the
+//    LDS reads of the next half slice and the copies are spread between
+//    them.  The workgroup barrier sits between the two halves: it publishes
+//    slice t+1 and retires slice t's stage.
+//
+// Used for M and N multiples of 256, K a multiple of 64 (groups of four
+// slices), 16-byte aligned rows and row pitches below 2^23 elements (so 64
+// rows of lane offsets fit 32 bits), when its tiles fill the CUs at least as
+// well as the 128 x 128 register-staged kernel's, which takes every other
+// shape.
+#include <cmath>
+
+#include "gemm_common.hpp"
+
+namespace dgt {
+
+namespace {
+
+constexpr int BM = 256, BN = 256, BK = 16, NT = 256, NSTAGE = 4;
+constexpr int KC_STAGE = 256 * 128;  // 32 KiB: 256 rows x 128 B (two slices)
+constexpr int MN_STAGE = BK * 1024;  // 16 KiB: 16 k-rows x 1024 B (one slice)
+constexpr int CPOL = 1;              // sc0 on the copies
+constexpr int64_t kMaxPitchF32 = int64_t(1) << 23;
+constexpr double kSlots256 = 256, kSlots128 = 512;  // resident tiles of each kernel
+
+typedef __attribute__((address_space(3))) void lds_void;
+
+__device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
+__device__ __forceinline__ int swz_mn(int k) { return ((k >> 3) & 1) * 8; }
+
+// s_waitcnt vmcnt(n) with expcnt and lgkmcnt at their maxima (gfx9
+// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in 6:4,
+// lgkmcnt in 11:8); WAIT_VMCNT_LGKM0 also drains this wave's LDS reads.
+#define WAIT_VMCNT(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
+#define WAIT_VMCNT_LGKM0(n) \
+    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0070)
+
+// Workgroup barrier without a memory fence: LDS data written by copies is
+// published by each wave waiting for its own copies first.
+__device__ __forceinline__ void barrier() {
+    asm volatile("" ::: "memory");
+    __builtin_amdgcn_s_barrier();
+    asm volatile("" ::: "memory");
+}
+
+// Stage I of an operand, chosen at compile time so that every LDS access
+// names one __shared__ object (the compiler's wait-count pass then sees that
+// a copy in flight into one stage does not alias reads of another).
+template <int I>
+__device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3) {
+    if constexpr (I == 0) return s0;
+    else if constexpr (I == 1) return s1;
+    else if constexpr (I == 2) return s2;
+    else return s3;
+}
+
+// A K-contiguous operand: stage = a pair of slices, 256 rows x 128 B.  Wave w
+// issues copy instructions j = 8w + i (i = 0..7) per pair, instruction j
+// filling rows 8j .. 8j+7 (8 lanes per row), as two halves of 4.  The wave's
+// descriptor covers its 64 rows; pair pr adds 128*pr bytes through the
+// scalar offset.
+struct KcOperand {
+    const float* base;  // row 64*wave of the tile (wave-uniform)
+    uint32_t voff[8];   // lane byte offsets from base, per instruction
+    uint32_t bytes;     // descriptor range: the wave's 64 rows
+    int off[4][2][2];   // LDS read offset: tile t, slice-in-pair u, half slice s
+    int npair;
+
+    __device__ void init(const float* X, int64_t ld, int mn0, int w, int wave, int lane, int nk,
+                         int K) {
+#pragma unroll
+        for (int i = 0; i < 8; ++i) {
+            const int row = 8 * (8 * wave + i) + (lane >> 3);
+            const int q = (lane & 7) ^ swz_kc(row);
+            voff[i] = (uint32_t)(((int64_t)(row - 64 * wave) * ld + 4 * q) * 4);
+        }
+        base = X + (int64_t)(mn0 + 64 * wave) * ld;
+        bytes = (uint32_t)((63 * ld + K) * 4);
+        // rows w*128 + t*32 + l%32; half-wave h, half slice s read chunk 4u + 2h + s
+        const int h = lane >> 5;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int row = w * 128 + t * 32 + (lane & 31);
+#pragma unroll
+            for (int u = 0; u < 2; ++u)
+#pragma unroll
+                for (int s = 0; s < 2; ++s)
+                    off[t][u][s] = row * 128 + (((4 * u + 2 * h + s) ^ swz_kc(row)) << 4);
+        }
+        npair = nk / 2;
+    }
+    // Half `half` of pair pr into stage st (past the end: the last pair).
+    __device__ void copy(uint8_t* st, int pr, int half, int wave) const {
+        pr = pr < npair ? pr : npair - 1;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufferRsrcW3);
+#pragma unroll
+        for (int i = 4 * half; i < 4 * half + 4; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
+                                                     voff[i], (uint32_t)pr * 128, 0, CPOL);
+    }
+    // Operands of half slice s of the slice in half u of stage st: f[t][j] is
+    // k = 8h + 4s + j of row w*128 + t*32 + l%32.
+    __device__ void frags(const uint8_t* st, int u, int s, u32x4 (&f)[4]) const {
+#pragma unroll
+        for (int t = 0; t < 4; ++t) f[t] = *reinterpret_cast<const u32x4*>(st + off[t][u][s]);
+    }
+    static constexpr int kReads = 4;  // LDS reads per half slice
+};
+
+// An MN-contiguous operand: stage = one slice, 16 k-rows x 1024 B.  Wave w
+// issues j = 4w + i (i = 0..3) per slice, instruction j filling k-row j, as
+// two halves of 2.
+struct MnOperand {
+    const float* base;  // k-row 4*wave of slice 0, first column of the tile
+    uint32_t voff[4];   // lane byte offsets from base, per instruction
+    uint32_t bytes;     // descriptor range: 4 k-rows
+    int off[4];
+    int64_t slice;
+    int nk;
+
+    __device__ void init(const float* X, int64_t ld, int mn0, int w, int wave, int lane, int nk_) {
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int krow = 4 * wave + i;
+            const int c = lane ^ swz_mn(krow);
+            voff[i] = (uint32_t)(((int64_t)i * ld + 4 * c) * 4);
+        }
+        base = X + (int64_t)(4 * wave) * ld + mn0;
+        bytes = (uint32_t)(4 * ld * 4);
+        // lane (h, l%32) reads k-rows 8h + 4s + j, column w*128 + t*32 + l%32
+        const int h = lane >> 5, r = lane & 31;
+#pragma unroll
+        for (int t = 0; t < 4; ++t) {
+            const int chunk = (w * 32 + t * 8 + (r >> 2)) ^ (8 * h);
+            off[t] = 8 * h * 1024 + chunk * 16 + (r & 3) * 4;
+        }
+        slice = (int64_t)BK * ld;
+        nk = nk_;
+    }
+    // Half `half` of slice kt into stage st (past the end: the last slice).
+    __device__ void copy(uint8_t* st, int kt, int half, int wave) const {
+        kt = kt < nk ? kt : nk - 1;
+        const __amdgpu_buffer_rsrc_t rs =
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, bytes, kBufferRsrcW3);
+#pragma unroll
+        for (int i = 2 * half; i < 2 * half + 2; ++i)
+            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16,
+                                                     voff[i], 0, 0, CPOL);
+    }
+    __device__ void frags(const uint8_t* st, int s, u32x4 (&f)[4]) const {
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j)
+                f[t][j] = *reinterpret_cast<const uint32_t*>(st + off[t] + (4 * s + j) * 1024);
+    }
+    static constexpr int kReads = 16;
+};
+
+// Copies a wave has issued after the last one that slice kt+1 needs, at the
+// wait in slice kt (steady state; the prologue is laid out to match).  Per
+// slice: K-contiguous operands copy half a pair before the barrier of even
+// slices and after the barrier of odd ones (4 instructions each);
+// MN-contiguous ones copy half a slice before and half after every barrier
+// (2 each), and are issued first.
+template <bool AK, bool BKc, bool kEven>
+constexpr int copies_after() {
+    if (AK != BKc) return kEven ? 16 : 4;  // one operand of each kind
+    if (AK) return kEven ? 16 : 0;         // both K-contiguous
+    return 16;                             // both MN-contiguous
+}
+
+// Copies issued by the prologue after the last one slice 0 needs: every
+// MN-contiguous operand still has slices 1 and 2 (8) and half of slice 3 (2)
+// after it, every K-contiguous one the first half of pair 1 (4).
+template <bool AK, bool BKc>
+constexpr int prologue_after() {
+    constexpr int nmn = (AK ? 0 : 1) + (BKc ? 0 : 1), nkc = 2 - nmn;
+    return nmn ? 10 * nmn + 4 * nkc : 4 * nkc;
+}
+
+// TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
+// K-contiguous when TB.
+template <bool TA, bool TB>
+__global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int tiles_m,
+                                                            int tiles_n, int grouped) {
+    const TileIdx tile = xcd_tile(tiles_m, tiles_n, grouped != 0);
+    select_problem(p, tile.z);
+    constexpr bool AK = !TA, BKc = TB;
+    using OpA = typename std::conditional<AK, KcOperand, MnOperand>::type;
+    using OpB = typename std::conditional<BKc, KcOperand, MnOperand>::type;
+    constexpr int SA01 = AK ? KC_STAGE : MN_STAGE, SA23 = AK ? 16 : MN_STAGE;
+    constexpr int SB01 = BKc ? KC_STAGE : MN_STAGE, SB23 = BKc ? 16 : MN_STAGE;
+    // One LDS object per operand and stage (K-contiguous operands use two).
+    __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA01];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA01];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA2[SA23];
+    __shared__ __attribute__((aligned(1024))) uint8_t sA3[SA23];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB0[SB01];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB1[SB01];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB2[SB23];
+    __shared__ __attribute__((aligned(1024))) uint8_t sB3[SB23];
+
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
+    const int m0 = tile.bm * BM;
+    const int n0 = tile.bn * BN;
+    const int nk = p.K / BK;  // slices, a multiple of four
+
+    OpA opa;
+    OpB opb;
+    if constexpr (AK) opa.init(static_cast<const float*>(p.A), p.lda, m0, wm, wave, lane, nk, p.K);
+    else opa.init(static_cast<const float*>(p.A), p.lda, m0, wm, wave, lane, nk);
+    if constexpr (BKc) opb.init(static_cast<const float*>(p.B), p.ldb, n0, wn, wave, lane, nk, p.K);
+    else opb.init(static_cast<const float*>(p.B), p.ldb, n0, wn, wave, lane, nk);
+
+    floatx16 acc[4][4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i)
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
+
+    // Operands of half slice s of slice position J (0..3 within a group of
+    // four slices: a K-contiguous operand has it in stage J/2, half J%2; an
+    // MN-contiguous one in stage J).
+    auto frags = [&](auto Jc, int s, u32x4 (&a)[4], u32x4 (&b)[4]) {
+        constexpr int J = decltype(Jc)::value;
+        if constexpr (AK) opa.frags(pick<J / 2>(sA0, sA1, sA2, sA3), J % 2, s, a);
+        else opa.frags(pick<J>(sA0, sA1, sA2, sA3), s, a);
+        if constexpr (BKc) opb.frags(pick<J / 2>(sB0, sB1, sB2, sB3), J % 2, s, b);
+        else opb.frags(pick<J>(sB0, sB1, sB2, sB3), s, b);
+    };
+
+    // 64 MFMAs on (a, b): four sub-steps of 4 x 4 tiles.  The LDS reads and
+    // the copies issued just before in program order are spread between
+    // them (the reads evenly, a copy after every eighth MFMA), so the address
+    // unit never sees a burst that would hold the wave, and its MFMA issue,
+    // back.
+    constexpr int RD_EVERY = 64 / (OpA::kReads + OpB::kReads);
+    auto mfma_step = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+#pragma unroll
+            for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+                for (int tj = 0; tj < 4; ++tj)
+                    acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
+                        __uint_as_float(a[ti][j]), __uint_as_float(b[tj][j]), acc[ti][tj], 0, 0,
+                        0);
+#pragma unroll
+        for (int m = 0; m < 64; ++m) {
+            __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
+            if (m % RD_EVERY == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+            if (m % 8 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
+        }
+        __builtin_amdgcn_sched_barrier(0);
+    };
+
+    u32x4 a0[4], b0[4], a1[4], b1[4];
+
+    // Slice kt at position J of its group of four.  Copies, per wave:
+    //   before the barrier: MN-contiguous operands the second half of slice
+    //     kt+3 (into stage (J+3)%4); for even J, K-contiguous operands the
+    //     second half of pair kt/2+1 (into the other pair stage);
+    //   after the barrier: MN-contiguous operands the first half of slice
+    //     kt+4 into stage J (just retired); for odd J, K-contiguous operands
+    //     the first half of pair (kt+3)/2 into the pair stage retired by this
+    //     barrier.
+    // The barrier of slice kt publishes slice kt+1.
+    auto slice = [&](auto Jc, int kt) {
+        constexpr int J = decltype(Jc)::value;
+        constexpr bool kEven = J % 2 == 0;
+        frags(Jc, 1, a1, b1);  // second half-slice operands of this slice
+        if constexpr (!AK) opa.copy(pick<(J + 3) % 4>(sA0, sA1, sA2, sA3), kt + 3, 1, wave);
+        if constexpr (!BKc) opb.copy(pick<(J + 3) % 4>(sB0, sB1, sB2, sB3), kt + 3, 1, wave);
+        if constexpr (kEven && AK) opa.copy(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
+        if constexpr (kEven && BKc) opb.copy(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
+        mfma_step(a0, b0);  // first half slice (operands read earlier)
+        WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>()));  // own copies landed, reads returned
+        barrier();                                           // ... for every wave
+        frags(std::integral_constant<int, (J + 1) % 4>{}, 0, a0, b0);  // next slice, first half
+        if constexpr (!AK) opa.copy(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
+        if constexpr (!BKc) opb.copy(pick<J>(sB0, sB1, sB2, sB3), kt + NSTAGE, 0, wave);
+        if constexpr (!kEven && AK) opa.copy(pick<((J + 3) / 2) % 2>(sA0, sA1, sA2, sA3), (kt + 3) / 2, 0, wave);
+        if constexpr (!kEven && BKc) opb.copy(pick<((J + 3) / 2) % 2>(sB0, sB1, sB2, sB3), (kt + 3) / 2, 0, wave);
+        mfma_step(a1, b1);  // second half slice
+    };
+
+    // Prologue: K-contiguous operands pair 0; MN-contiguous ones slices 0..2
+    // and the first half of slice 3; then K-contiguous ones the first half of
+    // pair 1.
+    if constexpr (AK) { opa.copy(sA0, 0, 0, wave); opa.copy(sA0, 0, 1, wave); }
+    if constexpr (BKc) { opb.copy(sB0, 0, 0, wave); opb.copy(sB0, 0, 1, wave); }
+    if constexpr (!AK) { opa.copy(sA0, 0, 0, wave); opa.copy(sA0, 0, 1, wave); }
+    if constexpr (!BKc) { opb.copy(sB0, 0, 0, wave); opb.copy(sB0, 0, 1, wave); }
+    if constexpr (!AK) { opa.copy(sA1, 1, 0, wave); opa.copy(sA1, 1, 1, wave); }
+    if constexpr (!BKc) { opb.copy(sB1, 1, 0, wave); opb.copy(sB1, 1, 1, wave); }
+    if constexpr (!AK) { opa.copy(sA2, 2, 0, wave); opa.copy(sA2, 2, 1, wave); }
+    if constexpr (!BKc) { opb.copy(sB2, 2, 0, wave); opb.copy(sB2, 2, 1, wave); }
+    if constexpr (!AK) opa.copy(sA3, 3, 0, wave);
+    if constexpr (!BKc) opb.copy(sB3, 3, 0, wave);
+    if constexpr (AK) opa.copy(sA1, 1, 0, wave);
+    if constexpr (BKc) opb.copy(sB1, 1, 0, wave);
+    WAIT_VMCNT((prologue_after<AK, BKc>()));  // slice 0 of both operands landed
+    barrier();
+    frags(std::integral_constant<int, 0>{}, 0, a0, b0);
+    for (int kt = 0; kt < nk; kt += NSTAGE) {
+        slice(std::integral_constant<int, 0>{}, kt);
+        slice(std::integral_constant<int, 1>{}, kt + 1);
+        slice(std::integral_constant<int, 2>{}, kt + 2);
+        slice(std::integral_constant<int, 3>{}, kt + 3);
+    }
+    WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
+
+    // 32x32 accumulator layout: register r of lane l is row
+    // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the MFMA tile.  C is read only
+    // when beta != 0, an MFMA tile at a time, before those values are
+    // stored.  Without a bias the epilogue adds -0.0, which leaves every
+    // value, signed zeros included, unchanged.
+    const int col0 = n0 + wn * 128 + (lane & 31);
+    float* cbase = p.C + (int64_t)(m0 + wm * 128 + 4 * h) * p.ldc + col0;
+    const float alpha = p.alpha, beta = p.beta;
+    float bias[4];
+#pragma unroll
+    for (int tj = 0; tj < 4; ++tj) bias[tj] = p.bias ? p.bias[col0 + tj * 32] : -0.0f;
+    if (beta == 0.0f) {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
+                        alpha * acc[ti][tj][r] + bias[tj];
+    } else {
+#pragma unroll
+        for (int ti = 0; ti < 4; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < 4; ++tj) {
+                float cv[16];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    cv[r] = cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32];
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
+                        (alpha * acc[ti][tj][r] + beta * cv[r]) + bias[tj];
+            }
+    }
+}
+
+}  // namespace
+
+// Whole tiles, aligned rows, pitches within the buffer offsets, and a launch
+// this kernel fills better than the 128 x 128 kernel: its tiles run one per
+// CU at ~0.96 of the MFMA peak, the smaller ones two per CU at ~0.83, and
+// each loses what its last wave of tiles leaves idle.
+bool mfma_f32_dma_eligible(const GemmParams& p) {
+    if (!operands_16b_aligned(p, 4) || p.M <= 0 || p.N <= 0 || p.K <= 0) return false;
+    if (p.M % BM != 0 || p.N % BN != 0 || p.K % (BK * NSTAGE) != 0) return false;
+    if (p.lda >= kMaxPitchF32 || p.ldb >= kMaxPitchF32) return false;
+    const double t256 = (double)(p.M / BM) * (p.N / BN) * p.batch, t128 = 4.0 * t256;
+    const double fill256 = t256 / (kSlots256 * std::ceil(t256 / kSlots256));
+    const double fill128 = t128 / (kSlots128 * std::ceil(t128 / kSlots128));
+    return fill256 * 0.96 >= fill128 * 0.83;
+}
+
+hipError_t launch_mfma_f32_dma(const GemmParams& p, hipStream_t s) {
+    const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+    const int64_t blocks = (int64_t)tiles_m * tiles_n;
+    if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    return with_layout(p, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        const dim3 grid((unsigned)blocks, p.batch);
+        hipLaunchKernelGGL((mfma_f32_dma_kernel<TA, TB>), grid, dim3(NT), 0, s, p, tiles_m, tiles_n,
+                           1);
+        return hipGetLastError();
+    });
+}
+
+}  // namespace dgt
