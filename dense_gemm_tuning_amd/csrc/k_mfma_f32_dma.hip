@@ -32,11 +32,15 @@
 //    them.  The workgroup barrier sits between the two halves: it publishes
 //    slice t+1 and retires slice t's stage.
 //
-// Used for M and N multiples of 256, K a multiple of 64 (groups of four
-// slices), 16-byte aligned rows and row pitches below 2^23 elements (so 64
-// rows of lane offsets fit 32 bits), when its tiles fill the CUs at least as
-// well as the 128 x 128 register-staged kernel's, which takes every other
-// shape.
+// Used for any M, N and K with 16-byte aligned rows and row pitches below
+// 2^23 elements (so 64 rows of lane offsets fit 32 bits), when a simple
+// model of both kernels' waves of tiles says it finishes before the 128 x
+// 128 register-staged kernel, which takes every other shape.  On edge tiles
+// the copy descriptors' ranges stop at the operands' last elements and the
+// epilogue stores only the valid part.  When K is not a multiple of 64 the
+// last group of 1 to 4 slices runs after the loop; in a partial last slice
+// the k-contiguous fragments are masked past K, and m/n-contiguous rows past
+// K read as zeros through the descriptor range.
 #include <cmath>
 
 #include "gemm_common.hpp"
@@ -53,6 +57,14 @@ constexpr int64_t kMaxPitchF32 = int64_t(1) << 23;
 constexpr double kSlots256 = 256, kSlots128 = 512;  // resident tiles of each kernel
 
 typedef __attribute__((address_space(3))) void lds_void;
+
+// A copy descriptor's range ends at an operand's last element rounded up to
+// a whole 16-byte chunk: the hardware returns zeros for a 16-byte load that
+// reaches past the range, even for its bytes inside it.  The rounding never
+// reads another page (a 16-byte aligned chunk lies within one), and what it
+// reads past the element only feeds outputs that are not stored or k that
+// are masked.
+__device__ __forceinline__ int round4(int n) { return (n + 3) & ~3; }
 
 __device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
 __device__ __forceinline__ int swz_mn(int k) { return ((k >> 3) & 1) * 8; }
@@ -96,8 +108,14 @@ struct KcOperand {
     int off[4][2][2];   // LDS read offset: tile t, slice-in-pair u, half slice s
     int npair;
 
+    // mn0: first row (m or n) of the workgroup tile; w: this wave's half of
+    // it (wm or wn); mn_lim: rows of the operand (M or N), K its row length.
+    // The descriptor range ends at the wave's last element (k = K - 1 of its
+    // last row, or of row mn_lim - 1 on an edge tile), so rows past mn_lim
+    // and the k past K of a final half pair are never read from memory.
+    template <bool kEdge>
     __device__ void init(const float* X, int64_t ld, int mn0, int w, int wave, int lane, int nk,
-                         int K) {
+                         int mn_lim, int K) {
 #pragma unroll
         for (int i = 0; i < 8; ++i) {
             const int row = 8 * (8 * wave + i) + (lane >> 3);
@@ -105,7 +123,9 @@ struct KcOperand {
             voff[i] = (uint32_t)(((int64_t)(row - 64 * wave) * ld + 4 * q) * 4);
         }
         base = X + (int64_t)(mn0 + 64 * wave) * ld;
-        bytes = (uint32_t)((63 * ld + K) * 4);
+        int rows = 64;
+        if constexpr (kEdge) rows = min(64, mn_lim - (mn0 + 64 * wave));
+        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round4(K)) * 4);
         // rows w*128 + t*32 + l%32; half-wave h, half slice s read chunk 4u + 2h + s
         const int h = lane >> 5;
 #pragma unroll
@@ -117,17 +137,32 @@ struct KcOperand {
                 for (int s = 0; s < 2; ++s)
                     off[t][u][s] = row * 128 + (((4 * u + 2 * h + s) ^ swz_kc(row)) << 4);
         }
-        npair = nk / 2;
+        npair = (nk + 1) / 2;  // an odd slice count ends with half a pair
     }
     // Half `half` of pair pr into stage st (past the end: the last pair).
+    // With a K tail (kTail) the descriptor starts at the pair, so the whole
+    // offset of every lane is range-checked (the scalar offset is not) and
+    // the k past K of a final half pair is never read; pair and range are
+    // wave-uniform, which readfirstlane tells the compiler.  Otherwise every
+    // k read is below K and the pair's offset goes in the scalar offset.
+    template <bool kEdge = false, bool kTail = false>
     __device__ void copy(uint8_t* st, int pr, int half, int wave) const {
         pr = pr < npair ? pr : npair - 1;
+        const uint8_t* from = reinterpret_cast<const uint8_t*>(base);
+        uint32_t range = bytes, soff = (uint32_t)pr * 128;
+        if constexpr (kTail) {
+            pr = __builtin_amdgcn_readfirstlane(pr);
+            const uint32_t skip = (uint32_t)pr * 128;
+            range = __builtin_amdgcn_readfirstlane(bytes > skip ? bytes - skip : 0u);
+            from += skip;
+            soff = 0;
+        }
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)base, 0, bytes, kBufferRsrcW3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)from, 0, range, kBufferRsrcW3);
 #pragma unroll
         for (int i = 4 * half; i < 4 * half + 4; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
-                                                     voff[i], (uint32_t)pr * 128, 0, CPOL);
+                                                     voff[i], soff, 0, CPOL);
     }
     // Operands of half slice s of the slice in half u of stage st: f[t][j] is
     // k = 8h + 4s + j of row w*128 + t*32 + l%32.
@@ -148,8 +183,18 @@ struct MnOperand {
     int off[4];
     int64_t slice;
     int nk;
+    int64_t ld_;
+    int rows_left0;     // k-rows from this wave's first one to the end
+    int cols;           // valid columns of the tile, rounded to a chunk (edge tiles)
 
-    __device__ void init(const float* X, int64_t ld, int mn0, int w, int wave, int lane, int nk_) {
+    // mn_lim, K: columns and rows of the stored operand.  On an edge tile the
+    // range of slice kt's descriptor stops at the operand's last element;
+    // columns past mn_lim in earlier rows are read (they belong to the next
+    // row) but only feed outputs the epilogue does not store, and k-rows
+    // past K read as zeros.
+    template <bool kEdge>
+    __device__ void init(const float* X, int64_t ld, int mn0, int w, int wave, int lane, int nk_,
+                         int mn_lim, int K) {
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
             const int krow = 4 * wave + i;
@@ -167,12 +212,21 @@ struct MnOperand {
         }
         slice = (int64_t)BK * ld;
         nk = nk_;
+        ld_ = ld;
+        rows_left0 = K - 4 * wave;
+        cols = kEdge ? round4(mn_lim - mn0) : 0;
     }
     // Half `half` of slice kt into stage st (past the end: the last slice).
+    template <bool kEdge = false, bool kTail = false>
     __device__ void copy(uint8_t* st, int kt, int half, int wave) const {
         kt = kt < nk ? kt : nk - 1;
+        uint32_t range = bytes;
+        if constexpr (kEdge) {
+            const int64_t end = (int64_t)(rows_left0 - BK * kt - 1) * ld_ + cols;  // elements
+            if (end < 4 * ld_) range = end <= 0 ? 0u : (uint32_t)(end * 4);
+        }
         const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, bytes, kBufferRsrcW3);
+            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, range, kBufferRsrcW3);
 #pragma unroll
         for (int i = 2 * half; i < 2 * half + 2; ++i)
             __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16,
@@ -212,7 +266,11 @@ constexpr int prologue_after() {
 
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
-template <bool TA, bool TB>
+// kEdge: M or N not a multiple of the tile (edge tiles read through
+// clipped descriptor ranges and store only their valid part).  kTail: K is
+// not a multiple of 64 (a last group of 1 to 4 slices after the loop, the
+// last slice possibly partial).
+template <bool TA, bool TB, bool kEdge, bool kTail>
 __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int tiles_m,
                                                             int tiles_n, int grouped) {
     const TileIdx tile = xcd_tile(tiles_m, tiles_n, grouped != 0);
@@ -237,14 +295,14 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
     const int m0 = tile.bm * BM;
     const int n0 = tile.bn * BN;
-    const int nk = p.K / BK;  // slices, a multiple of four
+    const int nk = (p.K + BK - 1) / BK;  // slices (the last one partial when K % 16 != 0)
 
     OpA opa;
     OpB opb;
-    if constexpr (AK) opa.init(static_cast<const float*>(p.A), p.lda, m0, wm, wave, lane, nk, p.K);
-    else opa.init(static_cast<const float*>(p.A), p.lda, m0, wm, wave, lane, nk);
-    if constexpr (BKc) opb.init(static_cast<const float*>(p.B), p.ldb, n0, wn, wave, lane, nk, p.K);
-    else opb.init(static_cast<const float*>(p.B), p.ldb, n0, wn, wave, lane, nk);
+    opa.template init<kEdge>(static_cast<const float*>(p.A), p.lda, m0, wm, wave, lane, nk, p.M,
+                             p.K);
+    opb.template init<kEdge>(static_cast<const float*>(p.B), p.ldb, n0, wn, wave, lane, nk, p.N,
+                             p.K);
 
     floatx16 acc[4][4];
 #pragma unroll
@@ -301,48 +359,78 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     //     the first half of pair (kt+3)/2 into the pair stage retired by this
     //     barrier.
     // The barrier of slice kt publishes slice kt+1.
-    auto slice = [&](auto Jc, int kt) {
+    // In a partial last slice (K % 16 != 0), k-contiguous fragments hold
+    // whatever follows k = K - 1 in the row; they are masked to zero element
+    // by element (a lane's fragment of half slice s holds k = 16kt + 8h + 4s
+    // .. +3).  m/n-contiguous operands need no mask: their rows past K lie
+    // past the copy descriptor's range and read as zeros.
+    auto mask_k = [&](int kt, int s, u32x4 (&f)[4]) {
+        const int valid = p.K - (BK * kt + 8 * h + 4 * s);  // of the 4 still below K
+#pragma unroll
+        for (int t = 0; t < 4; ++t)
+#pragma unroll
+            for (int j = 0; j < 4; ++j) f[t][j] = j < valid ? f[t][j] : 0u;
+    };
+    auto slice = [&](auto Jc, int kt, auto maskc) {
         constexpr int J = decltype(Jc)::value;
         constexpr bool kEven = J % 2 == 0;
+        constexpr bool kMask = decltype(maskc)::value;
         frags(Jc, 1, a1, b1);  // second half-slice operands of this slice
-        if constexpr (!AK) opa.copy(pick<(J + 3) % 4>(sA0, sA1, sA2, sA3), kt + 3, 1, wave);
-        if constexpr (!BKc) opb.copy(pick<(J + 3) % 4>(sB0, sB1, sB2, sB3), kt + 3, 1, wave);
-        if constexpr (kEven && AK) opa.copy(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
-        if constexpr (kEven && BKc) opb.copy(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
+        if constexpr (kMask) {
+            if (kt == nk - 1 && p.K % BK != 0) {
+                if constexpr (AK) { mask_k(kt, 0, a0); mask_k(kt, 1, a1); }
+                if constexpr (BKc) { mask_k(kt, 0, b0); mask_k(kt, 1, b1); }
+            }
+        }
+        if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<(J + 3) % 4>(sA0, sA1, sA2, sA3), kt + 3, 1, wave);
+        if constexpr (!BKc) opb.template copy<kEdge, kTail>(pick<(J + 3) % 4>(sB0, sB1, sB2, sB3), kt + 3, 1, wave);
+        if constexpr (kEven && AK) opa.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
+        if constexpr (kEven && BKc) opb.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
         mfma_step(a0, b0);  // first half slice (operands read earlier)
         WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>()));  // own copies landed, reads returned
         barrier();                                           // ... for every wave
         frags(std::integral_constant<int, (J + 1) % 4>{}, 0, a0, b0);  // next slice, first half
-        if constexpr (!AK) opa.copy(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
-        if constexpr (!BKc) opb.copy(pick<J>(sB0, sB1, sB2, sB3), kt + NSTAGE, 0, wave);
-        if constexpr (!kEven && AK) opa.copy(pick<((J + 3) / 2) % 2>(sA0, sA1, sA2, sA3), (kt + 3) / 2, 0, wave);
-        if constexpr (!kEven && BKc) opb.copy(pick<((J + 3) / 2) % 2>(sB0, sB1, sB2, sB3), (kt + 3) / 2, 0, wave);
+        if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
+        if constexpr (!BKc) opb.template copy<kEdge, kTail>(pick<J>(sB0, sB1, sB2, sB3), kt + NSTAGE, 0, wave);
+        if constexpr (!kEven && AK) opa.template copy<kEdge, kTail>(pick<((J + 3) / 2) % 2>(sA0, sA1, sA2, sA3), (kt + 3) / 2, 0, wave);
+        if constexpr (!kEven && BKc) opb.template copy<kEdge, kTail>(pick<((J + 3) / 2) % 2>(sB0, sB1, sB2, sB3), (kt + 3) / 2, 0, wave);
         mfma_step(a1, b1);  // second half slice
     };
 
     // Prologue: K-contiguous operands pair 0; MN-contiguous ones slices 0..2
     // and the first half of slice 3; then K-contiguous ones the first half of
     // pair 1.
-    if constexpr (AK) { opa.copy(sA0, 0, 0, wave); opa.copy(sA0, 0, 1, wave); }
-    if constexpr (BKc) { opb.copy(sB0, 0, 0, wave); opb.copy(sB0, 0, 1, wave); }
-    if constexpr (!AK) { opa.copy(sA0, 0, 0, wave); opa.copy(sA0, 0, 1, wave); }
-    if constexpr (!BKc) { opb.copy(sB0, 0, 0, wave); opb.copy(sB0, 0, 1, wave); }
-    if constexpr (!AK) { opa.copy(sA1, 1, 0, wave); opa.copy(sA1, 1, 1, wave); }
-    if constexpr (!BKc) { opb.copy(sB1, 1, 0, wave); opb.copy(sB1, 1, 1, wave); }
-    if constexpr (!AK) { opa.copy(sA2, 2, 0, wave); opa.copy(sA2, 2, 1, wave); }
-    if constexpr (!BKc) { opb.copy(sB2, 2, 0, wave); opb.copy(sB2, 2, 1, wave); }
-    if constexpr (!AK) opa.copy(sA3, 3, 0, wave);
-    if constexpr (!BKc) opb.copy(sB3, 3, 0, wave);
-    if constexpr (AK) opa.copy(sA1, 1, 0, wave);
-    if constexpr (BKc) opb.copy(sB1, 1, 0, wave);
+    if constexpr (AK) { opa.template copy<kEdge, kTail>(sA0, 0, 0, wave); opa.template copy<kEdge, kTail>(sA0, 0, 1, wave); }
+    if constexpr (BKc) { opb.template copy<kEdge, kTail>(sB0, 0, 0, wave); opb.template copy<kEdge, kTail>(sB0, 0, 1, wave); }
+    if constexpr (!AK) { opa.template copy<kEdge, kTail>(sA0, 0, 0, wave); opa.template copy<kEdge, kTail>(sA0, 0, 1, wave); }
+    if constexpr (!BKc) { opb.template copy<kEdge, kTail>(sB0, 0, 0, wave); opb.template copy<kEdge, kTail>(sB0, 0, 1, wave); }
+    if constexpr (!AK) { opa.template copy<kEdge, kTail>(sA1, 1, 0, wave); opa.template copy<kEdge, kTail>(sA1, 1, 1, wave); }
+    if constexpr (!BKc) { opb.template copy<kEdge, kTail>(sB1, 1, 0, wave); opb.template copy<kEdge, kTail>(sB1, 1, 1, wave); }
+    if constexpr (!AK) { opa.template copy<kEdge, kTail>(sA2, 2, 0, wave); opa.template copy<kEdge, kTail>(sA2, 2, 1, wave); }
+    if constexpr (!BKc) { opb.template copy<kEdge, kTail>(sB2, 2, 0, wave); opb.template copy<kEdge, kTail>(sB2, 2, 1, wave); }
+    if constexpr (!AK) opa.template copy<kEdge, kTail>(sA3, 3, 0, wave);
+    if constexpr (!BKc) opb.template copy<kEdge, kTail>(sB3, 3, 0, wave);
+    if constexpr (AK) opa.template copy<kEdge, kTail>(sA1, 1, 0, wave);
+    if constexpr (BKc) opb.template copy<kEdge, kTail>(sB1, 1, 0, wave);
     WAIT_VMCNT((prologue_after<AK, BKc>()));  // slice 0 of both operands landed
     barrier();
     frags(std::integral_constant<int, 0>{}, 0, a0, b0);
-    for (int kt = 0; kt < nk; kt += NSTAGE) {
-        slice(std::integral_constant<int, 0>{}, kt);
-        slice(std::integral_constant<int, 1>{}, kt + 1);
-        slice(std::integral_constant<int, 2>{}, kt + 2);
-        slice(std::integral_constant<int, 3>{}, kt + 3);
+    using NoMask = std::false_type;
+    int kt = 0;
+    // with a K tail the last group (1 to 4 slices, the last possibly
+    // partial) runs after the loop
+    for (; kt + NSTAGE < nk + (kTail ? 0 : 1); kt += NSTAGE) {
+        slice(std::integral_constant<int, 0>{}, kt, NoMask{});
+        slice(std::integral_constant<int, 1>{}, kt + 1, NoMask{});
+        slice(std::integral_constant<int, 2>{}, kt + 2, NoMask{});
+        slice(std::integral_constant<int, 3>{}, kt + 3, NoMask{});
+    }
+    if constexpr (kTail) {
+        const int rest = nk - kt;
+        slice(std::integral_constant<int, 0>{}, kt, std::true_type{});
+        if (rest >= 2) slice(std::integral_constant<int, 1>{}, kt + 1, std::true_type{});
+        if (rest >= 3) slice(std::integral_constant<int, 2>{}, kt + 2, std::true_type{});
+        if (rest >= 4) slice(std::integral_constant<int, 3>{}, kt + 3, std::true_type{});
     }
     WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
 
@@ -350,13 +438,22 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the MFMA tile.  C is read only
     // when beta != 0, an MFMA tile at a time, before those values are
     // stored.  Without a bias the epilogue adds -0.0, which leaves every
-    // value, signed zeros included, unchanged.
-    const int col0 = n0 + wn * 128 + (lane & 31);
-    float* cbase = p.C + (int64_t)(m0 + wm * 128 + 4 * h) * p.ldc + col0;
+    // value, signed zeros included, unchanged.  The lane index is counted
+    // afresh here rather than kept live through the K loop.
+    const int el = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
+    const int eh = el >> 5;
+    const int col0 = n0 + wn * 128 + (el & 31);
+    float* cbase = p.C + (int64_t)(m0 + wm * 128 + 4 * eh) * p.ldc + col0;
     const float alpha = p.alpha, beta = p.beta;
     float bias[4];
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj) bias[tj] = p.bias ? p.bias[col0 + tj * 32] : -0.0f;
+    for (int tj = 0; tj < 4; ++tj)
+        bias[tj] = p.bias && (!kEdge || col0 + tj * 32 < p.N) ? p.bias[col0 + tj * 32] : -0.0f;
+    // on edge tiles only rows < M and columns < N are stored
+    const int row0 = m0 + wm * 128 + 4 * eh;
+    auto ok = [&](int ti, int tj, int r) {
+        return !kEdge || (row0 + ti * 32 + 8 * (r >> 2) + (r & 3) < p.M && col0 + tj * 32 < p.N);
+    };
     if (beta == 0.0f) {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -364,8 +461,9 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
             for (int tj = 0; tj < 4; ++tj)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
-                        alpha * acc[ti][tj][r] + bias[tj];
+                    if (ok(ti, tj, r))
+                        cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
+                            alpha * acc[ti][tj][r] + bias[tj];
     } else {
 #pragma unroll
         for (int ti = 0; ti < 4; ++ti)
@@ -374,40 +472,52 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
                 float cv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    cv[r] = cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32];
+                    cv[r] = ok(ti, tj, r)
+                                ? cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32]
+                                : 0.0f;
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
-                    cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
-                        (alpha * acc[ti][tj][r] + beta * cv[r]) + bias[tj];
+                    if (ok(ti, tj, r))
+                        cbase[(int64_t)(ti * 32 + 8 * (r >> 2) + (r & 3)) * p.ldc + tj * 32] =
+                            (alpha * acc[ti][tj][r] + beta * cv[r]) + bias[tj];
             }
     }
 }
 
 }  // namespace
 
-// Whole tiles, aligned rows, pitches within the buffer offsets, and a launch
-// this kernel fills better than the 128 x 128 kernel: its tiles run one per
-// CU at ~0.96 of the MFMA peak, the smaller ones two per CU at ~0.83, and
-// each loses what its last wave of tiles leaves idle.
+// Aligned rows, pitches within the buffer offsets, and a launch this kernel
+// finishes sooner than the 128 x 128 kernel by a simple model: its tiles run
+// one per CU at ~0.96 of the MFMA peak, the smaller ones two per CU at ~0.83
+// (each a quarter of the work), and each kernel takes as many waves of
+// tiles as its resident slots need.
 bool mfma_f32_dma_eligible(const GemmParams& p) {
     if (!operands_16b_aligned(p, 4) || p.M <= 0 || p.N <= 0 || p.K <= 0) return false;
-    if (p.M % BM != 0 || p.N % BN != 0 || p.K % (BK * NSTAGE) != 0) return false;
     if (p.lda >= kMaxPitchF32 || p.ldb >= kMaxPitchF32) return false;
-    const double t256 = (double)(p.M / BM) * (p.N / BN) * p.batch, t128 = 4.0 * t256;
-    const double fill256 = t256 / (kSlots256 * std::ceil(t256 / kSlots256));
-    const double fill128 = t128 / (kSlots128 * std::ceil(t128 / kSlots128));
-    return fill256 * 0.96 >= fill128 * 0.83;
+    const double t256 = (double)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
+    const double t128 = (double)((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    const double time256 = std::ceil(t256 / kSlots256) * 4.0 / 0.96;
+    const double time128 = std::ceil(t128 / kSlots128) * 2.0 / 0.83;
+    return time256 <= time128;
 }
 
 hipError_t launch_mfma_f32_dma(const GemmParams& p, hipStream_t s) {
-    const int tiles_m = p.M / BM, tiles_n = p.N / BN;
+    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool edge = p.M % BM != 0 || p.N % BN != 0;
+    const bool tail = p.K % (BK * NSTAGE) != 0;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         const dim3 grid((unsigned)blocks, p.batch);
-        hipLaunchKernelGGL((mfma_f32_dma_kernel<TA, TB>), grid, dim3(NT), 0, s, p, tiles_m, tiles_n,
-                           1);
+        auto go = [&](auto kernel) {
+            hipLaunchKernelGGL(kernel, grid, dim3(NT), 0, s, p, tiles_m, tiles_n, 1);
+        };
+        // a K tail takes the edge-tile instance whatever M and N (its guards
+        // then always pass)
+        if (tail) go(mfma_f32_dma_kernel<TA, TB, true, true>);
+        else if (edge) go(mfma_f32_dma_kernel<TA, TB, true, false>);
+        else go(mfma_f32_dma_kernel<TA, TB, false, false>);
         return hipGetLastError();
     });
 }
