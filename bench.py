@@ -69,7 +69,7 @@ DOMINANT = {
     "f16_8192": ("mfma16_dma_kernel<F16, NN>", "k_mfma_bf16_dma.hip",
                  r"mfma16_dma_kernel<\(dgt::In\)2, false, false, false, false>"),
     "f32_4096": ("mfma_f32_dma_kernel<NN>", "k_mfma_f32_dma.hip",
-                 r"mfma_f32_dma_kernel<false, false>"),
+                 r"mfma_f32_dma_kernel<false, false, false, false>"),
     "bf16_skinny_8x28672x8192": ("skinny16_kernel<BF16, NN, 1 row block>", "k_skinny16.hip",
                                  r"skinny16_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_8192_nt": ("mfma16_dma_kernel<BF16, NT>", "k_mfma_bf16_dma.hip",
