@@ -194,8 +194,8 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
 
 }  // namespace
 
-// Whole 256 x 256 tiles with enough of them for every CU take the DMA kernel
-// (one wavefront per SIMD, 128 x 128 per wavefront); other shapes this one.
+// Operands with 16-byte aligned rows take the DMA kernel (256- or 128-tiles
+// held in accumulation registers); unaligned ones this one.
 hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
     if (mfma_f32_dma_eligible(p)) return launch_mfma_f32_dma(p, s);
     const int tiles_n = (p.N + BN - 1) / BN;

@@ -1,13 +1,13 @@
-// k_mfma_f32_dma.hip -- FP32 GEMM on whole 256 x 256 tiles: global -> LDS by
-// DMA up to three K slices ahead, one wavefront per SIMD.
+// k_mfma_f32_dma.hip -- FP32 GEMM: global -> LDS by DMA up to three K
+// slices ahead, a wavefront's tile of C held in accumulation registers.
 //
 // The pages' register-tiled SGEMM (dilfish.github.io 5.4: block tile, a
 // per-thread register tile, double buffering) becomes, on the matrix cores,
-// a 128 x 128 tile of C per wavefront held in accumulation registers
-// (4 x 4 v_mfma_f32_32x32x2_f32 tiles, 256 fp32 per lane) and a 2 x 2 grid
-// of wavefronts per workgroup.  It is the 16-bit DMA kernel's structure with
-// fp32 elements: the byte geometry of its LDS stages is the same, so are its
-// copy counts per slice, waits and barrier placement.
+// an R/2 x R/2 tile of C per wavefront (R/64 x R/64 v_mfma_f32_32x32x2_f32
+// tiles) and a 2 x 2 grid of wavefronts per R x R workgroup tile.  It is
+// the 16-bit DMA kernel's structure with fp32 elements: at R = 256 the byte
+// geometry of its LDS stages is the same, so are its copy counts per slice,
+// waits and barrier placement.
 //
 //  * K advances in slices of 16.  Copies use buffer_load_dwordx4 ... lds:
 //    lane l's 16 bytes land at LDS base + 16*l; a swizzle is applied by the
@@ -15,46 +15,60 @@
 //    rows through a buffer descriptor (wave-uniform base, 32-bit lane
 //    offsets).
 //  * K-contiguous operand (A as M x K, B transposed as N x K): two LDS stages
-//    of two slices each, 256 rows of 128 B (32 floats; chunk q of row r at
+//    of two slices each, R rows of 128 B (32 floats; chunk q of row r at
 //    q ^ ((r ^ r>>3) & 7)).  A lane reads its 4 k of a half slice with one
 //    16-byte LDS read.
 //  * MN-contiguous operand (B as K x N, A transposed as K x M): four stages
-//    of one slice, 16 k-rows of 1024 B; chunk c of k-row k at c ^ 8((k>>3)&1),
-//    so the two half-wavefronts, which read k-rows 8 apart, use opposite
-//    halves of the LDS banks.  A lane reads one float per k (no transposing
-//    LDS read exists for 32-bit data).
+//    of one slice, 16 k-rows of 4R bytes; chunk c of k-row k at
+//    c ^ 8((k>>3)&1), so the two half-wavefronts, which read k-rows 8 apart,
+//    use opposite halves of the LDS banks.  A lane reads one float per k (no
+//    transposing LDS read exists for 32-bit data).
 //  * The 32x32x2 instruction sums over two k, one per half-wavefront: half
 //    h feeds k = 8h + 4s + j at sub-step j of half slice s, so a lane's 4 k of
 //    a k-contiguous operand are adjacent; every product still lands in the
 //    same sum.
-//  * Per slice each wavefront issues 128 MFMAs in two half slices of 64; the
-//    LDS reads of the next half slice and the copies are spread between
+//  * Per slice each wavefront issues 8 (R/64)^2 MFMAs in two half slices;
+//    the LDS reads of the next half slice and the copies are spread between
 //    them.  The workgroup barrier sits between the two halves: it publishes
 //    slice t+1 and retires slice t's stage.
 //
-// Used for any M, N and K with 16-byte aligned rows and row pitches below
-// 2^23 elements (so 64 rows of lane offsets fit 32 bits), when a simple
-// model of both kernels' waves of tiles says it finishes before the 128 x
-// 128 register-staged kernel, which takes every other shape.  On edge tiles
+// Tiles of 256 x 256 (one workgroup per CU) or 128 x 128 (two per CU, each
+// wave 64 x 64), chosen per launch by the waves of tiles the CUs work
+// through.  Used for any M, N and K with 16-byte aligned rows and row
+// pitches below 2^23 elements (so a wave's rows of lane offsets fit 32
+// bits); the register-staged 128 x 128 kernel takes unaligned operands.  On edge tiles
 // the copy descriptors' ranges stop at the operands' last elements and the
 // epilogue stores only the valid part.  When K is not a multiple of 64 the
 // last group of 1 to 4 slices runs after the loop; in a partial last slice
 // the k-contiguous fragments are masked past K, and m/n-contiguous rows past
 // K read as zeros through the descriptor range.
-#include <cmath>
-
 #include "gemm_common.hpp"
 
 namespace dgt {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 16, NT = 256, NSTAGE = 4;
-constexpr int KC_STAGE = 256 * 128;  // 32 KiB: 256 rows x 128 B (two slices)
-constexpr int MN_STAGE = BK * 1024;  // 16 KiB: 16 k-rows x 1024 B (one slice)
+constexpr int BK = 16, NT = 256, NSTAGE = 4;
 constexpr int CPOL = 1;              // sc0 on the copies
+
+// Geometry of a workgroup tile of R x R (R = 256 or 128; a 2 x 2 grid of
+// wavefronts of R/2 x R/2).  A k-contiguous stage holds R rows of 128 B (two
+// slices), copied 8 rows per instruction; an m/n-contiguous stage holds 16
+// k-rows of 4R bytes, 256/R k-rows per instruction; each wave copies a
+// quarter of either.
+template <int R>
+struct Geo {
+    static constexpr int TM = R / 64;         // 32 x 32 MFMA tiles per wave and dimension
+    static constexpr int KC_ROWS = R / 4;     // k-contiguous rows per wave
+    static constexpr int KC_INSTR = R / 32;   // their copy instructions per pair
+    static constexpr int KC_STAGE = R * 128;  // bytes
+    static constexpr int MN_ROW = 4 * R;      // bytes per k-row
+    static constexpr int MN_LPR = R / 4;      // 16-byte chunks (lanes) per k-row
+    static constexpr int MN_INSTR = R / 64;   // copy instructions per slice and wave
+    static constexpr int MN_STAGE = BK * MN_ROW;
+};
 constexpr int64_t kMaxPitchF32 = int64_t(1) << 23;
-constexpr double kSlots256 = 256, kSlots128 = 512;  // resident tiles of each kernel
+constexpr int64_t kCUs = 256;
 
 typedef __attribute__((address_space(3))) void lds_void;
 
@@ -85,6 +99,17 @@ __device__ __forceinline__ void barrier() {
     asm volatile("" ::: "memory");
 }
 
+// One 16-byte-per-lane copy, global -> LDS, through a buffer descriptor of
+// `range` bytes from `base`: lane l's bytes at base + voff + soff land at
+// lds + 16*l.  (A plain function: the host pass of the templates below then
+// never sees the device-only descriptor type.)
+__device__ __forceinline__ void dma16(const void* base, uint32_t range, uint8_t* lds,
+                                      uint32_t voff, uint32_t soff) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, range, kBufferRsrcW3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, CPOL);
+}
+
 // Stage I of an operand, chosen at compile time so that every LDS access
 // names one __shared__ object (the compiler's wait-count pass then sees that
 // a copy in flight into one stage does not alias reads of another).
@@ -96,16 +121,17 @@ __device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, 
     else return s3;
 }
 
-// A K-contiguous operand: stage = a pair of slices, 256 rows x 128 B.  Wave w
-// issues copy instructions j = 8w + i (i = 0..7) per pair, instruction j
-// filling rows 8j .. 8j+7 (8 lanes per row), as two halves of 4.  The wave's
-// descriptor covers its 64 rows; pair pr adds 128*pr bytes through the
-// scalar offset.
+// A K-contiguous operand: stage = a pair of slices, R rows x 128 B.  Wave w
+// issues copy instructions j = (R/32)w + i per pair, instruction j filling
+// rows 8j .. 8j+7 (8 lanes per row), as two halves.  The wave's descriptor
+// covers its R/4 rows; pair pr adds 128*pr bytes through the scalar offset.
+template <int R>
 struct KcOperand {
-    const float* base;  // row 64*wave of the tile (wave-uniform)
-    uint32_t voff[8];   // lane byte offsets from base, per instruction
-    uint32_t bytes;     // descriptor range: the wave's 64 rows
-    int off[4][2][2];   // LDS read offset: tile t, slice-in-pair u, half slice s
+    using G = Geo<R>;
+    const float* base;             // row (R/4)*wave of the tile (wave-uniform)
+    uint32_t voff[G::KC_INSTR];    // lane byte offsets from base, per instruction
+    uint32_t bytes;                // descriptor range: the wave's rows
+    int off[G::TM][2][2];          // LDS read offset: tile t, slice-in-pair u, half slice s
     int npair;
 
     // mn0: first row (m or n) of the workgroup tile; w: this wave's half of
@@ -117,20 +143,20 @@ struct KcOperand {
     __device__ void init(const float* X, int64_t ld, int mn0, int w, int wave, int lane, int nk,
                          int mn_lim, int K) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = 8 * (8 * wave + i) + (lane >> 3);
+        for (int i = 0; i < G::KC_INSTR; ++i) {
+            const int row = 8 * (G::KC_INSTR * wave + i) + (lane >> 3);
             const int q = (lane & 7) ^ swz_kc(row);
-            voff[i] = (uint32_t)(((int64_t)(row - 64 * wave) * ld + 4 * q) * 4);
+            voff[i] = (uint32_t)(((int64_t)(row - G::KC_ROWS * wave) * ld + 4 * q) * 4);
         }
-        base = X + (int64_t)(mn0 + 64 * wave) * ld;
-        int rows = 64;
-        if constexpr (kEdge) rows = min(64, mn_lim - (mn0 + 64 * wave));
+        base = X + (int64_t)(mn0 + G::KC_ROWS * wave) * ld;
+        int rows = G::KC_ROWS;
+        if constexpr (kEdge) rows = min(G::KC_ROWS, mn_lim - (mn0 + G::KC_ROWS * wave));
         bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round4(K)) * 4);
-        // rows w*128 + t*32 + l%32; half-wave h, half slice s read chunk 4u + 2h + s
+        // rows w*R/2 + t*32 + l%32; half-wave h, half slice s read chunk 4u + 2h + s
         const int h = lane >> 5;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int row = w * 128 + t * 32 + (lane & 31);
+        for (int t = 0; t < G::TM; ++t) {
+            const int row = w * (R / 2) + t * 32 + (lane & 31);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -157,30 +183,32 @@ struct KcOperand {
             from += skip;
             soff = 0;
         }
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)from, 0, range, kBufferRsrcW3);
+        constexpr int HALF = G::KC_INSTR / 2;
 #pragma unroll
-        for (int i = 4 * half; i < 4 * half + 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
-                                                     voff[i], soff, 0, CPOL);
+        for (int i = HALF * half; i < HALF * half + HALF; ++i)
+            dma16(from, range, st + (G::KC_INSTR * wave + i) * 1024, voff[i], soff);
     }
     // Operands of half slice s of the slice in half u of stage st: f[t][j] is
-    // k = 8h + 4s + j of row w*128 + t*32 + l%32.
-    __device__ void frags(const uint8_t* st, int u, int s, u32x4 (&f)[4]) const {
+    // k = 8h + 4s + j of row w*R/2 + t*32 + l%32.
+    __device__ void frags(const uint8_t* st, int u, int s, u32x4 (&f)[G::TM]) const {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) f[t] = *reinterpret_cast<const u32x4*>(st + off[t][u][s]);
+        for (int t = 0; t < G::TM; ++t) f[t] = *reinterpret_cast<const u32x4*>(st + off[t][u][s]);
     }
-    static constexpr int kReads = 4;  // LDS reads per half slice
+    static constexpr int kReads = G::TM;        // LDS reads per half slice
+    static constexpr int kHalfCopies = G::KC_INSTR / 2;
+    static constexpr int kStage = G::KC_STAGE;
 };
 
-// An MN-contiguous operand: stage = one slice, 16 k-rows x 1024 B.  Wave w
-// issues j = 4w + i (i = 0..3) per slice, instruction j filling k-row j, as
-// two halves of 2.
+// An MN-contiguous operand: stage = one slice, 16 k-rows x 4R bytes.  Wave w
+// copies k-rows 4w .. 4w+3 with R/64 instructions (256/R k-rows each, R/4
+// lanes per k-row), as two halves.
+template <int R>
 struct MnOperand {
-    const float* base;  // k-row 4*wave of slice 0, first column of the tile
-    uint32_t voff[4];   // lane byte offsets from base, per instruction
-    uint32_t bytes;     // descriptor range: 4 k-rows
-    int off[4];
+    using G = Geo<R>;
+    const float* base;           // k-row 4*wave of slice 0, first column of the tile
+    uint32_t voff[G::MN_INSTR];  // lane byte offsets from base, per instruction
+    uint32_t bytes;              // descriptor range: 4 k-rows
+    int off[G::TM];
     int64_t slice;
     int nk;
     int64_t ld_;
@@ -196,19 +224,19 @@ struct MnOperand {
     __device__ void init(const float* X, int64_t ld, int mn0, int w, int wave, int lane, int nk_,
                          int mn_lim, int K) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int krow = 4 * wave + i;
-            const int c = lane ^ swz_mn(krow);
-            voff[i] = (uint32_t)(((int64_t)i * ld + 4 * c) * 4);
+        for (int i = 0; i < G::MN_INSTR; ++i) {
+            const int krow = 4 * wave + (256 / R) * i + lane / G::MN_LPR;
+            const int c = (lane % G::MN_LPR) ^ swz_mn(krow);
+            voff[i] = (uint32_t)(((int64_t)(krow - 4 * wave) * ld + 4 * c) * 4);
         }
         base = X + (int64_t)(4 * wave) * ld + mn0;
         bytes = (uint32_t)(4 * ld * 4);
-        // lane (h, l%32) reads k-rows 8h + 4s + j, column w*128 + t*32 + l%32
+        // lane (h, l%32) reads k-rows 8h + 4s + j, column w*R/2 + t*32 + l%32
         const int h = lane >> 5, r = lane & 31;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int chunk = (w * 32 + t * 8 + (r >> 2)) ^ (8 * h);
-            off[t] = 8 * h * 1024 + chunk * 16 + (r & 3) * 4;
+        for (int t = 0; t < G::TM; ++t) {
+            const int chunk = (w * (R / 8) + t * 8 + (r >> 2)) ^ (8 * h);
+            off[t] = 8 * h * G::MN_ROW + chunk * 16 + (r & 3) * 4;
         }
         slice = (int64_t)BK * ld;
         nk = nk_;
@@ -225,44 +253,53 @@ struct MnOperand {
             const int64_t end = (int64_t)(rows_left0 - BK * kt - 1) * ld_ + cols;  // elements
             if (end < 4 * ld_) range = end <= 0 ? 0u : (uint32_t)(end * 4);
         }
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, range, kBufferRsrcW3);
+        constexpr int HALF = G::MN_INSTR / 2;
 #pragma unroll
-        for (int i = 2 * half; i < 2 * half + 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16,
-                                                     voff[i], 0, 0, CPOL);
+        for (int i = HALF * half; i < HALF * half + HALF; ++i)
+            dma16(base + kt * slice, range, st + (G::MN_INSTR * wave + i) * 1024, voff[i], 0);
     }
-    __device__ void frags(const uint8_t* st, int s, u32x4 (&f)[4]) const {
+    __device__ void frags(const uint8_t* st, int s, u32x4 (&f)[G::TM]) const {
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < G::TM; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j)
-                f[t][j] = *reinterpret_cast<const uint32_t*>(st + off[t] + (4 * s + j) * 1024);
+                f[t][j] = *reinterpret_cast<const uint32_t*>(st + off[t] + (4 * s + j) * G::MN_ROW);
     }
-    static constexpr int kReads = 16;
+    static constexpr int kReads = 4 * G::TM;
+    static constexpr int kHalfCopies = G::MN_INSTR / 2;
+    static constexpr int kStage = G::MN_STAGE;
 };
 
 // Copies a wave has issued after the last one that slice kt+1 needs, at the
-// wait in slice kt (steady state; the prologue is laid out to match).  Per
-// slice: K-contiguous operands copy half a pair before the barrier of even
-// slices and after the barrier of odd ones (4 instructions each);
-// MN-contiguous ones copy half a slice before and half after every barrier
-// (2 each), and are issued first.
+// wait in slice kt (steady state; the prologue is laid out to match), for
+// ckc copy instructions per half pair of a K-contiguous operand and cmn per
+// half slice of an MN-contiguous one.  Per slice: K-contiguous operands
+// copy half a pair before the barrier of even slices and after the barrier
+// of odd ones; MN-contiguous ones copy half a slice before and half after
+// every barrier, and are issued first.  With one operand of each kind the
+// last copy slice kt+1 needs is the K-contiguous half pair issued before
+// the barrier of slice kt-2 (kt even) or kt-1 (kt odd); with two
+// MN-contiguous ones, the second's half slice before the barrier of kt-2.
 template <bool AK, bool BKc, bool kEven>
-constexpr int copies_after() {
-    if (AK != BKc) return kEven ? 16 : 4;  // one operand of each kind
-    if (AK) return kEven ? 16 : 0;         // both K-contiguous
-    return 16;                             // both MN-contiguous
+constexpr int copies_after(int ckc, int cmn) {
+    if (AK != BKc) return kEven ? 4 * cmn + 2 * ckc : 2 * cmn;  // one operand of each kind
+    if (AK) return kEven ? 4 * ckc : 0;                         // both K-contiguous
+    return 8 * cmn;                                             // both MN-contiguous
 }
 
 // Copies issued by the prologue after the last one slice 0 needs: every
-// MN-contiguous operand still has slices 1 and 2 (8) and half of slice 3 (2)
-// after it, every K-contiguous one the first half of pair 1 (4).
+// MN-contiguous operand still has slices 1 and 2 and half of slice 3 after
+// it (5 half slices), every K-contiguous one the first half of pair 1.
 template <bool AK, bool BKc>
-constexpr int prologue_after() {
+constexpr int prologue_after(int ckc, int cmn) {
     constexpr int nmn = (AK ? 0 : 1) + (BKc ? 0 : 1), nkc = 2 - nmn;
-    return nmn ? 10 * nmn + 4 * nkc : 4 * nkc;
+    return nmn ? 5 * cmn * nmn + ckc * nkc : ckc * nkc;
 }
+static_assert(copies_after<true, false, true>(4, 2) == 16 && copies_after<true, false, false>(4, 2) == 4 &&
+              copies_after<true, true, true>(4, 2) == 16 && copies_after<false, false, true>(4, 2) == 16 &&
+              prologue_after<true, false>(4, 2) == 14 && prologue_after<true, true>(4, 2) == 8 &&
+              prologue_after<false, false>(4, 2) == 20,
+              "the 256-tile counts are those of the 16-bit DMA kernel");
 
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
@@ -270,16 +307,22 @@ constexpr int prologue_after() {
 // clipped descriptor ranges and store only their valid part).  kTail: K is
 // not a multiple of 64 (a last group of 1 to 4 slices after the loop, the
 // last slice possibly partial).
-template <bool TA, bool TB, bool kEdge, bool kTail>
-__global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int tiles_m,
-                                                            int tiles_n, int grouped) {
+// R: workgroup tile R x R (256: one workgroup per CU; 128: two).
+template <int R, bool TA, bool TB, bool kEdge, bool kTail>
+__global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(GemmParams p,
+                                                                          int tiles_m,
+                                                                          int tiles_n,
+                                                                          int grouped) {
     const TileIdx tile = xcd_tile(tiles_m, tiles_n, grouped != 0);
     select_problem(p, tile.z);
     constexpr bool AK = !TA, BKc = TB;
-    using OpA = typename std::conditional<AK, KcOperand, MnOperand>::type;
-    using OpB = typename std::conditional<BKc, KcOperand, MnOperand>::type;
-    constexpr int SA01 = AK ? KC_STAGE : MN_STAGE, SA23 = AK ? 16 : MN_STAGE;
-    constexpr int SB01 = BKc ? KC_STAGE : MN_STAGE, SB23 = BKc ? 16 : MN_STAGE;
+    constexpr int TM = Geo<R>::TM;
+    using OpA = typename std::conditional<AK, KcOperand<R>, MnOperand<R>>::type;
+    using OpB = typename std::conditional<BKc, KcOperand<R>, MnOperand<R>>::type;
+    constexpr int SA01 = OpA::kStage, SA23 = AK ? 16 : OpA::kStage;
+    constexpr int SB01 = OpB::kStage, SB23 = BKc ? 16 : OpB::kStage;
+    constexpr int CKC = AK ? OpA::kHalfCopies : BKc ? OpB::kHalfCopies : 0;
+    constexpr int CMN = !AK ? OpA::kHalfCopies : !BKc ? OpB::kHalfCopies : 0;
     // One LDS object per operand and stage (K-contiguous operands use two).
     __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA01];
     __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA01];
@@ -293,8 +336,8 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-    const int m0 = tile.bm * BM;
-    const int n0 = tile.bn * BN;
+    const int m0 = tile.bm * R;
+    const int n0 = tile.bn * R;
     const int nk = (p.K + BK - 1) / BK;  // slices (the last one partial when K % 16 != 0)
 
     OpA opa;
@@ -304,18 +347,18 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     opb.template init<kEdge>(static_cast<const float*>(p.B), p.ldb, n0, wn, wave, lane, nk, p.N,
                              p.K);
 
-    floatx16 acc[4][4];
+    floatx16 acc[TM][TM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // Operands of half slice s of slice position J (0..3 within a group of
     // four slices: a K-contiguous operand has it in stage J/2, half J%2; an
     // MN-contiguous one in stage J).
-    auto frags = [&](auto Jc, int s, u32x4 (&a)[4], u32x4 (&b)[4]) {
+    auto frags = [&](auto Jc, int s, u32x4 (&a)[TM], u32x4 (&b)[TM]) {
         constexpr int J = decltype(Jc)::value;
         if constexpr (AK) opa.frags(pick<J / 2>(sA0, sA1, sA2, sA3), J % 2, s, a);
         else opa.frags(pick<J>(sA0, sA1, sA2, sA3), s, a);
@@ -323,32 +366,34 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
         else opb.frags(pick<J>(sB0, sB1, sB2, sB3), s, b);
     };
 
-    // 64 MFMAs on (a, b): four sub-steps of 4 x 4 tiles.  The LDS reads and
-    // the copies issued just before in program order are spread between
-    // them (the reads evenly, a copy after every eighth MFMA), so the address
-    // unit never sees a burst that would hold the wave, and its MFMA issue,
-    // back.
-    constexpr int RD_EVERY = 64 / (OpA::kReads + OpB::kReads);
-    auto mfma_step = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+    // 4 TM^2 MFMAs on (a, b): four sub-steps of TM x TM tiles.  The LDS reads
+    // and the copies issued just before in program order are spread between
+    // them (both evenly, up to 8 copy slots), so the address unit never sees
+    // a burst that would hold the wave, and its MFMA issue, back.
+    constexpr int NMFMA = 4 * TM * TM;
+    constexpr int RD_EVERY = NMFMA / (OpA::kReads + OpB::kReads) > 0
+                                 ? NMFMA / (OpA::kReads + OpB::kReads) : 1;
+    constexpr int CP_EVERY = NMFMA / 8;
+    auto mfma_step = [&](const u32x4 (&a)[TM], const u32x4 (&b)[TM]) {
 #pragma unroll
         for (int j = 0; j < 4; ++j)
 #pragma unroll
-            for (int ti = 0; ti < 4; ++ti)
+            for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-                for (int tj = 0; tj < 4; ++tj)
+                for (int tj = 0; tj < TM; ++tj)
                     acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                         __uint_as_float(a[ti][j]), __uint_as_float(b[tj][j]), acc[ti][tj], 0, 0,
                         0);
 #pragma unroll
-        for (int m = 0; m < 64; ++m) {
+        for (int m = 0; m < NMFMA; ++m) {
             __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);                 // MFMA
             if (m % RD_EVERY == 0) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-            if (m % 8 == 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
+            if (m % CP_EVERY == 1 % CP_EVERY) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    u32x4 a0[4], b0[4], a1[4], b1[4];
+    u32x4 a0[TM], b0[TM], a1[TM], b1[TM];
 
     // Slice kt at position J of its group of four.  Copies, per wave:
     //   before the barrier: MN-contiguous operands the second half of slice
@@ -364,10 +409,10 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     // by element (a lane's fragment of half slice s holds k = 16kt + 8h + 4s
     // .. +3).  m/n-contiguous operands need no mask: their rows past K lie
     // past the copy descriptor's range and read as zeros.
-    auto mask_k = [&](int kt, int s, u32x4 (&f)[4]) {
+    auto mask_k = [&](int kt, int s, u32x4 (&f)[TM]) {
         const int valid = p.K - (BK * kt + 8 * h + 4 * s);  // of the 4 still below K
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < TM; ++t)
 #pragma unroll
             for (int j = 0; j < 4; ++j) f[t][j] = j < valid ? f[t][j] : 0u;
     };
@@ -387,7 +432,7 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
         if constexpr (kEven && AK) opa.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
         if constexpr (kEven && BKc) opb.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
         mfma_step(a0, b0);  // first half slice (operands read earlier)
-        WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>()));  // own copies landed, reads returned
+        WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>(CKC, CMN)));  // own copies landed, reads returned
         barrier();                                           // ... for every wave
         frags(std::integral_constant<int, (J + 1) % 4>{}, 0, a0, b0);  // next slice, first half
         if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
@@ -412,7 +457,7 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     if constexpr (!BKc) opb.template copy<kEdge, kTail>(sB3, 3, 0, wave);
     if constexpr (AK) opa.template copy<kEdge, kTail>(sA1, 1, 0, wave);
     if constexpr (BKc) opb.template copy<kEdge, kTail>(sB1, 1, 0, wave);
-    WAIT_VMCNT((prologue_after<AK, BKc>()));  // slice 0 of both operands landed
+    WAIT_VMCNT((prologue_after<AK, BKc>(CKC, CMN)));  // slice 0 of both operands landed
     barrier();
     frags(std::integral_constant<int, 0>{}, 0, a0, b0);
     using NoMask = std::false_type;
@@ -442,23 +487,23 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
     // afresh here rather than kept live through the K loop.
     const int el = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int eh = el >> 5;
-    const int col0 = n0 + wn * 128 + (el & 31);
-    float* cbase = p.C + (int64_t)(m0 + wm * 128 + 4 * eh) * p.ldc + col0;
+    const int col0 = n0 + wn * (R / 2) + (el & 31);
+    float* cbase = p.C + (int64_t)(m0 + wm * (R / 2) + 4 * eh) * p.ldc + col0;
     const float alpha = p.alpha, beta = p.beta;
-    float bias[4];
+    float bias[TM];
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj)
+    for (int tj = 0; tj < TM; ++tj)
         bias[tj] = p.bias && (!kEdge || col0 + tj * 32 < p.N) ? p.bias[col0 + tj * 32] : -0.0f;
     // on edge tiles only rows < M and columns < N are stored
-    const int row0 = m0 + wm * 128 + 4 * eh;
+    const int row0 = m0 + wm * (R / 2) + 4 * eh;
     auto ok = [&](int ti, int tj, int r) {
         return !kEdge || (row0 + ti * 32 + 8 * (r >> 2) + (r & 3) < p.M && col0 + tj * 32 < p.N);
     };
     if (beta == 0.0f) {
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+        for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < TM; ++tj)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (ok(ti, tj, r))
@@ -466,9 +511,9 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
                             alpha * acc[ti][tj][r] + bias[tj];
     } else {
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+        for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
+            for (int tj = 0; tj < TM; ++tj) {
                 float cv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -486,26 +531,21 @@ __global__ __launch_bounds__(NT, 1) void mfma_f32_dma_kernel(GemmParams p, int t
 
 }  // namespace
 
-// Aligned rows, pitches within the buffer offsets, and a launch this kernel
-// finishes sooner than the 128 x 128 kernel by a simple model: its tiles run
-// one per CU at ~0.96 of the MFMA peak, the smaller ones two per CU at ~0.83
-// (each a quarter of the work), and each kernel takes as many waves of
-// tiles as its resident slots need.
+// Aligned rows and pitches within the buffer offsets: every other shape
+// takes the register-staged 128 x 128 kernel.
 bool mfma_f32_dma_eligible(const GemmParams& p) {
     if (!operands_16b_aligned(p, 4) || p.M <= 0 || p.N <= 0 || p.K <= 0) return false;
-    if (p.lda >= kMaxPitchF32 || p.ldb >= kMaxPitchF32) return false;
-    const double t256 = (double)((p.M + BM - 1) / BM) * ((p.N + BN - 1) / BN) * p.batch;
-    const double t128 = (double)((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
-    const double time256 = std::ceil(t256 / kSlots256) * 4.0 / 0.96;
-    const double time128 = std::ceil(t128 / kSlots128) * 2.0 / 0.83;
-    return time256 <= time128;
+    return p.lda < kMaxPitchF32 && p.ldb < kMaxPitchF32;
 }
 
-hipError_t launch_mfma_f32_dma(const GemmParams& p, hipStream_t s) {
-    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+namespace {
+
+template <int R>
+hipError_t launch_tiles(const GemmParams& p, hipStream_t s) {
+    const int tiles_m = (p.M + R - 1) / R, tiles_n = (p.N + R - 1) / R;
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool edge = p.M % BM != 0 || p.N % BN != 0;
+    const bool edge = p.M % R != 0 || p.N % R != 0;
     const bool tail = p.K % (BK * NSTAGE) != 0;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
@@ -515,11 +555,25 @@ hipError_t launch_mfma_f32_dma(const GemmParams& p, hipStream_t s) {
         };
         // a K tail takes the edge-tile instance whatever M and N (its guards
         // then always pass)
-        if (tail) go(mfma_f32_dma_kernel<TA, TB, true, true>);
-        else if (edge) go(mfma_f32_dma_kernel<TA, TB, true, false>);
-        else go(mfma_f32_dma_kernel<TA, TB, false, false>);
+        if (tail) go(mfma_f32_dma_kernel<R, TA, TB, true, true>);
+        else if (edge) go(mfma_f32_dma_kernel<R, TA, TB, true, false>);
+        else go(mfma_f32_dma_kernel<R, TA, TB, false, false>);
         return hipGetLastError();
     });
+}
+
+}  // namespace
+
+// Tile size by the waves of tiles the CUs work through: both sizes reach
+// ~0.96 of the MFMA peak (a CU runs one 256-tile or two 128-tiles at a
+// time), so a CU's time is its share of tiles rounded up, counted in
+// 128-tiles (a 256-tile is four).  Ties keep the larger tile.
+hipError_t launch_mfma_f32_dma(const GemmParams& p, hipStream_t s) {
+    const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+    const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    const int64_t time256 = (t256 + kCUs - 1) / kCUs * 4;
+    const int64_t time128 = (t128 + kCUs - 1) / kCUs;
+    return time128 < time256 ? launch_tiles<128>(p, s) : launch_tiles<256>(p, s);
 }
 
 }  // namespace dgt

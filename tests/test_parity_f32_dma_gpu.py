@@ -1,11 +1,12 @@
-"""GPU parity for the FP32 whole-tile DMA kernel (256 x 256 tiles, one
-wavefront per SIMD) against the CPU oracle, through the C ABI.
+"""GPU parity for the FP32 DMA kernel against the CPU oracle, through the
+C ABI.
 
-The automatic choice takes that kernel for 16-byte aligned rows when a
-model of both kernels' waves of tiles says it finishes first (a strided
-batch counts every problem's tiles: 256 tiles of 256 x 256 against at least
-513 of 128 x 128 qualifies); the cases below meet that with one 4096 x 4096
-or 4000 x 4000 problem, or with batches of small ones.  Covered, for every
+The automatic choice takes that kernel for 16-byte aligned rows, with
+256 x 256 tiles (one workgroup per CU) unless 128 x 128 tiles (two per CU)
+take fewer waves (a strided batch counts every problem's tiles): one
+4096 x 4096, 4000 x 4000 or 4000 x 3968 problem and a batch of 256
+one-tile 256 x 256 problems run 256-tiles; batches of smaller ragged
+problems and the single small problems run 128-tiles.  Covered, for every
 stored layout: integer inputs bit-exact on whole tiles (K = 64, 128 and 192:
 one to three groups of four 16-deep slices), on edge tiles, and with K not
 a multiple of 64 (a last group of 1 to 4 slices) or of 16 (a partial last
@@ -21,7 +22,7 @@ import pytest
 import gemm_inputs as gi
 import oracle
 from gates import assert_bit_exact, assert_close
-from gpu_util import say, to_dev
+from gpu_util import run_gemm, say, to_dev
 
 torch = pytest.importorskip("torch")
 import dense_gemm_tuning_amd as dgt  # noqa: E402
@@ -230,3 +231,64 @@ def test_large_ragged_real_inputs(layout):
     say(f"f32 dma large ragged {layout}: oracle")
     R = oracle.gemm(A, B, C0, 0.75, -1.25, "f32", trans_a=ta, trans_b=tb)
     assert_close(outs[0], R, K, 0.75, what=f"f32 dma large ragged {layout}")
+
+
+# The same edge and ragged-K shapes as one problem each: too few tiles for
+# 256 x 256, so the launch takes 128 x 128 tiles, two workgroups per CU.
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_128_tiles_edge_and_ragged_k_integer_bit_exact(layout):
+    ta, tb = LAYOUTS[layout]
+    shapes = [(M, N, K) for (M, N, K, _) in EDGE_BATCHED] + [(512, 384, 256), (128, 128, 64),
+                                                            (2048, 2048, 192)]
+    for idx, (M, N, K) in enumerate(shapes):
+        sa, sb = stored(M, N, K, ta, tb)
+        A = gi.draw(4000 + idx, *sa, "int")
+        B = gi.draw(4020 + idx, *sb, "int")
+        C0 = gi.draw(4040 + idx, M, N, "int")
+        for alpha, beta in [(1.0, 0.0), (1.5, 0.5)]:
+            say(f"f32 dma128 {layout} {M}x{N}x{K} a={alpha} b={beta}")
+            st, C = run_gemm("auto", "f32", A, B, C0 if beta else None, alpha, beta,
+                             trans_a=ta, trans_b=tb)
+            assert st == 0, dgt.gemm_status_string(st)
+            R = oracle.round_f32(oracle.gemm(A, B, C0 if beta else None, alpha, beta, "f32",
+                                             trans_a=ta, trans_b=tb))
+            assert_bit_exact(C, R, f"f32 dma128 {layout} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", ["nn", "tn"])
+def test_128_tiles_real_inputs(layout):
+    """2048^3 (256 tiles of 128 x 128) and 1000^3 with alpha / beta, real
+    inputs, against the oracle."""
+    ta, tb = LAYOUTS[layout]
+    for idx, (M, N, K, alpha, beta) in enumerate([(2048, 2048, 2048, 1.0, 0.0),
+                                                  (1000, 1000, 1000, 1.5, 0.5)]):
+        sa, sb = stored(M, N, K, ta, tb)
+        A = gi.draw(4100 + idx, *sa, "uniform")
+        B = gi.draw(4110 + idx, *sb, "uniform")
+        C0 = gi.draw(4120 + idx, M, N, "uniform")
+        say(f"f32 dma128 real {layout} {M}x{N}x{K}")
+        st, C = run_gemm("auto", "f32", A, B, C0, alpha, beta, trans_a=ta, trans_b=tb)
+        assert st == 0
+        R = oracle.gemm(A, B, C0, alpha, beta, "f32", trans_a=ta, trans_b=tb)
+        assert_close(C, R, K, alpha, what=f"f32 dma128 real {layout} {M}x{N}x{K}")
+
+
+@pytest.mark.parametrize("layout", list(LAYOUTS))
+def test_256_tiles_edge_and_ragged_k_integer_bit_exact(layout):
+    """Edge tiles in both dimensions with K = 136 (a partial last slice) and
+    K = 1000 (a partial last slice after 15 whole groups), 256-tiles."""
+    ta, tb = LAYOUTS[layout]
+    for idx, (M, N, K) in enumerate([(4000, 3968, 136), (3968, 4000, 1000)]):
+        sa, sb = stored(M, N, K, ta, tb)
+        A = gi.draw(4200 + idx, *sa, "int")
+        B = gi.draw(4210 + idx, *sb, "int")
+        C0 = gi.draw(4220 + idx, M, N, "int")
+        dA, dB = to_dev(A, "f32"), to_dev(B, "f32")
+        say(f"f32 dma256 edge {layout} {M}x{N}x{K}")
+        dC = torch.from_numpy(C0).cuda()
+        st = dgt.gemm(dA, dB, dC, 1.5, 0.5, trans_a=ta, trans_b=tb)
+        torch.cuda.synchronize()
+        assert st == 0, dgt.gemm_status_string(st)
+        R = oracle.round_f32(oracle.gemm(A, B, C0, 1.5, 0.5, "f32", trans_a=ta, trans_b=tb))
+        assert_bit_exact(dC.cpu().numpy(), R, f"f32 dma256 edge {layout} {M}x{N}x{K}")
+        del dC
