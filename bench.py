@@ -65,37 +65,37 @@ SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
 # edge-tile and K-tail flags, false for whole tiles).
 DOMINANT = {
     "bf16_8192": ("mfma16_dma_kernel<BF16, NN>", "k_mfma_bf16_dma.hip",
-                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
+                  r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, false, false, false>"),
     "f16_8192": ("mfma16_dma_kernel<F16, NN>", "k_mfma_bf16_dma.hip",
-                 r"mfma16_dma_kernel<\(dgt::In\)2, false, false, false, false>"),
-    "f32_4096": ("mfma_f32_dma_kernel<NN>", "k_mfma_f32_dma.hip",
-                 r"mfma_f32_dma_kernel<false, false, false, false>"),
+                 r"mfma16_dma_kernel<\(dgt::In\)2, 256, false, false, false, false>"),
+    "f32_4096": ("mfma_f32_dma_kernel<NN, 256-tiles>", "k_mfma_f32_dma.hip",
+                 r"mfma_f32_dma_kernel<256, false, false, false, false>"),
     "bf16_skinny_8x28672x8192": ("skinny16_kernel<BF16, NN, 1 row block>", "k_skinny16.hip",
                                  r"skinny16_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_8192_nt": ("mfma16_dma_kernel<BF16, NT>", "k_mfma_bf16_dma.hip",
-                     r"mfma16_dma_kernel<\(dgt::In\)1, false, true, false, false>"),
+                     r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
     "bf16_8192_tn": ("mfma16_dma_kernel<BF16, TN>", "k_mfma_bf16_dma.hip",
-                     r"mfma16_dma_kernel<\(dgt::In\)1, true, false, false, false>"),
+                     r"mfma16_dma_kernel<\(dgt::In\)1, 256, true, false, false, false>"),
     "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 1 row block>", "k_skinny16.hip",
                                     r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 1>"),
     "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
-                                 r"mfma16_dma_kernel<\(dgt::In\)1, false, true, false, false>"),
+                                 r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
     "bf16_decode_64x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 4 row blocks>",
                                      "k_skinny16.hip",
                                      r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 4>"),
-    "f32_1000_splitk": ("mfma_f32_kernel<NN, guarded> x 8 K slices + reduce (per call)",
-                        "k_mfma_f32.hip+k_splitk.hip", r"mfma_f32_kernel<true, true, false, false>"),
-    "bf16_splitk_1024x1024x16384": ("mfma16_dma_kernel<BF16, NN> x 16 K slices + reduce "
-                                    "(per call)", "k_mfma_bf16_dma.hip+k_splitk.hip",
-                                    r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
+    "f32_1000_splitk": ("mfma_f32_dma_kernel<NN, 128-tiles, edge> x 8 K slices + reduce (per call)",
+                        "k_mfma_f32_dma.hip+k_splitk.hip",
+                        r"mfma_f32_dma_kernel<128, false, false, true, (?:false|true)>"),
+    "bf16_splitk_1024x1024x16384": ("mfma16_dma_kernel<BF16, NN, 128-tiles> x 8 K slices + "
+                                    "reduce (per call)", "k_mfma_bf16_dma.hip+k_splitk.hip",
+                                    r"mfma16_dma_kernel<\(dgt::In\)1, 128, false, false, false, false>"),
     "bf16_skinny_shard_8x3584x8192": ("skinny16_kernel<BF16, NN, 1 row block> x 8 K slices + "
                                       "reduce (per call)", "k_skinny16.hip+k_splitk.hip",
                                       r"skinny16_kernel<\(dgt::In\)1, true, false, false, 1>"),
-    "bf16_shard_8192x1024x8192": ("mfma16_dma_kernel<BF16, NN> x 2 K slices + reduce (per call)",
-                                  "k_mfma_bf16_dma.hip+k_splitk.hip",
-                                  r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
+    "bf16_shard_8192x1024x8192": ("mfma16_dma_kernel<BF16, NN, 128-tiles>", "k_mfma_bf16_dma.hip",
+                                  r"mfma16_dma_kernel<\(dgt::In\)1, 128, false, false, false, false>"),
     "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
-                         r"mfma16_dma_kernel<\(dgt::In\)1, false, false, false, false>"),
+                         r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, false, false, false>"),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")

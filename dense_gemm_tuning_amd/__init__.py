@@ -39,8 +39,11 @@ VARIANT_NAIVE = 1
 VARIANT_LDS = 2
 VARIANT_MFMA = 3
 VARIANT_SKINNY = 4
+VARIANT_MFMA_T256 = 5
+VARIANT_MFMA_T128 = 6
 VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
-            "mfma": VARIANT_MFMA, "skinny": VARIANT_SKINNY}
+            "mfma": VARIANT_MFMA, "skinny": VARIANT_SKINNY, "mfma256": VARIANT_MFMA_T256,
+            "mfma128": VARIANT_MFMA_T128}
 
 # Every symbol the header declares (the tests check the library exports them).
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",

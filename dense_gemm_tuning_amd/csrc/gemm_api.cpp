@@ -104,6 +104,13 @@ hipError_t dispatch(DType t, int variant, const GemmParams& p, bool reads_ab, hi
             return t == DType::F32    ? dgt::launch_skinny_f32(p, s)
                    : t == DType::BF16 ? dgt::launch_skinny16<In::BF16>(p, s)
                                       : dgt::launch_skinny16<In::F16>(p, s);
+        case GEMM_VARIANT_MFMA_T256:
+        case GEMM_VARIANT_MFMA_T128: {
+            const int tile = variant == GEMM_VARIANT_MFMA_T128 ? 128 : 256;
+            return t == DType::F32    ? dgt::launch_mfma_f32_dma_tile(p, s, tile)
+                   : t == DType::BF16 ? dgt::launch_mfma16_dma_tile<In::BF16>(p, s, tile)
+                                      : dgt::launch_mfma16_dma_tile<In::F16>(p, s, tile);
+        }
         default:
             return hipErrorInvalidConfiguration;
     }
@@ -121,7 +128,7 @@ int run(const Call& c) {
         return GEMM_ERR_ARG;
     int st = check_shape(c.ta, c.tb, c.M, c.N, c.K, c.lda, c.ldb, c.ldc);
     if (st != GEMM_OK) return st;
-    if (c.variant < GEMM_VARIANT_AUTO || c.variant > GEMM_VARIANT_SKINNY)
+    if (c.variant < GEMM_VARIANT_AUTO || c.variant > GEMM_VARIANT_MFMA_T128)
         return GEMM_ERR_VARIANT;
     if (c.M == 0 || c.N == 0 || c.batch == 0) return GEMM_OK;  // empty C: nothing to do
     const bool reads_ab = (c.alpha != 0.0f) && (c.K > 0);
@@ -159,7 +166,14 @@ int run(const Call& c) {
     p.stride_c = c.stride_c;
     p.stride_bias = c.stride_bias;
     p.bias = c.bias;
+    p.batch = std::min(kMaxBatchPerLaunch, c.batch);
     hipStream_t s = static_cast<hipStream_t>(c.stream);
+    // the fixed-tile rungs run only the DMA kernels (16-byte aligned rows)
+    if (reads_ab && (variant == GEMM_VARIANT_MFMA_T256 || variant == GEMM_VARIANT_MFMA_T128)) {
+        const bool ok = c.t == DType::F32 ? dgt::mfma_f32_dma_eligible(p)
+                                          : dgt::mfma16_dma_eligible(p);
+        if (!ok) return GEMM_ERR_VARIANT;
+    }
 
     for (int z0 = 0; z0 < c.batch; z0 += kMaxBatchPerLaunch) {
         GemmParams q = p;
@@ -199,12 +213,9 @@ void tile_budget(DType t, int M, int N, int64_t& tiles, int64_t& slots) {
         const int cols = t == DType::F32 ? 64 : 128;
         tiles = (N + cols - 1) / cols;
         slots = 256;
-    } else if (t == DType::F32) {  // 128 x 128 tiles, two workgroups per CU
+    } else {  // 128 x 128 tiles, two workgroups per CU (the smaller DMA tile)
         tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
         slots = 512;
-    } else {  // 256 x 256 tiles, one workgroup per CU
-        tiles = (int64_t)((M + 255) / 256) * ((N + 255) / 256);
-        slots = 256;
     }
 }
 

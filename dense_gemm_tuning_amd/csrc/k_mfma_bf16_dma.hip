@@ -55,10 +55,27 @@ namespace dgt {
 
 namespace {
 
-constexpr int BM = 256, BN = 256, BK = 32, NT = 256, NSTAGE = 4;
-constexpr int KC_STAGE = 256 * 2 * BK * 2;  // 32 KiB: 256 rows x 128 B (two slices)
-constexpr int MN_STAGE = BK * 256 * 2;      // 16 KiB: 32 k-rows x 512 B (one slice)
+constexpr int BK = 32, NT = 256, NSTAGE = 4;
 constexpr int CPOL = 1;                     // sc0 on the copies
+constexpr int64_t kCUs = 256;
+constexpr double kCost128 = 1.22;           // a 128-tile's time, in quarters of a 256-tile's
+
+// Geometry of a workgroup tile of R x R (R = 256 or 128; a 2 x 2 grid of
+// wavefronts of R/2 x R/2).  A k-contiguous stage holds R rows of 128 B (two
+// slices), copied 8 rows per instruction; an m/n-contiguous stage holds 32
+// k-rows of 2R bytes, 512/R k-rows per instruction; each wave copies a
+// quarter of either.
+template <int R>
+struct Geo {
+    static constexpr int TM = R / 64;          // 32 x 32 MFMA tiles per wave and dimension
+    static constexpr int KC_ROWS = R / 4;      // k-contiguous rows per wave
+    static constexpr int KC_INSTR = R / 32;    // their copy instructions per pair
+    static constexpr int KC_STAGE = R * 128;   // bytes
+    static constexpr int MN_ROW = 2 * R;       // bytes per k-row
+    static constexpr int MN_LPR = R / 8;       // 16-byte chunks (lanes) per k-row
+    static constexpr int MN_INSTR = R / 64;    // copy instructions per slice and wave
+    static constexpr int MN_STAGE = BK * MN_ROW;
+};
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
@@ -72,6 +89,17 @@ typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 // reads past the element only feeds outputs that are not stored or k that
 // are masked.
 __device__ __forceinline__ int round8(int n) { return (n + 7) & ~7; }
+
+// One 16-byte-per-lane copy, global -> LDS, through a buffer descriptor of
+// `range` bytes from `base`: lane l's bytes at base + voff + soff land at
+// lds + 16*l.  (A plain function: the host pass of the templates below then
+// never sees the device-only descriptor type.)
+__device__ __forceinline__ void dma16(const void* base, uint32_t range, uint8_t* lds,
+                                      uint32_t voff, uint32_t soff) {
+    const __amdgpu_buffer_rsrc_t rs =
+        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, range, kBufferRsrcW3);
+    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, CPOL);
+}
 
 // K-contiguous rows are 128 B = 8 chunks of 16 B; chunk q of row r sits at
 // q ^ swz_kc(r).
@@ -104,16 +132,17 @@ __device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, 
     else return s3;
 }
 
-// A K-contiguous operand: stage = a pair of slices, 256 rows x 128 B.  Wave w
-// issues copy instructions j = 8w + i (i = 0..7) per pair, instruction j
-// filling rows 8j .. 8j+7 (8 lanes per row).  A pair takes 8 instructions per
-// wave, issued as two halves of 4.  The wave's descriptor covers its 64 rows;
-// pair pr adds 128*pr bytes through the scalar offset.
+// A K-contiguous operand: stage = a pair of slices, R rows x 128 B.  Wave w
+// issues copy instructions j = (R/32)w + i per pair, instruction j filling
+// rows 8j .. 8j+7 (8 lanes per row), as two halves.  The wave's descriptor
+// covers its R/4 rows; pair pr adds 128*pr bytes through the scalar offset.
+template <int R>
 struct KcOperand {
-    const uint16_t* base;  // row 64*wave of the tile (wave-uniform)
-    uint32_t voff[8];      // lane byte offsets from base, per instruction
-    uint32_t bytes;        // descriptor range: 64 rows
-    int off[4][2][2];      // LDS read offset: tile t, slice-in-pair u, step s
+    using G = Geo<R>;
+    const uint16_t* base;         // row (R/4)*wave of the tile (wave-uniform)
+    uint32_t voff[G::KC_INSTR];   // lane byte offsets from base, per instruction
+    uint32_t bytes;               // descriptor range: the wave's rows
+    int off[G::TM][2][2];         // LDS read offset: tile t, slice-in-pair u, step s
     int npair;
 
     // mn0: first row (m or n) of the workgroup tile; w: this wave's half of
@@ -127,20 +156,20 @@ struct KcOperand {
     __device__ void init(const uint16_t* X, int64_t ld, int mn0, int w, int wave, int lane,
                          int nk, int mn_lim, int K) {
 #pragma unroll
-        for (int i = 0; i < 8; ++i) {
-            const int row = 8 * (8 * wave + i) + (lane >> 3);
+        for (int i = 0; i < G::KC_INSTR; ++i) {
+            const int row = 8 * (G::KC_INSTR * wave + i) + (lane >> 3);
             const int q = (lane & 7) ^ swz_kc(row);
-            voff[i] = (uint32_t)(((int64_t)(row - 64 * wave) * ld + 8 * q) * 2);
+            voff[i] = (uint32_t)(((int64_t)(row - G::KC_ROWS * wave) * ld + 8 * q) * 2);
         }
-        base = X + (int64_t)(mn0 + 64 * wave) * ld;
-        int rows = 64;
-        if constexpr (kEdge) rows = min(64, mn_lim - (mn0 + 64 * wave));
+        base = X + (int64_t)(mn0 + G::KC_ROWS * wave) * ld;
+        int rows = G::KC_ROWS;
+        if constexpr (kEdge) rows = min(G::KC_ROWS, mn_lim - (mn0 + G::KC_ROWS * wave));
         bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round8(K)) * 2);
-        // rows w*128 + t*32 + l%32; half-wave h reads chunk 4u + 2s + h
+        // rows w*R/2 + t*32 + l%32; half-wave h reads chunk 4u + 2s + h
         const int h = lane >> 5;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int row = w * 128 + t * 32 + (lane & 31);
+        for (int t = 0; t < G::TM; ++t) {
+            const int row = w * (R / 2) + t * 32 + (lane & 31);
 #pragma unroll
             for (int u = 0; u < 2; ++u)
 #pragma unroll
@@ -167,29 +196,37 @@ struct KcOperand {
             from += skip;
             soff = 0;
         }
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)from, 0, range, kBufferRsrcW3);
+        constexpr int HALF = G::KC_INSTR / 2;
 #pragma unroll
-        for (int i = 4 * half; i < 4 * half + 4; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (8 * wave + i) * 1024), 16,
-                                                     voff[i], soff, 0, CPOL);
+        for (int i = HALF * half; i < HALF * half + HALF; ++i)
+            dma16(from, range, st + (G::KC_INSTR * wave + i) * 1024, voff[i], soff);
     }
     // Operands of step s of the slice in half u of stage st.
-    __device__ void frags(const uint8_t* st, int u, int s, u32x4 (&f)[4]) const {
+    __device__ void frags(const uint8_t* st, int u, int s, u32x4 (&f)[G::TM]) const {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) f[t] = *reinterpret_cast<const u32x4*>(st + off[t][u][s]);
+        for (int t = 0; t < G::TM; ++t) f[t] = *reinterpret_cast<const u32x4*>(st + off[t][u][s]);
     }
-    static constexpr int kReads = 4;  // LDS reads per step
+    static constexpr int kReads = G::TM;  // LDS reads per step
+    static constexpr int kHalfCopies = G::KC_INSTR / 2;
+    static constexpr int kStage = G::KC_STAGE;
 };
 
-// An MN-contiguous operand: stage = one slice, 32 k-rows x 512 B.  Wave w
-// issues j = 4w + i (i = 0..3) per slice, instruction j filling k-rows 2j
-// and 2j+1 (32 lanes per row), as two halves of 2.
+// Transposing LDS read of 4 k-rows x 4 columns per 16-lane group (a plain
+// function, like dma16).
+__device__ __forceinline__ shortx4 read_tr16(const uint8_t* p) {
+    return __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)p);
+}
+
+// An MN-contiguous operand: stage = one slice, 32 k-rows x 2R bytes.  Wave w
+// copies k-rows 8w .. 8w+7 with R/64 instructions (512/R k-rows each, R/8
+// lanes per k-row), as two halves.
+template <int R>
 struct MnOperand {
-    const uint16_t* base;  // k-row 8*wave of slice 0, first column of the tile
-    uint32_t voff[4];      // lane byte offsets from base, per instruction
-    uint32_t bytes;        // descriptor range: 8 k-rows
-    int off[4];
+    using G = Geo<R>;
+    const uint16_t* base;        // k-row 8*wave of slice 0, first column of the tile
+    uint32_t voff[G::MN_INSTR];  // lane byte offsets from base, per instruction
+    uint32_t bytes;              // descriptor range: 8 k-rows
+    int off[G::TM];
     int64_t slice;
     int nk;
     int64_t ld_;
@@ -204,9 +241,9 @@ struct MnOperand {
     __device__ void init(const uint16_t* X, int64_t ld, int mn0, int w, int wave, int lane,
                          int nk_, int mn_lim, int K) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int krow = 2 * (4 * wave + i) + (lane >> 5);
-            const int c = (lane & 31) ^ (4 * (krow & 3));
+        for (int i = 0; i < G::MN_INSTR; ++i) {
+            const int krow = 8 * wave + (512 / R) * i + lane / G::MN_LPR;
+            const int c = (lane % G::MN_LPR) ^ (4 * (krow & 3));
             voff[i] = (uint32_t)(((int64_t)(krow - 8 * wave) * ld + 8 * c) * 2);
         }
         base = X + (int64_t)(8 * wave) * ld + mn0;
@@ -215,13 +252,13 @@ struct MnOperand {
         rows_left0 = K - 8 * wave;
         cols = kEdge ? round8(mn_lim - mn0) : 0;
         // Source lane 4r+q of 16-lane group G reads k-row 16s + 8h + 4t + r,
-        // columns w*128 + tile*32 + 16*(G%2) + 4q .. +3 (t = which of the two
+        // columns w*R/2 + tile*32 + 16*(G%2) + 4q .. +3 (t = which of the two
         // reads); k & 3 == r.
         const int r = (lane & 15) >> 2, q = lane & 3, g = (lane >> 4) & 1, h = lane >> 5;
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const int chunk = (w * 16 + t * 4 + 2 * g + (q >> 1)) ^ (4 * r);
-            off[t] = (8 * h + r) * 512 + chunk * 16 + (q & 1) * 8;
+        for (int t = 0; t < G::TM; ++t) {
+            const int chunk = (w * (R / 16) + t * 4 + 2 * g + (q >> 1)) ^ (4 * r);
+            off[t] = (8 * h + r) * G::MN_ROW + chunk * 16 + (q & 1) * 8;
         }
         slice = (int64_t)BK * ld;
         nk = nk_;
@@ -235,47 +272,56 @@ struct MnOperand {
             const int64_t end = (int64_t)(rows_left0 - BK * kt - 1) * ld_ + cols;  // elements
             if (end < 8 * ld_) range = end <= 0 ? 0u : (uint32_t)(end * 2);
         }
-        const __amdgpu_buffer_rsrc_t rs =
-            __builtin_amdgcn_make_buffer_rsrc((void*)(base + kt * slice), 0, range, kBufferRsrcW3);
+        constexpr int HALF = G::MN_INSTR / 2;
 #pragma unroll
-        for (int i = 2 * half; i < 2 * half + 2; ++i)
-            __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)(st + (4 * wave + i) * 1024), 16,
-                                                     voff[i], 0, 0, CPOL);
+        for (int i = HALF * half; i < HALF * half + HALF; ++i)
+            dma16(base + kt * slice, range, st + (G::MN_INSTR * wave + i) * 1024, voff[i], 0);
     }
-    __device__ void frags(const uint8_t* st, int s, u32x4 (&f)[4]) const {
+    __device__ void frags(const uint8_t* st, int s, u32x4 (&f)[G::TM]) const {
 #pragma unroll
-        for (int t = 0; t < 4; ++t) {
-            const uint8_t* base = st + off[t] + s * 8192;
-            const shortx4 lo = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base));
-            const shortx4 hi = __builtin_amdgcn_ds_read_tr16_b64_v4i16((lds_shortx4*)(base + 2048));
+        for (int t = 0; t < G::TM; ++t) {
+            const uint8_t* base = st + off[t] + s * 16 * G::MN_ROW;
+            const shortx4 lo = read_tr16(base);
+            const shortx4 hi = read_tr16(base + 4 * G::MN_ROW);
             const shortx8 v = __builtin_shufflevector(lo, hi, 0, 1, 2, 3, 4, 5, 6, 7);
             f[t] = __builtin_bit_cast(u32x4, v);
         }
     }
-    static constexpr int kReads = 8;
+    static constexpr int kReads = 2 * G::TM;
+    static constexpr int kHalfCopies = G::MN_INSTR / 2;
+    static constexpr int kStage = G::MN_STAGE;
 };
 
 // Copies a wave has issued after the last one that slice kt+1 needs, at the
 // wait in slice kt (steady state; the prologue is laid out to match).  Per
 // slice: K-contiguous operands copy half a pair before the barrier of even
-// slices and after the barrier of odd ones (4 instructions each);
-// MN-contiguous ones copy half a slice before and half after every barrier
-// (2 each), and are issued first.
+// slices and after the barrier of odd ones; MN-contiguous ones copy half a
+// slice before and half after every barrier, and are issued first.
+// ckc / cmn: copy instructions per half pair of a K-contiguous operand and
+// per half slice of an MN-contiguous one.  With one operand of each kind
+// the last copy slice kt+1 needs is the K-contiguous half pair issued
+// before the barrier of slice kt-2 (kt even) or kt-1 (kt odd); with two
+// MN-contiguous ones, the second's half slice before the barrier of kt-2.
 template <bool AK, bool BKc, bool kEven>
-constexpr int copies_after() {
-    if (AK != BKc) return kEven ? 16 : 4;  // one operand of each kind
-    if (AK) return kEven ? 16 : 0;         // both K-contiguous
-    return 16;                             // both MN-contiguous
+constexpr int copies_after(int ckc, int cmn) {
+    if (AK != BKc) return kEven ? 4 * cmn + 2 * ckc : 2 * cmn;  // one operand of each kind
+    if (AK) return kEven ? 4 * ckc : 0;                         // both K-contiguous
+    return 8 * cmn;                                             // both MN-contiguous
 }
 
 // Copies issued by the prologue after the last one slice 0 needs: every
-// MN-contiguous operand still has slices 1 and 2 (8) and half of slice 3 (2)
-// after it, every K-contiguous one the first half of pair 1 (4).
+// MN-contiguous operand still has slices 1 and 2 and half of slice 3 after
+// it (5 half slices), every K-contiguous one the first half of pair 1.
 template <bool AK, bool BKc>
-constexpr int prologue_after() {
+constexpr int prologue_after(int ckc, int cmn) {
     constexpr int nmn = (AK ? 0 : 1) + (BKc ? 0 : 1), nkc = 2 - nmn;
-    return nmn ? 10 * nmn + 4 * nkc : 4 * nkc;
+    return nmn ? 5 * cmn * nmn + ckc * nkc : ckc * nkc;
 }
+static_assert(copies_after<true, false, true>(4, 2) == 16 && copies_after<true, false, false>(4, 2) == 4 &&
+              copies_after<true, true, true>(4, 2) == 16 && copies_after<true, true, false>(4, 2) == 0 &&
+              copies_after<false, false, true>(4, 2) == 16 && prologue_after<true, false>(4, 2) == 14 &&
+              prologue_after<true, true>(4, 2) == 8 && prologue_after<false, false>(4, 2) == 20,
+              "the 256-tile wait counts");
 
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
@@ -283,16 +329,22 @@ constexpr int prologue_after() {
 // clipped descriptor ranges and store only their valid part).  kTail: K is
 // not a multiple of 128 (a last group of 1 to 4 slices after the loop, the
 // last slice possibly partial).
-template <In T, bool TA, bool TB, bool kEdge, bool kTail>
-__global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int tiles_m,
-                                                          int tiles_n, int grouped) {
+// R: workgroup tile R x R (256: one workgroup per CU; 128: two).
+template <In T, int R, bool TA, bool TB, bool kEdge, bool kTail>
+__global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma16_dma_kernel(GemmParams p,
+                                                                        int tiles_m,
+                                                                        int tiles_n,
+                                                                        int grouped) {
     const TileIdx tile = xcd_tile(tiles_m, tiles_n, grouped != 0);
     select_problem(p, tile.z);
     constexpr bool AK = !TA, BKc = TB;
-    using OpA = typename std::conditional<AK, KcOperand, MnOperand>::type;
-    using OpB = typename std::conditional<BKc, KcOperand, MnOperand>::type;
-    constexpr int SA01 = AK ? KC_STAGE : MN_STAGE, SA23 = AK ? 16 : MN_STAGE;
-    constexpr int SB01 = BKc ? KC_STAGE : MN_STAGE, SB23 = BKc ? 16 : MN_STAGE;
+    constexpr int TM = Geo<R>::TM;
+    using OpA = typename std::conditional<AK, KcOperand<R>, MnOperand<R>>::type;
+    using OpB = typename std::conditional<BKc, KcOperand<R>, MnOperand<R>>::type;
+    constexpr int SA01 = OpA::kStage, SA23 = AK ? 16 : OpA::kStage;
+    constexpr int SB01 = OpB::kStage, SB23 = BKc ? 16 : OpB::kStage;
+    constexpr int CKC = AK ? OpA::kHalfCopies : BKc ? OpB::kHalfCopies : 0;
+    constexpr int CMN = !AK ? OpA::kHalfCopies : !BKc ? OpB::kHalfCopies : 0;
     // One LDS object per operand and stage (K-contiguous operands use two).
     __shared__ __attribute__((aligned(1024))) uint8_t sA0[SA01];
     __shared__ __attribute__((aligned(1024))) uint8_t sA1[SA01];
@@ -306,8 +358,8 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-    const int m0 = tile.bm * BM;
-    const int n0 = tile.bn * BN;
+    const int m0 = tile.bm * R;
+    const int n0 = tile.bn * R;
     const int nk = (p.K + BK - 1) / BK;  // slices (the last one partial when K % 32 != 0)
 
     OpA opa;
@@ -317,18 +369,18 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     opb.template init<kEdge>(static_cast<const uint16_t*>(p.B), p.ldb, n0, wn, wave, lane, nk,
                              p.N, p.K);
 
-    floatx16 acc[4][4];
+    floatx16 acc[TM][TM];
 #pragma unroll
-    for (int i = 0; i < 4; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 4; ++j)
+        for (int j = 0; j < TM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
     // Operands of step s of slice position J (0..3 within a group of four
     // slices: a K-contiguous operand has it in stage J/2, half J%2; an
     // MN-contiguous one in stage J).
-    auto frags = [&](auto Jc, int s, u32x4 (&a)[4], u32x4 (&b)[4]) {
+    auto frags = [&](auto Jc, int s, u32x4 (&a)[TM], u32x4 (&b)[TM]) {
         constexpr int J = decltype(Jc)::value;
         if constexpr (AK) opa.frags(pick<J / 2>(sA0, sA1, sA2, sA3), J % 2, s, a);
         else opa.frags(pick<J>(sA0, sA1, sA2, sA3), s, a);
@@ -340,26 +392,36 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     // in program order are spread between them (per 4 MFMAs: 2 to 4 LDS
     // reads; a copy after every second MFMA), so the address unit never sees
     // a burst that would hold the wave, and its MFMA issue, back.
+    // (At 128 x 128 a step is 4 MFMAs: after each, two LDS reads and a copy.)
     constexpr int DS_PER = (OpA::kReads + OpB::kReads) / 4;
-    auto mfma_step = [&](const u32x4 (&a)[4], const u32x4 (&b)[4]) {
+    auto mfma_step = [&](const u32x4 (&a)[TM], const u32x4 (&b)[TM]) {
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+        for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < TM; ++tj)
                 acc[ti][tj] = mfma32x32x16<T>(a[ti], b[tj], acc[ti][tj]);
+        if constexpr (TM == 4) {
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
+            for (int i = 0; i < 4; ++i) {
 #pragma unroll
-            for (int m = 0; m < 4; ++m) {
-                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-                if (m < DS_PER) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
-                if (m & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // copy
+                for (int m = 0; m < 4; ++m) {
+                    __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+                    if (m < DS_PER) __builtin_amdgcn_sched_group_barrier(0x100, 1, 0);  // LDS read
+                    if (m & 1) __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);      // copy
+                }
+            }
+        } else {
+#pragma unroll
+            for (int m = 0; m < TM * TM; ++m) {
+                __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);  // MFMA
+                __builtin_amdgcn_sched_group_barrier(0x100, 2, 0);  // LDS reads
+                __builtin_amdgcn_sched_group_barrier(0x020, 1, 0);  // copy
             }
         }
         __builtin_amdgcn_sched_barrier(0);
     };
 
-    u32x4 a0[4], b0[4], a1[4], b1[4];
+    u32x4 a0[TM], b0[TM], a1[TM], b1[TM];
 
 
     // Slice kt at position J of its group of four.  Copies, per wave:
@@ -376,14 +438,14 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     // by element (a lane's fragment of step s holds k = 32kt + 16s + 8h ..
     // +7).  m/n-contiguous operands need no mask: their rows past K lie past
     // the copy descriptor's range and read as zeros.
-    auto mask_k = [&](int kt, int s, u32x4 (&f)[4]) {
+    auto mask_k = [&](int kt, int s, u32x4 (&f)[TM]) {
         const int valid = p.K - (BK * kt + 16 * s + 8 * h);  // elements of the 8 still below K
         uint32_t m[4];
 #pragma unroll
         for (int e = 0; e < 4; ++e)
             m[e] = (2 * e < valid ? 0x0000ffffu : 0u) | (2 * e + 1 < valid ? 0xffff0000u : 0u);
 #pragma unroll
-        for (int t = 0; t < 4; ++t)
+        for (int t = 0; t < TM; ++t)
 #pragma unroll
             for (int e = 0; e < 4; ++e) f[t][e] &= m[e];
     };
@@ -403,7 +465,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
         if constexpr (kEven && AK) opa.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
         if constexpr (kEven && BKc) opb.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
         mfma_step(a0, b0);  // step 1 (operands read earlier)
-        WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>()));  // own copies landed, reads returned
+        WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>(CKC, CMN)));  // own copies landed, reads returned
         barrier();                                           // ... for every wave
         frags(std::integral_constant<int, (J + 1) % 4>{}, 0, a0, b0);  // next slice, step 1
         if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
@@ -428,7 +490,7 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     if constexpr (!BKc) opb.template copy<kEdge, kTail>(sB3, 3, 0, wave);
     if constexpr (AK) opa.template copy<kEdge, kTail>(sA1, 1, 0, wave);
     if constexpr (BKc) opb.template copy<kEdge, kTail>(sB1, 1, 0, wave);
-    WAIT_VMCNT((prologue_after<AK, BKc>()));  // slice 0 of both operands landed
+    WAIT_VMCNT((prologue_after<AK, BKc>(CKC, CMN)));  // slice 0 of both operands landed
     barrier();
     frags(std::integral_constant<int, 0>{}, 0, a0, b0);
     using NoMask = std::false_type;
@@ -458,23 +520,23 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
     // 6% of the 8192^3 time); stores marked non-temporal drain ~2% sooner.  A lane's four bias values (one per column tile)
     // are read once; without a bias it adds -0.0, which leaves every value,
     // signed zeros included, unchanged.
-    const int col0 = n0 + wn * 128 + (lane & 31);
-    float* cbase = p.C + (int64_t)(m0 + wm * 128 + 4 * h) * p.ldc + col0;
+    const int col0 = n0 + wn * (R / 2) + (lane & 31);
+    float* cbase = p.C + (int64_t)(m0 + wm * (R / 2) + 4 * h) * p.ldc + col0;
     const float alpha = p.alpha, beta = p.beta;
-    float bias[4];
+    float bias[TM];
 #pragma unroll
-    for (int tj = 0; tj < 4; ++tj)
+    for (int tj = 0; tj < TM; ++tj)
         bias[tj] = p.bias && (!kEdge || col0 + tj * 32 < p.N) ? p.bias[col0 + tj * 32] : -0.0f;
     // on edge tiles only rows < M and columns < N are stored
-    const int row0 = m0 + wm * 128 + 4 * h;
+    const int row0 = m0 + wm * (R / 2) + 4 * h;
     auto ok = [&](int ti, int tj, int r) {
         return !kEdge || (row0 + ti * 32 + 8 * (r >> 2) + (r & 3) < p.M && col0 + tj * 32 < p.N);
     };
     if (beta == 0.0f) {
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+        for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj)
+            for (int tj = 0; tj < TM; ++tj)
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
                     if (ok(ti, tj, r))
@@ -485,9 +547,9 @@ __global__ __launch_bounds__(NT, 1) void mfma16_dma_kernel(GemmParams p, int til
         // C is read one 32 x 32 MFMA tile (16 values a lane) at a time
         // before those values are stored, so the reads of a tile overlap.
 #pragma unroll
-        for (int ti = 0; ti < 4; ++ti)
+        for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-            for (int tj = 0; tj < 4; ++tj) {
+            for (int tj = 0; tj < TM; ++tj) {
                 float cv[16];
 #pragma unroll
                 for (int r = 0; r < 16; ++r)
@@ -513,12 +575,14 @@ bool mfma16_dma_eligible(const GemmParams& p) {
            p.lda < kMaxBufferPitch && p.ldb < kMaxBufferPitch;
 }
 
-template <In T>
-hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
-    const int tiles_m = (p.M + BM - 1) / BM, tiles_n = (p.N + BN - 1) / BN;
+namespace {
+
+template <In T, int R>
+hipError_t launch_tiles(const GemmParams& p, hipStream_t s) {
+    const int tiles_m = (p.M + R - 1) / R, tiles_n = (p.N + R - 1) / R;
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool edge = p.M % BM != 0 || p.N % BN != 0;
+    const bool edge = p.M % R != 0 || p.N % R != 0;
     const bool tail = p.K % (BK * NSTAGE) != 0;
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
@@ -530,13 +594,37 @@ hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
         };
         // a K tail takes the edge-tile instance whatever M and N (its guards
         // then always pass); built without edges it spills registers
-        if (tail) go(mfma16_dma_kernel<T, TA, TB, true, true>);
-        else if (edge) go(mfma16_dma_kernel<T, TA, TB, true, false>);
-        else go(mfma16_dma_kernel<T, TA, TB, false, false>);
+        if (tail) go(mfma16_dma_kernel<T, R, TA, TB, true, true>);
+        else if (edge) go(mfma16_dma_kernel<T, R, TA, TB, true, false>);
+        else go(mfma16_dma_kernel<T, R, TA, TB, false, false>);
         return hipGetLastError();
     });
 }
+
+}  // namespace
+
+template <In T>
+hipError_t launch_mfma16_dma_tile(const GemmParams& p, hipStream_t s, int tile) {
+    return tile == 128 ? launch_tiles<T, 128>(p, s) : launch_tiles<T, 256>(p, s);
+}
+
+// Tile size by the waves of tiles the CUs work through.  A CU runs one
+// 256-tile, or two 128-tiles side by side (alone, a 128-tile leaves the CU
+// about as slow as a pair does), and a 128-tile costs kCost128 quarters of a
+// 256-tile's time (measured at 8192^3: 0.932 against 0.766 ms).  In units
+// of a quarter 256-tile: 4 per wave of 256 tiles against 2 * kCost128 per
+// wave of 512.  Ties keep the larger tile.
+template <In T>
+hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s) {
+    const int64_t t256 = (int64_t)((p.M + 255) / 256) * ((p.N + 255) / 256) * p.batch;
+    const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    const double time256 = (double)((t256 + kCUs - 1) / kCUs) * 4.0;
+    const double time128 = (double)((t128 + 2 * kCUs - 1) / (2 * kCUs)) * 2.0 * kCost128;
+    return time128 < time256 ? launch_tiles<T, 128>(p, s) : launch_tiles<T, 256>(p, s);
+}
 template hipError_t launch_mfma16_dma<In::BF16>(const GemmParams&, hipStream_t);
 template hipError_t launch_mfma16_dma<In::F16>(const GemmParams&, hipStream_t);
+template hipError_t launch_mfma16_dma_tile<In::BF16>(const GemmParams&, hipStream_t, int);
+template hipError_t launch_mfma16_dma_tile<In::F16>(const GemmParams&, hipStream_t, int);
 
 }  // namespace dgt

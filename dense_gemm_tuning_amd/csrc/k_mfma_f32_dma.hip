@@ -564,6 +564,10 @@ hipError_t launch_tiles(const GemmParams& p, hipStream_t s) {
 
 }  // namespace
 
+hipError_t launch_mfma_f32_dma_tile(const GemmParams& p, hipStream_t s, int tile) {
+    return tile == 128 ? launch_tiles<128>(p, s) : launch_tiles<256>(p, s);
+}
+
 // Tile size by the waves of tiles the CUs work through: both sizes reach
 // ~0.96 of the MFMA peak (a CU runs one 256-tile or two 128-tiles at a
 // time), so a CU's time is its share of tiles rounded up, counted in

@@ -228,13 +228,14 @@ WORKLOADS = {
                                             splits=0),
     # One GPU's share when the two headline BF16 products are split by
     # columns of B / C over 8 GPUs: 8 x 8192 x 3584 (skinny, 58.7 MB of B) and
-    # 8192 x 1024 x 8192.  Each has too few column strips / tiles to fill the
-    # GPU on its own, so both run split-K (automatic slice count).
+    # 8192 x 1024 x 8192.  The skinny share has too few column strips to fill
+    # the GPU and runs split-K (automatic slice count); the other fills it
+    # with 512 tiles of 128 x 128 and runs unsplit.
     "bf16_skinny_shard_8x3584x8192": Workload("bf16_skinny_shard_8x3584x8192", "bf16", 8, 3584,
                                               8192, 1.0, 0.0, "normal", sigma=0.02,
                                               seed_base=15000, splits=0),
     "bf16_shard_8192x1024x8192": Workload("bf16_shard_8192x1024x8192", "bf16", 8192, 1024, 8192,
-                                          1.0, 0.0, "normal", seed_base=16000, splits=0),
+                                          1.0, 0.0, "normal", seed_base=16000),
 }
 
 

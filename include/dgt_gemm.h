@@ -109,12 +109,24 @@ enum gemm_variant {
     GEMM_VARIANT_MFMA = 3,      /* LDS-staged macro tiles, double-buffered,
                                    per-wavefront MFMA micro-tiles, masked
                                    ragged edges (dilfish.github.io 5.4-5.5;
-                                   qwbw.cn section 三)                        */
-    GEMM_VARIANT_SKINNY = 4     /* M <= 64: streams B once from HBM, A held in
+                                   qwbw.cn section 三); the workgroup tile
+                                   (256 x 256 or 128 x 128) is chosen per
+                                   launch                                     */
+    GEMM_VARIANT_SKINNY = 4,    /* M <= 64: streams B once from HBM, A held in
                                    registers per step (up to four 16-row
                                    blocks), K split over waves and reduced
                                    in LDS (dilfish.github.io 5.1 GEMV row and
                                    batching; qwbw.cn section 四)              */
+    GEMM_VARIANT_MFMA_T256 = 5, /* the MFMA rung's global->LDS DMA kernel with
+                                   a fixed 256 x 256 workgroup tile (one
+                                   workgroup per CU): the block-size choice
+                                   of dilfish.github.io 5.3-5.4 made
+                                   explicit.  Needs 16-byte aligned operand
+                                   rows (pitch and base) and pitches below
+                                   2^23 (fp32) or 2^24 (16-bit) elements;
+                                   GEMM_ERR_VARIANT otherwise                */
+    GEMM_VARIANT_MFMA_T128 = 6  /* the same with 128 x 128 tiles, two
+                                   workgroups per CU                          */
 };
 
 /* C <- alpha*A*B + beta*C, fp32 inputs, fp32 accumulate/output. */
@@ -135,8 +147,10 @@ int gemm_f16(int M, int N, int K, float alpha, const uint16_t* A, int lda,
              void* stream);
 
 /* Same as gemm_f32 / gemm_bf16 / gemm_f16 with an explicit ladder rung (enum
- * gemm_variant).  GEMM_VARIANT_SKINNY requires M <= 64 and returns
- * GEMM_ERR_VARIANT otherwise. */
+ * gemm_variant).  GEMM_VARIANT_SKINNY requires M <= 64, and the fixed-tile
+ * MFMA rungs 16-byte aligned operand rows, and return GEMM_ERR_VARIANT
+ * otherwise (checked on the host before anything is queued; alpha == 0 or
+ * K == 0 never reads A or B and so never fails this check). */
 int gemm_f32_variant(int variant, int M, int N, int K, float alpha,
                      const float* A, int lda, const float* B, int ldb,
                      float beta, float* C, int ldc, void* stream);

@@ -86,6 +86,28 @@ def test_variant_checks(lib):
         assert fn(dgt.VARIANT_SKINNY, 65, 4, 4, 1.0, A_, 4, B_, 4, 0.0,
                   C_, 4) == dgt.GEMM_ERR_VARIANT
         assert fn(99, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
+    assert v(dgt.VARIANT_MFMA_T128 + 1, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == \
+        dgt.GEMM_ERR_VARIANT
+
+
+def test_fixed_tile_rungs_need_aligned_rows(lib):
+    """The fixed-tile MFMA rungs run only the DMA kernels: rows that are not
+    16-byte aligned (pitch or base) are refused on the host, before any HIP
+    call; alpha == 0 reads neither operand and is not refused (NULL C stops
+    that call before its launch)."""
+    M = N = K = 64
+    for rung in (dgt.VARIANT_MFMA_T256, dgt.VARIANT_MFMA_T128):
+        # fp32: a pitch of 66 floats is 264 bytes, not a multiple of 16
+        assert dgt.gemm_f32_variant(rung, M, N, K, 1.0, A_, 66, B_, N, 0.0, C_, N) == \
+            dgt.GEMM_ERR_VARIANT
+        assert dgt.gemm_f32_variant(rung, M, N, K, 1.0, A_ + 4, K, B_, N, 0.0, C_, N) == \
+            dgt.GEMM_ERR_VARIANT
+        # 16-bit: a pitch of 68 elements is 136 bytes
+        for fn in (dgt.gemm_bf16_variant, dgt.gemm_f16_variant):
+            assert fn(rung, M, N, K, 1.0, A_, K, B_, 68, 0.0, C_, N) == dgt.GEMM_ERR_VARIANT
+            assert fn(rung, M, N, K, 1.0, A_, K, B_ + 2, N, 0.0, C_, N) == dgt.GEMM_ERR_VARIANT
+        assert dgt.gemm_f32_variant(rung, M, N, K, 0.0, A_, 66, B_, N, 0.0, 0, N) == \
+            dgt.GEMM_ERR_NULL
 
 
 def test_alpha_zero_does_not_need_a_or_b(lib):
@@ -209,8 +231,10 @@ def test_splitk_planning(lib):
     # of 128 (the last 104 deep)
     assert sl(F32, 1000, 1000, 1000, 0) == 8
     assert ws(F32, 1000, 1000, 1000, 0) == 8 * 1000 * 1000 * 4
-    # 1024 x 1024 bf16 with K = 16384: 16 tiles of 256 x 256 -> 16 slices
-    assert sl(BF16, 1024, 1024, 16384, 0) == 16
+    # 1024 x 1024 bf16 with K = 16384: 64 tiles of 128 x 128 -> 8 slices
+    assert sl(BF16, 1024, 1024, 16384, 0) == 8
+    # 8192 x 1024 bf16: 512 tiles of 128 x 128 fill the slots unsplit
+    assert sl(BF16, 8192, 1024, 8192, 0) == 1
     # enough tiles already, or K too short to split: one slice, no workspace
     assert sl(BF16, 8192, 8192, 8192, 0) == 1 and ws(BF16, 8192, 8192, 8192, 0) == 0
     assert sl(F32, 1000, 1000, 128, 0) == 1       # one 128-deep slice covers K

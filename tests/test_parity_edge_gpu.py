@@ -1,8 +1,8 @@
 """GPU parity for the whole-tile BF16/FP16 path on shapes that are not whole
 tiles, against the CPU oracle, through the C ABI.
 
-M and N that are not multiples of 256 run the global->LDS DMA kernel with
-edge tiles: the copy descriptors' ranges stop at each operand's last
+M and N that are not multiples of the workgroup tile (256 or 128; the
+fixed-tile rungs run each) run the global->LDS DMA kernel with edge tiles: the copy descriptors' ranges stop at each operand's last
 element and the epilogue stores only rows < M and columns < N.  Any K runs
 there too: when K is not a multiple of 128 the last group of 1 to 4 slices
 runs after the main loop, and in a partial last slice the k-contiguous
@@ -58,27 +58,34 @@ def stored(M, N, K, ta, tb):
     return ((K, M) if ta else (M, K)), ((N, K) if tb else (K, N))
 
 
+@pytest.mark.parametrize("tile", ["mfma256", "mfma128"])
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("dtype", ["bf16", "f16"])
-def test_edge_and_ragged_k_integer_bit_exact(dtype, layout):
+def test_edge_and_ragged_k_integer_bit_exact(dtype, layout, tile):
+    """Every shape with both workgroup tiles (the fixed-tile rungs), except
+    the one whose rows are not 16-byte aligned, which runs the automatic
+    choice (the register-staged kernel)."""
     ta, tb = LAYOUTS[layout]
     for idx, (M, N, K) in enumerate(EDGE + RAGGED_K):
         sa, sb = stored(M, N, K, ta, tb)
+        aligned = sa[1] % 8 == 0 and sb[1] % 8 == 0
         A = gi.draw(1600 + idx, *sa, "int", dtype=dtype)
         B = gi.draw(1700 + idx, *sb, "int", dtype=dtype)
         C0 = gi.draw(1800 + idx, M, N, "int")
         for alpha, beta in [(1.0, 0.0), (1.5, 0.5)]:
             c0 = C0 if beta else None  # beta = 0: C starts NaN and must not be read
-            say(f"edge {dtype} {layout} {M}x{N}x{K} a={alpha} b={beta}")
-            st, C = run_gemm("mfma", dtype, A, B, c0, alpha, beta, trans_a=ta, trans_b=tb)
+            say(f"edge {dtype} {layout} {tile} {M}x{N}x{K} a={alpha} b={beta}")
+            st, C = run_gemm(tile if aligned else "mfma", dtype, A, B, c0, alpha, beta,
+                             trans_a=ta, trans_b=tb)
             assert st == 0, dgt.gemm_status_string(st)
             R = oracle.round_f32(oracle.gemm(A, B, c0, alpha, beta, dtype, trans_a=ta,
                                              trans_b=tb))
             assert_bit_exact(C, R, f"{dtype}/{layout} {M}x{N}x{K} a={alpha} b={beta}")
 
 
+@pytest.mark.parametrize("tile", ["mfma256", "mfma128"])
 @pytest.mark.parametrize("layout", list(LAYOUTS))
-def test_k_not_multiple_of_8_on_padded_storage(layout):
+def test_k_not_multiple_of_8_on_padded_storage(layout, tile):
     """Pitches padded to multiples of 8 elements keep 16-byte rows, so K that
     is not a multiple of 8 still runs the DMA kernel: the last slice's
     fragments are masked element by element (K = 5 and 77 fit in one or
@@ -100,16 +107,17 @@ def test_k_not_multiple_of_8_on_padded_storage(layout):
 
         dA, dB = padded(A), padded(B)
         dC = torch.from_numpy(C0).cuda()
-        say(f"padded K {layout} {M}x{N}x{K}")
-        st = dgt.gemm(dA, dB, dC, 1.5, 0.5, trans_a=ta, trans_b=tb)
+        say(f"padded K {layout} {tile} {M}x{N}x{K}")
+        st = dgt.gemm(dA, dB, dC, 1.5, 0.5, variant=tile, trans_a=ta, trans_b=tb)
         torch.cuda.synchronize()
         assert st == 0, dgt.gemm_status_string(st)
         R = oracle.round_f32(oracle.gemm(A, B, C0, 1.5, 0.5, "bf16", trans_a=ta, trans_b=tb))
         assert_bit_exact(dC.cpu().numpy(), R, f"padded K {layout} {M}x{N}x{K}")
 
 
+@pytest.mark.parametrize("tile", ["mfma256", "mfma128"])
 @pytest.mark.parametrize("layout", list(LAYOUTS))
-def test_edge_guard_band(layout):
+def test_edge_guard_band(layout, tile):
     """C padded (ldc > N) inside a canary-filled buffer: an edge tile stores
     only its valid part, so the padding and the elements after C keep the
     canary; the same with a K remainder (two passes over C)."""
@@ -123,8 +131,8 @@ def test_edge_guard_band(layout):
         base = torch.full((M * ldc + 300,), canary, device="cuda")
         dC = base[:M * ldc].view(M, ldc)[:, :N]
         dC.copy_(torch.from_numpy(C0).cuda())
-        say(f"edge guard band {layout} {M}x{N}x{K}")
-        st = dgt.gemm(to_dev(A, "bf16"), to_dev(B, "bf16"), dC, 1.5, 0.5, variant="mfma",
+        say(f"edge guard band {layout} {tile} {M}x{N}x{K}")
+        st = dgt.gemm(to_dev(A, "bf16"), to_dev(B, "bf16"), dC, 1.5, 0.5, variant=tile,
                       trans_a=ta, trans_b=tb)
         torch.cuda.synchronize()
         assert st == 0
