@@ -4,8 +4,11 @@
 //
 // Tiling as in the register-staged kernel (256 x 256 workgroup tile, 2 x 2
 // wavefronts of 128 x 128, v_mfma_f32_32x32x16: dilfish.github.io 5.3-5.5,
-// qwbw.cn Level 2), with a deeper software pipeline than the pages' double
-// buffer (dilfish.github.io 5.4; qwbw.cn's double-buffering row):
+// qwbw.cn Level 2), or, for launches with few such tiles, 128 x 128 (two
+// workgroups per CU, wavefronts of 64 x 64), with a deeper software
+// pipeline than the pages' double buffer (dilfish.github.io 5.4; qwbw.cn's
+// double-buffering row).  The notes below give the 256 x 256 sizes; at 128
+// a stage holds half the rows or columns and each wave half the copies:
 //
 //  * K advances in slices of 32.  Copies use buffer_load_dwordx4 ... lds:
 //    lane l's 16 bytes land at LDS base + 16*l, so one instruction fills
@@ -40,7 +43,7 @@
 //    first operands of slice t+1 are read while step 2 of slice t computes.
 //
 // Used for any M, N and K with 16-byte aligned rows and row pitches below
-// 2^24 elements (so that 64 rows of lane offsets fit 32 bits).  On edge
+// 2^24 elements (so that a wave's rows of lane offsets fit 32 bits).  On edge
 // tiles the copy descriptors' ranges stop at the operands' last elements and
 // the epilogue stores only the valid part.  When K is not a multiple of 128
 // the K loop runs in groups of four 32-deep slices and the last group (1 to
