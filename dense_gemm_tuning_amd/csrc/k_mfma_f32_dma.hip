@@ -36,9 +36,9 @@
 // wave 64 x 64), chosen per launch by the waves of tiles the CUs work
 // through.  Used for any M, N and K with 16-byte aligned rows and row
 // pitches below 2^23 elements (so a wave's rows of lane offsets fit 32
-// bits); the register-staged 128 x 128 kernel takes unaligned operands.  On edge tiles
-// the copy descriptors' ranges stop at the operands' last elements and the
-// epilogue stores only the valid part.  When K is not a multiple of 64 the
+// bits); the register-staged 128 x 128 kernel takes unaligned operands.
+// On edge tiles the copy descriptors' ranges stop at the operands' last
+// elements and the epilogue stores only the valid part.  When K is not a multiple of 64 the
 // last group of 1 to 4 slices runs after the loop; in a partial last slice
 // the k-contiguous fragments are masked past K, and m/n-contiguous rows past
 // K read as zeros through the descriptor range.
