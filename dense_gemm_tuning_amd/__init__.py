@@ -205,7 +205,9 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
     K x M tensor, B the stored N x K tensor.
 
     A and B are float32, bfloat16 or float16 (16-bit bits are passed as-is),
-    C float32.
+    C float32.  ``variant`` is a ladder rung (enum gemm_variant) or its name
+    in VARIANTS: "auto", "naive", "lds", "mfma", "skinny", or "mfma256" /
+    "mfma128" for the DMA kernels with a fixed workgroup tile.
     Returns the status code; the work is queued on ``stream`` (default: torch's
     current stream) and not waited for.
     """
