@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 5
+#define DGT_GEMM_ABI_VERSION 6
 
 /* Input formats (the dtype argument of gemm_ex and gemm_select_variant). */
 enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };

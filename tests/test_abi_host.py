@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 5
+    assert dgt.gemm_abi_version() == 6
     for code in range(0, -9, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
