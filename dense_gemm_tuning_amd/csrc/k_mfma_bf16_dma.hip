@@ -52,15 +52,15 @@
 // k-contiguous fragments are masked past K, and m/n-contiguous rows past K
 // read as zeros through the descriptor range.  The register-staged kernel
 // handles unaligned operands.
-#include "gemm_common.hpp"
+#include "dma_common.hpp"
 
 namespace dgt {
 
 namespace {
 
+using namespace dma;
+
 constexpr int BK = 32, NT = 256, NSTAGE = 4;
-constexpr int CPOL = 1;                     // sc0 on the copies
-constexpr int64_t kCUs = 256;
 constexpr double kCost128 = 1.22;           // a 128-tile's time, in quarters of a 256-tile's
 
 // Geometry of a workgroup tile of R x R (R = 256 or 128; a 2 x 2 grid of
@@ -82,58 +82,13 @@ struct Geo {
 
 typedef short shortx4 __attribute__((ext_vector_type(4)));
 typedef short shortx8 __attribute__((ext_vector_type(8)));
-typedef __attribute__((address_space(3))) void lds_void;
 typedef __attribute__((address_space(3))) shortx4 lds_shortx4;
 
-// A copy descriptor's range ends at an operand's last element rounded up to
-// a whole 16-byte chunk: the hardware returns zeros for a 16-byte load that
-// reaches past the range, even for its bytes inside it.  The rounding never
-// reads another page (a 16-byte aligned chunk lies within one), and what it
-// reads past the element only feeds outputs that are not stored or k that
-// are masked.
-__device__ __forceinline__ int round8(int n) { return (n + 7) & ~7; }
 
-// One 16-byte-per-lane copy, global -> LDS, through a buffer descriptor of
-// `range` bytes from `base`: lane l's bytes at base + voff + soff land at
-// lds + 16*l.  (A plain function: the host pass of the templates below then
-// never sees the device-only descriptor type.)
-__device__ __forceinline__ void dma16(const void* base, uint32_t range, uint8_t* lds,
-                                      uint32_t voff, uint32_t soff) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, range, kBufferRsrcW3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, CPOL);
-}
 
-// K-contiguous rows are 128 B = 8 chunks of 16 B; chunk q of row r sits at
-// q ^ swz_kc(r).
-__device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
 
-// s_waitcnt vmcnt(n) with expcnt and lgkmcnt left at their maxima (gfx9
-// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in 6:4,
-// lgkmcnt in 11:8); WAIT_VMCNT_LGKM0 also drains this wave's LDS reads.
-#define WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
-#define WAIT_VMCNT_LGKM0(n) \
-    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0070)
 
-// Workgroup barrier without a memory fence: LDS data written by copies is
-// published by each wave waiting for its own copies first.
-__device__ __forceinline__ void barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
 
-// Stage I of an operand, chosen at compile time so that every LDS access
-// names one __shared__ object (the compiler then sees that a copy in flight
-// into one stage does not alias reads of another).
-template <int I>
-__device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3) {
-    if constexpr (I == 0) return s0;
-    else if constexpr (I == 1) return s1;
-    else if constexpr (I == 2) return s2;
-    else return s3;
-}
 
 // A K-contiguous operand: stage = a pair of slices, R rows x 128 B.  Wave w
 // issues copy instructions j = (R/32)w + i per pair, instruction j filling
@@ -167,7 +122,7 @@ struct KcOperand {
         base = X + (int64_t)(mn0 + G::KC_ROWS * wave) * ld;
         int rows = G::KC_ROWS;
         if constexpr (kEdge) rows = min(G::KC_ROWS, mn_lim - (mn0 + G::KC_ROWS * wave));
-        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round8(K)) * 2);
+        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round_chunk<8>(K)) * 2);
         // rows w*R/2 + t*32 + l%32; half-wave h reads chunk 4u + 2s + h
         const int h = lane >> 5;
 #pragma unroll
@@ -253,7 +208,7 @@ struct MnOperand {
         bytes = (uint32_t)(8 * ld * 2);
         ld_ = ld;
         rows_left0 = K - 8 * wave;
-        cols = kEdge ? round8(mn_lim - mn0) : 0;
+        cols = kEdge ? round_chunk<8>(mn_lim - mn0) : 0;
         // Source lane 4r+q of 16-lane group G reads k-row 16s + 8h + 4t + r,
         // columns w*R/2 + tile*32 + 16*(G%2) + 4q .. +3 (t = which of the two
         // reads); k & 3 == r.
@@ -295,36 +250,6 @@ struct MnOperand {
     static constexpr int kStage = G::MN_STAGE;
 };
 
-// Copies a wave has issued after the last one that slice kt+1 needs, at the
-// wait in slice kt (steady state; the prologue is laid out to match).  Per
-// slice: K-contiguous operands copy half a pair before the barrier of even
-// slices and after the barrier of odd ones; MN-contiguous ones copy half a
-// slice before and half after every barrier, and are issued first.
-// ckc / cmn: copy instructions per half pair of a K-contiguous operand and
-// per half slice of an MN-contiguous one.  With one operand of each kind
-// the last copy slice kt+1 needs is the K-contiguous half pair issued
-// before the barrier of slice kt-2 (kt even) or kt-1 (kt odd); with two
-// MN-contiguous ones, the second's half slice before the barrier of kt-2.
-template <bool AK, bool BKc, bool kEven>
-constexpr int copies_after(int ckc, int cmn) {
-    if (AK != BKc) return kEven ? 4 * cmn + 2 * ckc : 2 * cmn;  // one operand of each kind
-    if (AK) return kEven ? 4 * ckc : 0;                         // both K-contiguous
-    return 8 * cmn;                                             // both MN-contiguous
-}
-
-// Copies issued by the prologue after the last one slice 0 needs: every
-// MN-contiguous operand still has slices 1 and 2 and half of slice 3 after
-// it (5 half slices), every K-contiguous one the first half of pair 1.
-template <bool AK, bool BKc>
-constexpr int prologue_after(int ckc, int cmn) {
-    constexpr int nmn = (AK ? 0 : 1) + (BKc ? 0 : 1), nkc = 2 - nmn;
-    return nmn ? 5 * cmn * nmn + ckc * nkc : ckc * nkc;
-}
-static_assert(copies_after<true, false, true>(4, 2) == 16 && copies_after<true, false, false>(4, 2) == 4 &&
-              copies_after<true, true, true>(4, 2) == 16 && copies_after<true, true, false>(4, 2) == 0 &&
-              copies_after<false, false, true>(4, 2) == 16 && prologue_after<true, false>(4, 2) == 14 &&
-              prologue_after<true, true>(4, 2) == 8 && prologue_after<false, false>(4, 2) == 20,
-              "the 256-tile wait counts");
 
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
@@ -468,7 +393,7 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma16_dma_kernel(GemmPa
         if constexpr (kEven && AK) opa.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
         if constexpr (kEven && BKc) opb.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
         mfma_step(a0, b0);  // step 1 (operands read earlier)
-        WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>(CKC, CMN)));  // own copies landed, reads returned
+        DMA_WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>(CKC, CMN)));  // own copies landed, reads returned
         barrier();                                           // ... for every wave
         frags(std::integral_constant<int, (J + 1) % 4>{}, 0, a0, b0);  // next slice, step 1
         if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
@@ -493,7 +418,7 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma16_dma_kernel(GemmPa
     if constexpr (!BKc) opb.template copy<kEdge, kTail>(sB3, 3, 0, wave);
     if constexpr (AK) opa.template copy<kEdge, kTail>(sA1, 1, 0, wave);
     if constexpr (BKc) opb.template copy<kEdge, kTail>(sB1, 1, 0, wave);
-    WAIT_VMCNT((prologue_after<AK, BKc>(CKC, CMN)));  // slice 0 of both operands landed
+    DMA_WAIT_VMCNT((prologue_after<AK, BKc>(CKC, CMN)));  // slice 0 of both operands landed
     barrier();
     frags(std::integral_constant<int, 0>{}, 0, a0, b0);
     using NoMask = std::false_type;
@@ -513,7 +438,7 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma16_dma_kernel(GemmPa
         if (rest >= 3) slice(std::integral_constant<int, 2>{}, kt + 2, std::true_type{});
         if (rest >= 4) slice(std::integral_constant<int, 3>{}, kt + 3, std::true_type{});
     }
-    WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
+    DMA_WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
 
     // 32x32 accumulator layout: register r of lane l is row
     // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the MFMA tile.  C is read

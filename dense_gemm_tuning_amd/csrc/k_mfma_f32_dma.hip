@@ -42,14 +42,15 @@
 // last group of 1 to 4 slices runs after the loop; in a partial last slice
 // the k-contiguous fragments are masked past K, and m/n-contiguous rows past
 // K read as zeros through the descriptor range.
-#include "gemm_common.hpp"
+#include "dma_common.hpp"
 
 namespace dgt {
 
 namespace {
 
+using namespace dma;
+
 constexpr int BK = 16, NT = 256, NSTAGE = 4;
-constexpr int CPOL = 1;              // sc0 on the copies
 
 // Geometry of a workgroup tile of R x R (R = 256 or 128; a 2 x 2 grid of
 // wavefronts of R/2 x R/2).  A k-contiguous stage holds R rows of 128 B (two
@@ -68,58 +69,11 @@ struct Geo {
     static constexpr int MN_STAGE = BK * MN_ROW;
 };
 constexpr int64_t kMaxPitchF32 = int64_t(1) << 23;
-constexpr int64_t kCUs = 256;
 
-typedef __attribute__((address_space(3))) void lds_void;
-
-// A copy descriptor's range ends at an operand's last element rounded up to
-// a whole 16-byte chunk: the hardware returns zeros for a 16-byte load that
-// reaches past the range, even for its bytes inside it.  The rounding never
-// reads another page (a 16-byte aligned chunk lies within one), and what it
-// reads past the element only feeds outputs that are not stored or k that
-// are masked.
-__device__ __forceinline__ int round4(int n) { return (n + 3) & ~3; }
-
-__device__ __forceinline__ int swz_kc(int r) { return (r ^ (r >> 3)) & 7; }
+// m/n-contiguous k-rows: chunk c of k-row k sits at c ^ swz_mn(k), so the
+// two half-wavefronts, which read k-rows 8 apart, use opposite halves of
+// the LDS banks.
 __device__ __forceinline__ int swz_mn(int k) { return ((k >> 3) & 1) * 8; }
-
-// s_waitcnt vmcnt(n) with expcnt and lgkmcnt at their maxima (gfx9
-// encoding: vmcnt[3:0] in bits 3:0, vmcnt[5:4] in bits 15:14, expcnt in 6:4,
-// lgkmcnt in 11:8); WAIT_VMCNT_LGKM0 also drains this wave's LDS reads.
-#define WAIT_VMCNT(n) \
-    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0F70)
-#define WAIT_VMCNT_LGKM0(n) \
-    __builtin_amdgcn_s_waitcnt((((n) & 15) | (((n) >> 4) << 14)) | 0x0070)
-
-// Workgroup barrier without a memory fence: LDS data written by copies is
-// published by each wave waiting for its own copies first.
-__device__ __forceinline__ void barrier() {
-    asm volatile("" ::: "memory");
-    __builtin_amdgcn_s_barrier();
-    asm volatile("" ::: "memory");
-}
-
-// One 16-byte-per-lane copy, global -> LDS, through a buffer descriptor of
-// `range` bytes from `base`: lane l's bytes at base + voff + soff land at
-// lds + 16*l.  (A plain function: the host pass of the templates below then
-// never sees the device-only descriptor type.)
-__device__ __forceinline__ void dma16(const void* base, uint32_t range, uint8_t* lds,
-                                      uint32_t voff, uint32_t soff) {
-    const __amdgpu_buffer_rsrc_t rs =
-        __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(base), 0, range, kBufferRsrcW3);
-    __builtin_amdgcn_raw_ptr_buffer_load_lds(rs, (lds_void*)lds, 16, voff, soff, 0, CPOL);
-}
-
-// Stage I of an operand, chosen at compile time so that every LDS access
-// names one __shared__ object (the compiler's wait-count pass then sees that
-// a copy in flight into one stage does not alias reads of another).
-template <int I>
-__device__ __forceinline__ uint8_t* pick(uint8_t* s0, uint8_t* s1, uint8_t* s2, uint8_t* s3) {
-    if constexpr (I == 0) return s0;
-    else if constexpr (I == 1) return s1;
-    else if constexpr (I == 2) return s2;
-    else return s3;
-}
 
 // A K-contiguous operand: stage = a pair of slices, R rows x 128 B.  Wave w
 // issues copy instructions j = (R/32)w + i per pair, instruction j filling
@@ -151,7 +105,7 @@ struct KcOperand {
         base = X + (int64_t)(mn0 + G::KC_ROWS * wave) * ld;
         int rows = G::KC_ROWS;
         if constexpr (kEdge) rows = min(G::KC_ROWS, mn_lim - (mn0 + G::KC_ROWS * wave));
-        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round4(K)) * 4);
+        bytes = rows <= 0 ? 0u : (uint32_t)(((int64_t)(rows - 1) * ld + round_chunk<4>(K)) * 4);
         // rows w*R/2 + t*32 + l%32; half-wave h, half slice s read chunk 4u + 2h + s
         const int h = lane >> 5;
 #pragma unroll
@@ -242,7 +196,7 @@ struct MnOperand {
         nk = nk_;
         ld_ = ld;
         rows_left0 = K - 4 * wave;
-        cols = kEdge ? round4(mn_lim - mn0) : 0;
+        cols = kEdge ? round_chunk<4>(mn_lim - mn0) : 0;
     }
     // Half `half` of slice kt into stage st (past the end: the last slice).
     template <bool kEdge = false, bool kTail = false>
@@ -270,36 +224,6 @@ struct MnOperand {
     static constexpr int kStage = G::MN_STAGE;
 };
 
-// Copies a wave has issued after the last one that slice kt+1 needs, at the
-// wait in slice kt (steady state; the prologue is laid out to match), for
-// ckc copy instructions per half pair of a K-contiguous operand and cmn per
-// half slice of an MN-contiguous one.  Per slice: K-contiguous operands
-// copy half a pair before the barrier of even slices and after the barrier
-// of odd ones; MN-contiguous ones copy half a slice before and half after
-// every barrier, and are issued first.  With one operand of each kind the
-// last copy slice kt+1 needs is the K-contiguous half pair issued before
-// the barrier of slice kt-2 (kt even) or kt-1 (kt odd); with two
-// MN-contiguous ones, the second's half slice before the barrier of kt-2.
-template <bool AK, bool BKc, bool kEven>
-constexpr int copies_after(int ckc, int cmn) {
-    if (AK != BKc) return kEven ? 4 * cmn + 2 * ckc : 2 * cmn;  // one operand of each kind
-    if (AK) return kEven ? 4 * ckc : 0;                         // both K-contiguous
-    return 8 * cmn;                                             // both MN-contiguous
-}
-
-// Copies issued by the prologue after the last one slice 0 needs: every
-// MN-contiguous operand still has slices 1 and 2 and half of slice 3 after
-// it (5 half slices), every K-contiguous one the first half of pair 1.
-template <bool AK, bool BKc>
-constexpr int prologue_after(int ckc, int cmn) {
-    constexpr int nmn = (AK ? 0 : 1) + (BKc ? 0 : 1), nkc = 2 - nmn;
-    return nmn ? 5 * cmn * nmn + ckc * nkc : ckc * nkc;
-}
-static_assert(copies_after<true, false, true>(4, 2) == 16 && copies_after<true, false, false>(4, 2) == 4 &&
-              copies_after<true, true, true>(4, 2) == 16 && copies_after<false, false, true>(4, 2) == 16 &&
-              prologue_after<true, false>(4, 2) == 14 && prologue_after<true, true>(4, 2) == 8 &&
-              prologue_after<false, false>(4, 2) == 20,
-              "the 256-tile counts are those of the 16-bit DMA kernel");
 
 // TA / TB: A / B stored transposed.  A is K-contiguous unless TA, B is
 // K-contiguous when TB.
@@ -432,7 +356,7 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(Gemm
         if constexpr (kEven && AK) opa.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sA0, sA1, sA2, sA3), kt / 2 + 1, 1, wave);
         if constexpr (kEven && BKc) opb.template copy<kEdge, kTail>(pick<(J / 2 + 1) % 2>(sB0, sB1, sB2, sB3), kt / 2 + 1, 1, wave);
         mfma_step(a0, b0);  // first half slice (operands read earlier)
-        WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>(CKC, CMN)));  // own copies landed, reads returned
+        DMA_WAIT_VMCNT_LGKM0((copies_after<AK, BKc, kEven>(CKC, CMN)));  // own copies landed, reads returned
         barrier();                                           // ... for every wave
         frags(std::integral_constant<int, (J + 1) % 4>{}, 0, a0, b0);  // next slice, first half
         if constexpr (!AK) opa.template copy<kEdge, kTail>(pick<J>(sA0, sA1, sA2, sA3), kt + NSTAGE, 0, wave);
@@ -457,7 +381,7 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(Gemm
     if constexpr (!BKc) opb.template copy<kEdge, kTail>(sB3, 3, 0, wave);
     if constexpr (AK) opa.template copy<kEdge, kTail>(sA1, 1, 0, wave);
     if constexpr (BKc) opb.template copy<kEdge, kTail>(sB1, 1, 0, wave);
-    WAIT_VMCNT((prologue_after<AK, BKc>(CKC, CMN)));  // slice 0 of both operands landed
+    DMA_WAIT_VMCNT((prologue_after<AK, BKc>(CKC, CMN)));  // slice 0 of both operands landed
     barrier();
     frags(std::integral_constant<int, 0>{}, 0, a0, b0);
     using NoMask = std::false_type;
@@ -477,7 +401,7 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(Gemm
         if (rest >= 3) slice(std::integral_constant<int, 2>{}, kt + 2, std::true_type{});
         if (rest >= 4) slice(std::integral_constant<int, 3>{}, kt + 3, std::true_type{});
     }
-    WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
+    DMA_WAIT_VMCNT(0);  // no copy may still target LDS when the workgroup ends
 
     // 32x32 accumulator layout: register r of lane l is row
     // 8*(r/4) + 4*(l/32) + r%4, column l%32 of the MFMA tile.  C is read only
