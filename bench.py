@@ -61,8 +61,9 @@ SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
 # template arguments: input format, then vector / guard flags where the
-# kernel has them, then trans_a, trans_b; the DMA kernel's end with its
-# edge-tile and K-tail flags, false for whole tiles).
+# kernel has them, then trans_a, trans_b; the DMA GEMM kernels' end with
+# their edge-tile and K-tail flags, false for whole tiles; the skinny DMA
+# kernel's are the row-block count, waves and ring stages).
 DOMINANT = {
     "bf16_8192": ("mfma16_dma_kernel<BF16, NN>", "k_mfma_bf16_dma.hip",
                   r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, false, false, false>"),
@@ -76,13 +77,14 @@ DOMINANT = {
                      r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
     "bf16_8192_tn": ("mfma16_dma_kernel<BF16, TN>", "k_mfma_bf16_dma.hip",
                      r"mfma16_dma_kernel<\(dgt::In\)1, 256, true, false, false, false>"),
-    "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 1 row block>", "k_skinny16.hip",
-                                    r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 1>"),
+    "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 1 row block, 8 waves>",
+                                    "k_skinny16_dma.hip",
+                                    r"skinny16_bt_dma_kernel<\(dgt::In\)1, 1, 8, 2>"),
     "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
                                  r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
-    "bf16_decode_64x28672x8192_nt": ("skinny16_bt_kernel<BF16, NT, 4 row blocks>",
-                                     "k_skinny16.hip",
-                                     r"skinny16_bt_kernel<\(dgt::In\)1, true, false, false, 4>"),
+    "bf16_decode_64x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 4 row blocks, 4 waves>",
+                                     "k_skinny16_dma.hip",
+                                     r"skinny16_bt_dma_kernel<\(dgt::In\)1, 4, 4, 4>"),
     "f32_1000_splitk": ("mfma_f32_dma_kernel<NN, 128-tiles, edge> x 8 K slices + reduce (per call)",
                         "k_mfma_f32_dma.hip+k_splitk.hip",
                         r"mfma_f32_dma_kernel<128, false, false, true, (?:false|true)>"),
@@ -146,7 +148,8 @@ def source_digest(fname: str) -> str:
     joined by '+', with the headers they include."""
     h = hashlib.sha256()
     files = fname.split("+")
-    extra = ("skinny_common.hpp",) if any(f.startswith("k_skinny") for f in files) else ()
+    extra = (("skinny_common.hpp",) if any(f.startswith("k_skinny") for f in files) else ()) + \
+        (("dma_common.hpp",) if any(f.endswith("_dma.hip") for f in files) else ())
     for f in (*files, "gemm_common.hpp", *extra):
         with open(os.path.join(ROOT, "dense_gemm_tuning_amd", "csrc", f), "rb") as fh:
             h.update(fh.read())

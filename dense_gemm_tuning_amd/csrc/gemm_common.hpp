@@ -178,6 +178,8 @@ hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* W, int splits, int M, int N, float alpha,
                                 float beta, float* C, int64_t ldc, hipStream_t s);
 template <In T> hipError_t launch_skinny16(const GemmParams& p, hipStream_t s);
+bool skinny16_bt_dma_eligible(const GemmParams& p);
+template <In T> hipError_t launch_skinny16_bt_dma(const GemmParams& p, hipStream_t s);
 
 // Largest M the skinny (decode) path accepts: four blocks of 16 rows.
 constexpr int kSkinnyMaxM = 64;
