@@ -3,10 +3,11 @@
 against the CPU oracle, through the C ABI.
 
 The skinny rung takes that kernel when K is a multiple of 8 and every row
-is 16-byte aligned; it runs eight waves with a two-stage ring per wave for
-M <= 32 and four waves with a four-stage ring above, each wave one K-range
-of a 128-column strip.  Covered: every row-block count (M = 1 .. 64, both
-wave layouts), ragged column strips (N not a multiple of 128, fewer
+is 16-byte aligned; each wave takes one K-range of a 128-column strip: eight
+waves with 128-deep steps and a two-stage ring per wave for M <= 32, eight
+with 64-deep steps and four stages for M <= 48, four with 128-deep steps and
+four stages above.  Covered: every row-block count (M = 1 .. 64, all three
+configurations), ragged column strips (N not a multiple of 128, fewer
 columns than one group), K tails (K not a multiple of the 128-deep step,
 down to K = 8, where most waves have no step), integer inputs bit-exact
 for bf16 and f16; alpha / beta and the bias through the strided batch; row
@@ -46,8 +47,8 @@ def ints(seed, r, c, dtype):
     return gi.draw(seed, r, c, "int", dtype=dtype)
 
 
-# (M, N, K): row blocks 1..4 on both sides of the 8-wave / 4-wave split,
-# ragged strips, K tails and a K shorter than one step.
+# (M, N, K): row blocks 1..4 across the three configurations, ragged
+# strips, K tails (of both step depths) and a K shorter than one step.
 SHAPES = [
     (1, 128, 128), (5, 3, 16), (8, 1000, 1032), (16, 4097, 8), (17, 130, 136),
     (24, 256, 2048), (32, 129, 4104), (33, 777, 520), (40, 128, 1000), (48, 1, 264),
@@ -149,7 +150,7 @@ def test_real_inputs_decode_like(M):
     assert np.all(np.isfinite(C))
 
 
-@pytest.mark.parametrize("M", [16, 64])
+@pytest.mark.parametrize("M", [16, 40, 64])
 def test_deterministic(M):
     N, K = 1000, 4096
     dA = to_dev(gi.draw(6400, M, K, "normal", dtype="bf16"), "bf16")
