@@ -85,7 +85,7 @@ DOMINANT = {
     "bf16_decode_64x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 4 row blocks, 4 waves>",
                                      "k_skinny16_dma.hip",
                                      r"skinny16_bt_dma_kernel<\(dgt::In\)1, 4, 4, 4, 128>"),
-    "f32_1000_splitk": ("mfma_f32_dma_kernel<NN, 128-tiles, edge> x 8 K slices + reduce (per call)",
+    "f32_1000_splitk": ("mfma_f32_dma_kernel<NN, 128-tiles, edge> x 4 K slices + reduce (per call)",
                         "k_mfma_f32_dma.hip+k_splitk.hip",
                         r"mfma_f32_dma_kernel<128, false, false, true, (?:false|true)>"),
     "bf16_splitk_1024x1024x16384": ("mfma16_dma_kernel<BF16, NN, 128-tiles> x 8 K slices + "

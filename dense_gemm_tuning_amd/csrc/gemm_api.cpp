@@ -65,6 +65,7 @@ struct Call {
     int64_t stride_bias;  // floats
     int batch;
     void* stream;
+    int k_last = 0;  // K of the last problem when > 0 (a split-K tail slice)
 };
 
 // [lo, hi) byte range covered by `batch` problems of `span` bytes, `stride`
@@ -132,6 +133,7 @@ int run(const Call& c) {
         return GEMM_ERR_ARG;
     int st = check_shape(c.ta, c.tb, c.M, c.N, c.K, c.lda, c.ldb, c.ldc);
     if (st != GEMM_OK) return st;
+    if (c.k_last < 0 || c.k_last > c.K) return GEMM_ERR_ARG;
     if (c.variant < GEMM_VARIANT_AUTO || c.variant > GEMM_VARIANT_MFMA_T128)
         return GEMM_ERR_VARIANT;
     if (c.M == 0 || c.N == 0 || c.batch == 0) return GEMM_OK;  // empty C: nothing to do
@@ -144,12 +146,19 @@ int run(const Call& c) {
     if (c.batch > 1 && (uint64_t)c.stride_c * 4 < c_span) return GEMM_ERR_OVERLAP;
     const Range rc = batch_range(c.C, c_span, c.stride_c * 4, c.batch);
     if (reads_ab) {
-        const uint64_t a_span =
-            c.ta ? span_bytes(c.K, c.M, c.lda, esz) : span_bytes(c.M, c.K, c.lda, esz);
-        const uint64_t b_span =
-            c.tb ? span_bytes(c.N, c.K, c.ldb, esz) : span_bytes(c.K, c.N, c.ldb, esz);
-        if (overlaps(rc, batch_range(c.A, a_span, c.stride_a * esz, c.batch)) ||
-            overlaps(rc, batch_range(c.B, b_span, c.stride_b * esz, c.batch)))
+        // operand z spans span(K_z) bytes from its start; with a shorter last
+        // problem (k_last) the others and the last are checked apart
+        auto reads = [&](const void* X, int64_t stride, bool rows_k, int rows, int ld) {
+            auto span = [&](int k) {
+                return rows_k ? span_bytes(k, rows, ld, esz) : span_bytes(rows, k, ld, esz);
+            };
+            const int64_t sb = stride * esz;
+            if (c.k_last == 0) return overlaps(rc, batch_range(X, span(c.K), sb, c.batch));
+            const void* last = static_cast<const char*>(X) + (int64_t)(c.batch - 1) * sb;
+            return overlaps(rc, batch_range(X, span(c.K), sb, c.batch - 1)) ||
+                   overlaps(rc, batch_range(last, span(c.k_last), 0, 1));
+        };
+        if (reads(c.A, c.stride_a, c.ta, c.M, c.lda) || reads(c.B, c.stride_b, !c.tb, c.N, c.ldb))
             return GEMM_ERR_OVERLAP;
     }
     if (c.bias && overlaps(rc, batch_range(c.bias, (uint64_t)c.N * 4, c.stride_bias * 4, c.batch)))
@@ -186,6 +195,7 @@ int run(const Call& c) {
         q.B = static_cast<const char*>(p.B) + (int64_t)z0 * p.stride_b;
         q.C = p.C + (int64_t)z0 * p.stride_c;
         if (p.bias) q.bias = p.bias + (int64_t)z0 * p.stride_bias;
+        q.k_last = z0 + q.batch == c.batch ? c.k_last : 0;
         const hipError_t e = dispatch(c.t, variant, q, reads_ab, s);
         if (e == hipErrorInvalidConfiguration) return GEMM_ERR_VARIANT;
         if (e != hipSuccess) return GEMM_ERR_LAUNCH;
@@ -217,9 +227,14 @@ void tile_budget(DType t, int M, int N, int64_t& tiles, int64_t& slots) {
         const int cols = t == DType::F32 ? 64 : 128;
         tiles = (N + cols - 1) / cols;
         slots = 256;
-    } else {  // 128 x 128 tiles, two workgroups per CU (the smaller DMA tile)
+    } else {  // 128 x 128 tiles (the smaller DMA tile)
         tiles = (int64_t)((M + 127) / 128) * ((N + 127) / 128);
-        slots = 512;
+        // 16-bit: two workgroups per CU.  FP32: one; a second on the same CU
+        // only shares its matrix cores (an FP32 MFMA is twice as long as a
+        // 16-bit one per k) while doubling the partials the reduction reads
+        // (1000^3: 4 slices 32 us, 8 slices 37 us; 512^2 x 8192: 16 slices
+        // 42 us, 32 slices 48 us).
+        slots = t == DType::F32 ? 256 : 512;
     }
 }
 
@@ -294,26 +309,16 @@ int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float 
         overlaps(rw, batch_range(B, b_span, 0, 1)))
         return GEMM_ERR_OVERLAP;
 
-    // Phase 1: slice z covers k in [z*kc, z*kc + K_z): a strided batch of the
-    // equal slices, then the shorter last one, each into W + z*M*N.
+    // Phase 1: slice z covers k in [z*kc, z*kc + K_z), into W + z*M*N: one
+    // strided batch, whose last problem takes the shorter last slice.
     const int64_t sa = trans_a ? (int64_t)plan.kc * lda : plan.kc;   // elements
     const int64_t sb = trans_b ? plan.kc : (int64_t)plan.kc * ldb;
     const int last_k = K - (plan.splits - 1) * plan.kc;
-    const int full = last_k == plan.kc ? plan.splits : plan.splits - 1;
     Call c{t, trans_a, trans_b, GEMM_VARIANT_AUTO, M, N, plan.kc, 1.0f, 0.0f, A, lda, sa, B,
-           ldb, sb, W, N, (int64_t)M * N, nullptr, 0, full, stream};
+           ldb, sb, W, N, (int64_t)M * N, nullptr, 0, plan.splits, stream};
+    c.k_last = last_k == plan.kc ? 0 : last_k;
     st = run(c);
     if (st != GEMM_OK) return st;
-    if (full < plan.splits) {
-        Call l = c;
-        l.K = last_k;
-        l.A = static_cast<const char*>(A) + (int64_t)full * sa * esz;
-        l.B = static_cast<const char*>(B) + (int64_t)full * sb * esz;
-        l.C = W + (int64_t)full * M * N;
-        l.batch = 1;
-        st = run(l);
-        if (st != GEMM_OK) return st;
-    }
     // Phase 2: C <- alpha * sum_z W_z + beta * C, in slice order.
     const hipError_t e = dgt::launch_splitk_reduce(W, plan.splits, M, N, alpha, beta, C, ldc,
                                                    static_cast<hipStream_t>(stream));

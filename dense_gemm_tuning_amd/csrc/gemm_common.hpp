@@ -36,10 +36,14 @@ struct GemmParams {
     int64_t stride_a, stride_b, stride_c, stride_bias;
     const float* bias;
     int batch;
+    // K of the launch's last problem when > 0 (split-K's shorter last
+    // slice); otherwise every problem has K.
+    int k_last = 0;
 };
 
 // Point p at problem z of a strided batch.
 __device__ __forceinline__ void select_problem(GemmParams& p, int64_t z) {
+    if (p.k_last > 0 && z == p.batch - 1) p.K = p.k_last;
     p.A = static_cast<const char*>(p.A) + z * p.stride_a;
     p.B = static_cast<const char*>(p.B) + z * p.stride_b;
     p.C += z * p.stride_c;
@@ -200,6 +204,11 @@ inline bool rows_16b_aligned(const void* base, int64_t ld, int elem_size) {
 
 // The same for A and B of every problem of a batch (batch strides are in
 // bytes and must keep the alignment too).
+// True when every problem's K (the last one's too) is a multiple of q.
+inline bool k_multiple(const GemmParams& p, int q) {
+    return p.K % q == 0 && (p.k_last <= 0 || p.k_last % q == 0);
+}
+
 inline bool operands_16b_aligned(const GemmParams& p, int elem_size) {
     return rows_16b_aligned(p.A, p.lda, elem_size) && rows_16b_aligned(p.B, p.ldb, elem_size) &&
            p.stride_a % 16 == 0 && p.stride_b % 16 == 0;

@@ -511,7 +511,7 @@ hipError_t launch_tiles(const GemmParams& p, hipStream_t s) {
     const int64_t blocks = (int64_t)tiles_m * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool edge = p.M % R != 0 || p.N % R != 0;
-    const bool tail = p.K % (BK * NSTAGE) != 0;
+    const bool tail = !k_multiple(p, BK * NSTAGE);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         // linear order only for one problem with both operands k-contiguous

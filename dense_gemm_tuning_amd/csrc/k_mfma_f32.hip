@@ -202,7 +202,7 @@ hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = operands_16b_aligned(p, 4);
-    const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && p.K % BK == 0;
+    const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && k_multiple(p, BK);
     const dim3 grid((unsigned)blocks, p.batch), block(NT);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;

@@ -303,7 +303,7 @@ hipError_t launch_rb(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + COLS - 1) / COLS;
     const bool vec = operands_16b_aligned(p, 2);
     const int kstep = p.tb ? BT_KSTEP : KSTEP;
-    const bool full = vec && p.N % COLS == 0 && p.K % kstep == 0;
+    const bool full = vec && p.N % COLS == 0 && k_multiple(p, kstep);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         const dim3 grid(blocks, p.batch), block(NTH);

@@ -331,7 +331,7 @@ hipError_t launch_rb(const GemmParams& p, hipStream_t s) {
 // rows, and every offset within a descriptor below 2^31 (at most 64 rows of
 // A or 32 of B per descriptor).
 bool skinny16_bt_dma_eligible(const GemmParams& p) {
-    if (p.ta || !p.tb || p.M < 1 || p.M > kSkinnyMaxM || p.N < 1 || p.K < 8 || p.K % 8 != 0 ||
+    if (p.ta || !p.tb || p.M < 1 || p.M > kSkinnyMaxM || p.N < 1 || p.K < 8 || !k_multiple(p, 8) ||
         !operands_16b_aligned(p, 2) || p.lda < p.K || p.ldb < p.K)
         return false;
     const int64_t lim = int64_t(1) << 31;

@@ -208,7 +208,9 @@ int gemm_strided_batched(int dtype, int trans_a, int trans_b, int variant,
  * after the launch code), and this is the case where the whole grid is too
  * small: the reduction dimension supplies the missing parallelism.
  * `splits` = 0 picks the number of slices that fills the GPU's workgroup
- * slots (each slice at least 128 deep); a positive value is a request (at
+ * slots (128 x 128 tiles: one per CU for fp32, two for 16-bit inputs; a
+ * skinny column strip per CU for M <= 64; each slice at least 128 deep)
+ * and runs them as one launch; a positive value is a request (at
  * most 64; rounding of the slice length may give fewer).  With one slice
  * the call is gemm_ex and needs no workspace.  The workspace (device
  * memory, 16-byte aligned, at least gemm_splitk_workspace_size bytes) must

@@ -227,11 +227,14 @@ def test_strided_batched_argument_checks(lib):
 def test_splitk_planning(lib):
     sl, ws = dgt.gemm_splitk_slices, dgt.gemm_splitk_workspace_size
     F32, BF16 = dgt.DTYPE_F32, dgt.DTYPE_BF16
-    # 1000^3 fp32: 64 tiles of 128 x 128 for 512 workgroup slots -> 8 slices
-    # of 128 (the last 104 deep)
-    assert sl(F32, 1000, 1000, 1000, 0) == 8
-    assert ws(F32, 1000, 1000, 1000, 0) == 8 * 1000 * 1000 * 4
-    # 1024 x 1024 bf16 with K = 16384: 64 tiles of 128 x 128 -> 8 slices
+    # 1000^3 fp32: 64 tiles of 128 x 128 for 256 workgroup slots (one per CU)
+    # -> 4 slices of 256 (the last 232 deep)
+    assert sl(F32, 1000, 1000, 1000, 0) == 4
+    assert ws(F32, 1000, 1000, 1000, 0) == 4 * 1000 * 1000 * 4
+    # 512 x 512 fp32 with K = 8192: 16 tiles -> 16 slices of 512
+    assert sl(F32, 512, 512, 8192, 0) == 16
+    # 1024 x 1024 bf16 with K = 16384: 64 tiles of 128 x 128 for 512 slots
+    # (two per CU) -> 8 slices
     assert sl(BF16, 1024, 1024, 16384, 0) == 8
     # 8192 x 1024 bf16: 512 tiles of 128 x 128 fill the slots unsplit
     assert sl(BF16, 8192, 1024, 8192, 0) == 1

@@ -5,8 +5,8 @@ The K range is cut into slices whose fp32 partial products go to a
 caller-provided workspace and are summed in a fixed order; the result is
 the same operation as gemm_ex.  Covered: fp32 / bf16 / fp16, stored layouts
 NN / NT / TN, automatic and requested slice counts, K not a multiple of the
-slice length, slices that take the skinny path (M <= 64) and the whole-tile
-DMA kernel, integer inputs bit-exact, real inputs within the gates, beta on
+slice length (the shorter last slice runs in the same launch), slices that
+take the skinny path (M <= 64) and the whole-tile DMA kernel, integer inputs bit-exact, real inputs within the gates, beta on
 and off, a guard band after the workspace and around C, and run-to-run
 determinism.
 """
@@ -26,12 +26,14 @@ pytestmark = pytest.mark.gpu
 
 LAYOUTS = {"nn": (False, False), "nt": (False, True), "tn": (True, False)}
 CODE = {"f32": 0, "bf16": 1, "f16": 2}
-# (M, N, K, splits): automatic (the 1000^3 shape gets 8 slices), requests,
-# K not a multiple of the slice, slices on the skinny path and on whole tiles,
-# and one GPU's share of the skinny shape under an 8-way column split
-# (8 x 3584 x 8192, 8 automatic slices)
+# (M, N, K, splits): automatic (the 1000^3 shape gets 4 fp32 or 8 16-bit
+# slices), requests, K not a multiple of the slice (the shorter last slice is
+# the last problem of the same launch), slices on the skinny paths (the one
+# for B stored N x K included, K a multiple of 8) and on whole tiles, and one
+# GPU's share of the skinny shape under an 8-way column split (8 x 3584 x
+# 8192, 8 automatic slices)
 CASES = [(1000, 1000, 1000, 0), (300, 260, 1000, 3), (64, 64, 4096, 4), (1, 1, 300, 2),
-         (256, 256, 2048, 0), (130, 70, 700, 5), (8, 3584, 8192, 0)]
+         (256, 256, 2048, 0), (130, 70, 700, 5), (8, 3584, 8192, 0), (40, 500, 1000, 3)]
 
 
 @pytest.fixture(scope="module", autouse=True)
