@@ -63,7 +63,8 @@ SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
 # template arguments: input format, then vector / guard flags where the
 # kernel has them, then trans_a, trans_b; the DMA GEMM kernels' end with
 # their edge-tile and K-tail flags, false for whole tiles; the skinny DMA
-# kernel's are the row-block count, waves, ring stages and step depth).
+# kernel's are the row-block count, waves, ring stages, step depth and
+# whether A has one register buffer).
 DOMINANT = {
     "bf16_8192": ("mfma16_dma_kernel<BF16, NN>", "k_mfma_bf16_dma.hip",
                   r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, false, false, false>"),
@@ -79,12 +80,12 @@ DOMINANT = {
                      r"mfma16_dma_kernel<\(dgt::In\)1, 256, true, false, false, false>"),
     "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 1 row block, 8 waves>",
                                     "k_skinny16_dma.hip",
-                                    r"skinny16_bt_dma_kernel<\(dgt::In\)1, 1, 8, 2, 128>"),
+                                    r"skinny16_bt_dma_kernel<\(dgt::In\)1, 1, 8, 2, 128, false>"),
     "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
                                  r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
-    "bf16_decode_64x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 4 row blocks, 4 waves>",
+    "bf16_decode_64x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 4 row blocks, 8 waves>",
                                      "k_skinny16_dma.hip",
-                                     r"skinny16_bt_dma_kernel<\(dgt::In\)1, 4, 4, 4, 128>"),
+                                     r"skinny16_bt_dma_kernel<\(dgt::In\)1, 4, 8, 4, 64, true>"),
     "f32_1000_splitk": ("mfma_f32_dma_kernel<NN, 128-tiles, edge> x 4 K slices + reduce (per call)",
                         "k_mfma_f32_dma.hip+k_splitk.hip",
                         r"mfma_f32_dma_kernel<128, false, false, true, (?:false|true)>"),

@@ -16,11 +16,13 @@
 // register-staged waves with one or two).  So the configuration per row
 // count is the one with the most waves that fits without spilling (a
 // kernel that spills is also held to fewer concurrent waves by its scratch):
-//   M <= 32: eight waves, 128-deep steps, two stages (one group in flight);
-//   M <= 48: eight waves, 64-deep steps (4-KiB groups, half the A
-//            registers), four stages;
-//   M <= 64: four waves, 128-deep steps, four stages (its 128 accumulator
-//            registers leave no room for eight).
+//   M <= 32: eight waves, 128-deep steps, two stages (one group in flight),
+//            A for the next step loaded a step ahead into a second buffer;
+//   M <= 64: eight waves, 64-deep steps (4-KiB groups, half the A
+//            registers), four stages, and one A buffer reloaded after each
+//            step's last MFMAs: at four row blocks the 128 accumulator
+//            registers leave no room for a second (with it the kernel
+//            spills), and one buffer is faster at three as well.
 // Splitting a strip's columns over two waves instead (halving the
 // accumulators) was slower: both waves then read every A slice, and the
 // extra A requests cost more than the waves gain.
@@ -83,8 +85,9 @@ __device__ __forceinline__ void copy_b(const void* base, uint32_t range, uint8_t
 
 // NW waves (one K-range each), a ring of NS stages per wave (NS divides the
 // four groups of a step, so group cp of any step uses stage cp % NS), steps
-// SK deep.
-template <In T, int RB, int NW, int NS, int SK>
+// SK deep; kSingleA: one register buffer of A operands, reloaded after each
+// step's last MFMAs (else two, the next step's loaded one step ahead).
+template <In T, int RB, int NW, int NS, int SK, bool kSingleA>
 __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams p) {
     using G = Geo<SK>;
     static_assert(NS == 2 || NS == 4, "a step's four groups map onto the ring");
@@ -209,16 +212,23 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
     };
 
     // Group cp of step s.  Before reading it the wave copies the group D
-    // places ahead (group cp + D of this step, or of the next), and at cp = 0
-    // of a step that is not its last it loads A of the next step right after
-    // that copy.  The wait then lets through everything issued after the copy
-    // of group cp: the D later groups' copies (INSTR instructions each), plus
-    // the RB x U A loads when they came after it, which is when that copy was
-    // issued in this step's cp = 0 phase or earlier (cp <= D).  A loads of
-    // earlier steps always precede it.  In the wave's last step nothing is
-    // loaded past its group 3, so only min(D, 3 - cp) copies follow.  The
-    // prologue loads A of the first step and then copies its groups 0 .. D-1,
-    // which gives the first step the same counts.
+    // places ahead (group cp + D of this step, or of the next).  The wait then
+    // lets through everything issued after the copy of group cp: the D later
+    // groups' copies (INSTR instructions each; in the wave's last step nothing
+    // is copied past its group 3, so only min(D, 3 - cp)), plus the RB x U A
+    // loads when they came after it.
+    //  * Two A buffers: at cp = 0 of a step that is not its last, A of the
+    //    next step is loaded right after that phase's copy; it follows the
+    //    copy of group cp when that copy was issued in this cp = 0 phase or
+    //    earlier (cp <= D).  The prologue loads A of the first step and then
+    //    copies its groups 0 .. D-1, which gives the first step the same
+    //    counts, and no A load follows any copy of the wave's last step.
+    //  * One A buffer: A of step s is loaded at the end of the previous step's
+    //    cp = 3 phase, after that phase's copy, so it follows the copy of
+    //    group cp of step s when that copy was issued in the previous step's
+    //    cp = 3 phase or earlier (cp <= D - 1), the last step included.  The
+    //    prologue copies groups 0 .. D-1 and then loads A of the first step,
+    //    which again gives the same counts.
     using AOps = u32x4[RB][G::U];
     auto phase = [&](auto cpc, auto lastc, int s, const AOps& a, AOps& an) {
         constexpr int cp = decltype(cpc)::value;
@@ -229,17 +239,22 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
             issue(std::integral_constant<int, ahead % 4>{}, s + ahead / 4);
             fence();
         }
-        if constexpr (!kLast && cp == 0) {
+        if constexpr (!kSingleA && !kLast && cp == 0) {
             load_a(s + 1, an);
             fence();
         }
-        constexpr int after = kLast ? G::INSTR * (D < 3 - cp ? D : 3 - cp)
-                                    : G::INSTR * D + (cp <= D ? RB * G::U : 0);
+        constexpr int copies = G::INSTR * (kLast ? (D < 3 - cp ? D : 3 - cp) : D);
+        constexpr bool a_after = kSingleA ? cp <= D - 1 : (!kLast && cp <= D);
+        constexpr int after = copies + (a_after ? RB * G::U : 0);
         static_assert(after <= 63, "vmcnt holds 6 bits");
         DMA_WAIT_VMCNT(after);
         fence();
         compute(cpc, a);
         fence();
+        if constexpr (kSingleA && !kLast && cp == 3) {  // a and an are one buffer
+            load_a(s + 1, an);
+            fence();
+        }
     };
     auto step = [&](auto lastc, int s, const AOps& a, AOps& an) {
         phase(std::integral_constant<int, 0>{}, lastc, s, a, an);
@@ -248,27 +263,40 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
         phase(std::integral_constant<int, 3>{}, lastc, s, a, an);
     };
 
-    if (s0 < s1) {
-        AOps a0, a1;
-        load_a(s0, a0);
-        fence();
+    using Full = std::false_type;
+    using Last = std::true_type;
+    auto prologue_copies = [&] {
         issue(std::integral_constant<int, 0>{}, s0);
         if constexpr (D > 1) issue(std::integral_constant<int, 1>{}, s0);
         if constexpr (D > 2) issue(std::integral_constant<int, 2>{}, s0);
         fence();
-        // Unrolled by two so that the A buffers alternate without copies.
-        using Full = std::false_type;
-        using Last = std::true_type;
-        int s = s0;
-        for (; s + 2 < s1; s += 2) {
-            step(Full{}, s, a0, a1);
-            step(Full{}, s + 1, a1, a0);
-        }
-        if (s + 1 < s1) {
-            step(Full{}, s, a0, a1);
-            step(Last{}, s + 1, a1, a0);
+    };
+    if (s0 < s1) {
+        if constexpr (kSingleA) {
+            AOps a0;
+            prologue_copies();
+            load_a(s0, a0);
+            fence();
+            int s = s0;
+            for (; s + 1 < s1; ++s) step(Full{}, s, a0, a0);
+            step(Last{}, s, a0, a0);
         } else {
-            step(Last{}, s, a0, a1);
+            AOps a0, a1;
+            load_a(s0, a0);
+            fence();
+            prologue_copies();
+            // Unrolled by two so that the A buffers alternate without copies.
+            int s = s0;
+            for (; s + 2 < s1; s += 2) {
+                step(Full{}, s, a0, a1);
+                step(Full{}, s + 1, a1, a0);
+            }
+            if (s + 1 < s1) {
+                step(Full{}, s, a0, a1);
+                step(Last{}, s + 1, a1, a0);
+            } else {
+                step(Last{}, s, a0, a1);
+            }
         }
     }
 
@@ -310,18 +338,18 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
         }
 }
 
-template <In T, int RB, int NW, int NS, int SK>
+template <In T, int RB, int NW, int NS, int SK, bool kSingleA>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
     const dim3 grid((p.N + COLS - 1) / COLS, p.batch), block(NW * 64);
-    hipLaunchKernelGGL((skinny16_bt_dma_kernel<T, RB, NW, NS, SK>), grid, block, 0, s, p);
+    hipLaunchKernelGGL((skinny16_bt_dma_kernel<T, RB, NW, NS, SK, kSingleA>), grid, block, 0, s,
+                       p);
     return hipGetLastError();
 }
 
 template <In T, int RB>
 hipError_t launch_rb(const GemmParams& p, hipStream_t s) {
-    if constexpr (RB <= 2) return launch_cfg<T, RB, 8, 2, 128>(p, s);
-    else if constexpr (RB == 3) return launch_cfg<T, RB, 8, 4, 64>(p, s);
-    else return launch_cfg<T, RB, 4, 4, 128>(p, s);
+    if constexpr (RB <= 2) return launch_cfg<T, RB, 8, 2, 128, false>(p, s);
+    else return launch_cfg<T, RB, 8, 4, 64, true>(p, s);
 }
 
 }  // namespace

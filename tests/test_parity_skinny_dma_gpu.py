@@ -3,11 +3,11 @@
 against the CPU oracle, through the C ABI.
 
 The skinny rung takes that kernel when K is a multiple of 8 and every row
-is 16-byte aligned; each wave takes one K-range of a 128-column strip: eight
-waves with 128-deep steps and a two-stage ring per wave for M <= 32, eight
-with 64-deep steps and four stages for M <= 48, four with 128-deep steps and
-four stages above.  Covered: every row-block count (M = 1 .. 64, all three
-configurations), ragged column strips (N not a multiple of 128, fewer
+is 16-byte aligned; each wave takes one K-range of a 128-column strip, eight
+waves per workgroup: 128-deep steps, a two-stage ring per wave and two A
+buffers for M <= 32; 64-deep steps, four stages and one A buffer above.
+Covered: every row-block count (M = 1 .. 64, both configurations), ragged
+column strips (N not a multiple of 128, fewer
 columns than one group), K tails (K not a multiple of the 128-deep step,
 down to K = 8, where most waves have no step), integer inputs bit-exact
 for bf16 and f16; alpha / beta and the bias through the strided batch; row
@@ -47,7 +47,7 @@ def ints(seed, r, c, dtype):
     return gi.draw(seed, r, c, "int", dtype=dtype)
 
 
-# (M, N, K): row blocks 1..4 across the three configurations, ragged
+# (M, N, K): row blocks 1..4 across both configurations, ragged
 # strips, K tails (of both step depths) and a K shorter than one step.
 SHAPES = [
     (1, 128, 128), (5, 3, 16), (8, 1000, 1032), (16, 4097, 8), (17, 130, 136),
