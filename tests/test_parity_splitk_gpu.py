@@ -7,7 +7,8 @@ the same operation as gemm_ex.  Covered: fp32 / bf16 / fp16, stored layouts
 NN / NT / TN, automatic and requested slice counts, K not a multiple of the
 slice length (the shorter last slice runs in the same launch), slices that
 take the skinny path (M <= 64) and the whole-tile DMA kernel, integer inputs bit-exact, real inputs within the gates, beta on
-and off, a guard band after the workspace and around C, and run-to-run
+and off, a guard band after the workspace and around C, a workspace that
+starts right after A when the last slice is shorter, and run-to-run
 determinism.
 """
 
@@ -138,3 +139,34 @@ def test_splitk_workspace_errors_on_gpu():
     # one slice needs no workspace at all
     assert dgt.gemm_split(A, B, C, splits=1) == 0
     torch.cuda.synchronize()
+
+
+@pytest.mark.parametrize("ta", [False, True])
+def test_splitk_workspace_right_after_a(ta):
+    """The workspace starts at the byte after A's last element while the last
+    slice is shorter than the others: the overlap check must measure that
+    slice's operand span with its own K (not the full slice length), so the
+    call runs, and the result is exact."""
+    M, N, K, splits = 100, 64, 1000, 3      # slices of 384, 384, 232
+    code = CODE["f32"]
+    assert dgt.gemm_splitk_slices(code, M, N, K, splits) == 3
+    need = dgt.gemm_splitk_workspace_size(code, M, N, K, splits)
+    sa = (K, M) if ta else (M, K)
+    A = gi.draw(1600, *sa, "int")
+    B = gi.draw(1601, K, N, "int")
+    n_a = sa[0] * sa[1]                       # A's elements, packed (lda = its row length)
+    buf = torch.zeros((n_a + need // 4 + 64,), device="cuda")
+    dA = buf[:n_a].view(*sa)
+    dA.copy_(torch.from_numpy(A).cuda())
+    ws_ptr = buf.data_ptr() + n_a * 4         # 16-byte aligned: n_a * 4 = 400000
+    dB = to_dev(B, "f32")
+    dC = torch.full((M, N), float("nan"), device="cuda")
+    say(f"split-K workspace after A, ta={ta}")
+    st = dgt.gemm_splitk(code, ta, False, M, N, K, 1.0, dA.data_ptr(), sa[1], dB.data_ptr(), N,
+                         0.0, dC.data_ptr(), N, splits, ws_ptr, need,
+                         torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    assert st == 0, dgt.gemm_status_string(st)
+    R = oracle.round_f32(oracle.gemm(A, B, None, 1.0, 0.0, "f32", trans_a=ta))
+    assert_bit_exact(dC.cpu().numpy(), R, f"split-K, workspace after A, ta={ta}")
+    assert np.array_equal(dA.cpu().numpy(), A), "A was written"
