@@ -3,29 +3,42 @@
 
 One step = one GEMM call C = alpha*A*B + beta*C on the headline workload
 (BF16 inputs, FP32 accumulate/output, M = N = K = 8192), inputs already
-resident in HBM.  W untimed warm-up calls (the pages ask for warm-up before
-quoting numbers: dilfish.github.io 5.7; here they also let the power-managed
-clock settle, which takes some 40-80 calls of the 8192^3 GEMM after the GPU
-has idled while the next inputs were generated), then K timed calls
-bracketed by device synchronisation, timed with HIP events on the stream the
-kernels run on.  TFLOP/s = 2MNK / time (chongfengling.github.io section 1 counts K
-multiplies and K adds per output; 2*2048^3 = 17.18e9 in its section 2.5).
+resident in HBM.  Before the W untimed warm-up calls the workload runs
+untimed for --settle-ms (default 300 ms): after the GPU has idled (while the
+host generates the next inputs) its power-managed clock overshoots and then
+settles over some 40-80 calls of the 8192^3 GEMM, and the pages ask for
+warm-up before numbers are quoted because the first runs include that ramp
+(dilfish.github.io 5.7).  Then K timed calls bracketed by device
+synchronisation, timed with HIP events on the stream the kernels run on.
+TFLOP/s = 2MNK / time (chongfengling.github.io section 1 counts K multiplies
+and K adds per output; 2*2048^3 = 17.18e9 in its section 2.5).
 
-The same JSON line carries, under "also", the FP32 4096^3 case (against the
-fp32 matrix-core peak), the FP16-input 8192^3 case (against the fp16 peak,
-equal to bf16's), the skinny decode-shaped case M=8, N=28672,
+The same JSON line carries, under "also", the small FP32 cases (256^3, and
+the ragged 1000^3 with alpha = 1.5, beta = 0.5), the FP32 4096^3 case
+(against the fp32 matrix-core peak), the FP16-input 8192^3 case (against the
+fp16 peak, equal to bf16's), the skinny decode-shaped case M=8, N=28672,
 K=8192 (against HBM bandwidth: its time is the time to stream B once,
 dilfish.github.io 5.1 GEMV row), the BF16 square and skinny cases with a
 linear layer's operand storage (B stored N x K, A stored K x M), that
-layer's forward with its bias fused, and a strided batch of 16 x 2048^3,
-plus:
-  * "roofline": the dominant kernel's algorithmic FLOP per launch over its
-    measured launch time, against the published MI355X peak;
+layer's forward with its bias fused, a strided batch of 16 x 2048^3, and the
+split-K and one-GPU-share shapes, plus:
+  * "roofline": the dominant kernel's algorithmic FLOP (or bytes) per launch
+    over its measured launch time, against the published MI355X peak, and
+    the same against the peak scaled to the engine clock measured during
+    the timed calls ("clock");
+  * "clock": the graphics clock and socket power the GPU's own telemetry
+    reports before, during and after the timed calls (amdsmi gpu metrics);
+  * "pcie": one host-to-device copy of A and B and one device-to-host copy
+    of C, timed apart from the metric (dilfish.github.io 5.7: transfers are
+    part of what a caller pays, but not of the kernel's time);
   * "cpu_baseline": the CPU oracle timed on a bounded row sample of the same
-    workload on this host's cores (a reported baseline, not a target).
+    workload on this host's cores (a reported baseline, not a target), and
+    on the two small FP32 cases with one thread and with all of them.
 
 Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only bf16_8192 --no-cpu   (one workload, for profiling)
+       python bench.py --ladder                    (every rung at FP32 4096^3, BF16 8192^3)
+       python bench.py --counter-check             (the naive rung once at FP32 2048^3)
        python bench.py --copy-calibration          (copy kernel of known size)
 """
 
@@ -52,8 +65,8 @@ PEAK_TFLOPS = {"bf16": 2500.0, "f16": 2500.0, "f32": 157.3}
 HBM_PEAK_GBS = 8000.0
 
 PRIMARY = "bf16_8192"
-SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
-             "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
+SECONDARY = ["f32_256", "f32_1000_ragged", "f32_4096", "f16_8192", "bf16_skinny_8x28672x8192",
+             "bf16_8192_nt", "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
              "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt", "f32_1000_splitk",
              "bf16_splitk_1024x1024x16384", "bf16_skinny_shard_8x3584x8192",
              "bf16_shard_8192x1024x8192"]
@@ -66,6 +79,10 @@ SECONDARY = ["f32_4096", "f16_8192", "bf16_skinny_8x28672x8192", "bf16_8192_nt",
 # kernel's are the row-block count, waves, ring stages, step depth and
 # whether A has one register buffer).
 DOMINANT = {
+    "f32_256": ("mfma_f32_dma_kernel<NN, 128-tiles>", "k_mfma_f32_dma.hip",
+                r"mfma_f32_dma_kernel<128, false, false, false, false>"),
+    "f32_1000_ragged": ("mfma_f32_dma_kernel<NN, 128-tiles, edge, K tail>", "k_mfma_f32_dma.hip",
+                        r"mfma_f32_dma_kernel<128, false, false, true, true>"),
     "bf16_8192": ("mfma16_dma_kernel<BF16, NN>", "k_mfma_bf16_dma.hip",
                   r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, false, false, false>"),
     "f16_8192": ("mfma16_dma_kernel<F16, NN>", "k_mfma_bf16_dma.hip",
@@ -180,60 +197,163 @@ def to_dev(torch, x, dtype):
     return torch.from_numpy(np.ascontiguousarray(x)).cuda()
 
 
-def time_workload(torch, dgt, w, steps, warmup, copies=1):
-    """Average and spread of one GEMM call's duration (ms) on the current stream."""
-    import gemm_inputs as gi
-    t0 = time.perf_counter()
-    A, B, C0 = gi.make_inputs(w)
-    log(f"[{w.name}] inputs generated in {time.perf_counter() - t0:.1f} s")
-    bias = gi.make_bias(w)
-    dA = [to_dev(torch, A, w.dtype) for _ in range(copies)]
-    dB = [to_dev(torch, B, w.dtype) for _ in range(copies)]
-    dC = (torch.from_numpy(C0).cuda() if C0 is not None
-          else torch.zeros((w.batch, w.M, w.N), dtype=torch.float32, device="cuda"))
-    dbias = torch.from_numpy(bias).cuda() if bias is not None else None
-    stream = torch.cuda.current_stream()
-    sptr = stream.cuda_stream
-    lda, ldb = w.a_shape[1], w.b_shape[1]  # packed stored rows
+# ------------------------------------------------------------ GPU telemetry
+
+class Telemetry:
+    """The graphics clock and socket power the GPU's firmware reports (amdsmi
+    gpu metrics), read from a host thread while kernels run, so the reading
+    costs the GPU nothing.  ``current_gfxclks`` holds one clock per XCD; their
+    mean is the engine clock.  Disabled (every reading None) when amdsmi is
+    missing or cannot open the device torch uses."""
+
+    def __init__(self, torch):
+        self.handle, self.error = None, None
+        try:
+            import amdsmi
+            amdsmi.amdsmi_init()
+            self.smi = amdsmi
+            handles = amdsmi.amdsmi_get_processor_handles()
+            props = torch.cuda.get_device_properties(0)
+            want = None
+            if hasattr(props, "pci_bus_id"):
+                want = (getattr(props, "pci_domain_id", 0), props.pci_bus_id,
+                        getattr(props, "pci_device_id", 0))
+            for h in handles:
+                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
+                dom, bus, rest = bdf.split(":")
+                if want is None or (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+                    self.handle = h
+                    break
+            if self.handle is None:
+                self.error = f"no amdsmi device matches torch's device 0 ({want})"
+        except Exception as e:  # telemetry is optional; the metric does not depend on it
+            self.error = f"{type(e).__name__}: {e}"
+
+    def read(self):
+        """(mean graphics clock over the XCDs in MHz, socket power in W,
+        energy counter in J) or Nones."""
+        if self.handle is None:
+            return None, None, None
+        try:
+            m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
+        except Exception:
+            return None, None, None
+        clk = m.get("current_gfxclks")
+        vals = [c for c in clk if isinstance(c, (int, float)) and c > 0] if isinstance(clk, list) else []
+        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+            vals = [m["current_gfxclk"]]
+        mhz = sum(vals) / len(vals) if vals else None
+        pw = m.get("current_socket_power")
+        if not isinstance(pw, (int, float)):
+            pw = m.get("average_socket_power")
+        pw = pw if isinstance(pw, (int, float)) else None
+        en = m.get("energy_accumulator")
+        # the accumulator counts in units of 15.259 uJ (2^-16 J)
+        en = en * 15.259e-6 if isinstance(en, (int, float)) else None
+        return mhz, pw, en
+
+    def sampler(self):
+        return _Sampler(self)
+
+
+class _Sampler:
+    """Reads the telemetry every ~2 ms on a host thread between start() and
+    stop(); summary() gives the mean clock and power of those readings and
+    the mean power from the energy counter over the whole interval."""
+
+    def __init__(self, tel):
+        import threading
+        self.tel, self.samples, self._stop = tel, [], threading.Event()
+        self._th = threading.Thread(target=self._run, daemon=True)
+
+    def _run(self):
+        while not self._stop.is_set():
+            self.samples.append(self.tel.read())
+            self._stop.wait(0.002)
+
+    def start(self):
+        self.e0, self.t0 = self.tel.read()[2], time.perf_counter()
+        self._th.start()
+        return self
+
+    def stop(self):
+        self._stop.set()
+        self._th.join()
+        self.e1, self.t1 = self.tel.read()[2], time.perf_counter()
+        return self
+
+    def summary(self):
+        clk = [s[0] for s in self.samples if s[0] is not None]
+        pw = [s[1] for s in self.samples if s[1] is not None]
+        out = {"gfxclk_mhz": round(sum(clk) / len(clk), 1) if clk else None,
+               "gfxclk_mhz_min": min(clk) if clk else None,
+               "gfxclk_mhz_max": max(clk) if clk else None,
+               "socket_power_w": round(sum(pw) / len(pw), 1) if pw else None,
+               "samples": len(clk)}
+        if self.e0 is not None and self.e1 is not None and self.t1 > self.t0 and self.e1 > self.e0:
+            out["energy_power_w"] = round((self.e1 - self.e0) / (self.t1 - self.t0), 1)
+        return out
+
+
+# ------------------------------------------------------------ timing
+
+def make_fn(torch, dgt, w, dbias):
+    """The library call the bench times for workload w, as
+    fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream) -> status,
+    and the workspace it holds (allocated here, outside any timing)."""
     code = {"f32": dgt.DTYPE_F32, "bf16": dgt.DTYPE_BF16, "f16": dgt.DTYPE_F16}[w.dtype]
     if w.splits != 1:
         need = dgt.gemm_splitk_workspace_size(code, w.M, w.N, w.K, w.splits)
-        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")  # outside the timing
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
 
         def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s):
             return dgt.gemm_splitk(code, w.trans_a, w.trans_b, M, N, K, alpha, A, lda, B, ldb,
                                    beta, C, ldc, w.splits, ws.data_ptr(), need, s)
-    elif w.batch > 1 or bias is not None:
+        return fn, ws
+    if w.batch > 1 or dbias is not None:
         def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s):
             return dgt.gemm_strided_batched(
                 code, w.trans_a, w.trans_b, dgt.VARIANT_AUTO, M, N, K, alpha,
                 A, lda, w.a_shape[0] * lda, B, ldb, w.b_shape[0] * ldb, beta, C, ldc, M * N,
                 dbias.data_ptr() if dbias is not None else 0, N, w.batch, s)
-    elif w.trans_a or w.trans_b:
+        return fn, None
+    if w.trans_a or w.trans_b:
         def fn(*args):
             return dgt.gemm_ex(code, w.trans_a, w.trans_b, dgt.VARIANT_AUTO, *args)
-    else:
-        fn = {"f32": dgt.gemm_f32, "bf16": dgt.gemm_bf16, "f16": dgt.gemm_f16}[w.dtype]
+        return fn, None
+    return {"f32": dgt.gemm_f32, "bf16": dgt.gemm_bf16, "f16": dgt.gemm_f16}[w.dtype], None
 
-    def launch(i):
-        st = fn(w.M, w.N, w.K, w.alpha, dA[i % copies].data_ptr(), lda,
-                dB[i % copies].data_ptr(), ldb, w.beta, dC.data_ptr(), w.N, sptr)
-        if st != 0:
-            raise RuntimeError(dgt.gemm_status_string(st))
 
+def time_calls(torch, launch, steps, warmup, settle_ms, tel=None):
+    """Settle, warm up, then time `steps` back-to-back calls of launch(i)
+    between one pair of events on the current stream; a second pass with an
+    event after every call gives the per-call spread."""
+    stream = torch.cuda.current_stream()
+    n_settle = 0
+    if settle_ms > 0:
+        t_end = time.perf_counter() + settle_ms * 1e-3
+        while time.perf_counter() < t_end:
+            launch(n_settle)
+            n_settle += 1
+            if n_settle % 8 == 0:
+                torch.cuda.synchronize()  # keep the queue short so the wall clock means GPU time
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    # timed region: K back-to-back launches between one pair of events
+    before = tel.read() if tel else (None, None, None)
+    smp = tel.sampler().start() if tel else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
         launch(i)
     end.record(stream)
     torch.cuda.synchronize()
+    if smp:
+        smp.stop()
+    after = tel.read() if tel else (None, None, None)
     total = start.elapsed_time(end)
-    # spread: a second pass with an event after every launch (the markers add
-    # a little time of their own, so this pass does not feed the average)
+    # spread: the markers add a little time of their own, so this pass does
+    # not feed the average
     ev = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
     ev[0].record(stream)
     for i in range(steps):
@@ -242,10 +362,78 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1):
     torch.cuda.synchronize()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
     res = {"ms_avg": total / steps, "ms_median": per[len(per) // 2],
-           "ms_min": per[0], "ms_max": per[-1]}
-    del dA, dB, dC
+           "ms_min": per[0], "ms_max": per[-1], "settle_calls": n_settle}
+    if tel:
+        clock = smp.summary()
+        clock["before_mhz"] = before[0]
+        clock["after_mhz"] = after[0]
+        res["clock"] = clock
+    return res
+
+
+def time_workload(torch, dgt, w, steps, warmup, copies=1, settle_ms=300.0, tel=None,
+                  pcie=False):
+    """Average and spread of one GEMM call's duration (ms) on the current stream."""
+    import gemm_inputs as gi
+    t0 = time.perf_counter()
+    A, B, C0 = gi.make_inputs(w)
+    log(f"[{w.name}] inputs generated in {time.perf_counter() - t0:.1f} s")
+    bias = gi.make_bias(w)
+    pcie_res = measure_pcie(torch, w, A, B) if pcie else None
+    dA = [to_dev(torch, A, w.dtype) for _ in range(copies)]
+    dB = [to_dev(torch, B, w.dtype) for _ in range(copies)]
+    dC = (torch.from_numpy(C0).cuda() if C0 is not None
+          else torch.zeros((w.batch, w.M, w.N), dtype=torch.float32, device="cuda"))
+    dbias = torch.from_numpy(bias).cuda() if bias is not None else None
+    sptr = torch.cuda.current_stream().cuda_stream
+    lda, ldb = w.a_shape[1], w.b_shape[1]  # packed stored rows
+    fn, ws = make_fn(torch, dgt, w, dbias)
+
+    def launch(i):
+        st = fn(w.M, w.N, w.K, w.alpha, dA[i % copies].data_ptr(), lda,
+                dB[i % copies].data_ptr(), ldb, w.beta, dC.data_ptr(), w.N, sptr)
+        if st != 0:
+            raise RuntimeError(dgt.gemm_status_string(st))
+
+    res = time_calls(torch, launch, steps, warmup, settle_ms, tel)
+    if pcie_res is not None:
+        res["pcie"] = pcie_res
+    del dA, dB, dC, ws
     torch.cuda.empty_cache()
     return res, (A, B, C0)
+
+
+def measure_pcie(torch, w, A, B, reps=3):
+    """Host <-> device copies of the workload's operands from and to pinned
+    host memory, timed with events (best of `reps`): A and B in, C out."""
+    import numpy as np
+    stream = torch.cuda.current_stream()
+    in_bytes = 4 if w.dtype == "f32" else 2
+    hA = torch.from_numpy(np.ascontiguousarray(A).view(np.uint8).reshape(-1)).pin_memory()
+    hB = torch.from_numpy(np.ascontiguousarray(B).view(np.uint8).reshape(-1)).pin_memory()
+    hC = torch.empty(w.batch * w.M * w.N * 4, dtype=torch.uint8).pin_memory()
+    dA, dB = torch.empty_like(hA, device="cuda"), torch.empty_like(hB, device="cuda")
+    dC = torch.empty_like(hC, device="cuda")
+    best_in, best_out = math.inf, math.inf
+    for _ in range(reps):
+        e = [torch.cuda.Event(enable_timing=True) for _ in range(3)]
+        e[0].record(stream)
+        dA.copy_(hA, non_blocking=True)
+        dB.copy_(hB, non_blocking=True)
+        e[1].record(stream)
+        hC.copy_(dC, non_blocking=True)
+        e[2].record(stream)
+        torch.cuda.synchronize()
+        best_in = min(best_in, e[0].elapsed_time(e[1]))
+        best_out = min(best_out, e[1].elapsed_time(e[2]))
+    nin = (w.M * w.K + w.K * w.N) * in_bytes * w.batch
+    nout = w.batch * w.M * w.N * 4
+    del dA, dB, dC
+    return {"h2d_ms": round(best_in, 3), "h2d_bytes": nin,
+            "h2d_gbs": round(nin / (best_in * 1e-3) / 1e9, 1),
+            "d2h_ms": round(best_out, 3), "d2h_bytes": nout,
+            "d2h_gbs": round(nout / (best_out * 1e-3) / 1e9, 1),
+            "memory": "pinned host buffers (best of %d)" % reps}
 
 
 def streams_b(w) -> bool:
@@ -268,7 +456,10 @@ def input_copies(w) -> int:
     return max(2, -(-2 * INFINITY_CACHE_BYTES // b_bytes))
 
 
-def roofline(w, ms_avg):
+SPEC_CLOCK_MHZ = 2400.0
+
+
+def roofline(w, ms_avg, clock_mhz=None):
     kern, _, _ = DOMINANT[w.name]
     fl = gemm_flops(w.M, w.N, w.K) * w.batch
     by = algorithmic_bytes(w.M, w.N, w.K, 4 if w.dtype == "f32" else 2, w.beta) * w.batch
@@ -282,9 +473,26 @@ def roofline(w, ms_avg):
                 "traffic": traffic, "kernel": kern, "algorithmic_bytes": by}
     ach = fl / (ms_avg * 1e-3) / 1e12
     peak = PEAK_TFLOPS[w.dtype]
-    return {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
-            "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
-            "kernel": kern, "algorithmic_flops": fl}
+    out = {"bound": "mfma", "achieved": round(ach, 2), "peak": peak,
+           "unit": "TFLOP/s", "frac": round(ach / peak, 4), "traffic": traffic,
+           "kernel": kern, "algorithmic_flops": fl}
+    if clock_mhz:
+        # the matrix cores' peak scales with the engine clock: the same
+        # kernel against what the chip could issue at the clock it ran at
+        p = peak * clock_mhz / SPEC_CLOCK_MHZ
+        out["at_measured_clock"] = {"clock_mhz": clock_mhz, "peak": round(p, 1),
+                                    "frac": round(ach / p, 4)}
+    return out
+
+
+def cpu_model() -> str:
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
 
 
 def cpu_baseline(w, A, B, C0, target_s=12.0):
@@ -303,7 +511,36 @@ def cpu_baseline(w, A, B, C0, target_s=12.0):
     return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
             "cores": oracle.num_threads(), "kind": "oracle",
             "sample": f"first {rows} of {w.M} rows of {w.name} "
-                      f"({rows}x{w.N}x{w.K}, {dt:.1f} s incl. fp64 widening of B)"}
+                      f"({rows}x{w.N}x{w.K}, {dt:.1f} s incl. fp64 widening of B)",
+            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+
+
+def cpu_small_cases(names=("f32_256", "f32_1000_ragged")):
+    """The oracle on the two small FP32 cases, whole, with one thread and with
+    all of them (the pages: below a size of about 128 a CPU can beat the
+    GPU once launch and transfer costs count, dilfish.github.io 5.6)."""
+    import gemm_inputs as gi
+    import oracle
+    oracle.build(force=False)
+    full = oracle.num_threads()
+    out = []
+    for name in names:
+        w = gi.WORKLOADS[name]
+        A, B, C0 = gi.make_inputs(w)
+        entry = {"workload": name, "M": w.M, "N": w.N, "K": w.K}
+        for threads in (1, full):
+            oracle.set_num_threads(threads)
+            best = math.inf
+            for _ in range(3):
+                t0 = time.perf_counter()
+                oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype)
+                best = min(best, time.perf_counter() - t0)
+            key = "one_thread" if threads == 1 else f"{threads}_threads"
+            entry[key] = {"ms": round(best * 1e3, 3),
+                          "gflops": round(gemm_flops(w.M, w.N, w.K) / best / 1e9, 2)}
+        out.append(entry)
+    oracle.set_num_threads(full)
+    return out
 
 
 def copy_calibration(torch, nbytes=1 << 30, reps=5):
@@ -317,17 +554,99 @@ def copy_calibration(torch, nbytes=1 << 30, reps=5):
                       "copy_calibration_bytes_written": nbytes, "reps": reps}))
 
 
+# ------------------------------------------------------------ the ladder
+
+# The rungs of the kernel ladder, slowest first (the pages' naive -> shared
+# tiles -> register tiles -> matrix units -> deeper pipeline progression,
+# qwbw.cn section 三 table; dilfish.github.io 5.2-5.5), by library variant.
+LADDER = [("naive", "one lane per output, two global loads per FMA"),
+          ("lds", "LDS-staged 128x128 tiles, 8x8 outputs per lane on the vector ALU"),
+          ("mfma_regs", "register-staged LDS tiles, MFMA micro-tiles"),
+          ("mfma128", "global->LDS DMA pipeline, 128x128 tiles, MFMA"),
+          ("mfma256", "global->LDS DMA pipeline, 256x256 tiles, MFMA"),
+          ("auto", "what gemm_f32 / gemm_bf16 pick")]
+LADDER_WORKLOADS = ("f32_4096", "bf16_8192")
+
+
+def ladder(torch, dgt, steps, warmup, settle_ms, tel):
+    """Every rung on the FP32 4096^3 and BF16 8192^3 workloads: time per call,
+    TFLOP/s and fraction of the matrix-core peak."""
+    import gemm_inputs as gi
+    out = []
+    for name in LADDER_WORKLOADS:
+        w = gi.WORKLOADS[name]
+        A, B, _ = gi.make_inputs(w)
+        dA, dB = to_dev(torch, A, w.dtype), to_dev(torch, B, w.dtype)
+        dC = torch.zeros((w.M, w.N), dtype=torch.float32, device="cuda")
+        sptr = torch.cuda.current_stream().cuda_stream
+        var_fn = {"f32": dgt.gemm_f32_variant, "bf16": dgt.gemm_bf16_variant}[w.dtype]
+        for rung, what in LADDER:
+            v = dgt.VARIANTS[rung]
+            slow = rung in ("naive", "lds")
+            n, wu, settle = (max(2, steps // 10), 1, 0.0) if slow else (steps, warmup, settle_ms)
+
+            def launch(i, v=v):
+                st = var_fn(v, w.M, w.N, w.K, w.alpha, dA.data_ptr(), w.K, dB.data_ptr(), w.N,
+                            w.beta, dC.data_ptr(), w.N, sptr)
+                if st != 0:
+                    raise RuntimeError(f"{rung}: {dgt.gemm_status_string(st)}")
+
+            log(f"[ladder] {name} {rung}: {n} timed calls")
+            r = time_calls(torch, launch, n, wu, settle, tel)
+            clk = r.get("clock", {}).get("gfxclk_mhz")
+            rf = roofline(w, r["ms_avg"], clk)
+            out.append({"workload": name, "rung": rung, "what": what,
+                        "ms_per_call": round(r["ms_avg"], 4), "calls": n,
+                        "tflops": rf["achieved"], "frac": rf["frac"], "peak": rf["peak"],
+                        "clock_mhz": clk,
+                        "frac_at_measured_clock": rf.get("at_measured_clock", {}).get("frac")})
+            log(f"[ladder] {name} {rung}: {r['ms_avg']:.3f} ms, {rf['achieved']} TFLOP/s, "
+                f"{rf['frac']:.3f} of peak")
+        del dA, dB, dC
+        torch.cuda.empty_cache()
+    return out
+
+
+def counter_check(torch, dgt):
+    """One call of the naive rung at FP32 2048^3 (chongfengling.github.io
+    section 2.3's counter case), for a rocprofv3 counter pass: each wavefront
+    of 64 lanes issues one vector load of A and one of B per k, so the
+    kernel issues 2 * K * (M*N/64) vector load instructions."""
+    import gemm_inputs as gi
+    M = N = K = 2048
+    A = gi.draw(2048 + 1, M, K, "uniform")
+    B = gi.draw(2048 + 2, K, N, "uniform")
+    dA, dB = to_dev(torch, A, "f32"), to_dev(torch, B, "f32")
+    dC = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+    st = dgt.gemm_f32_variant(dgt.VARIANT_NAIVE, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(),
+                              N, 0.0, dC.data_ptr(), N, torch.cuda.current_stream().cuda_stream)
+    torch.cuda.synchronize()
+    if st != 0:
+        raise RuntimeError(dgt.gemm_status_string(st))
+    print(json.dumps({"counter_check": "naive_kernel<F32>", "M": M, "N": N, "K": K,
+                      "wavefronts": M * N // 64,
+                      "expected_vector_load_instructions": naive_load_requests(M, N, K, 64),
+                      "flops": gemm_flops(M, N, K)}), flush=True)
+
+
+# ------------------------------------------------------------ main
+
 def main(argv=None):
     ap = argparse.ArgumentParser(description=__doc__,
                                  formatter_class=argparse.RawDescriptionHelpFormatter)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=50)
-    # The power-managed clock overshoots and then settles over the first
-    # ~40-80 launches of an 8192^3 GEMM after the GPU has idled (per-launch
-    # times 0.82, 1.1, ..., 0.81 ms); 100 untimed launches reach steady state.
     ap.add_argument("--warmup", type=int, default=100)
+    # After an idle period the power-managed clock overshoots and then
+    # settles over ~40-80 calls of an 8192^3 GEMM (per-call times 0.82, 1.1,
+    # ..., 0.81 ms); each workload first runs untimed for this long.
+    ap.add_argument("--settle-ms", type=float, default=300.0)
     ap.add_argument("--only", default=None, help="time a single workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
+    ap.add_argument("--ladder", action="store_true",
+                    help="time every rung at FP32 4096^3 and BF16 8192^3")
+    ap.add_argument("--counter-check", action="store_true",
+                    help="run the naive rung once at FP32 2048^3 (for a counter pass)")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
 
@@ -350,19 +669,33 @@ def main(argv=None):
     if args.copy_calibration:
         copy_calibration(torch)
         return 0
+    if args.counter_check:
+        counter_check(torch, dgt)
+        return 0
+
+    tel = Telemetry(torch)
+    if tel.error:
+        log(f"[telemetry] unavailable: {tel.error}")
+    if args.ladder:
+        rows = ladder(torch, dgt, args.steps, args.warmup, args.settle_ms, tel)
+        print(json.dumps({"ladder": rows, "telemetry_error": tel.error}), flush=True)
+        return 0
 
     names = [args.only] if args.only else [PRIMARY] + SECONDARY
     results = {}
     for name in names:
         w = gi.WORKLOADS[name]
         copies = input_copies(w)
-        log(f"[{name}] {w.M}x{w.N}x{w.K} {w.dtype}: warmup {args.warmup}, steps {args.steps}")
-        res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies)
-        res["roofline"] = roofline(w, res["ms_avg"])
+        log(f"[{name}] {w.M}x{w.N}x{w.K} {w.dtype}: settle {args.settle_ms:.0f} ms, "
+            f"warmup {args.warmup}, steps {args.steps}")
+        res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies,
+                                    args.settle_ms, tel, pcie=(name == names[0]))
+        clk = res.get("clock", {}).get("gfxclk_mhz")
+        res["roofline"] = roofline(w, res["ms_avg"], clk)
         res["tflops"] = gemm_flops(w.M, w.N, w.K) * w.batch / (res["ms_avg"] * 1e-3) / 1e12
         log(f"[{name}] {res['ms_avg']:.4f} ms  {res['tflops']:.1f} TFLOP/s  "
-            f"roofline frac {res['roofline']['frac']:.3f}")
-        results[name] = (w, res, inputs)
+            f"roofline frac {res['roofline']['frac']:.3f}  clock {clk} MHz")
+        results[name] = (w, res, inputs if name == names[0] else None)
 
     head = names[0]
     w, res, (A, B, C0) = results[head]
@@ -371,14 +704,17 @@ def main(argv=None):
         log("[cpu] timing the oracle on a row sample ...")
         cpu = cpu_baseline(w, A, B, C0)
         log(f"[cpu] {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
+        cpu["small_cases"] = cpu_small_cases()
 
     also = []
     for name in names[1:]:
         w2, r2, _ = results[name]
         entry = {"workload": name, "M": w2.M, "N": w2.N, "K": w2.K, "dtype": w2.dtype,
                  "trans_a": w2.trans_a, "trans_b": w2.trans_b, "batch": w2.batch,
-                 "bias": w2.bias, "ms_per_step": round(r2["ms_avg"], 5),
-                 "tflops": round(r2["tflops"], 2), "roofline": r2["roofline"]}
+                 "bias": w2.bias, "alpha": w2.alpha, "beta": w2.beta,
+                 "ms_per_step": round(r2["ms_avg"], 5),
+                 "tflops": round(r2["tflops"], 2), "roofline": r2["roofline"],
+                 "clock": r2.get("clock")}
         if streams_b(w2):
             entry["gbs"] = r2["roofline"]["achieved"]
         also.append(entry)
@@ -399,7 +735,12 @@ def main(argv=None):
         "config": {"workload": head, "M": w.M, "N": w.N, "K": w.K,
                    "alpha": w.alpha, "beta": w.beta,
                    "inputs": w.dtype, "accumulate": "f32", "output": "f32"},
+        "settle_ms": args.settle_ms,
+        "settle_calls": res["settle_calls"],
         "launch_ms": {k: round(res[k], 5) for k in ("ms_median", "ms_min", "ms_max")},
+        "clock": res.get("clock"),
+        "telemetry_error": tel.error,
+        "pcie": res.get("pcie"),
         "roofline": res["roofline"],
         "cpu_baseline": cpu,
         "also": also,

@@ -41,9 +41,10 @@ VARIANT_MFMA = 3
 VARIANT_SKINNY = 4
 VARIANT_MFMA_T256 = 5
 VARIANT_MFMA_T128 = 6
+VARIANT_MFMA_REGS = 7
 VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
             "mfma": VARIANT_MFMA, "skinny": VARIANT_SKINNY, "mfma256": VARIANT_MFMA_T256,
-            "mfma128": VARIANT_MFMA_T128}
+            "mfma128": VARIANT_MFMA_T128, "mfma_regs": VARIANT_MFMA_REGS}
 
 # Every symbol the header declares (the tests check the library exports them).
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",
@@ -198,6 +199,47 @@ def _ld(t) -> int:
     return t.stride(0)
 
 
+def _check_layout(named, dims=(2,)):
+    """Structure checks of the torch-facing calls, run before anything reaches
+    the library: each (name, tensor) has a dimension count in ``dims`` and,
+    unless it is empty, unit stride along its last axis (row-major rows).  A
+    column-strided view would otherwise pass the leading-dimension check and
+    read the wrong elements."""
+    for name, t in named:
+        if t.dim() not in dims:
+            raise ValueError(f"{name} must have {' or '.join(map(str, dims))} dimensions, "
+                             f"got {t.dim()}")
+        if t.numel() > 0 and t.stride(-1) != 1:
+            raise ValueError(f"{name} must be row-major with unit column stride")
+
+
+def _check_device(named, device):
+    """Every non-empty (name, tensor) must live on the GPU ``device``: a host
+    tensor would hand a host pointer to a kernel."""
+    for name, t in named:
+        if t.numel() > 0 and (not t.is_cuda or t.device != device):
+            raise ValueError(f"{name} must be a GPU tensor on {device}, got {t.device}")
+
+
+def _dtype_code(A, B, C):
+    import torch
+    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16, torch.float16):
+        raise TypeError("A and B must both be float32, both bfloat16 or both float16")
+    if C.dtype != torch.float32:
+        raise TypeError("C must be float32")
+    return {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
+            torch.float16: DTYPE_F16}[A.dtype]
+
+
+def _stream_handle(stream):
+    import torch
+    if stream is None:
+        return torch.cuda.current_stream().cuda_stream
+    if hasattr(stream, "cuda_stream"):
+        return stream.cuda_stream
+    return stream
+
+
 def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
          stream=None, trans_a: bool = False, trans_b: bool = False) -> int:
     """C <- alpha*op(A)*op(B) + beta*C on torch tensors (row-major, unit column
@@ -206,38 +248,27 @@ def gemm(A, B, C, alpha: float = 1.0, beta: float = 0.0, variant=VARIANT_AUTO,
 
     A and B are float32, bfloat16 or float16 (16-bit bits are passed as-is),
     C float32.  ``variant`` is a ladder rung (enum gemm_variant) or its name
-    in VARIANTS: "auto", "naive", "lds", "mfma", "skinny", or "mfma256" /
-    "mfma128" for the DMA kernels with a fixed workgroup tile.
+    in VARIANTS: "auto", "naive", "lds", "mfma", "skinny", "mfma256" /
+    "mfma128" for the DMA kernels with a fixed workgroup tile, or
+    "mfma_regs" for the register-staged MFMA kernel.
     Returns the status code; the work is queued on ``stream`` (default: torch's
     current stream) and not waited for.
     """
-    import torch
-
     if isinstance(variant, str):
         variant = VARIANTS[variant]
-    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16, torch.float16):
-        raise TypeError("A and B must both be float32, both bfloat16 or both float16")
-    if C.dtype != torch.float32:
-        raise TypeError("C must be float32")
-    for t in (A, B, C):
-        if t.dim() != 2 or (t.numel() > 0 and t.stride(1) != 1):
-            raise ValueError("operands must be 2-D row-major with unit column stride")
-        if t.numel() > 0 and not t.is_cuda:
-            raise ValueError("operands must be GPU tensors")
+    dtype = _dtype_code(A, B, C)
+    named = (("A", A), ("B", B), ("C", C))
+    _check_layout(named)
     M, K = A.shape[::-1] if trans_a else A.shape
     K2, N = B.shape[::-1] if trans_b else B.shape
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
                          f"C {tuple(C.shape)}")
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    _check_device(named, C.device)
+    stream = _stream_handle(stream)
     lda, ldb, ldc = _ld(A), _ld(B), _ld(C)
     args = (M, N, K, float(alpha), A.data_ptr(), lda, B.data_ptr(), ldb,
             float(beta), C.data_ptr(), ldc, stream)
-    dtype = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
-             torch.float16: DTYPE_F16}[A.dtype]
     if trans_a or trans_b:
         return gemm_ex(dtype, trans_a, trans_b, variant, *args)
     auto_fn, var_fn = {DTYPE_F32: (gemm_f32, gemm_f32_variant),
@@ -256,31 +287,30 @@ def gemm_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, bias=None,
     A, B and C are 3-D (batch first; a batch stride of 0, e.g. from
     ``expand``, shares one matrix) or 2-D for an operand shared by every
     problem; each matrix is row-major with unit column stride.  bias is None,
-    a 1-D tensor of N floats (shared) or a 2-D [batch, N] tensor.  Returns
-    the status code of gemm_strided_batched.
+    a 1-D tensor of N floats or a [1, N] tensor (shared by every problem), or
+    a [batch, N] tensor (one row per problem).  Every tensor must be on C's
+    GPU.  Returns the status code of gemm_strided_batched.
     """
     import torch
 
     if isinstance(variant, str):
         variant = VARIANTS[variant]
-    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16, torch.float16):
-        raise TypeError("A and B must both be float32, both bfloat16 or both float16")
-    if C.dtype != torch.float32 or C.dim() != 3:
+    dtype = _dtype_code(A, B, C)
+    if C.dim() != 3:
         raise TypeError("C must be a 3-D float32 tensor")
+    _check_layout((("A", A), ("B", B)), dims=(2, 3))
+    _check_layout((("C", C),), dims=(3,))
     batch = C.shape[0]
 
     def mat(t, name):
         if t.dim() == 2:
             return t, 0
-        if t.dim() != 3 or t.shape[0] not in (batch, 1):
+        if t.shape[0] not in (batch, 1):
             raise ValueError(f"{name} must be 2-D or [batch, rows, cols]")
         return t[0] if t.shape[0] == 1 else t, (0 if t.shape[0] == 1 else t.stride(0))
 
     def pitch(t):
-        m = t if t.dim() == 2 else t[0]
-        if m.numel() > 0 and m.stride(1) != 1:
-            raise ValueError("matrices must be row-major with unit column stride")
-        return _ld(m)
+        return _ld(t if t.dim() == 2 else t[0])
 
     A2, sa = mat(A, "A")
     B2, sb = mat(B, "B")
@@ -293,20 +323,22 @@ def gemm_batched(A, B, C, alpha: float = 1.0, beta: float = 0.0, bias=None,
                          f"C {tuple(C.shape)}")
     bias_ptr, sbias = 0, 0
     if bias is not None:
-        if bias.dtype != torch.float32 or bias.shape[-1] != N or bias.stride(-1) != 1:
-            raise ValueError("bias must be float32 [N] or [batch, N] with unit stride")
+        if bias.dtype != torch.float32 or bias.dim() not in (1, 2) or bias.shape[-1] != N:
+            raise ValueError("bias must be float32 [N], [1, N] or [batch, N]")
+        if bias.dim() == 2 and bias.shape[0] not in (1, batch):
+            raise ValueError(f"a 2-D bias must have 1 or batch = {batch} rows, "
+                             f"got {bias.shape[0]}")
+        _check_layout((("bias", bias),), dims=(1, 2))
         bias_ptr = bias.data_ptr()
-        sbias = bias.stride(0) if bias.dim() == 2 else 0
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
-    dtype = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
-             torch.float16: DTYPE_F16}[A.dtype]
+        # one row shared by every problem reads with stride 0; otherwise row z
+        # starts bias.stride(0) floats after row z - 1
+        sbias = bias.stride(0) if bias.dim() == 2 and bias.shape[0] > 1 else 0
+    _check_device((("A", A), ("B", B), ("C", C)) + ((("bias", bias),) if bias is not None
+                                                     else ()), C.device)
     return gemm_strided_batched(dtype, trans_a, trans_b, variant, M, N, K, float(alpha),
                                 A2.data_ptr(), pitch(A2), sa, B2.data_ptr(), pitch(B2), sb,
                                 float(beta), C.data_ptr(), pitch(C), C.stride(0),
-                                bias_ptr, sbias, batch, stream)
+                                bias_ptr, sbias, batch, _stream_handle(stream))
 
 
 def gemm_split(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0,
@@ -314,32 +346,32 @@ def gemm_split(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0,
                trans_b: bool = False) -> int:
     """Split-K form of ``gemm`` on torch tensors (gemm_splitk).  ``workspace``
     is a device tensor of at least gemm_splitk_workspace_size bytes; when None
-    one is allocated here with torch (the library itself allocates nothing).
+    one is allocated here with torch (the library itself allocates nothing);
+    a caller's workspace must be a contiguous GPU tensor on C's device.
     Returns the status code."""
     import torch
 
-    if A.dtype != B.dtype or A.dtype not in (torch.float32, torch.bfloat16, torch.float16):
-        raise TypeError("A and B must both be float32, both bfloat16 or both float16")
-    if C.dtype != torch.float32:
-        raise TypeError("C must be float32")
+    dtype = _dtype_code(A, B, C)
+    named = (("A", A), ("B", B), ("C", C))
+    _check_layout(named)
     M, K = A.shape[::-1] if trans_a else A.shape
     K2, N = B.shape[::-1] if trans_b else B.shape
     if K2 != K or tuple(C.shape) != (M, N):
         raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
                          f"C {tuple(C.shape)}")
-    dtype = {torch.float32: DTYPE_F32, torch.bfloat16: DTYPE_BF16,
-             torch.float16: DTYPE_F16}[A.dtype]
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _check_device(named + ((("workspace", workspace),) if workspace is not None else ()),
+                  C.device)
     need = gemm_splitk_workspace_size(dtype, M, N, K, splits)
     if need < 0:
         return need
     if workspace is None and need > 0:
         workspace = torch.empty(need, dtype=torch.uint8, device=C.device)
-    ws_ptr = workspace.data_ptr() if workspace is not None else 0
-    ws_bytes = workspace.numel() * workspace.element_size() if workspace is not None else 0
-    if stream is None:
-        stream = torch.cuda.current_stream().cuda_stream
-    elif hasattr(stream, "cuda_stream"):
-        stream = stream.cuda_stream
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr = workspace.data_ptr() if workspace.numel() > 0 else 0
+        ws_bytes = workspace.numel() * workspace.element_size()
     return gemm_splitk(dtype, trans_a, trans_b, M, N, K, float(alpha), A.data_ptr(), _ld(A),
                        B.data_ptr(), _ld(B), float(beta), C.data_ptr(), _ld(C), splits,
-                       ws_ptr, ws_bytes, stream)
+                       ws_ptr, ws_bytes, _stream_handle(stream))

@@ -109,6 +109,10 @@ hipError_t dispatch(DType t, int variant, const GemmParams& p, bool reads_ab, hi
                                         : dgt::launch_skinny16_bt_dma<In::F16>(p, s);
             return t == DType::BF16 ? dgt::launch_skinny16<In::BF16>(p, s)
                                     : dgt::launch_skinny16<In::F16>(p, s);
+        case GEMM_VARIANT_MFMA_REGS:
+            return t == DType::F32    ? dgt::launch_mfma_f32_regs(p, s)
+                   : t == DType::BF16 ? dgt::launch_mfma16_regs<In::BF16>(p, s)
+                                      : dgt::launch_mfma16_regs<In::F16>(p, s);
         case GEMM_VARIANT_MFMA_T256:
         case GEMM_VARIANT_MFMA_T128: {
             const int tile = variant == GEMM_VARIANT_MFMA_T128 ? 128 : 256;
@@ -134,7 +138,7 @@ int run(const Call& c) {
     int st = check_shape(c.ta, c.tb, c.M, c.N, c.K, c.lda, c.ldb, c.ldc);
     if (st != GEMM_OK) return st;
     if (c.k_last < 0 || c.k_last > c.K) return GEMM_ERR_ARG;
-    if (c.variant < GEMM_VARIANT_AUTO || c.variant > GEMM_VARIANT_MFMA_T128)
+    if (c.variant < GEMM_VARIANT_AUTO || c.variant > GEMM_VARIANT_MFMA_REGS)
         return GEMM_ERR_VARIANT;
     if (c.M == 0 || c.N == 0 || c.batch == 0) return GEMM_OK;  // empty C: nothing to do
     const bool reads_ab = (c.alpha != 0.0f) && (c.K > 0);
@@ -267,26 +271,10 @@ bool dtype_of(int dtype, DType& t) {
     return true;
 }
 
-}  // namespace
-
-extern "C" {
-
-int gemm_splitk_slices(int dtype, int M, int N, int K, int splits) {
-    DType t;
-    if (!dtype_of(dtype, t) || splits < 0) return GEMM_ERR_ARG;
-    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
-    return plan_splitk(t, M, N, K, splits).splits;
-}
-
-int64_t gemm_splitk_workspace_size(int dtype, int M, int N, int K, int splits) {
-    const int s = gemm_splitk_slices(dtype, M, N, K, splits);
-    if (s < 0) return s;
-    return s > 1 ? (int64_t)s * M * N * 4 : 0;
-}
-
-int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
-                const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
-                int splits, void* workspace, int64_t workspace_bytes, void* stream) {
+// Split-K into the caller's workspace of workspace_bytes.
+int splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+           const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
+           int splits, void* workspace, int64_t workspace_bytes, void* stream) {
     DType t;
     if (!dtype_of(dtype, t) || splits < 0 || workspace_bytes < 0) return GEMM_ERR_ARG;
     int st = check_shape(trans_a, trans_b, M, N, K, lda, ldb, ldc);
@@ -325,6 +313,29 @@ int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float 
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }
 
+}  // namespace
+
+extern "C" {
+
+int gemm_splitk_slices(int dtype, int M, int N, int K, int splits) {
+    DType t;
+    if (!dtype_of(dtype, t) || splits < 0) return GEMM_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    return plan_splitk(t, M, N, K, splits).splits;
+}
+
+int64_t gemm_splitk_workspace_size(int dtype, int M, int N, int K, int splits) {
+    const int s = gemm_splitk_slices(dtype, M, N, K, splits);
+    if (s < 0) return s;
+    return s > 1 ? (int64_t)s * M * N * 4 : 0;
+}
+
+int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
+                int splits, void* workspace, int64_t workspace_bytes, void* stream) {
+    return splitk(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                  workspace, workspace_bytes, stream);
+}
 
 int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
              const float* B, int ldb, float beta, float* C, int ldc, void* stream) {

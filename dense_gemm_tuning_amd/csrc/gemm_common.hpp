@@ -171,10 +171,12 @@ hipError_t launch_scale(const GemmParams& p, hipStream_t s);
 template <In T> hipError_t launch_naive(const GemmParams& p, hipStream_t s);
 template <In T> hipError_t launch_lds(const GemmParams& p, hipStream_t s);
 hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s);
+hipError_t launch_mfma_f32_regs(const GemmParams& p, hipStream_t s);
 bool mfma_f32_dma_eligible(const GemmParams& p);
 hipError_t launch_mfma_f32_dma(const GemmParams& p, hipStream_t s);
 hipError_t launch_mfma_f32_dma_tile(const GemmParams& p, hipStream_t s, int tile);
 template <In T> hipError_t launch_mfma16(const GemmParams& p, hipStream_t s);
+template <In T> hipError_t launch_mfma16_regs(const GemmParams& p, hipStream_t s);
 bool mfma16_dma_eligible(const GemmParams& p);
 template <In T> hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s);
 template <In T> hipError_t launch_mfma16_dma_tile(const GemmParams& p, hipStream_t s, int tile);

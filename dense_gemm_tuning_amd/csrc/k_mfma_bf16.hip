@@ -255,5 +255,7 @@ hipError_t launch_mfma16(const GemmParams& p, hipStream_t s) {
 
 template hipError_t launch_mfma16<In::BF16>(const GemmParams&, hipStream_t);
 template hipError_t launch_mfma16<In::F16>(const GemmParams&, hipStream_t);
+template hipError_t launch_mfma16_regs<In::BF16>(const GemmParams&, hipStream_t);
+template hipError_t launch_mfma16_regs<In::F16>(const GemmParams&, hipStream_t);
 
 }  // namespace dgt

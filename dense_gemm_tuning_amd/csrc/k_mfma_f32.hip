@@ -196,8 +196,9 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
 
 // Operands with 16-byte aligned rows take the DMA kernel (256- or 128-tiles
 // held in accumulation registers); unaligned ones this one.
-hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
-    if (mfma_f32_dma_eligible(p)) return launch_mfma_f32_dma(p, s);
+// The register-staged kernel for any operands (the ladder's explicit rung,
+// and what operands whose rows are not 16-byte aligned take).
+hipError_t launch_mfma_f32_regs(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
@@ -217,6 +218,11 @@ hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
                                tiles_n);
         return hipGetLastError();
     });
+}
+
+hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
+    if (mfma_f32_dma_eligible(p)) return launch_mfma_f32_dma(p, s);
+    return launch_mfma_f32_regs(p, s);
 }
 
 }  // namespace dgt

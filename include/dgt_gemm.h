@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 6
+#define DGT_GEMM_ABI_VERSION 7
 
 /* Input formats (the dtype argument of gemm_ex and gemm_select_variant). */
 enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };
@@ -125,8 +125,15 @@ enum gemm_variant {
                                    rows (pitch and base) and pitches below
                                    2^23 (fp32) or 2^24 (16-bit) elements;
                                    GEMM_ERR_VARIANT otherwise                */
-    GEMM_VARIANT_MFMA_T128 = 6  /* the same with 128 x 128 tiles, two
+    GEMM_VARIANT_MFMA_T128 = 6, /* the same with 128 x 128 tiles, two
                                    workgroups per CU                          */
+    GEMM_VARIANT_MFMA_REGS = 7  /* the MFMA rung without the DMA pipeline:
+                                   LDS tiles filled through registers by
+                                   128-bit loads, double-buffered
+                                   (dilfish.github.io 5.4's double buffer),
+                                   MFMA micro-tiles; any alignment.  GEMM_VARIANT_MFMA
+                                   uses it only for operands whose rows are
+                                   not 16-byte aligned                        */
 };
 
 /* C <- alpha*A*B + beta*C, fp32 inputs, fp32 accumulate/output. */

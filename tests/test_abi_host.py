@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 6
+    assert dgt.gemm_abi_version() == 7
     for code in range(0, -9, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
@@ -86,7 +86,7 @@ def test_variant_checks(lib):
         assert fn(dgt.VARIANT_SKINNY, 65, 4, 4, 1.0, A_, 4, B_, 4, 0.0,
                   C_, 4) == dgt.GEMM_ERR_VARIANT
         assert fn(99, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == dgt.GEMM_ERR_VARIANT
-    assert v(dgt.VARIANT_MFMA_T128 + 1, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == \
+    assert v(dgt.VARIANT_MFMA_REGS + 1, 4, 4, 4, 1.0, A_, 4, B_, 4, 0.0, C_, 4) == \
         dgt.GEMM_ERR_VARIANT
 
 
@@ -205,7 +205,7 @@ def test_strided_batched_argument_checks(lib):
     assert call(dtype=5) == dgt.GEMM_ERR_ARG
     assert call(tb=2) == dgt.GEMM_ERR_ARG
     assert call(lda=K - 1) == dgt.GEMM_ERR_LD
-    assert call(variant=7) == dgt.GEMM_ERR_VARIANT
+    assert call(variant=dgt.VARIANT_MFMA_REGS + 1) == dgt.GEMM_ERR_VARIANT
     # empty batch or empty C: nothing to do, no pointer needed
     assert call(batch=0, A=0, B=0, C=0) == dgt.GEMM_OK
     assert call(M=0, A=0, B=0, C=0) == dgt.GEMM_OK

@@ -51,7 +51,7 @@ def dev3(x, dtype):
     return to_dev(np.ascontiguousarray(x), dtype)
 
 
-@pytest.mark.parametrize("bias_mode", ["none", "shared", "per_problem"])
+@pytest.mark.parametrize("bias_mode", ["none", "shared", "shared_row", "per_problem"])
 @pytest.mark.parametrize("layout", list(LAYOUTS))
 @pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("variant", RUNGS)
@@ -72,6 +72,8 @@ def test_batched_integer_bit_exact(variant, dtype, layout, bias_mode):
             bias = None
         elif bias_mode == "shared":
             bias = gi.draw(790 + idx, 1, N, "int")[0]
+        elif bias_mode == "shared_row":  # a [1, N] tensor: one row for every problem
+            bias = gi.draw(790 + idx, 1, N, "int")
         else:
             bias = draw3(795 + 10 * idx, nb, (1, N), "int", "f32")[:, 0, :]
         dA = dev3(A, dtype)
@@ -84,7 +86,8 @@ def test_batched_integer_bit_exact(variant, dtype, layout, bias_mode):
         torch.cuda.synchronize()
         assert st == 0, dgt.gemm_status_string(st)
         Bs = [B[0]] * nb if shared_b else list(B)
-        biases = (None if bias is None else [bias] * nb if bias_mode == "shared" else list(bias))
+        biases = (None if bias is None else [bias] * nb if bias_mode == "shared"
+                  else [bias[0]] * nb if bias_mode == "shared_row" else list(bias))
         R = oracle.gemm_batched(list(A), Bs, list(C0), 1.5, 0.5, dtype, trans_a=ta,
                                 trans_b=tb, biases=biases)
         assert_bit_exact(dC.cpu().numpy(), oracle.round_f32(R),

@@ -139,6 +139,10 @@ def test_splitk_workspace_errors_on_gpu():
     # one slice needs no workspace at all
     assert dgt.gemm_split(A, B, C, splits=1) == 0
     torch.cuda.synchronize()
+    # a host workspace would hand a host pointer to the kernels: refused
+    # by the binding before anything is queued
+    with pytest.raises(ValueError, match="workspace"):
+        dgt.gemm_split(A, B, C, splits=4, workspace=torch.zeros(1 << 20, dtype=torch.uint8))
 
 
 @pytest.mark.parametrize("ta", [False, True])

@@ -28,7 +28,7 @@ import dense_gemm_tuning_amd as dgt  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-RUNGS = ["naive", "lds", "mfma", "skinny", "auto"]
+RUNGS = ["naive", "lds", "mfma", "mfma_regs", "skinny", "auto"]
 DTYPES = ["f32", "bf16", "f16"]
 LAYOUTS = {"nt": (False, True), "tn": (True, False), "tt": (True, True)}
 
@@ -152,20 +152,23 @@ def _strided(rows, cols, ld, dtype, offset, fill):
 @pytest.mark.parametrize("variant", RUNGS)
 @pytest.mark.parametrize("pad,offset", [(8, 0), (3, 0), (8, 1)],
                          ids=["aligned_pad", "odd_pad", "misaligned"])
-@pytest.mark.parametrize("skinny_m", [13, 40])
-def test_padded_and_misaligned_storage(variant, dtype, layout, pad, offset, skinny_m):
+def test_padded_and_misaligned_storage(variant, dtype, layout, pad, offset):
     """Padded pitches of the stored operands, optionally misaligned bases; C's
     padding and the elements past its end must stay untouched.  The skinny
-    rung runs with one row block (8 waves) and with three (4 waves)."""
+    rung runs with one row block (8 waves, M = 13) and with three (4 waves,
+    M = 40); the other rungs at M = 256."""
     ta, tb = LAYOUTS[layout]
-    if variant != "skinny" and skinny_m != 13:
-        pytest.skip("row count only varies for the skinny rung")
-    M, N, K = (skinny_m if variant == "skinny" else 256), 256, 256
+    for M in ([13, 40] if variant == "skinny" else [256]):
+        _padded_case(variant, dtype, layout, pad, offset, ta, tb, M)
+
+
+def _padded_case(variant, dtype, layout, pad, offset, ta, tb, M):
+    N, K = 256, 256
     sa, sb = stored(M, N, K, ta, tb)
     A = gi.draw(61, *sa, "int", dtype=dtype)
     B = gi.draw(62, *sb, "int", dtype=dtype)
     C0 = gi.draw(63, M, N, "int")
-    say(f"storage {variant} {dtype} {layout} pad={pad} offset={offset}")
+    say(f"storage {variant} {dtype} {layout} M={M} pad={pad} offset={offset}")
     _, dA = _strided(*sa, sa[1] + pad, dtype, offset, 0.0)
     _, dB = _strided(*sb, sb[1] + pad, dtype, offset, 0.0)
     canary = -12345.0
@@ -178,12 +181,12 @@ def test_padded_and_misaligned_storage(variant, dtype, layout, pad, offset, skin
     torch.cuda.synchronize()
     assert st == 0
     R = oracle.round_f32(oracle.gemm(A, B, C0, 1.5, 0.5, dtype, trans_a=ta, trans_b=tb))
-    assert_bit_exact(dC.cpu().numpy(), R, "strided C")
+    assert_bit_exact(dC.cpu().numpy(), R, f"strided C, M={M}")
     full = cbase.cpu().numpy()
     mask = np.ones(full.shape, bool)
     body = np.arange(offset, offset + M * ldc).reshape(M, ldc)[:, :N]
     mask[body.ravel()] = False
-    assert np.all(full[mask] == canary), "kernel wrote outside C"
+    assert np.all(full[mask] == canary), f"kernel wrote outside C (M={M})"
 
 
 @pytest.mark.parametrize("layout", list(LAYOUTS))
