@@ -33,6 +33,8 @@ GEMM_ERR_VARIANT = -5
 GEMM_ERR_LAUNCH = -6
 GEMM_ERR_ARG = -7
 GEMM_ERR_WORKSPACE = -8
+GEMM_ERR_SCRATCH = -9
+NOALLOC_SCRATCH_BYTES = 64 << 20  # DGT_GEMM_NOALLOC_SCRATCH_BYTES
 
 VARIANT_AUTO = 0
 VARIANT_NAIVE = 1
@@ -49,7 +51,8 @@ VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
 # Every symbol the header declares (the tests check the library exports them).
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",
            "gemm_f16_variant", "gemm_ex", "gemm_strided_batched", "gemm_splitk",
-           "gemm_splitk_slices", "gemm_splitk_workspace_size", "gemm_select_variant",
+           "gemm_splitk_noalloc", "gemm_splitk_slices", "gemm_splitk_workspace_size",
+           "gemm_select_variant",
            "gemm_status_string", "gemm_abi_version")
 
 DTYPE_F32 = 0
@@ -89,6 +92,8 @@ def _load() -> ctypes.CDLL:
         i64 = ctypes.c_int64
         lib.gemm_splitk.restype = i
         lib.gemm_splitk.argtypes = [i, i, i, *core[:11], i, p, i64, p]
+        lib.gemm_splitk_noalloc.restype = i
+        lib.gemm_splitk_noalloc.argtypes = [i, i, i, *core[:11], i, p]
         lib.gemm_splitk_slices.restype = i
         lib.gemm_splitk_slices.argtypes = [i, i, i, i, i]
         lib.gemm_splitk_workspace_size.restype = i64
@@ -161,6 +166,12 @@ def gemm_splitk(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C
     return _load().gemm_splitk(int(dtype), int(trans_a), int(trans_b), M, N, K, alpha, A, lda,
                                B, ldb, beta, C, ldc, int(splits), workspace,
                                int(workspace_bytes), stream)
+
+
+def gemm_splitk_noalloc(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                        splits, stream=0) -> int:
+    return _load().gemm_splitk_noalloc(int(dtype), int(trans_a), int(trans_b), M, N, K, alpha, A,
+                                       lda, B, ldb, beta, C, ldc, int(splits), stream)
 
 
 def gemm_splitk_slices(dtype, M, N, K, splits) -> int:

@@ -12,6 +12,9 @@
 #include "../../include/dgt_gemm.h"
 #include "gemm_common.hpp"
 
+static_assert(dgt::kScratchBytes == DGT_GEMM_NOALLOC_SCRATCH_BYTES,
+              "the header states the scratch size of gemm_splitk_noalloc");
+
 namespace {
 
 using dgt::GemmParams;
@@ -271,10 +274,12 @@ bool dtype_of(int dtype, DType& t) {
     return true;
 }
 
-// Split-K into the caller's workspace of workspace_bytes.
+// Both split-K entry points.  noalloc: the partials go to the library's fixed
+// scratch (shapes whose partials exceed it are refused, nothing is
+// allocated); otherwise to the caller's workspace of workspace_bytes.
 int splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
            const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
-           int splits, void* workspace, int64_t workspace_bytes, void* stream) {
+           int splits, void* workspace, int64_t workspace_bytes, bool noalloc, void* stream) {
     DType t;
     if (!dtype_of(dtype, t) || splits < 0 || workspace_bytes < 0) return GEMM_ERR_ARG;
     int st = check_shape(trans_a, trans_b, M, N, K, lda, ldb, ldc);
@@ -286,6 +291,12 @@ int splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha
                     beta, C, ldc, stream);
     if (C == nullptr || A == nullptr || B == nullptr) return GEMM_ERR_NULL;
     const int64_t ws_need = (int64_t)plan.splits * M * N * 4;
+    if (noalloc) {
+        if (ws_need > dgt::kScratchBytes) return GEMM_ERR_SCRATCH;
+        if (dgt::splitk_scratch(&workspace) != hipSuccess || workspace == nullptr)
+            return GEMM_ERR_LAUNCH;
+        workspace_bytes = dgt::kScratchBytes;
+    }
     if (workspace == nullptr || workspace_bytes < ws_need) return GEMM_ERR_WORKSPACE;
     float* W = static_cast<float*>(workspace);
     const int esz = elem_size(t);
@@ -334,7 +345,14 @@ int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float 
                 const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
                 int splits, void* workspace, int64_t workspace_bytes, void* stream) {
     return splitk(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
-                  workspace, workspace_bytes, stream);
+                  workspace, workspace_bytes, false, stream);
+}
+
+int gemm_splitk_noalloc(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                        const void* A, int lda, const void* B, int ldb, float beta, float* C,
+                        int ldc, int splits, void* stream) {
+    return splitk(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, splits,
+                  nullptr, 0, true, stream);
 }
 
 int gemm_f32(int M, int N, int K, float alpha, const float* A, int lda,
@@ -421,6 +439,7 @@ const char* gemm_status_string(int status) {
         case GEMM_ERR_LAUNCH: return "GEMM_ERR_LAUNCH: the HIP runtime rejected the launch";
         case GEMM_ERR_ARG: return "GEMM_ERR_ARG: unknown dtype or transpose flag, negative batch, splits or size, or stride out of range";
         case GEMM_ERR_WORKSPACE: return "GEMM_ERR_WORKSPACE: workspace missing or smaller than gemm_splitk_workspace_size";
+        case GEMM_ERR_SCRATCH: return "GEMM_ERR_SCRATCH: gemm_splitk_noalloc: the partials (slices x M x N x 4 bytes) exceed the library's fixed scratch of DGT_GEMM_NOALLOC_SCRATCH_BYTES";
         default: return "unknown gemm status";
     }
 }

@@ -183,6 +183,10 @@ template <In T> hipError_t launch_mfma16_dma_tile(const GemmParams& p, hipStream
 hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* W, int splits, int M, int N, float alpha,
                                 float beta, float* C, int64_t ldc, hipStream_t s);
+// Fixed split-K scratch of gemm_splitk_noalloc: its size, and its device
+// address on the current GPU.
+constexpr int64_t kScratchBytes = int64_t(64) << 20;
+hipError_t splitk_scratch(void** ptr);
 template <In T> hipError_t launch_skinny16(const GemmParams& p, hipStream_t s);
 bool skinny16_bt_dma_eligible(const GemmParams& p);
 template <In T> hipError_t launch_skinny16_bt_dma(const GemmParams& p, hipStream_t s);

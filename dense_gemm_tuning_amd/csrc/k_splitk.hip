@@ -12,6 +12,8 @@
 // summing the slices in a fixed order, so results are deterministic.  It is
 // bound by HBM: S reads of M*N floats and one write (a read too when
 // beta != 0), in 16-byte pieces along rows when the row pitch allows.
+#include <mutex>
+
 #include "gemm_common.hpp"
 
 namespace dgt {
@@ -19,6 +21,23 @@ namespace dgt {
 namespace {
 
 constexpr int NT = 256;
+
+// The split-K partials of gemm_splitk_noalloc: a fixed device array instead
+// of a caller's workspace, for callers that cannot allocate (code under HIP
+// graph capture, serving loops, harnesses that forbid allocation).  Every
+// GPU the library runs on holds its own copy until the process ends; every
+// call on that GPU shares it, so such calls must not overlap in time.
+// Phase 1 writes every element of every slice it later reads, so nothing in
+// it needs clearing between calls.
+static __device__ __align__(256) uint8_t scratch[kScratchBytes];
+
+// The scratch array's device address on each GPU.  In host code the array's
+// name stands for a host-side shadow, never a device address: kernels get
+// only the address hipGetSymbolAddress returns for the current device.
+constexpr int kMaxDevices = 64;
+std::once_flag g_scratch_once[kMaxDevices];
+void* g_scratch_ptr[kMaxDevices];
+hipError_t g_scratch_err[kMaxDevices];
 
 template <bool kVec>
 __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* W, int splits, int M,
@@ -60,6 +79,22 @@ __global__ __launch_bounds__(NT) void splitk_reduce_kernel(const float* W, int s
 }
 
 }  // namespace
+
+// Device address of this GPU's scratch array (looked up once per device,
+// with that device current), or the HIP error of the lookup.
+hipError_t splitk_scratch(void** ptr) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return e;
+    if (dev < 0 || dev >= kMaxDevices) return hipErrorInvalidDevice;
+    std::call_once(g_scratch_once[dev], [dev] {
+        void* p = nullptr;
+        g_scratch_err[dev] = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+        g_scratch_ptr[dev] = g_scratch_err[dev] == hipSuccess ? p : nullptr;
+    });
+    *ptr = g_scratch_ptr[dev];
+    return g_scratch_err[dev];
+}
 
 hipError_t launch_splitk_reduce(const float* W, int splits, int M, int N, float alpha,
                                 float beta, float* C, int64_t ldc, hipStream_t s) {

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 7
+#define DGT_GEMM_ABI_VERSION 8
 
 /* Input formats (the dtype argument of gemm_ex and gemm_select_variant). */
 enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };
@@ -88,8 +88,11 @@ enum gemm_status {
                                    other than 0 or 1, a negative batch,
                                    splits or workspace size, or a stride
                                    outside [0, 2^48)                         */
-    GEMM_ERR_WORKSPACE = -8     /* gemm_splitk: workspace NULL or smaller
+    GEMM_ERR_WORKSPACE = -8,    /* gemm_splitk: workspace NULL or smaller
                                    than gemm_splitk_workspace_size           */
+    GEMM_ERR_SCRATCH = -9       /* gemm_splitk_noalloc: the shape's partials
+                                   (gemm_splitk_workspace_size) exceed
+                                   DGT_GEMM_NOALLOC_SCRATCH_BYTES            */
 };
 
 /* Kernel ladder (for measurement and tests; GEMM_VARIANT_AUTO is what
@@ -227,6 +230,32 @@ int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K,
                 float alpha, const void* A, int lda, const void* B, int ldb,
                 float beta, float* C, int ldc, int splits, void* workspace,
                 int64_t workspace_bytes, void* stream);
+
+/* gemm_splitk for callers that cannot allocate device memory at all --
+ * code recorded under HIP graph capture, tight serving loops, harnesses
+ * that forbid allocation -- and so cannot hand in a workspace either.
+ * Same operation, arguments, slicing and kernels as gemm_splitk (results
+ * are bit-identical to it), but the fp32 partials go to a fixed scratch
+ * array of DGT_GEMM_NOALLOC_SCRATCH_BYTES that the library holds on every
+ * GPU it has run on until the process ends.  The call allocates nothing:
+ * no hipMalloc, no hipFree, no allocating library routine.
+ *   - Size limit: a shape whose partials (gemm_splitk_workspace_size for
+ *     the same dtype, shape and splits) exceed the scratch returns
+ *     GEMM_ERR_SCRATCH before anything is queued; a shape that needs no
+ *     split runs as gemm_ex and uses no scratch.
+ *   - Sharing: all calls on one GPU share that GPU's scratch, which keeps
+ *     the last call's partials.  Calls on one GPU must not overlap in time
+ *     (queue them on one stream, or order their streams); overlapping calls
+ *     race on the scratch and give wrong results.  No part of the scratch
+ *     needs to start at zero (every partial is written before it is read).
+ *   - The first call on a GPU looks up that GPU's scratch address (a host
+ *     query, no allocation); a failure there returns GEMM_ERR_LAUNCH.
+ * Every other error is as for gemm_splitk. */
+#define DGT_GEMM_NOALLOC_SCRATCH_BYTES (64ll << 20)
+int gemm_splitk_noalloc(int dtype, int trans_a, int trans_b, int M, int N,
+                        int K, float alpha, const void* A, int lda,
+                        const void* B, int ldb, float beta, float* C, int ldc,
+                        int splits, void* stream);
 
 /* Number of K slices gemm_splitk uses for this shape and request (>= 1), or
  * a negative status.  Host only. */

@@ -39,8 +39,8 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 7
-    for code in range(0, -9, -1):
+    assert dgt.gemm_abi_version() == 8
+    for code in range(0, -10, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
     assert dgt.gemm_status_string(12345) == "unknown gemm status"
@@ -281,3 +281,31 @@ def test_splitk_argument_checks(lib):
     assert call(splits=1, ws=0, wsb=0, C=0) == dgt.GEMM_ERR_NULL
     # empty C: nothing to do
     assert call(M=0, A=0, B=0, C=0, ws=0) == dgt.GEMM_OK
+
+
+def test_splitk_noalloc_argument_checks(lib):
+    """gemm_splitk_noalloc refuses a shape whose partials exceed the fixed
+    scratch, and every other argument error as gemm_splitk does, on the host
+    before any HIP call (fake pointers: nothing here reaches a launch)."""
+    f = dgt.gemm_splitk_noalloc
+
+    def call(dtype=0, ta=0, tb=0, M=64, N=64, K=4096, A=A_, lda=4096, B=B_, ldb=64, C=C_,
+             ldc=64, splits=4):
+        return f(dtype, ta, tb, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, ldc, splits)
+
+    # 8 slices of 2048 x 2048 fp32 partials = 128 MiB > the 64 MiB scratch
+    assert dgt.gemm_splitk_workspace_size(0, 2048, 2048, 16384, 8) > dgt.NOALLOC_SCRATCH_BYTES
+    assert call(M=2048, N=2048, K=16384, lda=16384, ldb=2048, ldc=2048, splits=8) == \
+        dgt.GEMM_ERR_SCRATCH
+    assert call(splits=-1) == dgt.GEMM_ERR_ARG
+    assert call(dtype=3) == dgt.GEMM_ERR_ARG
+    assert call(ta=2) == dgt.GEMM_ERR_ARG
+    assert call(lda=100) == dgt.GEMM_ERR_LD
+    assert call(M=-1) == dgt.GEMM_ERR_DIM
+    assert call(C=0) == dgt.GEMM_ERR_NULL
+    assert call(A=0) == dgt.GEMM_ERR_NULL
+    # one slice is plain gemm_ex (stops at the NULL C); an empty C does nothing
+    assert call(splits=1, C=0) == dgt.GEMM_ERR_NULL
+    assert call(M=0, A=0, B=0, C=0) == dgt.GEMM_OK
+    assert dgt.NOALLOC_SCRATCH_BYTES == 64 << 20
+    assert "GEMM_ERR_SCRATCH" in dgt.gemm_status_string(dgt.GEMM_ERR_SCRATCH)
