@@ -24,10 +24,13 @@ layer's forward with its bias fused, a strided batch of 16 x 2048^3, and the
 split-K and one-GPU-share shapes, plus:
   * "roofline": the dominant kernel's algorithmic FLOP (or bytes) per launch
     over its measured launch time, against the published MI355X peak, and
-    the same against the peak scaled to the engine clock measured during
-    the timed calls ("clock");
-  * "clock": the graphics clock and socket power the GPU's own telemetry
-    reports before, during and after the timed calls (amdsmi gpu metrics);
+    the same against the peak scaled to the engine clock the workload runs
+    at ("clock");
+  * "clock": the graphics clock (mean over the 8 XCDs) and socket power the
+    GPU's own telemetry reports while the workload runs back to back for
+    --telemetry-s seconds after its timed calls (amdsmi gpu metrics; the
+    firmware refreshes them about once a second, too slowly to sample the
+    timed calls themselves);
   * "pcie": one host-to-device copy of A and B and one device-to-host copy
     of C, timed apart from the metric (dilfish.github.io 5.7: transfers are
     part of what a caller pays, but not of the kernel's time);
@@ -200,11 +203,20 @@ def to_dev(torch, x, dtype):
 # ------------------------------------------------------------ GPU telemetry
 
 class Telemetry:
-    """The graphics clock and socket power the GPU's firmware reports (amdsmi
-    gpu metrics), read from a host thread while kernels run, so the reading
-    costs the GPU nothing.  ``current_gfxclks`` holds one clock per XCD; their
-    mean is the engine clock.  Disabled (every reading None) when amdsmi is
-    missing or cannot open the device torch uses."""
+    """The graphics clock, socket power and energy counter the GPU's firmware
+    reports (amdsmi gpu metrics), read from a host thread while kernels run,
+    so reading them costs the GPU nothing.  The firmware refreshes the table
+    about once a second (its system_clock_counter, in ns, says when), so a
+    reading describes the second before it: the bench therefore runs each
+    workload for a few seconds in a telemetry pass of its own and keeps only
+    the tables produced well inside that pass.  ``current_gfxclks`` holds
+    one clock per XCD; their mean is the engine clock.  Disabled (error set,
+    every reading None) when amdsmi is missing or cannot open the device
+    torch uses."""
+
+    # the energy accumulator counts in units of 15.3 uJ (amdsmi's
+    # counter_resolution on this part)
+    ENERGY_UJ = 15.3
 
     def __init__(self, torch):
         self.handle, self.error = None, None
@@ -212,16 +224,13 @@ class Telemetry:
             import amdsmi
             amdsmi.amdsmi_init()
             self.smi = amdsmi
-            handles = amdsmi.amdsmi_get_processor_handles()
             props = torch.cuda.get_device_properties(0)
-            want = None
-            if hasattr(props, "pci_bus_id"):
-                want = (getattr(props, "pci_domain_id", 0), props.pci_bus_id,
-                        getattr(props, "pci_device_id", 0))
-            for h in handles:
-                bdf = amdsmi.amdsmi_get_gpu_device_bdf(h)  # "dddd:bb:dd.f"
-                dom, bus, rest = bdf.split(":")
-                if want is None or (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16)) == want:
+            want = (getattr(props, "pci_domain_id", 0), getattr(props, "pci_bus_id", None),
+                    getattr(props, "pci_device_id", 0))
+            for h in amdsmi.amdsmi_get_processor_handles():
+                dom, bus, rest = amdsmi.amdsmi_get_gpu_device_bdf(h).split(":")  # dddd:bb:dd.f
+                got = (int(dom, 16), int(bus, 16), int(rest.split(".")[0], 16))
+                if want[1] is None or got == want:
                     self.handle = h
                     break
             if self.handle is None:
@@ -230,69 +239,72 @@ class Telemetry:
             self.error = f"{type(e).__name__}: {e}"
 
     def read(self):
-        """(mean graphics clock over the XCDs in MHz, socket power in W,
-        energy counter in J) or Nones."""
+        """(firmware timestamp ns, mean graphics clock over the XCDs in MHz,
+        socket power in W, energy counter in J), or None."""
         if self.handle is None:
-            return None, None, None
+            return None
         try:
             m = self.smi.amdsmi_get_gpu_metrics_info(self.handle)
         except Exception:
-            return None, None, None
+            return None
+
+        def num(x):
+            return x if isinstance(x, (int, float)) else None
         clk = m.get("current_gfxclks")
-        vals = [c for c in clk if isinstance(c, (int, float)) and c > 0] if isinstance(clk, list) else []
-        if not vals and isinstance(m.get("current_gfxclk"), (int, float)):
+        vals = [c for c in clk if num(c) and c > 0] if isinstance(clk, list) else []
+        if not vals and num(m.get("current_gfxclk")):
             vals = [m["current_gfxclk"]]
-        mhz = sum(vals) / len(vals) if vals else None
-        pw = m.get("current_socket_power")
-        if not isinstance(pw, (int, float)):
-            pw = m.get("average_socket_power")
-        pw = pw if isinstance(pw, (int, float)) else None
-        en = m.get("energy_accumulator")
-        # the accumulator counts in units of 15.259 uJ (2^-16 J)
-        en = en * 15.259e-6 if isinstance(en, (int, float)) else None
-        return mhz, pw, en
-
-    def sampler(self):
-        return _Sampler(self)
+        en = num(m.get("energy_accumulator"))
+        return (num(m.get("system_clock_counter")), sum(vals) / len(vals) if vals else None,
+                num(m.get("current_socket_power")),
+                en * self.ENERGY_UJ * 1e-6 if en is not None else None)
 
 
-class _Sampler:
-    """Reads the telemetry every ~2 ms on a host thread between start() and
-    stop(); summary() gives the mean clock and power of those readings and
-    the mean power from the energy counter over the whole interval."""
+def telemetry_pass(torch, launch, tel, seconds):
+    """Run launch(i) back to back for `seconds` while a host thread polls the
+    telemetry every 20 ms; summarise the firmware tables first seen at least
+    1.2 s into the pass (each describes the second before it, so they cover
+    steady running only).  Returns None without telemetry."""
+    import threading
+    if tel is None or tel.handle is None or seconds <= 0:
+        return None
+    seen, stop = {}, threading.Event()
+    t0 = time.perf_counter()
 
-    def __init__(self, tel):
-        import threading
-        self.tel, self.samples, self._stop = tel, [], threading.Event()
-        self._th = threading.Thread(target=self._run, daemon=True)
-
-    def _run(self):
-        while not self._stop.is_set():
-            self.samples.append(self.tel.read())
-            self._stop.wait(0.002)
-
-    def start(self):
-        self.e0, self.t0 = self.tel.read()[2], time.perf_counter()
-        self._th.start()
-        return self
-
-    def stop(self):
-        self._stop.set()
-        self._th.join()
-        self.e1, self.t1 = self.tel.read()[2], time.perf_counter()
-        return self
-
-    def summary(self):
-        clk = [s[0] for s in self.samples if s[0] is not None]
-        pw = [s[1] for s in self.samples if s[1] is not None]
-        out = {"gfxclk_mhz": round(sum(clk) / len(clk), 1) if clk else None,
-               "gfxclk_mhz_min": min(clk) if clk else None,
-               "gfxclk_mhz_max": max(clk) if clk else None,
-               "socket_power_w": round(sum(pw) / len(pw), 1) if pw else None,
-               "samples": len(clk)}
-        if self.e0 is not None and self.e1 is not None and self.t1 > self.t0 and self.e1 > self.e0:
-            out["energy_power_w"] = round((self.e1 - self.e0) / (self.t1 - self.t0), 1)
-        return out
+    def poll():
+        while not stop.is_set():
+            r = tel.read()
+            t = time.perf_counter() - t0
+            if r and r[0] is not None and r[0] not in seen:
+                seen[r[0]] = (t, r)
+            stop.wait(0.02)
+    th = threading.Thread(target=poll, daemon=True)
+    th.start()
+    n, last_sync = 0, t0
+    while time.perf_counter() - t0 < seconds:
+        launch(n)
+        n += 1
+        if time.perf_counter() - last_sync > 0.05:
+            torch.cuda.synchronize()  # bound the queue so the pass ends on time
+            last_sync = time.perf_counter()
+    torch.cuda.synchronize()
+    stop.set()
+    th.join()
+    tables = [r for (t, r) in sorted(seen.values(), key=lambda x: x[1][0]) if t >= 1.2]
+    if not tables:
+        return {"tables": 0, "calls": n}
+    clk = [r[1] for r in tables if r[1] is not None]
+    pw = [r[2] for r in tables if r[2] is not None]
+    out = {"gfxclk_mhz": round(sum(clk) / len(clk), 1) if clk else None,
+           "socket_power_w": round(sum(pw) / len(pw), 1) if pw else None,
+           "tables": len(tables), "calls": n, "seconds": seconds,
+           "source": "amdsmi gpu metrics (current_gfxclks mean over XCDs, "
+                     "current_socket_power, energy_accumulator)"}
+    if len(tables) >= 2 and tables[0][3] is not None and tables[-1][3] is not None:
+        dt = (tables[-1][0] - tables[0][0]) * 1e-9
+        if dt > 0:
+            out["energy_power_w"] = round((tables[-1][3] - tables[0][3]) / dt, 1)
+    return out
 
 
 # ------------------------------------------------------------ timing
@@ -324,7 +336,7 @@ def make_fn(torch, dgt, w, dbias):
     return {"f32": dgt.gemm_f32, "bf16": dgt.gemm_bf16, "f16": dgt.gemm_f16}[w.dtype], None
 
 
-def time_calls(torch, launch, steps, warmup, settle_ms, tel=None):
+def time_calls(torch, launch, steps, warmup, settle_ms):
     """Settle, warm up, then time `steps` back-to-back calls of launch(i)
     between one pair of events on the current stream; a second pass with an
     event after every call gives the per-call spread."""
@@ -340,17 +352,12 @@ def time_calls(torch, launch, steps, warmup, settle_ms, tel=None):
     for i in range(warmup):
         launch(i)
     torch.cuda.synchronize()
-    before = tel.read() if tel else (None, None, None)
-    smp = tel.sampler().start() if tel else None
     start, end = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
     start.record(stream)
     for i in range(steps):
         launch(i)
     end.record(stream)
     torch.cuda.synchronize()
-    if smp:
-        smp.stop()
-    after = tel.read() if tel else (None, None, None)
     total = start.elapsed_time(end)
     # spread: the markers add a little time of their own, so this pass does
     # not feed the average
@@ -361,18 +368,12 @@ def time_calls(torch, launch, steps, warmup, settle_ms, tel=None):
         ev[i + 1].record(stream)
     torch.cuda.synchronize()
     per = sorted(ev[i].elapsed_time(ev[i + 1]) for i in range(steps))
-    res = {"ms_avg": total / steps, "ms_median": per[len(per) // 2],
-           "ms_min": per[0], "ms_max": per[-1], "settle_calls": n_settle}
-    if tel:
-        clock = smp.summary()
-        clock["before_mhz"] = before[0]
-        clock["after_mhz"] = after[0]
-        res["clock"] = clock
-    return res
+    return {"ms_avg": total / steps, "ms_median": per[len(per) // 2],
+            "ms_min": per[0], "ms_max": per[-1], "settle_calls": n_settle}
 
 
 def time_workload(torch, dgt, w, steps, warmup, copies=1, settle_ms=300.0, tel=None,
-                  pcie=False):
+                  pcie=False, telemetry_s=0.0):
     """Average and spread of one GEMM call's duration (ms) on the current stream."""
     import gemm_inputs as gi
     t0 = time.perf_counter()
@@ -395,7 +396,8 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1, settle_ms=300.0, tel=N
         if st != 0:
             raise RuntimeError(dgt.gemm_status_string(st))
 
-    res = time_calls(torch, launch, steps, warmup, settle_ms, tel)
+    res = time_calls(torch, launch, steps, warmup, settle_ms)
+    res["clock"] = telemetry_pass(torch, launch, tel, telemetry_s)
     if pcie_res is not None:
         res["pcie"] = pcie_res
     del dA, dB, dC, ws
@@ -568,7 +570,7 @@ LADDER = [("naive", "one lane per output, two global loads per FMA"),
 LADDER_WORKLOADS = ("f32_4096", "bf16_8192")
 
 
-def ladder(torch, dgt, steps, warmup, settle_ms, tel):
+def ladder(torch, dgt, steps, warmup, settle_ms, tel, telemetry_s):
     """Every rung on the FP32 4096^3 and BF16 8192^3 workloads: time per call,
     TFLOP/s and fraction of the matrix-core peak."""
     import gemm_inputs as gi
@@ -592,13 +594,15 @@ def ladder(torch, dgt, steps, warmup, settle_ms, tel):
                     raise RuntimeError(f"{rung}: {dgt.gemm_status_string(st)}")
 
             log(f"[ladder] {name} {rung}: {n} timed calls")
-            r = time_calls(torch, launch, n, wu, settle, tel)
-            clk = r.get("clock", {}).get("gfxclk_mhz")
+            r = time_calls(torch, launch, n, wu, settle)
+            # the slow rungs' calls are long enough that the pass needs few
+            r["clock"] = telemetry_pass(torch, launch, tel, telemetry_s)
+            clk = (r["clock"] or {}).get("gfxclk_mhz")
             rf = roofline(w, r["ms_avg"], clk)
             out.append({"workload": name, "rung": rung, "what": what,
                         "ms_per_call": round(r["ms_avg"], 4), "calls": n,
                         "tflops": rf["achieved"], "frac": rf["frac"], "peak": rf["peak"],
-                        "clock_mhz": clk,
+                        "clock": r["clock"],
                         "frac_at_measured_clock": rf.get("at_measured_clock", {}).get("frac")})
             log(f"[ladder] {name} {rung}: {r['ms_avg']:.3f} ms, {rf['achieved']} TFLOP/s, "
                 f"{rf['frac']:.3f} of peak")
@@ -641,6 +645,9 @@ def main(argv=None):
     # settles over ~40-80 calls of an 8192^3 GEMM (per-call times 0.82, 1.1,
     # ..., 0.81 ms); each workload first runs untimed for this long.
     ap.add_argument("--settle-ms", type=float, default=300.0)
+    # The GPU's telemetry table refreshes about once a second: after the
+    # timed calls each workload runs this long again while it is sampled.
+    ap.add_argument("--telemetry-s", type=float, default=3.0)
     ap.add_argument("--only", default=None, help="time a single workload")
     ap.add_argument("--no-cpu", action="store_true", help="skip the CPU baseline")
     ap.add_argument("--ladder", action="store_true",
@@ -677,7 +684,7 @@ def main(argv=None):
     if tel.error:
         log(f"[telemetry] unavailable: {tel.error}")
     if args.ladder:
-        rows = ladder(torch, dgt, args.steps, args.warmup, args.settle_ms, tel)
+        rows = ladder(torch, dgt, args.steps, args.warmup, args.settle_ms, tel, args.telemetry_s)
         print(json.dumps({"ladder": rows, "telemetry_error": tel.error}), flush=True)
         return 0
 
@@ -689,8 +696,9 @@ def main(argv=None):
         log(f"[{name}] {w.M}x{w.N}x{w.K} {w.dtype}: settle {args.settle_ms:.0f} ms, "
             f"warmup {args.warmup}, steps {args.steps}")
         res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies,
-                                    args.settle_ms, tel, pcie=(name == names[0]))
-        clk = res.get("clock", {}).get("gfxclk_mhz")
+                                    args.settle_ms, tel, pcie=(name == names[0]),
+                                    telemetry_s=args.telemetry_s)
+        clk = (res.get("clock") or {}).get("gfxclk_mhz")
         res["roofline"] = roofline(w, res["ms_avg"], clk)
         res["tflops"] = gemm_flops(w.M, w.N, w.K) * w.batch / (res["ms_avg"] * 1e-3) / 1e12
         log(f"[{name}] {res['ms_avg']:.4f} ms  {res['tflops']:.1f} TFLOP/s  "
