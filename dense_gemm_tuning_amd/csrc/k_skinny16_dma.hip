@@ -28,8 +28,9 @@
 // extra A requests cost more than the waves gain.
 //
 // Work split as in the register-staged kernel: a workgroup owns a strip of
-// 128 columns (stored rows of B) over all of K, each wave one K-range; a
-// step is four groups of 32 stored rows.  The partial tiles are summed in
+// up to 128 columns (stored rows of B) over all of K, each wave one K-range;
+// a step is four groups of 32 stored rows.  The strip width is chosen per
+// launch so that the strips fill the 256 CUs (strip_cols).  The partial tiles are summed in
 // LDS in wave order (deterministic, no atomics, no workspace).  A (at most
 // 64 x K, shared by every workgroup and re-read from cache) is loaded into
 // registers one step ahead with plain buffer loads, so that a wave issues
@@ -41,6 +42,8 @@
 // valid stored row (k = K - 1), so rows past N read zeros; pieces at k >= K
 // (K a multiple of 8, so a piece is all inside or all outside) get an
 // offset at the range end and read zeros too, as do rows of A past M.
+#include <algorithm>
+
 #include "skinny_common.hpp"
 #include "dma_common.hpp"
 
@@ -88,7 +91,7 @@ __device__ __forceinline__ void copy_b(const void* base, uint32_t range, uint8_t
 // SK deep; kSingleA: one register buffer of A operands, reloaded after each
 // step's last MFMAs (else two, the next step's loaded one step ahead).
 template <In T, int RB, int NW, int NS, int SK, bool kSingleA>
-__global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams p) {
+__global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams p, int cols) {
     using G = Geo<SK>;
     static_assert(NS == 2 || NS == 4, "a step's four groups map onto the ring");
     constexpr int D = NS - 1;  // groups copied ahead of the one being read
@@ -106,7 +109,11 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
     const int lane = threadIdx.x & 63;
     const int wave = __builtin_amdgcn_readfirstlane(threadIdx.x >> 6);
     const int g = lane >> 4, i = lane & 15;
-    const int n0 = blockIdx.x * COLS;
+    // The workgroup's strip: `cols` (<= COLS, a multiple of 16) stored rows
+    // from n0; the four groups of a step always span COLS rows, and the rows
+    // past the strip read zeros through the group descriptors.
+    const int n0 = blockIdx.x * cols;
+    const int nlim = min(n0 + cols, p.N);
     const int64_t ldb2 = p.ldb * 2, lda2 = p.lda * 2;
 
     // Group cp of a step: stored rows n0 + 32cp .. +31; its descriptor ends
@@ -116,7 +123,7 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
 #pragma unroll
     for (int cp = 0; cp < 4; ++cp) {
         const int row0 = n0 + GR * cp;
-        const int rows = min(GR, p.N - row0);
+        const int rows = min(GR, nlim - row0);
         gbase[cp] = static_cast<const uint8_t*>(p.B) + (int64_t)row0 * ldb2;
         grange[cp] = rows <= 0 ? 0u : (uint32_t)((int64_t)(rows - 1) * ldb2 + 2 * (int64_t)p.K);
     }
@@ -327,7 +334,7 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
                 const int row = o / COLS, cl = o % COLS;
                 const int grow = RR * h + row;
                 const int m = 16 * rb + grow, n = n0 + cl;
-                if (m >= p.M || n >= p.N) continue;
+                if (m >= p.M || n >= nlim) continue;
                 const int at = row * COLS + (cl ^ (16 * ((grow >> 2) & 3)));
                 float sum = 0.0f;
 #pragma unroll
@@ -338,11 +345,37 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
         }
 }
 
+// Strip width.  A launch takes about the longer of the time HBM needs to
+// deliver B (about 6.5 TB/s to this kernel) and the time one CU needs to
+// stream its strips' share of B: (waves of workgroups) x (strip width) x K x
+// 2 bytes at the rate one workgroup pulls, measured on 28672 x 8192 weights:
+// 29 GB/s with one row block of A, 24 GB/s with four (A's loads compete with
+// B's), interpolated in between.  The width (a multiple of 16 from 64 to
+// COLS) with the least time wins, ties (within 1%) to the wider strip, which
+// re-reads A less.  So one row block keeps 128 on N = 28672 (224 strips
+// already saturate HBM: 71.8 us), four take 112 (256 strips, one per CU:
+// 83.5 us against 87.4 with 128), and a narrow N spreads over more CUs.
+int strip_cols(const GemmParams& p, int rb) {
+    constexpr int64_t kCUs = 256;
+    const double hbm = 6.5e12, per_wg = 29e9 - (rb - 1) * (29e9 - 24e9) / 3.0;
+    const double bytes_col = 2.0 * p.K;  // one column of B over all of K
+    const double floor_s = bytes_col * p.N * p.batch / hbm;
+    int best = COLS;
+    double best_t = 0.0;
+    for (int c = COLS; c >= 64; c -= 16) {
+        const int64_t wgs = (int64_t)((p.N + c - 1) / c) * p.batch;
+        const double t = std::max(floor_s, (double)((wgs + kCUs - 1) / kCUs) * c * bytes_col / per_wg);
+        if (c == COLS || t < 0.99 * best_t) best = c, best_t = t;
+    }
+    return best;
+}
+
 template <In T, int RB, int NW, int NS, int SK, bool kSingleA>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
-    const dim3 grid((p.N + COLS - 1) / COLS, p.batch), block(NW * 64);
+    const int cols = strip_cols(p, RB);
+    const dim3 grid((p.N + cols - 1) / cols, p.batch), block(NW * 64);
     hipLaunchKernelGGL((skinny16_bt_dma_kernel<T, RB, NW, NS, SK, kSingleA>), grid, block, 0, s,
-                       p);
+                       p, cols);
     return hipGetLastError();
 }
 
