@@ -42,6 +42,7 @@ Usage: python bench.py [--gpus 1] [--steps K] [--warmup W]
        python bench.py --only bf16_8192 --no-cpu   (one workload, for profiling)
        python bench.py --ladder                    (every rung at FP32 4096^3, BF16 8192^3)
        python bench.py --counter-check             (the naive rung once at FP32 2048^3)
+       python bench.py --tile-check                (both DMA tiles against the automatic choice)
        python bench.py --copy-calibration          (copy kernel of known size)
 """
 
@@ -260,11 +261,13 @@ class Telemetry:
                 en * self.ENERGY_UJ * 1e-6 if en is not None else None)
 
 
-def telemetry_pass(torch, launch, tel, seconds):
+def telemetry_pass(torch, launch, tel, seconds, ms_call):
     """Run launch(i) back to back for `seconds` while a host thread polls the
     telemetry every 20 ms; summarise the firmware tables first seen at least
     1.2 s into the pass (each describes the second before it, so they cover
-    steady running only).  Returns None without telemetry."""
+    steady running only).  The host queues at most ~20 ms of calls (ms_call
+    each) ahead of the GPU, so the pass ends on time however long a call
+    takes.  Returns None without telemetry."""
     import threading
     if tel is None or tel.handle is None or seconds <= 0:
         return None
@@ -280,13 +283,13 @@ def telemetry_pass(torch, launch, tel, seconds):
             stop.wait(0.02)
     th = threading.Thread(target=poll, daemon=True)
     th.start()
-    n, last_sync = 0, t0
+    ahead = max(1, int(20.0 / max(ms_call, 1e-3)))
+    n = 0
     while time.perf_counter() - t0 < seconds:
         launch(n)
         n += 1
-        if time.perf_counter() - last_sync > 0.05:
+        if n % ahead == 0:
             torch.cuda.synchronize()  # bound the queue so the pass ends on time
-            last_sync = time.perf_counter()
     torch.cuda.synchronize()
     stop.set()
     th.join()
@@ -397,7 +400,7 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1, settle_ms=300.0, tel=N
             raise RuntimeError(dgt.gemm_status_string(st))
 
     res = time_calls(torch, launch, steps, warmup, settle_ms)
-    res["clock"] = telemetry_pass(torch, launch, tel, telemetry_s)
+    res["clock"] = telemetry_pass(torch, launch, tel, telemetry_s, res["ms_avg"])
     if pcie_res is not None:
         res["pcie"] = pcie_res
     del dA, dB, dC, ws
@@ -596,7 +599,7 @@ def ladder(torch, dgt, steps, warmup, settle_ms, tel, telemetry_s):
             log(f"[ladder] {name} {rung}: {n} timed calls")
             r = time_calls(torch, launch, n, wu, settle)
             # the slow rungs' calls are long enough that the pass needs few
-            r["clock"] = telemetry_pass(torch, launch, tel, telemetry_s)
+            r["clock"] = telemetry_pass(torch, launch, tel, telemetry_s, r["ms_avg"])
             clk = (r["clock"] or {}).get("gfxclk_mhz")
             rf = roofline(w, r["ms_avg"], clk)
             out.append({"workload": name, "rung": rung, "what": what,
@@ -608,6 +611,59 @@ def ladder(torch, dgt, steps, warmup, settle_ms, tel, telemetry_s):
                 f"{rf['frac']:.3f} of peak")
         del dA, dB, dC
         torch.cuda.empty_cache()
+    return out
+
+
+# Shapes on which the automatic choice between the 256 x 256 and 128 x 128
+# workgroup tiles of the DMA kernels is checked against timing both.
+TILE_CHECK = {"bf16": [(1024, 1024, 1024), (2048, 2048, 2048), (3000, 3000, 3000),
+                       (4096, 4096, 4096), (6144, 6144, 6144), (8192, 8192, 8192),
+                       (8192, 1024, 8192), (4096, 2048, 4096), (2048, 2048, 8192),
+                       (1000, 1000, 1000), (8000, 8000, 8000), (1536, 1536, 4096)],
+              "f32": [(1024, 1024, 1024), (2048, 2048, 2048), (3000, 3000, 3000),
+                      (4096, 4096, 4096), (6144, 6144, 6144), (1000, 1000, 1000)]}
+
+
+def tile_check(torch, dgt, steps, warmup):
+    """Time the fixed-tile rungs (256 x 256, 128 x 128) and the automatic
+    choice on each TILE_CHECK shape, interleaved in one process, and report
+    whether the automatic choice is the faster tile (or within 2% of it)."""
+    import gemm_inputs as gi
+    out = []
+    for dtype, shapes in TILE_CHECK.items():
+        var_fn = {"f32": dgt.gemm_f32_variant, "bf16": dgt.gemm_bf16_variant}[dtype]
+        for (M, N, K) in shapes:
+            A = gi.draw(31, M, K, "normal" if dtype == "bf16" else "uniform", dtype=dtype)
+            B = gi.draw(32, K, N, "normal" if dtype == "bf16" else "uniform", dtype=dtype)
+            dA, dB = to_dev(torch, A, dtype), to_dev(torch, B, dtype)
+            dC = torch.zeros((M, N), dtype=torch.float32, device="cuda")
+            sptr = torch.cuda.current_stream().cuda_stream
+            times = {}
+            for rnd in range(3):  # interleaved rounds; the median round counts
+                for rung in ("mfma256", "mfma128", "auto"):
+                    v = dgt.VARIANTS[rung]
+
+                    def launch(i, v=v):
+                        st = var_fn(v, M, N, K, 1.0, dA.data_ptr(), K, dB.data_ptr(), N, 0.0,
+                                    dC.data_ptr(), N, sptr)
+                        if st != 0:
+                            raise RuntimeError(dgt.gemm_status_string(st))
+                    r = time_calls(torch, launch, steps, warmup if rnd == 0 else 5, 0.0)
+                    times.setdefault(rung, []).append(r["ms_avg"])
+            med = {k: sorted(v)[1] for k, v in times.items()}
+            fastest = min(("mfma256", "mfma128"), key=lambda k: med[k])
+            row = {"dtype": dtype, "M": M, "N": N, "K": K,
+                   "ms": {k: round(v, 4) for k, v in med.items()},
+                   "tflops": {k: round(gemm_flops(M, N, K) / (v * 1e-3) / 1e12, 1)
+                              for k, v in med.items()},
+                   "faster_tile": fastest,
+                   "auto_over_best": round(med["auto"] / med[fastest], 3)}
+            out.append(row)
+            log(f"[tile-check] {dtype} {M}x{N}x{K}: 256 {med['mfma256']:.4f} ms, "
+                f"128 {med['mfma128']:.4f} ms, auto {med['auto']:.4f} ms "
+                f"(auto/best {row['auto_over_best']})")
+            del dA, dB, dC
+            torch.cuda.empty_cache()
     return out
 
 
@@ -654,6 +710,8 @@ def main(argv=None):
                     help="time every rung at FP32 4096^3 and BF16 8192^3")
     ap.add_argument("--counter-check", action="store_true",
                     help="run the naive rung once at FP32 2048^3 (for a counter pass)")
+    ap.add_argument("--tile-check", action="store_true",
+                    help="time both DMA workgroup tiles and the automatic choice on a set of shapes")
     ap.add_argument("--copy-calibration", action="store_true")
     args = ap.parse_args(argv)
 
@@ -683,6 +741,10 @@ def main(argv=None):
     tel = Telemetry(torch)
     if tel.error:
         log(f"[telemetry] unavailable: {tel.error}")
+    if args.tile_check:
+        print(json.dumps({"tile_check": tile_check(torch, dgt, args.steps, args.warmup)}),
+              flush=True)
+        return 0
     if args.ladder:
         rows = ladder(torch, dgt, args.steps, args.warmup, args.settle_ms, tel, args.telemetry_s)
         print(json.dumps({"ladder": rows, "telemetry_error": tel.error}), flush=True)
