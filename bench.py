@@ -73,7 +73,7 @@ SECONDARY = ["f32_256", "f32_1000_ragged", "f32_4096", "f16_8192", "bf16_skinny_
              "bf16_8192_nt", "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
              "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt", "f32_1000_splitk",
              "bf16_splitk_1024x1024x16384", "bf16_skinny_shard_8x3584x8192",
-             "bf16_shard_8192x1024x8192"]
+             "bf16_shard_8192x1024x8192", "bf16_streamk_6144x4096x8192"]
 
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
@@ -120,6 +120,9 @@ DOMINANT = {
                                   r"mfma16_dma_kernel<\(dgt::In\)1, 128, false, false, false, false>"),
     "bf16_bmm_16x2048": ("mfma16_dma_kernel<BF16, NN>, batch 16", "k_mfma_bf16_dma.hip",
                          r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, false, false, false>"),
+    "bf16_streamk_6144x4096x8192": ("mfma16_streamk_kernel<BF16, NN> + fix-up (per call)",
+                                    "k_mfma_bf16_dma.hip",
+                                    r"mfma16_streamk_kernel<\(dgt::In\)1, false, false, false>"),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -317,6 +320,14 @@ def make_fn(torch, dgt, w, dbias):
     fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, stream) -> status,
     and the workspace it holds (allocated here, outside any timing)."""
     code = {"f32": dgt.DTYPE_F32, "bf16": dgt.DTYPE_BF16, "f16": dgt.DTYPE_F16}[w.dtype]
+    if w.streamk:
+        need = dgt.gemm_streamk_workspace_size(code, w.M, w.N, w.K)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+
+        def fn(M, N, K, alpha, A, lda, B, ldb, beta, C, ldc, s):
+            return dgt.gemm_streamk(code, w.trans_a, w.trans_b, M, N, K, alpha, A, lda, B, ldb,
+                                    beta, C, ldc, ws.data_ptr(), need, s)
+        return fn, ws
     if w.splits != 1:
         need = dgt.gemm_splitk_workspace_size(code, w.M, w.N, w.K, w.splits)
         ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")

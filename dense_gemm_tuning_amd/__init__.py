@@ -52,7 +52,7 @@ VARIANTS = {"auto": VARIANT_AUTO, "naive": VARIANT_NAIVE, "lds": VARIANT_LDS,
 EXPORTS = ("gemm_f32", "gemm_bf16", "gemm_f16", "gemm_f32_variant", "gemm_bf16_variant",
            "gemm_f16_variant", "gemm_ex", "gemm_strided_batched", "gemm_splitk",
            "gemm_splitk_noalloc", "gemm_splitk_slices", "gemm_splitk_workspace_size",
-           "gemm_select_variant",
+           "gemm_streamk", "gemm_streamk_workspace_size", "gemm_select_variant",
            "gemm_status_string", "gemm_abi_version")
 
 DTYPE_F32 = 0
@@ -94,6 +94,10 @@ def _load() -> ctypes.CDLL:
         lib.gemm_splitk.argtypes = [i, i, i, *core[:11], i, p, i64, p]
         lib.gemm_splitk_noalloc.restype = i
         lib.gemm_splitk_noalloc.argtypes = [i, i, i, *core[:11], i, p]
+        lib.gemm_streamk.restype = i
+        lib.gemm_streamk.argtypes = [i, i, i, *core[:11], p, i64, p]
+        lib.gemm_streamk_workspace_size.restype = i64
+        lib.gemm_streamk_workspace_size.argtypes = [i, i, i, i]
         lib.gemm_splitk_slices.restype = i
         lib.gemm_splitk_slices.argtypes = [i, i, i, i, i]
         lib.gemm_splitk_workspace_size.restype = i64
@@ -172,6 +176,16 @@ def gemm_splitk_noalloc(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb,
                         splits, stream=0) -> int:
     return _load().gemm_splitk_noalloc(int(dtype), int(trans_a), int(trans_b), M, N, K, alpha, A,
                                        lda, B, ldb, beta, C, ldc, int(splits), stream)
+
+
+def gemm_streamk(dtype, trans_a, trans_b, M, N, K, alpha, A, lda, B, ldb, beta, C, ldc,
+                 workspace, workspace_bytes, stream=0) -> int:
+    return _load().gemm_streamk(int(dtype), int(trans_a), int(trans_b), M, N, K, alpha, A, lda,
+                                B, ldb, beta, C, ldc, workspace, int(workspace_bytes), stream)
+
+
+def gemm_streamk_workspace_size(dtype, M, N, K) -> int:
+    return _load().gemm_streamk_workspace_size(int(dtype), M, N, K)
 
 
 def gemm_splitk_slices(dtype, M, N, K, splits) -> int:

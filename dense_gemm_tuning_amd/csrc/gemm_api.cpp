@@ -348,6 +348,61 @@ int gemm_splitk(int dtype, int trans_a, int trans_b, int M, int N, int K, float 
                   workspace, workspace_bytes, false, stream);
 }
 
+int64_t gemm_streamk_workspace_size(int dtype, int M, int N, int K) {
+    DType t;
+    if (!dtype_of(dtype, t)) return GEMM_ERR_ARG;
+    if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
+    if (t == DType::F32 || M <= dgt::kSkinnyMaxM || N == 0 || K == 0) return 0;
+    GemmParams p;
+    p.M = M; p.N = N; p.K = K;
+    return dgt::streamk_workspace_bytes(p);
+}
+
+int gemm_streamk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
+                 const void* A, int lda, const void* B, int ldb, float beta, float* C, int ldc,
+                 void* workspace, int64_t workspace_bytes, void* stream) {
+    DType t;
+    if (!dtype_of(dtype, t) || workspace_bytes < 0) return GEMM_ERR_ARG;
+    int st = check_shape(trans_a, trans_b, M, N, K, lda, ldb, ldc);
+    if (st != GEMM_OK) return st;
+    const bool reads_ab = alpha != 0.0f && K > 0;
+    GemmParams p;
+    p.M = M; p.N = N; p.K = K;
+    p.alpha = alpha; p.beta = beta;
+    p.A = A; p.lda = lda;
+    p.B = B; p.ldb = ldb;
+    p.C = C; p.ldc = ldc;
+    p.ta = trans_a; p.tb = trans_b;
+    p.stride_a = p.stride_b = p.stride_c = p.stride_bias = 0;
+    p.bias = nullptr;
+    p.batch = 1;
+    // what stream-K does not cover runs as gemm_ex with the automatic choice
+    if (t == DType::F32 || M <= dgt::kSkinnyMaxM || !reads_ab || M == 0 || N == 0 ||
+        !dgt::mfma16_dma_eligible(p))
+        return run1(t, trans_a, trans_b, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb,
+                    beta, C, ldc, stream);
+    if (C == nullptr || A == nullptr || B == nullptr) return GEMM_ERR_NULL;
+    const int64_t ws_need = dgt::streamk_workspace_bytes(p);
+    if (workspace == nullptr || workspace_bytes < ws_need ||
+        reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
+        return GEMM_ERR_WORKSPACE;
+    const int esz = elem_size(t);
+    const Range rw = batch_range(workspace, (uint64_t)ws_need, 0, 1);
+    const Range rc = batch_range(C, span_bytes(M, N, ldc, 4), 0, 1);
+    const uint64_t a_span = trans_a ? span_bytes(K, M, lda, esz) : span_bytes(M, K, lda, esz);
+    const uint64_t b_span = trans_b ? span_bytes(N, K, ldb, esz) : span_bytes(K, N, ldb, esz);
+    const Range ra = batch_range(A, a_span, 0, 1), rb = batch_range(B, b_span, 0, 1);
+    if (overlaps(rc, ra) || overlaps(rc, rb) || overlaps(rw, rc) || overlaps(rw, ra) ||
+        overlaps(rw, rb))
+        return GEMM_ERR_OVERLAP;
+    hipStream_t s = static_cast<hipStream_t>(stream);
+    const hipError_t e =
+        t == DType::BF16 ? dgt::launch_mfma16_streamk<dgt::In::BF16>(p, static_cast<float*>(workspace), s)
+                         : dgt::launch_mfma16_streamk<dgt::In::F16>(p, static_cast<float*>(workspace), s);
+    if (e == hipErrorInvalidConfiguration) return GEMM_ERR_VARIANT;
+    return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
+}
+
 int gemm_splitk_noalloc(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
                         const void* A, int lda, const void* B, int ldb, float beta, float* C,
                         int ldc, int splits, void* stream) {

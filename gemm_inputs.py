@@ -157,6 +157,7 @@ class Workload:
     batch: int = 1          # independent problems, stacked on a leading axis
     bias: bool = False      # a bias row of N floats per problem
     splits: int = 1         # split-K request (1: none, 0: automatic)
+    streamk: bool = False   # run through the stream-K entry point
 
     @property
     def a_shape(self):
@@ -236,6 +237,12 @@ WORKLOADS = {
                                               seed_base=15000, splits=0),
     "bf16_shard_8192x1024x8192": Workload("bf16_shard_8192x1024x8192", "bf16", 8192, 1024, 8192,
                                           1.0, 0.0, "normal", seed_base=16000),
+    # 384 tiles of 256 x 256 for 256 CUs (one and a half waves) with a long K:
+    # stream-K deals the K iterations out evenly instead of running a second,
+    # half-empty wave of tiles.
+    "bf16_streamk_6144x4096x8192": Workload("bf16_streamk_6144x4096x8192", "bf16", 6144, 4096,
+                                            8192, 1.0, 0.0, "normal", seed_base=17000,
+                                            streamk=True),
 }
 
 

@@ -266,6 +266,35 @@ int gemm_splitk_slices(int dtype, int M, int N, int K, int splits);
  * Host only. */
 int64_t gemm_splitk_workspace_size(int dtype, int M, int N, int K, int splits);
 
+/* Stream-K: the same operation and arguments as gemm_ex with
+ * GEMM_VARIANT_AUTO, for shapes whose 256 x 256 output tiles do not divide
+ * evenly among the 256 compute units (the last wave of tiles of a
+ * data-parallel launch then runs on part of the chip).  The pages note that
+ * a launch whose blocks are partly idle leaves compute unused
+ * (elainafan.one "朴素 CUDA 实现", after the launch code); stream-K deals out
+ * the tiles' K iterations (32 k each) in equal contiguous ranges to one
+ * workgroup per compute unit instead of whole tiles.  A tile covered by one
+ * workgroup is written directly; the parts of a tile split between
+ * workgroups go to the caller's `workspace` as fp32 partial sums, and a
+ * second kernel queued on `stream` sums them in k order and applies alpha,
+ * beta -- deterministic, no atomics, nothing allocated.
+ * Covered: BF16 / FP16 inputs, M > 64, operands whose stored rows are
+ * 16-byte aligned with pitches below 2^24 elements.  Anything else (FP32,
+ * M <= 64, unaligned operands, alpha == 0 or K == 0) runs as gemm_ex with
+ * GEMM_VARIANT_AUTO and needs no workspace.  The workspace (device memory,
+ * 16-byte aligned, at least gemm_streamk_workspace_size bytes: two
+ * 256 x 256 fp32 tiles per workgroup, 128 MiB at most) must not overlap A, B
+ * or C and must stay untouched until the work on `stream` has finished; its
+ * contents on return are unspecified.  Errors as for gemm_splitk. */
+int gemm_streamk(int dtype, int trans_a, int trans_b, int M, int N, int K,
+                 float alpha, const void* A, int lda, const void* B, int ldb,
+                 float beta, float* C, int ldc, void* workspace,
+                 int64_t workspace_bytes, void* stream);
+
+/* Bytes of workspace gemm_streamk needs for this shape (0 when the call
+ * runs as gemm_ex), or a negative status for bad arguments.  Host only. */
+int64_t gemm_streamk_workspace_size(int dtype, int M, int N, int K);
+
 /* The rung GEMM_VARIANT_AUTO picks for this call (dtype: enum gemm_dtype;
  * trans_a, trans_b as for gemm_ex), or a negative status if the arguments
  * are invalid.  Host only: touches no device and queues nothing. */

@@ -309,3 +309,41 @@ def test_splitk_noalloc_argument_checks(lib):
     assert call(M=0, A=0, B=0, C=0) == dgt.GEMM_OK
     assert dgt.NOALLOC_SCRATCH_BYTES == 64 << 20
     assert "GEMM_ERR_SCRATCH" in dgt.gemm_status_string(dgt.GEMM_ERR_SCRATCH)
+
+
+def test_streamk_argument_checks(lib):
+    """gemm_streamk's host checks (fake pointers: every call here fails
+    validation or needs no launch)."""
+    f = dgt.gemm_streamk
+    M, N, K = 1024, 1024, 1024
+    need = dgt.gemm_streamk_workspace_size(1, M, N, K)
+    # 16 tiles x 8 iterations of 128 k: 128 workgroups x two 256 x 256 fp32 tiles
+    assert need == 2 * 128 * 256 * 256 * 4
+    # 4 tiles x 2 iterations: 8 workgroups; 32 x 32 tiles x 64: 256 (the CUs)
+    assert dgt.gemm_streamk_workspace_size(1, 512, 512, 256) == 2 * 8 * 256 * 256 * 4
+    assert dgt.gemm_streamk_workspace_size(1, 8192, 8192, 8192) == 2 * 256 * 256 * 256 * 4
+    assert dgt.gemm_streamk_workspace_size(0, M, N, K) == 0      # FP32: runs as gemm_ex
+    assert dgt.gemm_streamk_workspace_size(1, 64, N, K) == 0     # skinny
+    assert dgt.gemm_streamk_workspace_size(1, M, N, 0) == 0
+    assert dgt.gemm_streamk_workspace_size(3, M, N, K) == dgt.GEMM_ERR_ARG
+    assert dgt.gemm_streamk_workspace_size(1, -1, N, K) == dgt.GEMM_ERR_DIM
+    # disjoint fake ranges: A and B 2 MiB each, C 4 MiB, the workspace 128 MiB
+    A, B, C, W = 0x1000000, 0x2000000, 0x3000000, 0x10000000
+
+    def call(dtype=1, ta=0, tb=0, M=M, N=N, K=K, A=A, lda=K, B=B, ldb=N, C=C, ldc=N, ws=W,
+             wsb=need):
+        return f(dtype, ta, tb, M, N, K, 1.0, A, lda, B, ldb, 0.0, C, ldc, ws, wsb)
+
+    assert call(dtype=3) == dgt.GEMM_ERR_ARG
+    assert call(wsb=-1) == dgt.GEMM_ERR_ARG
+    assert call(tb=2) == dgt.GEMM_ERR_ARG
+    assert call(lda=K - 1) == dgt.GEMM_ERR_LD
+    assert call(M=-1) == dgt.GEMM_ERR_DIM
+    assert call(C=0) == dgt.GEMM_ERR_NULL
+    assert call(ws=0) == dgt.GEMM_ERR_WORKSPACE
+    assert call(wsb=need - 16) == dgt.GEMM_ERR_WORKSPACE
+    assert call(ws=W + 8) == dgt.GEMM_ERR_WORKSPACE           # not 16-byte aligned
+    assert call(ws=C + 64) == dgt.GEMM_ERR_OVERLAP            # workspace overlaps C
+    assert call(ws=B - 1024) == dgt.GEMM_ERR_OVERLAP          # ... or B
+    assert call(C=A + 64) == dgt.GEMM_ERR_OVERLAP             # C overlaps A
+    assert call(M=0, A=0, B=0, C=0) == dgt.GEMM_OK            # empty C: nothing to do

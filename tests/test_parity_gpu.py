@@ -142,7 +142,21 @@ def test_workload_configs(name):
     A, B, C0 = gi.make_inputs(w)
     bias = gi.make_bias(w)
     say(f"workload {name}: running AUTO on the GPU")
-    if w.splits != 1:
+    if w.streamk:
+        # stream-K, as the bench times it
+        code = {"f32": dgt.DTYPE_F32, "bf16": dgt.DTYPE_BF16, "f16": dgt.DTYPE_F16}[w.dtype]
+        dA, dB = to_dev(A, w.dtype), to_dev(B, w.dtype)
+        dC = (torch.from_numpy(np.ascontiguousarray(C0, np.float32)).cuda() if C0 is not None
+              else torch.zeros((w.M, w.N), device="cuda"))
+        need = dgt.gemm_streamk_workspace_size(code, w.M, w.N, w.K)
+        ws = torch.empty(max(need, 16), dtype=torch.uint8, device="cuda")
+        st = dgt.gemm_streamk(code, w.trans_a, w.trans_b, w.M, w.N, w.K, w.alpha, dA.data_ptr(),
+                              A.shape[1], dB.data_ptr(), B.shape[1], w.beta, dC.data_ptr(), w.N,
+                              ws.data_ptr(), need, torch.cuda.current_stream().cuda_stream)
+        torch.cuda.synchronize()
+        A3, B3, C3 = A[None], B[None], dC.cpu().numpy()[None]
+        del dA, dB, dC, ws
+    elif w.splits != 1:
         # split-K, as the bench times it
         dC = (torch.from_numpy(np.ascontiguousarray(C0, np.float32)).cuda() if C0 is not None
               else torch.zeros((w.M, w.N), device="cuda"))
