@@ -83,10 +83,10 @@ SECONDARY = ["f32_256", "f32_1000_ragged", "f32_4096", "f16_8192", "bf16_skinny_
 # kernel's are the row-block count, waves, ring stages, step depth and
 # whether A has one register buffer).
 DOMINANT = {
-    "f32_256": ("mfma_f32_dma_kernel<NN, 128-tiles>", "k_mfma_f32_dma.hip",
-                r"mfma_f32_dma_kernel<128, false, false, false, false>"),
-    "f32_1000_ragged": ("mfma_f32_dma_kernel<NN, 128-tiles, edge, K tail>", "k_mfma_f32_dma.hip",
-                        r"mfma_f32_dma_kernel<128, false, false, true, true>"),
+    "f32_256": ("mfma_f32_kernel<NN, 64-tiles>", "k_mfma_f32.hip",
+                r"mfma_f32_kernel<true, false, false, false, 64>"),
+    "f32_1000_ragged": ("mfma_f32_kernel<NN, 64-tiles, guarded>", "k_mfma_f32.hip",
+                        r"mfma_f32_kernel<true, true, false, false, 64>"),
     "bf16_8192": ("mfma16_dma_kernel<BF16, NN>", "k_mfma_bf16_dma.hip",
                   r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, false, false, false>"),
     "f16_8192": ("mfma16_dma_kernel<F16, NN>", "k_mfma_bf16_dma.hip",
@@ -795,7 +795,7 @@ def main(argv=None):
                  "bias": w2.bias, "alpha": w2.alpha, "beta": w2.beta,
                  "ms_per_step": round(r2["ms_avg"], 5),
                  "tflops": round(r2["tflops"], 2), "roofline": r2["roofline"],
-                 "clock": r2.get("clock")}
+                 "clock": r2.get("clock"), "settle_calls": r2["settle_calls"]}
         if streams_b(w2):
             entry["gbs"] = r2["roofline"]["achieved"]
         also.append(entry)

@@ -39,9 +39,8 @@ namespace dgt {
 
 namespace {
 
-constexpr int BM = 128, BN = 128, BK = 16, NT = 256;
+constexpr int BK = 16, NT = 256;
 constexpr int KC_PITCH = BK + 4;    // floats, rows along k
-constexpr int MN_PITCH = BN + 4;    // floats, rows along m or n
 
 // 16-byte chunk of 4 floats at [col, col+4) of one row, zero outside.
 template <bool kVec, bool kGuard>
@@ -56,27 +55,31 @@ __device__ __forceinline__ float4 load4(const float* rowp, int col, int limit,
     return make_float4(v[0], v[1], v[2], v[3]);
 }
 
-// One operand's share of a K slice in LDS.  kKC (stored rows run along k:
-// A untransposed, B transposed): 128 mn-rows of 16 k, row pitch 20 floats,
-// and a lane reads its 8 k of one row as two 128-bit reads.  Otherwise
-// (stored rows run along m / n): 16 k-rows of 128, pitch 132, and a lane
-// reads one float per k.  Each lane moves two 16-byte chunks per slice.
-template <bool kVec, bool kGuard, bool kKC>
+// One operand's share of a K slice in LDS, for a T x T workgroup tile (T =
+// 128 or 64).  kKC (stored rows run along k: A untransposed, B transposed):
+// T mn-rows of 16 k, row pitch 20 floats, and a lane reads its 8 k of one
+// row as two 128-bit reads.  Otherwise (stored rows run along m / n): 16
+// k-rows of T, pitch T + 4, and a lane reads one float per k.  Each lane
+// moves T/64 16-byte chunks per slice.
+template <bool kVec, bool kGuard, bool kKC, int T>
 struct OpF32 {
-    static constexpr int SIZE = kKC ? 128 * KC_PITCH : BK * MN_PITCH;  // floats per buffer
-    float4 r[2];
+    static constexpr int MN_PITCH = T + 4;       // floats, rows along m or n
+    static constexpr int CH = T / 64;            // chunks per lane and slice
+    static constexpr int TM = T / 64;            // 32 x 32 MFMA tiles per wave and dimension
+    static constexpr int SIZE = kKC ? T * KC_PITCH : BK * MN_PITCH;  // floats per buffer
+    float4 r[CH];
 
     __device__ void load(const float* X, int64_t ld, int mn0, int mn_lim, int k0, int K,
                          int tid) {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < CH; ++c) {
             const int f = tid + NT * c;
             if (kKC) {  // chunk f: mn-row f/4, k 4*(f%4)
                 const int row = mn0 + (f >> 2), col = k0 + 4 * (f & 3);
                 const bool ok = row < mn_lim;
                 r[c] = load4<kVec, kGuard>(X + (int64_t)(ok ? row : 0) * ld, col, K, ok);
-            } else {    // chunk f: k-row f/32, mn 4*(f%32)
-                const int krow = k0 + (f >> 5), col = mn0 + 4 * (f & 31);
+            } else {    // chunk f: k-row f/(T/4), mn 4*(f%(T/4))
+                const int krow = k0 + f / (T / 4), col = mn0 + 4 * (f % (T / 4));
                 const bool ok = krow < K;
                 r[c] = load4<kVec, kGuard>(X + (int64_t)(ok ? krow : 0) * ld, col, mn_lim, ok);
             }
@@ -84,34 +87,37 @@ struct OpF32 {
     }
     __device__ void store(float* dst, int tid) const {
 #pragma unroll
-        for (int c = 0; c < 2; ++c) {
+        for (int c = 0; c < CH; ++c) {
             const int f = tid + NT * c;
             float* d = kKC ? &dst[(f >> 2) * KC_PITCH + 4 * (f & 3)]
-                           : &dst[(f >> 5) * MN_PITCH + 4 * (f & 31)];
+                           : &dst[(f / (T / 4)) * MN_PITCH + 4 * (f % (T / 4))];
             *reinterpret_cast<float4*>(d) = r[c];
         }
     }
-    // The operand of MFMA tile t (rows / columns w*64 + t*32 + l%32) for
+    // The operand of MFMA tile t (rows / columns w*T/2 + t*32 + l%32) for
     // k = 8h + j: for kKC all eight j at once into v[t][0..7] ...
-    __device__ void read_all(const float* src, int w, int h, int r32, float (&v)[2][8]) const {
+    __device__ void read_all(const float* src, int w, int h, int r32, float (&v)[TM][8]) const {
 #pragma unroll
-        for (int t = 0; t < 2; ++t) {
-            const float* a = &src[(w * 64 + t * 32 + r32) * KC_PITCH + 8 * h];
+        for (int t = 0; t < TM; ++t) {
+            const float* a = &src[(w * (T / 2) + t * 32 + r32) * KC_PITCH + 8 * h];
             *reinterpret_cast<float4*>(&v[t][0]) = *reinterpret_cast<const float4*>(a);
             *reinterpret_cast<float4*>(&v[t][4]) = *reinterpret_cast<const float4*>(a + 4);
         }
     }
     // ... otherwise one j at a time.
     __device__ float read_one(const float* src, int w, int h, int r32, int t, int j) const {
-        return src[(8 * h + j) * MN_PITCH + w * 64 + t * 32 + r32];
+        return src[(8 * h + j) * MN_PITCH + w * (T / 2) + t * 32 + r32];
     }
 };
 
-template <bool kVec, bool kGuard, bool TA, bool TB>
-__global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles_n) {
+// T x T workgroup tile (T = 128: waves of 64 x 64, two workgroups per CU;
+// T = 64: waves of 32 x 32, for launches with few 128-tiles, four per CU).
+template <bool kVec, bool kGuard, bool TA, bool TB, int T>
+__global__ __launch_bounds__(NT, T == 64 ? 4 : 2) void mfma_f32_kernel(GemmParams p, int tiles_n) {
+    constexpr int BM = T, BN = T, TM = T / 64;
     select_problem(p);
-    using OpA = OpF32<kVec, kGuard, !TA>;
-    using OpB = OpF32<kVec, kGuard, TB>;
+    using OpA = OpF32<kVec, kGuard, !TA, T>;
+    using OpB = OpF32<kVec, kGuard, TB, T>;
     __shared__ float As[2][OpA::SIZE];
     __shared__ float Bs[2][OpB::SIZE];
 
@@ -135,11 +141,11 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
         rb.store(Bs[buf], tid);
     };
 
-    floatx16 acc[2][2];
+    floatx16 acc[TM][TM];
 #pragma unroll
-    for (int i = 0; i < 2; ++i)
+    for (int i = 0; i < TM; ++i)
 #pragma unroll
-        for (int j = 0; j < 2; ++j)
+        for (int j = 0; j < TM; ++j)
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
@@ -153,21 +159,21 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
 
         // Operands: A rows wm*64 + ti*32 + r32, B columns wn*64 + tj*32 + r32,
         // k = 8h .. 8h+7 of the slice.
-        float a[2][8], b[2][8];
+        float a[TM][8], b[TM][8];
         if constexpr (!TA) ra.read_all(As[buf], wm, h, r32, a);
         if constexpr (TB) rb.read_all(Bs[buf], wn, h, r32, b);
 #pragma unroll
         for (int j = 0; j < 8; ++j) {
-            float aj[2], bj[2];
+            float aj[TM], bj[TM];
 #pragma unroll
-            for (int x = 0; x < 2; ++x) {
+            for (int x = 0; x < TM; ++x) {
                 aj[x] = TA ? ra.read_one(As[buf], wm, h, r32, x, j) : a[x][j];
                 bj[x] = TB ? b[x][j] : rb.read_one(Bs[buf], wn, h, r32, x, j);
             }
 #pragma unroll
-            for (int ti = 0; ti < 2; ++ti)
+            for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-                for (int tj = 0; tj < 2; ++tj)
+                for (int tj = 0; tj < TM; ++tj)
                     acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                         aj[ti], bj[tj], acc[ti][tj], 0, 0, 0);
         }
@@ -178,13 +184,13 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
     // Accumulator layout of a 32x32 MFMA tile: register r of lane l holds
     // row 8*(r/4) + 4*(l/32) + r%4, column l%32.
 #pragma unroll
-    for (int ti = 0; ti < 2; ++ti)
+    for (int ti = 0; ti < TM; ++ti)
 #pragma unroll
-        for (int tj = 0; tj < 2; ++tj) {
-            const int col = n0 + wn * 64 + tj * 32 + r32;
+        for (int tj = 0; tj < TM; ++tj) {
+            const int col = n0 + wn * (T / 2) + tj * 32 + r32;
 #pragma unroll
             for (int r = 0; r < 16; ++r) {
-                const int row = m0 + wm * 64 + ti * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
+                const int row = m0 + wm * (T / 2) + ti * 32 + 8 * (r >> 2) + 4 * h + (r & 3);
                 if (kGuard && (row >= p.M || col >= p.N)) continue;
                 float* c = p.C + (int64_t)row * p.ldc + col;
                 *c = epilogue(acc[ti][tj][r], p, c, col);
@@ -192,35 +198,48 @@ __global__ __launch_bounds__(NT, 2) void mfma_f32_kernel(GemmParams p, int tiles
         }
 }
 
-}  // namespace
-
-// Operands with 16-byte aligned rows take the DMA kernel (256- or 128-tiles
-// held in accumulation registers); unaligned ones this one.
-// The register-staged kernel for any operands (the ladder's explicit rung,
-// and what operands whose rows are not 16-byte aligned take).
-hipError_t launch_mfma_f32_regs(const GemmParams& p, hipStream_t s) {
-    const int tiles_n = (p.N + BN - 1) / BN;
-    const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
+template <int T>
+hipError_t launch_regs_tiles(const GemmParams& p, hipStream_t s) {
+    const int tiles_n = (p.N + T - 1) / T;
+    const int64_t blocks = (int64_t)((p.M + T - 1) / T) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = operands_16b_aligned(p, 4);
-    const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && k_multiple(p, BK);
+    const bool full = vec && p.M % T == 0 && p.N % T == 0 && k_multiple(p, BK);
     const dim3 grid((unsigned)blocks, p.batch), block(NT);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (full)
-            hipLaunchKernelGGL((mfma_f32_kernel<true, false, TA, TB>), grid, block, 0, s, p,
+            hipLaunchKernelGGL((mfma_f32_kernel<true, false, TA, TB, T>), grid, block, 0, s, p,
                                tiles_n);
         else if (vec)
-            hipLaunchKernelGGL((mfma_f32_kernel<true, true, TA, TB>), grid, block, 0, s, p,
+            hipLaunchKernelGGL((mfma_f32_kernel<true, true, TA, TB, T>), grid, block, 0, s, p,
                                tiles_n);
         else
-            hipLaunchKernelGGL((mfma_f32_kernel<false, true, TA, TB>), grid, block, 0, s, p,
+            hipLaunchKernelGGL((mfma_f32_kernel<false, true, TA, TB, T>), grid, block, 0, s, p,
                                tiles_n);
         return hipGetLastError();
     });
 }
 
+}  // namespace
+
+// The register-staged kernel on 128 x 128 tiles for any operands (the
+// ladder's explicit rung, and what operands whose rows are not 16-byte
+// aligned take when there are enough 128-tiles).
+hipError_t launch_mfma_f32_regs(const GemmParams& p, hipStream_t s) {
+    return launch_regs_tiles<128>(p, s);
+}
+
+// A launch with fewer 128-tiles than half the CUs leaves most of the chip
+// idle whichever 128- or 256-tile kernel runs it; 64-tiles (four workgroups
+// a CU) spread the same work over four times as many workgroups.
+bool mfma_f32_small(const GemmParams& p) {
+    const int64_t t128 = (int64_t)((p.M + 127) / 128) * ((p.N + 127) / 128) * p.batch;
+    return t128 * 2 <= 256;
+}
+
 hipError_t launch_mfma_f32(const GemmParams& p, hipStream_t s) {
+    if (mfma_f32_small(p)) return launch_regs_tiles<64>(p, s);
     if (mfma_f32_dma_eligible(p)) return launch_mfma_f32_dma(p, s);
     return launch_mfma_f32_regs(p, s);
 }

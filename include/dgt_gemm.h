@@ -113,8 +113,9 @@ enum gemm_variant {
                                    per-wavefront MFMA micro-tiles, masked
                                    ragged edges (dilfish.github.io 5.4-5.5;
                                    qwbw.cn section 三); the workgroup tile
-                                   (256 x 256 or 128 x 128) is chosen per
-                                   launch                                     */
+                                   (256 x 256 or 128 x 128; 64 x 64 for fp32
+                                   launches with at most 128 tiles of 128 x
+                                   128) is chosen per launch                  */
     GEMM_VARIANT_SKINNY = 4,    /* M <= 64: streams B once from HBM, A held in
                                    registers per step (up to four 16-row
                                    blocks), K split over waves and reduced
