@@ -14,8 +14,9 @@
 // Workgroup: 256 lanes = 4 wavefronts in a 2 x 2 grid over a 128 x 128 tile
 // of C; K advances in slices of 16.  Global -> LDS: each slice of A
 // (128 x 16) and B (16 x 128) is read with coalesced 128-bit loads into
-// registers one slice ahead and written to the other half of a double LDS
-// buffer (dilfish.github.io 5.4), one barrier per slice.  Each operand is
+// one of two register sets two slices ahead and written to the other half
+// of a double LDS buffer (dilfish.github.io 5.4 keeps one slice in flight;
+// two hide more of the load latency), one barrier per slice.  Each operand is
 // staged by how it is stored: rows along k (A, or B stored N x K) go to LDS
 // as 128 rows of 16 k; rows along m / n (B, or A stored K x M) as 16 rows of
 // 128.  Transposed operands therefore cost no extra pass.
@@ -42,18 +43,62 @@ namespace {
 constexpr int BK = 16, NT = 256;
 constexpr int KC_PITCH = BK + 4;    // floats, rows along k
 
-// 16-byte chunk of 4 floats at [col, col+4) of one row, zero outside.
-template <bool kVec, bool kGuard>
-__device__ __forceinline__ float4 load4(const float* rowp, int col, int limit,
-                                        bool row_ok) {
-    if (!kGuard) return *reinterpret_cast<const float4*>(rowp + col);
-    if (!row_ok) return make_float4(0.f, 0.f, 0.f, 0.f);
-    if (kVec && col + 4 <= limit) return *reinterpret_cast<const float4*>(rowp + col);
-    float v[4];
-#pragma unroll
-    for (int i = 0; i < 4; ++i) v[i] = (col + i < limit) ? rowp[col + i] : 0.0f;
-    return make_float4(v[0], v[1], v[2], v[3]);
+// All ones when ok, else zero, through an empty asm statement the optimiser
+// cannot see into, applied when the chunk is written to LDS: the load stays
+// an ordinary unconditional load whose wait comes only at that write.
+// (Zeroing by `ok ? v : 0` lets the optimiser recover the condition and turn
+// the load into a branch around it; the wait for such a load lands right
+// after it, at the branch's end, and the slice in flight no longer overlaps
+// the MFMAs.)
+__device__ __forceinline__ uint32_t keep_mask(bool ok) {
+    uint32_t m = ok ? 0xffffffffu : 0u;
+    asm("" : "+v"(m));
+    return m;
 }
+
+__device__ __forceinline__ float masked(float x, uint32_t m) {
+    return __uint_as_float(__float_as_uint(x) & m);
+}
+
+// A 16-byte chunk of 4 floats at [col, col+4) of one row, zero outside: the
+// raw load in v and, for the guarded forms, the mask(s) that zero what lies
+// outside (NMASK: one for the whole chunk, or one per float).  rowp is a row
+// that exists (a missing row is replaced by row 0 and row_ok is false); every
+// lane loads from an address inside the operand (column 0 of its row when
+// the chunk lies outside).  kVec with kGuard requires the limits (K, and M or
+// N) to be multiples of 4, so that a chunk is either wholly inside or wholly
+// outside; otherwise four 4-byte loads.
+template <bool kVec, bool kGuard>
+struct Chunk {
+    static constexpr int NMASK = kGuard && !kVec ? 4 : 1;
+    float4 v;
+    uint32_t m[NMASK];
+
+    __device__ __forceinline__ void load(const float* rowp, int col, int limit, bool row_ok) {
+        if (!kGuard) {
+            v = *reinterpret_cast<const float4*>(rowp + col);
+        } else if (kVec) {
+            const bool ok = row_ok && col < limit;
+            v = *reinterpret_cast<const float4*>(rowp + (ok ? col : 0));
+            m[0] = keep_mask(ok);
+        } else {
+            float x[4];
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const bool ok = row_ok && col + i < limit;
+                x[i] = rowp[ok ? col + i : 0];
+                m[i] = keep_mask(ok);
+            }
+            v = make_float4(x[0], x[1], x[2], x[3]);
+        }
+    }
+    __device__ __forceinline__ float4 value() const {
+        if (!kGuard) return v;
+        const uint32_t* mm = m;
+        return make_float4(masked(v.x, mm[0]), masked(v.y, mm[NMASK > 1 ? 1 : 0]),
+                           masked(v.z, mm[NMASK > 1 ? 2 : 0]), masked(v.w, mm[NMASK > 1 ? 3 : 0]));
+    }
+};
 
 // One operand's share of a K slice in LDS, for a T x T workgroup tile (T =
 // 128 or 64).  kKC (stored rows run along k: A untransposed, B transposed):
@@ -67,7 +112,7 @@ struct OpF32 {
     static constexpr int CH = T / 64;            // chunks per lane and slice
     static constexpr int TM = T / 64;            // 32 x 32 MFMA tiles per wave and dimension
     static constexpr int SIZE = kKC ? T * KC_PITCH : BK * MN_PITCH;  // floats per buffer
-    float4 r[CH];
+    Chunk<kVec, kGuard> r[CH];
 
     __device__ void load(const float* X, int64_t ld, int mn0, int mn_lim, int k0, int K,
                          int tid) {
@@ -77,11 +122,11 @@ struct OpF32 {
             if (kKC) {  // chunk f: mn-row f/4, k 4*(f%4)
                 const int row = mn0 + (f >> 2), col = k0 + 4 * (f & 3);
                 const bool ok = row < mn_lim;
-                r[c] = load4<kVec, kGuard>(X + (int64_t)(ok ? row : 0) * ld, col, K, ok);
+                r[c].load(X + (int64_t)(ok ? row : 0) * ld, col, K, ok);
             } else {    // chunk f: k-row f/(T/4), mn 4*(f%(T/4))
                 const int krow = k0 + f / (T / 4), col = mn0 + 4 * (f % (T / 4));
                 const bool ok = krow < K;
-                r[c] = load4<kVec, kGuard>(X + (int64_t)(ok ? krow : 0) * ld, col, mn_lim, ok);
+                r[c].load(X + (int64_t)(ok ? krow : 0) * ld, col, mn_lim, ok);
             }
         }
     }
@@ -91,7 +136,7 @@ struct OpF32 {
             const int f = tid + NT * c;
             float* d = kKC ? &dst[(f >> 2) * KC_PITCH + 4 * (f & 3)]
                            : &dst[(f / (T / 4)) * MN_PITCH + 4 * (f % (T / 4))];
-            *reinterpret_cast<float4*>(d) = r[c];
+            *reinterpret_cast<float4*>(d) = r[c].value();
         }
     }
     // The operand of MFMA tile t (rows / columns w*T/2 + t*32 + l%32) for
@@ -130,17 +175,6 @@ __global__ __launch_bounds__(NT, T == 64 ? 4 : 2) void mfma_f32_kernel(GemmParam
     const float* A = static_cast<const float*>(p.A);
     const float* B = static_cast<const float*>(p.B);
 
-    OpA ra;
-    OpB rb;
-    auto load_slice = [&](int k0) {
-        ra.load(A, p.lda, m0, p.M, k0, p.K, tid);
-        rb.load(B, p.ldb, n0, p.N, k0, p.K, tid);
-    };
-    auto store_slice = [&](int buf) {
-        ra.store(As[buf], tid);
-        rb.store(Bs[buf], tid);
-    };
-
     floatx16 acc[TM][TM];
 #pragma unroll
     for (int i = 0; i < TM; ++i)
@@ -149,16 +183,9 @@ __global__ __launch_bounds__(NT, T == 64 ? 4 : 2) void mfma_f32_kernel(GemmParam
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    const int nk = (p.K + BK - 1) / BK;
-    load_slice(0);
-    store_slice(0);
-    __syncthreads();
-    for (int t = 0; t < nk; ++t) {
-        const int buf = t & 1;
-        if (t + 1 < nk) load_slice((t + 1) * BK);
-
-        // Operands: A rows wm*64 + ti*32 + r32, B columns wn*64 + tj*32 + r32,
-        // k = 8h .. 8h+7 of the slice.
+    // One slice's MFMAs from LDS buffer buf.  Operands: A rows
+    // wm*T/2 + ti*32 + r32, B columns wn*T/2 + tj*32 + r32, k = 8h .. 8h+7.
+    auto compute = [&](const OpA& ra, const OpB& rb, int buf) {
         float a[TM][8], b[TM][8];
         if constexpr (!TA) ra.read_all(As[buf], wm, h, r32, a);
         if constexpr (TB) rb.read_all(Bs[buf], wn, h, r32, b);
@@ -177,8 +204,52 @@ __global__ __launch_bounds__(NT, T == 64 ? 4 : 2) void mfma_f32_kernel(GemmParam
                     acc[ti][tj] = __builtin_amdgcn_mfma_f32_32x32x2f32(
                         aj[ti], bj[tj], acc[ti][tj], 0, 0, 0);
         }
-        if (t + 1 < nk) store_slice(buf ^ 1);
+    };
+
+    const int nk = (p.K + BK - 1) / BK;
+    {
+        // Two slices in flight (a 64-tile gives a CU little compute per
+        // slice to hide a global load behind): slice s lives in register
+        // set s % 2 from its load (at the start of iteration s - 2) until it
+        // is written to LDS buffer s % 2 (at the end of iteration s - 1).
+        // The loads and writes are unconditional (past the last slice a set
+        // reloads slice nk - 1 and is written to the buffer no iteration
+        // reads), so that every iteration issues the same loads and the
+        // wait before a write covers only the older set's loads.
+        OpA ra0, ra1;
+        OpB rb0, rb1;
+        auto load = [&](OpA& ra, OpB& rb, int s) {
+            s = min(s, nk - 1);
+            ra.load(A, p.lda, m0, p.M, s * BK, p.K, tid);
+            rb.load(B, p.ldb, n0, p.N, s * BK, p.K, tid);
+            __builtin_amdgcn_sched_barrier(0);  // issue the loads before the MFMAs
+        };
+        auto store = [&](const OpA& ra, const OpB& rb, int buf) {
+            // keeps the masking of a guarded chunk (which waits for its
+            // load) from being scheduled ahead of this point
+            __builtin_amdgcn_sched_barrier(0);
+            ra.store(As[buf], tid);
+            rb.store(Bs[buf], tid);
+        };
+        load(ra0, rb0, 0);
+        load(ra1, rb1, 1);
+        store(ra0, rb0, 0);
         __syncthreads();
+        // iteration t: load slice t+2 into set t%2 (free: slice t is in LDS),
+        // compute slice t, write slice t+1 to LDS buffer (t+1)%2
+        auto iter = [&](int t, OpA& ra_cur, OpB& rb_cur, const OpA& ra_next,
+                        const OpB& rb_next) {
+            load(ra_cur, rb_cur, t + 2);
+            compute(ra_cur, rb_cur, t & 1);
+            store(ra_next, rb_next, (t + 1) & 1);
+            __syncthreads();
+        };
+        int t = 0;
+        for (; t + 1 < nk; t += 2) {
+            iter(t, ra0, rb0, ra1, rb1);
+            iter(t + 1, ra1, rb1, ra0, rb0);
+        }
+        if (t < nk) iter(t, ra0, rb0, ra1, rb1);
     }
 
     // Accumulator layout of a 32x32 MFMA tile: register r of lane l holds
@@ -205,13 +276,15 @@ hipError_t launch_regs_tiles(const GemmParams& p, hipStream_t s) {
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
     const bool vec = operands_16b_aligned(p, 4);
     const bool full = vec && p.M % T == 0 && p.N % T == 0 && k_multiple(p, BK);
+    // guarded 16-byte chunks need every limit a multiple of 4 (see Chunk)
+    const bool vec_edge = vec && p.M % 4 == 0 && p.N % 4 == 0 && p.K % 4 == 0;
     const dim3 grid((unsigned)blocks, p.batch), block(NT);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (full)
             hipLaunchKernelGGL((mfma_f32_kernel<true, false, TA, TB, T>), grid, block, 0, s, p,
                                tiles_n);
-        else if (vec)
+        else if (vec_edge)
             hipLaunchKernelGGL((mfma_f32_kernel<true, true, TA, TB, T>), grid, block, 0, s, p,
                                tiles_n);
         else
