@@ -387,7 +387,7 @@ def time_calls(torch, launch, steps, warmup, settle_ms):
 
 
 def time_workload(torch, dgt, w, steps, warmup, copies=1, settle_ms=300.0, tel=None,
-                  pcie=False, telemetry_s=0.0):
+                  pcie=False, telemetry_s=0.0, keep_c=False):
     """Average and spread of one GEMM call's duration (ms) on the current stream."""
     import gemm_inputs as gi
     t0 = time.perf_counter()
@@ -414,9 +414,11 @@ def time_workload(torch, dgt, w, steps, warmup, copies=1, settle_ms=300.0, tel=N
     res["clock"] = telemetry_pass(torch, launch, tel, telemetry_s, res["ms_avg"])
     if pcie_res is not None:
         res["pcie"] = pcie_res
+    # the result of the last call (every call writes the same C when beta == 0)
+    c_host = dC.cpu().numpy().reshape(w.batch, w.M, w.N)[0] if keep_c and w.beta == 0 else None
     del dA, dB, dC, ws
     torch.cuda.empty_cache()
-    return res, (A, B, C0)
+    return res, (A, B, C0, c_host)
 
 
 def measure_pcie(torch, w, A, B, reps=3):
@@ -511,24 +513,38 @@ def cpu_model() -> str:
     return "unknown"
 
 
-def cpu_baseline(w, A, B, C0, target_s=12.0):
-    """The oracle as it stands, on a row sample sized for ~target_s seconds."""
+def cpu_baseline(w, A, B, C0, target_s=12.0, c_gpu=None):
+    """The oracle as it stands, on a row sample sized for ~target_s seconds.
+    With the GPU's C of the timed calls (c_gpu), the same oracle rows also
+    give the accuracy of the timed result: normwise and largest elementwise
+    error against the oracle's fp64 values, beside the gates the tests
+    apply."""
+    import numpy as np
     import oracle
     oracle.build(force=False)
     rows = 8
     while True:
         t0 = time.perf_counter()
-        oracle.gemm(A[:rows], B, None if C0 is None else C0[:rows], w.alpha, w.beta, w.dtype)
+        R = oracle.gemm(A[:rows], B, None if C0 is None else C0[:rows], w.alpha, w.beta, w.dtype)
         dt = time.perf_counter() - t0
         if dt >= target_s / 3 or rows >= w.M:
             break
         rows = min(w.M, max(rows * 2, int(rows * target_s / max(dt, 1e-3))))
     fl = gemm_flops(rows, w.N, w.K)
-    return {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
-            "cores": oracle.num_threads(), "kind": "oracle",
-            "sample": f"first {rows} of {w.M} rows of {w.name} "
-                      f"({rows}x{w.N}x{w.K}, {dt:.1f} s incl. fp64 widening of B)",
-            "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    out = {"value": round(fl / dt / 1e12, 6), "unit": "TFLOP/s",
+           "cores": oracle.num_threads(), "kind": "oracle",
+           "sample": f"first {rows} of {w.M} rows of {w.name} "
+                     f"({rows}x{w.N}x{w.K}, {dt:.1f} s incl. fp64 widening of B)",
+           "cpu_model": cpu_model(), "affinity_cpus": len(os.sched_getaffinity(0))}
+    if c_gpu is not None:
+        d = np.asarray(c_gpu[:rows], np.float64) - R
+        nref = float(np.linalg.norm(R))
+        out["accuracy"] = {
+            "rows": rows, "normwise_rel": float(np.linalg.norm(d)) / nref if nref else None,
+            "max_abs": float(np.max(np.abs(d))),
+            "gate_normwise": 1e-5,
+            "gate_max_abs": 1e-4 * math.sqrt(w.K) * max(1.0, abs(w.alpha)) * w.sigma * w.sigma}
+    return out
 
 
 def cpu_small_cases(names=("f32_256", "f32_1000_ragged")):
@@ -770,7 +786,8 @@ def main(argv=None):
             f"warmup {args.warmup}, steps {args.steps}")
         res, inputs = time_workload(torch, dgt, w, args.steps, args.warmup, copies,
                                     args.settle_ms, tel, pcie=(name == names[0]),
-                                    telemetry_s=args.telemetry_s)
+                                    telemetry_s=args.telemetry_s,
+                                    keep_c=(name == names[0] and not args.no_cpu))
         clk = (res.get("clock") or {}).get("gfxclk_mhz")
         res["roofline"] = roofline(w, res["ms_avg"], clk)
         res["tflops"] = gemm_flops(w.M, w.N, w.K) * w.batch / (res["ms_avg"] * 1e-3) / 1e12
@@ -779,11 +796,11 @@ def main(argv=None):
         results[name] = (w, res, inputs if name == names[0] else None)
 
     head = names[0]
-    w, res, (A, B, C0) = results[head]
+    w, res, (A, B, C0, c_gpu) = results[head]
     cpu = None
     if not args.no_cpu:
         log("[cpu] timing the oracle on a row sample ...")
-        cpu = cpu_baseline(w, A, B, C0)
+        cpu = cpu_baseline(w, A, B, C0, c_gpu=c_gpu)
         log(f"[cpu] {cpu['value']:.4f} TFLOP/s on {cpu['cores']} threads")
         cpu["small_cases"] = cpu_small_cases()
 

@@ -76,3 +76,24 @@ def test_traffic_lines_parse_kernel_names_with_spaces(tmp_path, monkeypatch):
     assert bench.read_traffic("f32_4096") is None  # stale digest
     f.write_text(f"traffic workload={w} kernel={kern} src=ffff fetch_bytes=1000 write_bytes=24\n")
     assert bench.read_traffic(w) is None
+
+
+def test_cpu_baseline_reports_accuracy_of_a_result():
+    """The CPU-baseline leg times the oracle on a row sample and, given the
+    GPU's C, reports its error on those rows: zero-ish for the oracle's own
+    result rounded to fp32, and a planted error shows up in max_abs."""
+    import numpy as np
+
+    import gemm_inputs as gi
+    import oracle
+    w = gi.WORKLOADS["f32_256"].scaled(M=64, N=96, K=80)
+    A, B, C0 = gi.make_inputs(w)
+    exact = oracle.round_f32(oracle.gemm(A, B, C0, w.alpha, w.beta, w.dtype))
+    r = bench.cpu_baseline(w, A, B, C0, target_s=0.0, c_gpu=exact)
+    acc = r["accuracy"]
+    assert acc["rows"] >= 8 and acc["normwise_rel"] < 1e-7 and acc["max_abs"] < 1e-6
+    bad = exact.copy()
+    bad[3, 5] += 0.5
+    acc = bench.cpu_baseline(w, A, B, C0, target_s=0.0, c_gpu=bad)["accuracy"]
+    assert abs(acc["max_abs"] - 0.5) < 1e-3
+    assert acc["gate_max_abs"] == pytest.approx(1e-4 * np.sqrt(80))
