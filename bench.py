@@ -73,7 +73,7 @@ SECONDARY = ["f32_256", "f32_1000_ragged", "f32_4096", "f16_8192", "bf16_skinny_
              "bf16_8192_nt", "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
              "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt", "f32_1000_splitk",
              "bf16_splitk_1024x1024x16384", "bf16_skinny_shard_8x3584x8192",
-             "bf16_shard_8192x1024x8192", "bf16_streamk_6144x4096x8192"]
+             "bf16_shard_8192x1024x8192", "bf16_streamk_6144x4096x8192", "f32_streamk_3000"]
 
 # Kernel that dominates each workload's time, for the roofline: a readable
 # name, its source file, and a pattern for the name rocprofv3 prints (the
@@ -123,6 +123,9 @@ DOMINANT = {
     "bf16_streamk_6144x4096x8192": ("mfma16_streamk_kernel<BF16, NN> + fix-up (per call)",
                                     "k_mfma_bf16_dma.hip",
                                     r"mfma16_streamk_kernel<\(dgt::In\)1, false, false, false>"),
+    "f32_streamk_3000": ("mfma_f32_streamk_kernel<NN, ragged> + fix-up (per call)",
+                         "k_mfma_f32_dma.hip",
+                         r"mfma_f32_streamk_kernel<false, false, true>"),
 }
 
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "hbm_traffic.md")
@@ -170,13 +173,19 @@ def naive_load_requests(M: int, N: int, K: int, wave: int) -> int:
 
 def source_digest(fname: str) -> str:
     """Digest of the kernel sources a workload runs: one file, or several
-    joined by '+', with the headers they include."""
+    joined by '+', with the headers they include (followed transitively)."""
+    csrc = os.path.join(ROOT, "dense_gemm_tuning_amd", "csrc")
+    order, todo = [], list(fname.split("+"))
+    while todo:
+        f = todo.pop(0)
+        if f in order:
+            continue
+        order.append(f)
+        with open(os.path.join(csrc, f), "rb") as fh:
+            todo += [m.decode() for m in re.findall(rb'^#include "([^"]+)"', fh.read(), re.M)]
     h = hashlib.sha256()
-    files = fname.split("+")
-    extra = (("skinny_common.hpp",) if any(f.startswith("k_skinny") for f in files) else ()) + \
-        (("dma_common.hpp",) if any(f.endswith("_dma.hip") for f in files) else ())
-    for f in (*files, "gemm_common.hpp", *extra):
-        with open(os.path.join(ROOT, "dense_gemm_tuning_amd", "csrc", f), "rb") as fh:
+    for f in order:
+        with open(os.path.join(csrc, f), "rb") as fh:
             h.update(fh.read())
     return h.hexdigest()[:16]
 

@@ -352,10 +352,10 @@ int64_t gemm_streamk_workspace_size(int dtype, int M, int N, int K) {
     DType t;
     if (!dtype_of(dtype, t)) return GEMM_ERR_ARG;
     if (M < 0 || N < 0 || K < 0) return GEMM_ERR_DIM;
-    if (t == DType::F32 || M <= dgt::kSkinnyMaxM || N == 0 || K == 0) return 0;
+    if (M <= dgt::kSkinnyMaxM || N == 0 || K == 0) return 0;
     GemmParams p;
     p.M = M; p.N = N; p.K = K;
-    return dgt::streamk_workspace_bytes(p);
+    return dgt::streamk_workspace_bytes(p, t == DType::F32);
 }
 
 int gemm_streamk(int dtype, int trans_a, int trans_b, int M, int N, int K, float alpha,
@@ -377,12 +377,12 @@ int gemm_streamk(int dtype, int trans_a, int trans_b, int M, int N, int K, float
     p.bias = nullptr;
     p.batch = 1;
     // what stream-K does not cover runs as gemm_ex with the automatic choice
-    if (t == DType::F32 || M <= dgt::kSkinnyMaxM || !reads_ab || M == 0 || N == 0 ||
-        !dgt::mfma16_dma_eligible(p))
+    const bool dma = t == DType::F32 ? dgt::mfma_f32_dma_eligible(p) : dgt::mfma16_dma_eligible(p);
+    if (M <= dgt::kSkinnyMaxM || !reads_ab || M == 0 || N == 0 || !dma)
         return run1(t, trans_a, trans_b, GEMM_VARIANT_AUTO, M, N, K, alpha, A, lda, B, ldb,
                     beta, C, ldc, stream);
     if (C == nullptr || A == nullptr || B == nullptr) return GEMM_ERR_NULL;
-    const int64_t ws_need = dgt::streamk_workspace_bytes(p);
+    const int64_t ws_need = dgt::streamk_workspace_bytes(p, t == DType::F32);
     if (workspace == nullptr || workspace_bytes < ws_need ||
         reinterpret_cast<uintptr_t>(workspace) % 16 != 0)
         return GEMM_ERR_WORKSPACE;
@@ -396,9 +396,10 @@ int gemm_streamk(int dtype, int trans_a, int trans_b, int M, int N, int K, float
         overlaps(rw, rb))
         return GEMM_ERR_OVERLAP;
     hipStream_t s = static_cast<hipStream_t>(stream);
-    const hipError_t e =
-        t == DType::BF16 ? dgt::launch_mfma16_streamk<dgt::In::BF16>(p, static_cast<float*>(workspace), s)
-                         : dgt::launch_mfma16_streamk<dgt::In::F16>(p, static_cast<float*>(workspace), s);
+    float* ws = static_cast<float*>(workspace);
+    const hipError_t e = t == DType::F32    ? dgt::launch_mfma_f32_streamk(p, ws, s)
+                         : t == DType::BF16 ? dgt::launch_mfma16_streamk<dgt::In::BF16>(p, ws, s)
+                                            : dgt::launch_mfma16_streamk<dgt::In::F16>(p, ws, s);
     if (e == hipErrorInvalidConfiguration) return GEMM_ERR_VARIANT;
     return e == hipSuccess ? GEMM_OK : GEMM_ERR_LAUNCH;
 }

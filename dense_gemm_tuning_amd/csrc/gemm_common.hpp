@@ -181,9 +181,10 @@ bool mfma16_dma_eligible(const GemmParams& p);
 template <In T> hipError_t launch_mfma16_dma(const GemmParams& p, hipStream_t s);
 template <In T> hipError_t launch_mfma16_dma_tile(const GemmParams& p, hipStream_t s, int tile);
 // Stream-K on 256 x 256 tiles (one problem, DMA-eligible operands) into a
-// workspace of streamk_workspace_bytes(p).
-int64_t streamk_workspace_bytes(const GemmParams& p);
+// workspace of streamk_workspace_bytes(p, f32) bytes.
+int64_t streamk_workspace_bytes(const GemmParams& p, bool f32);
 template <In T> hipError_t launch_mfma16_streamk(const GemmParams& p, float* ws, hipStream_t s);
+hipError_t launch_mfma_f32_streamk(const GemmParams& p, float* ws, hipStream_t s);
 hipError_t launch_skinny_f32(const GemmParams& p, hipStream_t s);
 hipError_t launch_splitk_reduce(const float* W, int splits, int M, int N, float alpha,
                                 float beta, float* C, int64_t ldc, hipStream_t s);

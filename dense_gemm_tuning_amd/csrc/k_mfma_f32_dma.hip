@@ -43,6 +43,7 @@
 // the k-contiguous fragments are masked past K, and m/n-contiguous rows past
 // K read as zeros through the descriptor range.
 #include "dma_common.hpp"
+#include "streamk.hpp"
 
 namespace dgt {
 
@@ -232,13 +233,12 @@ struct MnOperand {
 // not a multiple of 64 (a last group of 1 to 4 slices after the loop, the
 // last slice possibly partial).
 // R: workgroup tile R x R (256: one workgroup per CU; 128: two).
+// One R x R output tile at (m0, n0) over k = 0 .. p.K-1 of p's operands:
+// the body of mfma_f32_dma_kernel, shared with the stream-K kernel.  raw ==
+// nullptr: the BLAS epilogue into p.C; otherwise the bare fp32 sums go to
+// raw (R x R, row pitch R, every element written; a stream-K partial tile).
 template <int R, bool TA, bool TB, bool kEdge, bool kTail>
-__global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(GemmParams p,
-                                                                          int tiles_m,
-                                                                          int tiles_n,
-                                                                          int grouped) {
-    const TileIdx tile = xcd_tile(tiles_m, tiles_n, grouped != 0);
-    select_problem(p, tile.z);
+__device__ __forceinline__ void f32_tile(const GemmParams& p, int m0, int n0, float* raw) {
     constexpr bool AK = !TA, BKc = TB;
     constexpr int TM = Geo<R>::TM;
     using OpA = typename std::conditional<AK, KcOperand<R>, MnOperand<R>>::type;
@@ -260,8 +260,6 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(Gemm
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int wm = wave >> 1, wn = wave & 1, h = lane >> 5;
-    const int m0 = tile.bm * R;
-    const int n0 = tile.bn * R;
     const int nk = (p.K + BK - 1) / BK;  // slices (the last one partial when K % 16 != 0)
 
     OpA opa;
@@ -411,6 +409,18 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(Gemm
     // afresh here rather than kept live through the K loop.
     const int el = __builtin_amdgcn_mbcnt_hi(~0u, __builtin_amdgcn_mbcnt_lo(~0u, 0u));
     const int eh = el >> 5;
+    if (raw) {
+        // stream-K partial: every element of the R x R tile, no epilogue
+        float* rbase = raw + (int64_t)(wm * (R / 2) + 4 * eh) * R + wn * (R / 2) + (el & 31);
+#pragma unroll
+        for (int ti = 0; ti < TM; ++ti)
+#pragma unroll
+            for (int tj = 0; tj < TM; ++tj)
+#pragma unroll
+                for (int r = 0; r < 16; ++r)
+                    rbase[(ti * 32 + 8 * (r >> 2) + (r & 3)) * R + tj * 32] = acc[ti][tj][r];
+        return;
+    }
     const int col0 = n0 + wn * (R / 2) + (el & 31);
     float* cbase = p.C + (int64_t)(m0 + wm * (R / 2) + 4 * eh) * p.ldc + col0;
     const float alpha = p.alpha, beta = p.beta;
@@ -453,7 +463,49 @@ __global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(Gemm
     }
 }
 
+template <int R, bool TA, bool TB, bool kEdge, bool kTail>
+__global__ __launch_bounds__(NT, R == 256 ? 1 : 2) void mfma_f32_dma_kernel(GemmParams p,
+                                                                          int tiles_m,
+                                                                          int tiles_n,
+                                                                          int grouped) {
+    const TileIdx tile = xcd_tile(tiles_m, tiles_n, grouped != 0);
+    select_problem(p, tile.z);
+    f32_tile<R, TA, TB, kEdge, kTail>(p, tile.bm * R, tile.bn * R, nullptr);
+}
+
+// Stream-K (streamk.hpp) on 256 x 256 tiles; an iteration is a group of
+// four 16-deep slices.
+static_assert(streamk::kIterKF32 == BK * NSTAGE, "a stream-K iteration is one group of four slices");
+
+template <bool TA, bool TB, bool kRagged>
+__global__ __launch_bounds__(NT, 1) void mfma_f32_streamk_kernel(GemmParams p, streamk::StreamK sk,
+                                                                 float* ws) {
+    streamk::walk<TA, TB, 4>(p, sk, ws, [&](const GemmParams& q, int m0, int n0, float* raw) {
+        f32_tile<streamk::R, TA, TB, kRagged, kRagged>(q, m0, n0, raw);
+    });
+}
+
 }  // namespace
+
+hipError_t launch_mfma_f32_streamk(const GemmParams& p, float* ws, hipStream_t s) {
+    if (p.batch != 1 || p.k_last > 0 || !mfma_f32_dma_eligible(p))
+        return hipErrorInvalidConfiguration;
+    const streamk::StreamK sk = streamk::plan(p, streamk::kIterKF32);
+    if (sk.T > 0x7fffffff) return hipErrorInvalidConfiguration;
+    const bool ragged = p.M % 256 != 0 || p.N % 256 != 0 || p.K % streamk::kIterKF32 != 0;
+    hipError_t e = with_layout(p, [&](auto ta, auto tb) {
+        constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
+        if (ragged)
+            hipLaunchKernelGGL((mfma_f32_streamk_kernel<TA, TB, true>), dim3(sk.G), dim3(NT), 0, s,
+                               p, sk, ws);
+        else
+            hipLaunchKernelGGL((mfma_f32_streamk_kernel<TA, TB, false>), dim3(sk.G), dim3(NT), 0, s,
+                               p, sk, ws);
+        return hipGetLastError();
+    });
+    if (e != hipSuccess) return e;
+    return streamk::launch_fixup(p, sk, ws, s);
+}
 
 // Aligned rows and pitches within the buffer offsets: every other shape
 // takes the register-staged 128 x 128 kernel.

@@ -243,6 +243,11 @@ WORKLOADS = {
     "bf16_streamk_6144x4096x8192": Workload("bf16_streamk_6144x4096x8192", "bf16", 6144, 4096,
                                             8192, 1.0, 0.0, "normal", seed_base=17000,
                                             streamk=True),
+    # FP32 3000^3: 144 tiles of 256 x 256 fill 144 of the 256 CUs and 576
+    # tiles of 128 x 128 take two waves of 512 slots, the second an eighth
+    # full; stream-K deals the 64-deep K iterations out evenly.
+    "f32_streamk_3000": Workload("f32_streamk_3000", "f32", 3000, 3000, 3000, 1.0, 0.0,
+                                 "uniform", seed_base=18000, streamk=True),
 }
 
 

@@ -66,7 +66,7 @@
 extern "C" {
 #endif
 
-#define DGT_GEMM_ABI_VERSION 8
+#define DGT_GEMM_ABI_VERSION 9
 
 /* Input formats (the dtype argument of gemm_ex and gemm_select_variant). */
 enum gemm_dtype { GEMM_DTYPE_F32 = 0, GEMM_DTYPE_BF16 = 1, GEMM_DTYPE_F16 = 2 };
@@ -273,16 +273,16 @@ int64_t gemm_splitk_workspace_size(int dtype, int M, int N, int K, int splits);
  * data-parallel launch then runs on part of the chip).  The pages note that
  * a launch whose blocks are partly idle leaves compute unused
  * (elainafan.one "朴素 CUDA 实现", after the launch code); stream-K deals out
- * the tiles' K iterations (32 k each) in equal contiguous ranges to one
- * workgroup per compute unit instead of whole tiles.  A tile covered by one
- * workgroup is written directly; the parts of a tile split between
- * workgroups go to the caller's `workspace` as fp32 partial sums, and a
- * second kernel queued on `stream` sums them in k order and applies alpha,
- * beta -- deterministic, no atomics, nothing allocated.
- * Covered: BF16 / FP16 inputs, M > 64, operands whose stored rows are
- * 16-byte aligned with pitches below 2^24 elements.  Anything else (FP32,
- * M <= 64, unaligned operands, alpha == 0 or K == 0) runs as gemm_ex with
- * GEMM_VARIANT_AUTO and needs no workspace.  The workspace (device memory,
+ * the tiles' K iterations (128 k each for 16-bit inputs, 64 k for FP32) in
+ * equal contiguous ranges to one workgroup per compute unit instead of whole
+ * tiles.  A tile covered by one workgroup is written directly; the parts of
+ * a tile split between workgroups go to the caller's `workspace` as fp32
+ * partial sums, and a second kernel queued on `stream` sums them in k order
+ * and applies alpha, beta -- deterministic, no atomics, nothing allocated.
+ * Covered: FP32, BF16 and FP16 inputs, M > 64, operands whose stored rows
+ * are 16-byte aligned with pitches below 2^24 elements (2^23 for FP32).
+ * Anything else (M <= 64, unaligned operands, alpha == 0 or K == 0) runs as
+ * gemm_ex with GEMM_VARIANT_AUTO and needs no workspace.  The workspace (device memory,
  * 16-byte aligned, at least gemm_streamk_workspace_size bytes: two
  * 256 x 256 fp32 tiles per workgroup, 128 MiB at most) must not overlap A, B
  * or C and must stay untouched until the work on `stream` has finished; its

@@ -39,7 +39,7 @@ def test_every_declared_symbol_is_exported(lib):
 
 
 def test_abi_version_and_status_strings(lib):
-    assert dgt.gemm_abi_version() == 8
+    assert dgt.gemm_abi_version() == 9
     for code in range(0, -10, -1):
         s = dgt.gemm_status_string(code)
         assert s.startswith("GEMM_")
@@ -322,7 +322,10 @@ def test_streamk_argument_checks(lib):
     # 4 tiles x 2 iterations: 8 workgroups; 32 x 32 tiles x 64: 256 (the CUs)
     assert dgt.gemm_streamk_workspace_size(1, 512, 512, 256) == 2 * 8 * 256 * 256 * 4
     assert dgt.gemm_streamk_workspace_size(1, 8192, 8192, 8192) == 2 * 256 * 256 * 256 * 4
-    assert dgt.gemm_streamk_workspace_size(0, M, N, K) == 0      # FP32: runs as gemm_ex
+    # FP32: iterations of 64 k (16 tiles x 16 = 256 workgroups); 4 tiles x 4
+    assert dgt.gemm_streamk_workspace_size(0, M, N, K) == 2 * 256 * 256 * 256 * 4
+    assert dgt.gemm_streamk_workspace_size(0, 512, 512, 256) == 2 * 16 * 256 * 256 * 4
+    assert dgt.gemm_streamk_workspace_size(0, 64, N, K) == 0     # skinny
     assert dgt.gemm_streamk_workspace_size(1, 64, N, K) == 0     # skinny
     assert dgt.gemm_streamk_workspace_size(1, M, N, 0) == 0
     assert dgt.gemm_streamk_workspace_size(3, M, N, K) == dgt.GEMM_ERR_ARG
@@ -347,3 +350,9 @@ def test_streamk_argument_checks(lib):
     assert call(ws=B - 1024) == dgt.GEMM_ERR_OVERLAP          # ... or B
     assert call(C=A + 64) == dgt.GEMM_ERR_OVERLAP             # C overlaps A
     assert call(M=0, A=0, B=0, C=0) == dgt.GEMM_OK            # empty C: nothing to do
+    # FP32 takes stream-K too (4-byte elements: A and B 4 MiB each, the
+    # workspace 128 MiB), so it needs the workspace
+    need32 = dgt.gemm_streamk_workspace_size(0, M, N, K)
+    assert call(dtype=0, ws=0, wsb=need32) == dgt.GEMM_ERR_WORKSPACE
+    assert call(dtype=0, wsb=need32 - 16) == dgt.GEMM_ERR_WORKSPACE
+    assert call(dtype=0, wsb=need32, ws=C + 64) == dgt.GEMM_ERR_OVERLAP

@@ -1,17 +1,18 @@
 """GPU parity for stream-K (gemm_streamk) against the CPU oracle, through
 the C ABI.
 
-The K iterations (32 k each) of all 256 x 256 tiles are dealt out in equal
-contiguous ranges to one workgroup per CU; a tile covered by one workgroup
-is written directly, the parts of a split tile go to the workspace and a
-second kernel sums them in k order.  Covered: integer inputs bit-exact for
-every stored layout on shapes where every tile is split into many parts
-(fewer iterations than workgroups), where ranges span one and a half tiles,
-with edge tiles and a partial last slice, and with alpha / beta; real inputs
-within the gates; run-to-run determinism; beta == 0 never reading a
-NaN-filled C; a padded C inside a canary band (the fix-up kernel writes only
-C); the calls stream-K does not cover (FP32, M <= 64, unaligned rows), which
-run as gemm_ex and need no workspace; a short workspace refused.
+The K iterations (128 k each for 16-bit inputs, 64 k for FP32) of all
+256 x 256 tiles are dealt out in equal contiguous ranges to one workgroup per
+CU; a tile covered by one workgroup is written directly, the parts of a split
+tile go to the workspace and a second kernel sums them in k order.  Covered,
+for FP32, BF16 and FP16: integer inputs bit-exact for every stored layout on
+shapes where every tile is split into many parts (fewer iterations than
+workgroups), where ranges span one and a half tiles, with edge tiles and a
+partial last slice, and with alpha / beta; real inputs within the gates;
+run-to-run determinism; beta == 0 never reading a NaN-filled C; a padded C
+inside a canary band (the fix-up kernel writes only C); the calls stream-K
+does not cover (M <= 64, unaligned rows), which run as gemm_ex; a short
+workspace refused.
 """
 
 import numpy as np
@@ -62,16 +63,17 @@ def run_streamk(dtype, A, B, C0, M, N, K, alpha, beta, ta=False, tb=False, ws_by
     return st, dC.cpu().numpy(), need
 
 
-# (M, N, K): 6 tiles x 32 slices < 256 workgroups (every tile in 32 parts);
-# 25 tiles x 64 slices (6.25 slices a workgroup); 384 tiles x 32 slices (one
-# and a half tiles a workgroup); edge tiles with K = 1000 (31 whole slices
-# and 8 k); edge tiles with K a multiple of 32 but not of 128
+# (M, N, K), with 16-bit / FP32 iterations: 6 tiles x 8 / 16 iterations <
+# 256 workgroups (every tile in several parts); 25 tiles x 16 / 32 (1.6 / 3.1
+# iterations a workgroup); 384 tiles x 8 / 16 (one and a half tiles a
+# workgroup); edge tiles with K = 1000 (a partial last slice); edge tiles with
+# K = 1120, a multiple of the slice but not of the iteration
 SHAPES = [(512, 768, 1024), (1280, 1280, 2048), (6144, 4096, 1024), (1000, 1000, 1000),
           (776, 1288, 1120)]
 
 
 @pytest.mark.parametrize("layout", list(LAYOUTS))
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_streamk_integer_bit_exact(dtype, layout):
     ta, tb = LAYOUTS[layout]
     for idx, (M, N, K) in enumerate(SHAPES):
@@ -90,7 +92,7 @@ def test_streamk_integer_bit_exact(dtype, layout):
             assert_bit_exact(C, R, f"stream-K {dtype}/{layout} {M}x{N}x{K} a={alpha} b={beta}")
 
 
-@pytest.mark.parametrize("dtype", ["bf16", "f16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 def test_streamk_real_inputs_and_determinism(dtype):
     M, N, K = 3072, 2560, 4096
     A = gi.draw(2430, M, K, "normal", dtype=dtype)
@@ -105,26 +107,27 @@ def test_streamk_real_inputs_and_determinism(dtype):
     assert_close(C1, R, K, 1.0, what=f"stream-K real {dtype}")
 
 
-def test_streamk_padded_c_guard_band():
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_streamk_padded_c_guard_band(dtype):
     M, N, K, pad = 600, 520, 768, 24
-    A = gi.draw(2440, M, K, "int", dtype="bf16")
-    B = gi.draw(2441, K, N, "int", dtype="bf16")
+    A = gi.draw(2440, M, K, "int", dtype=dtype)
+    B = gi.draw(2441, K, N, "int", dtype=dtype)
     C0 = gi.draw(2442, M, N, "int")
     ldc = N + pad
     canary = -777.0
     cbuf = torch.full((M * ldc + 64,), canary, device="cuda")
     dC = cbuf[:M * ldc].view(M, ldc)[:, :N]
     dC.copy_(torch.from_numpy(C0).cuda())
-    need = dgt.gemm_streamk_workspace_size(CODE["bf16"], M, N, K)
+    need = dgt.gemm_streamk_workspace_size(CODE[dtype], M, N, K)
     ws = torch.empty(need, dtype=torch.uint8, device="cuda")
-    dA, dB = to_dev(A, "bf16"), to_dev(B, "bf16")
-    st = dgt.gemm_streamk(CODE["bf16"], 0, 0, M, N, K, -2.0, dA.data_ptr(), K, dB.data_ptr(), N,
+    dA, dB = to_dev(A, dtype), to_dev(B, dtype)
+    st = dgt.gemm_streamk(CODE[dtype], 0, 0, M, N, K, -2.0, dA.data_ptr(), K, dB.data_ptr(), N,
                           1.0, dC.data_ptr(), ldc, ws.data_ptr(), need,
                           torch.cuda.current_stream().cuda_stream)
     torch.cuda.synchronize()
     assert st == 0, dgt.gemm_status_string(st)
-    R = oracle.round_f32(oracle.gemm(A, B, C0, -2.0, 1.0, "bf16"))
-    assert_bit_exact(dC.cpu().numpy(), R, "stream-K padded C")
+    R = oracle.round_f32(oracle.gemm(A, B, C0, -2.0, 1.0, dtype))
+    assert_bit_exact(dC.cpu().numpy(), R, f"stream-K padded C {dtype}")
     full = cbuf.cpu().numpy()
     mask = np.ones(full.shape, bool)
     mask[np.arange(M * ldc).reshape(M, ldc)[:, :N].ravel()] = False
@@ -132,13 +135,14 @@ def test_streamk_padded_c_guard_band():
 
 
 def test_streamk_uncovered_calls_run_as_gemm_ex():
-    """FP32 and M <= 64 need no workspace; rows that are not 16-byte aligned
-    (B's 260 bf16 = 520 bytes) leave the DMA kernel.  All three run as
+    """M <= 64 needs no workspace; rows that are not 16-byte aligned (B's
+    260 bf16 = 520 bytes, or 259 floats) leave the DMA kernels.  These run as
     gemm_ex and give the oracle's result."""
-    cases = [("f32", 300, 260, 512), ("bf16", 64, 512, 1024), ("bf16", 300, 260, 520)]
+    cases = [("bf16", 64, 512, 1024), ("f32", 48, 512, 1024), ("bf16", 300, 260, 520),
+             ("f32", 300, 259, 512)]
     for dtype, M, N, K in cases:
         need = dgt.gemm_streamk_workspace_size(CODE[dtype], M, N, K)
-        assert (need == 0) == (dtype == "f32" or M <= 64)
+        assert (need == 0) == (M <= 64)
         A = gi.draw(2450, M, K, "int", dtype=dtype)
         B = gi.draw(2451, K, N, "int", dtype=dtype)
         say(f"stream-K fallback {dtype} {M}x{N}x{K}")
