@@ -49,13 +49,38 @@ constexpr int CPR = BK / 8;  // 16-byte chunks per LDS row (8)
 
 __device__ __forceinline__ int swz(int r) { return (r ^ (r >> 3)) & 7; }
 
-// 8 bf16 at [col, col+8) of one row as a 16-byte chunk, zero outside.
+// 16 bytes from a 2-byte aligned address: one global_load_dwordx4 whatever
+// the row pitch (the GPU runs with unaligned memory access enabled; the
+// parity tests include pitches of a few elements past a 16-byte multiple).
+__device__ __forceinline__ uint4 load16(const uint16_t* src) {
+    uint4 v;
+    __builtin_memcpy(&v, src, 16);
+    return v;
+}
+
+// All ones when ok, else zero, through an empty asm statement the optimiser
+// cannot see into, applied when the chunk is written to LDS: the load stays
+// an ordinary unconditional load whose wait comes only at that write
+// (zeroing by a select lets the optimiser turn the load into a branch
+// around it, and the wait for it then comes right after it).
+__device__ __forceinline__ uint32_t keep_mask(bool ok) {
+    uint32_t m = ok ? 0xffffffffu : 0u;
+    asm("" : "+v"(m));
+    return m;
+}
+
+__device__ __forceinline__ uint4 masked(const uint4& v, uint32_t m) {
+    return make_uint4(v.x & m, v.y & m, v.z & m, v.w & m);
+}
+
+// 8 elements at [col, col+8) of one row as a 16-byte chunk, zero outside,
+// element by element (the form for limits that are not multiples of 8).
 template <bool kVec, bool kGuard>
 __device__ __forceinline__ uint4 load8(const uint16_t* rowp, int col, int limit,
                                        bool row_ok) {
-    if (!kGuard) return *reinterpret_cast<const uint4*>(rowp + col);
+    if (!kGuard) return load16(rowp + col);
     if (!row_ok) return make_uint4(0, 0, 0, 0);
-    if (kVec && col + 8 <= limit) return *reinterpret_cast<const uint4*>(rowp + col);
+    if (kVec && col + 8 <= limit) return load16(rowp + col);
     uint32_t w[4];
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
@@ -93,9 +118,32 @@ __device__ __forceinline__ u32x4 as_u32x4(const uint4& v) {
 // is row (tid>>3) + 32*i, chunk tid&7, stored unchanged.  Otherwise (stored
 // rows run along m / n): the lane covers stored rows (k) 8*(tid>>5) .. +7
 // and columns (mn) 8*(tid&31) .. +7, transposed in registers on the store.
+//
+// kVec with kGuard (limits, K and M or N, multiples of 8: a chunk is wholly
+// inside or wholly outside): every lane loads its chunk unconditionally from
+// an address inside the operand (column 0 of its row when the chunk lies
+// outside) and the chunk is masked when written to LDS.  Without kVec the
+// chunks are gathered element by element (load8).
 template <bool kVec, bool kGuard, bool kKC>
 struct Op16 {
+    static constexpr bool kMasked = kVec && kGuard;
     uint4 r[8];
+    uint32_t m[kMasked ? 8 : 1];
+
+    __device__ __forceinline__ void load_chunk(int i, const uint16_t* rowp, int col, int limit,
+                                               bool row_ok) {
+        if constexpr (kMasked) {
+            const bool ok = row_ok && col < limit;
+            r[i] = load16(rowp + (ok ? col : 0));
+            m[i] = keep_mask(ok);
+        } else {
+            r[i] = load8<kVec, kGuard>(rowp, col, limit, row_ok);
+        }
+    }
+    __device__ __forceinline__ uint4 chunk(int i) const {
+        if constexpr (kMasked) return masked(r[i], m[i]);
+        else return r[i];
+    }
 
     // mn0: first m (or n) of the tile, mn_lim: M (or N).
     __device__ void load(const uint16_t* X, int64_t ld, int mn0, int mn_lim, int k0, int K,
@@ -106,7 +154,7 @@ struct Op16 {
             for (int i = 0; i < 8; ++i) {
                 const int row = mn0 + row0 + 32 * i;
                 const bool ok = row < mn_lim;
-                r[i] = load8<kVec, kGuard>(X + (int64_t)(ok ? row : 0) * ld, k0 + 8 * q, K, ok);
+                load_chunk(i, X + (int64_t)(ok ? row : 0) * ld, k0 + 8 * q, K, ok);
             }
         } else {
             const int c = tid & 31, g = tid >> 5;
@@ -114,8 +162,7 @@ struct Op16 {
             for (int i = 0; i < 8; ++i) {
                 const int krow = k0 + 8 * g + i;
                 const bool ok = krow < K;
-                r[i] = load8<kVec, kGuard>(X + (int64_t)(ok ? krow : 0) * ld, mn0 + 8 * c,
-                                           mn_lim, ok);
+                load_chunk(i, X + (int64_t)(ok ? krow : 0) * ld, mn0 + 8 * c, mn_lim, ok);
             }
         }
     }
@@ -125,14 +172,17 @@ struct Op16 {
 #pragma unroll
             for (int i = 0; i < 8; ++i) {
                 const int row = row0 + 32 * i;
-                dst[row * CPR + (q ^ swz(row))] = r[i];
+                dst[row * CPR + (q ^ swz(row))] = chunk(i);
             }
         } else {
             const int c = tid & 31, g = tid >> 5;
+            uint4 v[8];
+#pragma unroll
+            for (int i = 0; i < 8; ++i) v[i] = chunk(i);
 #pragma unroll
             for (int j = 0; j < 8; ++j) {
                 const int n = 8 * c + j;
-                dst[n * CPR + (g ^ swz(n))] = column8(r, j);
+                dst[n * CPR + (g ^ swz(n))] = column8(v, j);
             }
         }
     }
@@ -172,13 +222,19 @@ __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
+    // One slice in flight.  The load is unconditional (past the last slice
+    // it reloads slice nk - 1, written to the buffer no iteration reads) so
+    // that the wait before the LDS write covers just this load; scheduling
+    // barriers keep the loads ahead of the MFMAs and the masking and writes
+    // after them.
     const int nk = (p.K + BK - 1) / BK;
     load_slice(0);
     store_slice(0);
     __syncthreads();
     for (int t = 0; t < nk; ++t) {
         const int buf = t & 1;
-        if (t + 1 < nk) load_slice((t + 1) * BK);
+        load_slice(min(t + 1, nk - 1) * BK);
+        __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             // half-wave h supplies k = 16s + 8h .. +7 for both operands
@@ -200,7 +256,8 @@ __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n
                 for (int tj = 0; tj < 4; ++tj)
                     acc[ti][tj] = mfma32x32x16<T>(a[ti], b[tj], acc[ti][tj]);
         }
-        if (t + 1 < nk) store_slice(buf ^ 1);
+        __builtin_amdgcn_sched_barrier(0);
+        store_slice(buf ^ 1);
         __syncthreads();
     }
 
@@ -228,15 +285,20 @@ hipError_t launch_mfma16_regs(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + BN - 1) / BN;
     const int64_t blocks = (int64_t)((p.M + BM - 1) / BM) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = operands_16b_aligned(p, 2);
+    // 16-byte loads need 2-byte aligned operands (any pitch); guarded ones
+    // limits that are multiples of 8 (see Op16)
+    const bool vec = reinterpret_cast<uintptr_t>(p.A) % 2 == 0 &&
+                     reinterpret_cast<uintptr_t>(p.B) % 2 == 0 && p.stride_a % 2 == 0 &&
+                     p.stride_b % 2 == 0;
     const bool full = vec && p.M % BM == 0 && p.N % BN == 0 && k_multiple(p, BK);
+    const bool vec_edge = vec && p.M % 8 == 0 && p.N % 8 == 0 && p.K % 8 == 0;
     const dim3 grid((unsigned)blocks, p.batch), block(NT);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;
         if (full)
             hipLaunchKernelGGL((mfma16_kernel<T, true, false, TA, TB>), grid, block, 0, s, p,
                                tiles_n);
-        else if (vec)
+        else if (vec_edge)
             hipLaunchKernelGGL((mfma16_kernel<T, true, true, TA, TB>), grid, block, 0, s, p,
                                tiles_n);
         else

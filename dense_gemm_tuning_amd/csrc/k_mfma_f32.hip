@@ -60,6 +60,15 @@ __device__ __forceinline__ float masked(float x, uint32_t m) {
     return __uint_as_float(__float_as_uint(x) & m);
 }
 
+// 16 bytes from a 4-byte aligned address: one global_load_dwordx4 whatever
+// the row pitch (the GPU runs with unaligned memory access enabled; the
+// parity tests include pitches of a few floats past a 16-byte multiple).
+__device__ __forceinline__ float4 load16(const float* src) {
+    float4 v;
+    __builtin_memcpy(&v, src, 16);
+    return v;
+}
+
 // A 16-byte chunk of 4 floats at [col, col+4) of one row, zero outside: the
 // raw load in v and, for the guarded forms, the mask(s) that zero what lies
 // outside (NMASK: one for the whole chunk, or one per float).  rowp is a row
@@ -76,10 +85,10 @@ struct Chunk {
 
     __device__ __forceinline__ void load(const float* rowp, int col, int limit, bool row_ok) {
         if (!kGuard) {
-            v = *reinterpret_cast<const float4*>(rowp + col);
+            v = load16(rowp + col);
         } else if (kVec) {
             const bool ok = row_ok && col < limit;
-            v = *reinterpret_cast<const float4*>(rowp + (ok ? col : 0));
+            v = load16(rowp + (ok ? col : 0));
             m[0] = keep_mask(ok);
         } else {
             float x[4];
@@ -274,7 +283,10 @@ hipError_t launch_regs_tiles(const GemmParams& p, hipStream_t s) {
     const int tiles_n = (p.N + T - 1) / T;
     const int64_t blocks = (int64_t)((p.M + T - 1) / T) * tiles_n;
     if (blocks > 0x7fffffff) return hipErrorInvalidConfiguration;
-    const bool vec = operands_16b_aligned(p, 4);
+    // 16-byte loads need 4-byte aligned operands (any pitch)
+    const bool vec = reinterpret_cast<uintptr_t>(p.A) % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(p.B) % 4 == 0 && p.stride_a % 4 == 0 &&
+                     p.stride_b % 4 == 0;
     const bool full = vec && p.M % T == 0 && p.N % T == 0 && k_multiple(p, BK);
     // guarded 16-byte chunks need every limit a multiple of 4 (see Chunk)
     const bool vec_edge = vec && p.M % 4 == 0 && p.N % 4 == 0 && p.K % 4 == 0;
