@@ -76,9 +76,12 @@ __device__ __forceinline__ void store_block(float (*red)[16][COLS + 4], const fl
                                             const GemmParams& p, int n0, int m0, bool first) {
     if (!first) __syncthreads();  // the previous block's sums have been read
 #pragma unroll
-    for (int c = 0; c < 8; ++c)
+    for (int c = 0; c < 8; ++c) {
+        const int cc = col_of(c, i);
+        if (cc < 0) continue;  // a column of the previous strip
 #pragma unroll
-        for (int r = 0; r < 4; ++r) red[wave][4 * g + r][col_of(c, i)] = acc[c][r];
+        for (int r = 0; r < 4; ++r) red[wave][4 * g + r][cc] = acc[c][r];
+    }
     __syncthreads();
     reduce_rows<NW, NTH, COLS>(red, p, n0, m0);
 }
@@ -94,6 +97,14 @@ __global__ __launch_bounds__((waves_for<RB, TA>() * 64), 1) void skinny16_kernel
     const int g = lane >> 4, i = lane & 15;
     const int n0 = blockIdx.x * COLS;
     const int col = n0 + 8 * i;
+    // A lane whose 8 columns run past N (the last strip of a ragged N) reads
+    // the row's last 8 columns instead, with whole 16-byte loads: its
+    // results for the columns below col repeat a neighbour's bit for bit
+    // (same operands, same order) and go to the same places.  Element-wise
+    // loads there instead would hold that strip's waves, and the launch,
+    // back at every load.
+    const int bcol = (kVec && kGuard && p.N >= 8 && col + 8 > p.N) ? p.N - 8 : col;
+    const int sh = col - bcol;
     const uint16_t* B = static_cast<const uint16_t*>(p.B);
     const ARows<uint16_t, RB, TA> ar(static_cast<const uint16_t*>(p.A), p, i);
 
@@ -115,7 +126,7 @@ __global__ __launch_bounds__((waves_for<RB, TA>() * 64), 1) void skinny16_kernel
             const int krow = kb + r;
             const bool ok = krow < p.K;
             dst[r] = load16<uint16_t, kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
-                                                    col, p.N, ok);
+                                                    bcol, p.N, ok);
         }
     };
     auto load_a = [&](int step, u32x4 (&a)[RB]) {
@@ -166,8 +177,8 @@ __global__ __launch_bounds__((waves_for<RB, TA>() * 64), 1) void skinny16_kernel
         compute(a0, b0);
     }
 
-    // MFMA c holds column 8*(l%16) + c of the strip.
-    auto col_of = [](int c, int ii) { return 8 * ii + c; };
+    // MFMA c holds column 8*(l%16) + c of the strip (less the lane's shift).
+    auto col_of = [sh](int c, int ii) { return 8 * ii + c - sh; };
 #pragma unroll
     for (int rb = 0; rb < RB; ++rb)
         store_block<NW, NTH>(red, acc[rb], wave, g, i, col_of, p, n0, 16 * rb, rb == 0);
@@ -301,7 +312,10 @@ template <In T, int RB>
 hipError_t launch_rb(const GemmParams& p, hipStream_t s) {
     const int NTH = (p.tb ? bt_waves_for<RB>() : p.ta ? waves_for<RB, true>() : waves_for<RB, false>()) * 64;
     const int blocks = (p.N + COLS - 1) / COLS;
-    const bool vec = operands_16b_aligned(p, 2);
+    // 16-byte loads need element-aligned operands (any pitch)
+    const bool vec = reinterpret_cast<uintptr_t>(p.A) % 2 == 0 &&
+                     reinterpret_cast<uintptr_t>(p.B) % 2 == 0 && p.stride_a % 2 == 0 &&
+                     p.stride_b % 2 == 0;
     const int kstep = p.tb ? BT_KSTEP : KSTEP;
     const bool full = vec && p.N % COLS == 0 && k_multiple(p, kstep);
     return with_layout(p, [&](auto ta, auto tb) {

@@ -29,6 +29,11 @@ __global__ __launch_bounds__(NTH, 1) void skinny_f32_kernel(GemmParams p) {
     const int g = lane >> 4, i = lane & 15;
     const int n0 = blockIdx.x * COLS;
     const int col = n0 + 4 * i;
+    // B as K x N: a lane whose 4 columns run past N reads the row's last 4
+    // columns instead, as in the 16-bit kernel (its duplicate results go to
+    // the same places, bit for bit).
+    const int bcol = (!TB && kVec && kGuard && p.N >= 4 && col + 4 > p.N) ? p.N - 4 : col;
+    const int sh = col - bcol;
     const float* B = static_cast<const float*>(p.B);
     const ARows<float, RB, TA> ar(static_cast<const float*>(p.A), p, i);
 
@@ -56,7 +61,7 @@ __global__ __launch_bounds__(NTH, 1) void skinny_f32_kernel(GemmParams p) {
                 const int krow = kb + t;
                 const bool ok = krow < p.K;
                 dst[t] = load16<float, kVec, kGuard>(B + (int64_t)(ok ? krow : 0) * p.ldb,
-                                                     col, p.N, ok);
+                                                     bcol, p.N, ok);
             }
         }
     };
@@ -125,9 +130,12 @@ __global__ __launch_bounds__(NTH, 1) void skinny_f32_kernel(GemmParams p) {
     for (int rb = 0; rb < RB; ++rb) {
         if (rb > 0) __syncthreads();
 #pragma unroll
-        for (int c = 0; c < 4; ++c)
+        for (int c = 0; c < 4; ++c) {
+            const int cc = 4 * i + c - sh;
+            if (cc < 0) continue;  // a column of the previous strip
 #pragma unroll
-            for (int r = 0; r < 4; ++r) red[wave][4 * g + r][4 * i + c] = acc[rb][c][r];
+            for (int r = 0; r < 4; ++r) red[wave][4 * g + r][cc] = acc[rb][c][r];
+        }
         __syncthreads();
         reduce_rows<NW, NTH, COLS>(red, p, n0, 16 * rb);
     }
@@ -136,7 +144,10 @@ __global__ __launch_bounds__(NTH, 1) void skinny_f32_kernel(GemmParams p) {
 template <int RB>
 hipError_t launch_rb(const GemmParams& p, hipStream_t s) {
     const int blocks = (p.N + COLS - 1) / COLS;
-    const bool vec = operands_16b_aligned(p, 4);
+    // 16-byte loads need element-aligned operands (any pitch)
+    const bool vec = reinterpret_cast<uintptr_t>(p.A) % 4 == 0 &&
+                     reinterpret_cast<uintptr_t>(p.B) % 4 == 0 && p.stride_a % 4 == 0 &&
+                     p.stride_b % 4 == 0;
     const bool full = vec && p.N % COLS == 0 && k_multiple(p, KSTEP);
     return with_layout(p, [&](auto ta, auto tb) {
         constexpr bool TA = decltype(ta)::value, TB = decltype(tb)::value;

@@ -26,12 +26,24 @@ namespace skinny {
 
 constexpr int KSTEP = 32;
 
+// A 16-byte piece at an element-aligned address: loaded as one
+// global_load_dwordx4 whatever the row pitch (the GPU runs with unaligned
+// memory access enabled; the parity tests include pitches of a few elements
+// past a 16-byte multiple).
+typedef uint32_t u32x4_any __attribute__((ext_vector_type(4), aligned(2)));
+
 // 16-byte piece [col, col + 16/esz) of one row, zero outside; streamed.
+// kVec: 16-byte loads (element-aligned operands, any pitch); pieces that
+// straddle the limit, and every piece without kVec, are gathered element by
+// element.
 template <typename T, bool kVec, bool kGuard>
 __device__ __forceinline__ u32x4 load16(const T* rowp, int col, int limit, bool row_ok) {
     constexpr int V = 16 / sizeof(T);
-    if (!kGuard || (row_ok && kVec && col + V <= limit))
-        return __builtin_nontemporal_load(reinterpret_cast<const u32x4*>(rowp + col));
+    if (!kGuard || (row_ok && kVec && col + V <= limit)) {
+        const u32x4_any v =
+            __builtin_nontemporal_load(reinterpret_cast<const u32x4_any*>(rowp + col));
+        return u32x4{v[0], v[1], v[2], v[3]};
+    }
     u32x4 out = {0u, 0u, 0u, 0u};
     if (!row_ok) return out;
     if constexpr (sizeof(T) == 4) {
@@ -55,8 +67,10 @@ __device__ __forceinline__ u32x4 load16(const T* rowp, int col, int limit, bool 
 template <typename T, bool kVec, bool kGuard>
 __device__ __forceinline__ u32x4 load16_cached(const T* rowp, int col, int limit, bool row_ok) {
     constexpr int V = 16 / sizeof(T);
-    if (!kGuard || (row_ok && kVec && col + V <= limit))
-        return *reinterpret_cast<const u32x4*>(rowp + col);
+    if (!kGuard || (row_ok && kVec && col + V <= limit)) {
+        const u32x4_any v = *reinterpret_cast<const u32x4_any*>(rowp + col);
+        return u32x4{v[0], v[1], v[2], v[3]};
+    }
     return load16<T, kVec, true>(rowp, col, limit, row_ok);
 }
 

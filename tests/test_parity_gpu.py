@@ -77,6 +77,32 @@ def test_integer_inputs_bit_exact(variant, dtype):
             assert_bit_exact(C, R, f"{variant}/{dtype} {M}x{N}x{K} a={alpha} b={beta}")
 
 
+# Skinny rung, B stored K x N with a ragged N: the last strip's lanes that
+# run past N read the row's last whole piece and repeat a neighbour's
+# columns; N = 128 + 3 leaves a last strip narrower than one piece.  Packed
+# and padded (odd) pitches of B.
+SKINNY_RAGGED = [(8, 131, 256), (16, 1027, 512), (33, 255, 96), (64, 1000, 520), (8, 28671, 64)]
+
+
+@pytest.mark.parametrize("dtype", DTYPES)
+def test_skinny_ragged_columns_bit_exact(dtype):
+    for idx, (M, N, K) in enumerate(SKINNY_RAGGED):
+        for pad in (0, 1, 8):
+            say(f"skinny ragged {dtype} M={M} N={N} K={K} ldb=N+{pad}")
+            A = ints(700 + idx, M, K, dtype)
+            Bw = ints(710 + idx, K, N + pad, dtype)
+            C0 = gi.draw(720 + idx, M, N, "int")
+            dA = to_dev(A, dtype)
+            dB = to_dev(Bw, dtype)[:, :N]
+            dC = torch.from_numpy(C0).cuda()
+            st = dgt.gemm(dA, dB, dC, 1.5, 0.5, variant="skinny")
+            torch.cuda.synchronize()
+            assert st == 0, dgt.gemm_status_string(st)
+            R = oracle.round_f32(oracle.gemm(A, np.ascontiguousarray(Bw[:, :N]), C0, 1.5, 0.5,
+                                             dtype))
+            assert_bit_exact(dC.cpu().numpy(), R, f"skinny ragged {dtype} {M}x{N}x{K} +{pad}")
+
+
 @pytest.mark.parametrize("dtype", DTYPES)
 @pytest.mark.parametrize("variant", ["mfma", "lds", "skinny"])
 def test_permutation_and_rank1(variant, dtype):
