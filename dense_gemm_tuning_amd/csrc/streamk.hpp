@@ -5,11 +5,13 @@
 // For launches whose 256 x 256 tiles do not divide evenly among the CUs, a
 // data-parallel launch runs its last wave of tiles on part of the chip, and
 // splitting K in equal slices for every tile multiplies the partial sums.
-// Here the T tiles x I iterations of work (an iteration is one group of the
-// tile body's four K slices: 128 k for 16-bit inputs, 64 k for fp32) are cut
-// into G equal contiguous ranges, one per workgroup, G = min(256, T*I):
-// workgroup g owns iterations [start(g), start(g+1)), start(g) =
-// floor(g * T*I / G), and walks them tile by tile.  A tile it covers whole
+// Here G = min(256, tiles * I) workgroups (an iteration is one group of the
+// tile body's four K slices: 128 k for 16-bit inputs, 64 k for fp32, I per
+// tile) first run the whole waves of tiles data-parallel (tile j*G + g of
+// wave j to workgroup g: the dp first tiles), then deal out the T remaining
+// tiles' T*I iterations: cut into GS = min(G, T*I) equal contiguous ranges,
+// workgroup g < GS owns iterations [start(g), start(g+1)), start(g) =
+// floor(g * T*I / GS), and walks them tile by tile.  A tile it covers whole
 // gets the ordinary epilogue into C; a part of a tile goes, as bare fp32
 // sums, to workspace slot 2g (the first tile of its range) or 2g + 1 (the
 // last).  A second kernel then sums each split tile's parts in k order
@@ -18,7 +20,9 @@
 // sub-range of k (A and B offset by the part's first k); whole-tile
 // launches with K a multiple of the iteration keep the whole-tile instance
 // (every part is then whole groups of slices), others take the edge-tile /
-// K-tail one.
+// K-tail one.  The data-parallel waves keep the tiles a wave's workgroups
+// on one XCD hold at one time in step along k (as in the data-parallel
+// kernels), which the dealt-out ranges do not.
 #pragma once
 
 #include "dma_common.hpp"
@@ -34,15 +38,17 @@ constexpr int kIterK16 = 128;   // k per iteration, 16-bit inputs (four 32-deep 
 constexpr int kIterKF32 = 64;   // k per iteration, fp32 inputs (four 16-deep slices)
 
 struct StreamK {
-    int64_t T, I, W;  // tiles, iterations per tile, T*I
+    int64_t T, I, W;  // dealt-out tiles (after the first dp), iterations per tile, T*I
+    int64_t dp;       // tiles run whole, a multiple of G
     int G;            // workgroups
+    int GS;           // workgroups sharing the dealt-out iterations (<= G; 0 when W == 0)
     int tiles_m, tiles_n;
     int IK;           // k per iteration
-    __host__ __device__ int64_t start(int g) const { return g * W / G; }
-    // the workgroup owning iteration x
+    __host__ __device__ int64_t start(int g) const { return g * W / GS; }
+    // the workgroup owning dealt-out iteration x
     __host__ __device__ int owner(int64_t x) const {
-        int g = (int)((x * G) / W);
-        while (g + 1 < G && start(g + 1) <= x) ++g;
+        int g = (int)((x * GS) / W);
+        while (g + 1 < GS && start(g + 1) <= x) ++g;
         while (g > 0 && start(g) > x) --g;
         return g;
     }
@@ -57,23 +63,26 @@ struct StreamK {
         bm = first_m + (int)(in_group % gm);
         bn = (int)(in_group / gm);
     }
-    // workspace slot of workgroup g's part of tile t
+    // workspace slot of workgroup g's part of dealt-out tile t
     __host__ __device__ int slot(int g, int64_t t) const {
         return t == start(g) / I ? 2 * g : 2 * g + 1;
     }
     // true when some tile is split between workgroups (the fix-up has work)
-    __host__ bool split() const { return !(W % G == 0 && (W / G) % I == 0); }
+    __host__ bool split() const { return W > 0 && !(W % GS == 0 && (W / GS) % I == 0); }
 };
 
 inline StreamK plan(const GemmParams& p, int iter_k) {
     StreamK sk;
     sk.tiles_m = (p.M + R - 1) / R;
     sk.tiles_n = (p.N + R - 1) / R;
-    sk.T = (int64_t)sk.tiles_m * sk.tiles_n;
+    const int64_t tiles = (int64_t)sk.tiles_m * sk.tiles_n;
     sk.IK = iter_k;
     sk.I = (p.K + iter_k - 1) / iter_k;
+    sk.G = (int)(tiles * sk.I < kCUs ? tiles * sk.I : kCUs);
+    sk.dp = sk.G > 0 ? tiles / sk.G * sk.G : 0;
+    sk.T = tiles - sk.dp;
     sk.W = sk.T * sk.I;
-    sk.G = (int)(sk.W < kCUs ? sk.W : kCUs);
+    sk.GS = (int)(sk.W < sk.G ? sk.W : sk.G);
     return sk;
 }
 
@@ -89,35 +98,47 @@ inline int64_t workspace_bytes(const GemmParams& p, int iter_k) {
 template <bool TA, bool TB, int ESZ, class Tile>
 __device__ __forceinline__ void walk(const GemmParams& p, const StreamK& sk, float* ws,
                                      Tile&& tile) {
-    // consecutive ranges on one XCD (workgroups reach the 8 XCDs round-robin)
+    // consecutive tiles / ranges on one XCD (workgroups reach the 8 XCDs
+    // round-robin)
     const int per = sk.G / kXcds;
     const int b = blockIdx.x;
     const int g = (sk.G % kXcds == 0) ? (b % kXcds) * per + b / kXcds : b;
-    const int64_t end = sk.start(g + 1);
-    for (int64_t a = sk.start(g); a < end;) {
-        const int64_t t = a / sk.I;
-        const int64_t e = end < (t + 1) * sk.I ? end : (t + 1) * sk.I;
-        const int s0 = (int)(a - t * sk.I), s1 = (int)(e - t * sk.I);
-        int bm, bn;
-        sk.coords(t, bm, bn);
+    // whole tiles g, g + G, ... below dp, then the dealt-out range (one call
+    // site for the tile body, so that it is inlined once)
+    int64_t t = g;
+    int64_t a = g < sk.GS ? sk.start(g) : 0;
+    const int64_t end = g < sk.GS ? sk.start(g + 1) : 0;
+    while (t < sk.dp || a < end) {
         GemmParams q = p;
-        const int k0 = s0 * sk.IK;
-        q.K = (s1 * sk.IK < p.K ? s1 * sk.IK : p.K) - k0;
-        q.A = static_cast<const char*>(p.A) + (TA ? (int64_t)k0 * p.lda : (int64_t)k0) * ESZ;
-        q.B = static_cast<const char*>(p.B) + (TB ? (int64_t)k0 : (int64_t)k0 * p.ldb) * ESZ;
-        const bool whole = s0 == 0 && s1 == sk.I;
-        float* raw = whole ? nullptr : ws + (int64_t)sk.slot(g, t) * R * R;
-        dma::barrier();  // every wave is done with the previous part's LDS stages
+        int64_t tile_id;
+        float* raw = nullptr;
+        if (t < sk.dp) {
+            tile_id = t;
+            t += sk.G;
+        } else {
+            const int64_t u = a / sk.I;  // dealt-out tile
+            const int64_t e = end < (u + 1) * sk.I ? end : (u + 1) * sk.I;
+            const int s0 = (int)(a - u * sk.I), s1 = (int)(e - u * sk.I);
+            const int k0 = s0 * sk.IK;
+            q.K = (s1 * sk.IK < p.K ? s1 * sk.IK : p.K) - k0;
+            q.A = static_cast<const char*>(p.A) + (TA ? (int64_t)k0 * p.lda : (int64_t)k0) * ESZ;
+            q.B = static_cast<const char*>(p.B) + (TB ? (int64_t)k0 : (int64_t)k0 * p.ldb) * ESZ;
+            if (!(s0 == 0 && s1 == sk.I)) raw = ws + (int64_t)sk.slot(g, u) * R * R;
+            tile_id = sk.dp + u;
+            a = e;
+        }
+        int bm, bn;
+        sk.coords(tile_id, bm, bn);
+        dma::barrier();  // every wave is done with the previous tile's LDS stages
         tile(q, bm * R, bn * R, raw);
-        a = e;
     }
 }
 
 namespace {
 
-// C <- alpha * (sum of a split tile's parts, in k order) + beta * C: a tile
-// of 256 x 256 in kFixSplit workgroups of 256 threads, each thread 4
-// consecutive columns per row it takes (tiles covered whole by one
+// C <- alpha * (sum of a split tile's parts, in k order) + beta * C: a
+// dealt-out tile of 256 x 256 in kFixSplit workgroups of 256 threads, each
+// thread 4 consecutive columns per row it takes (tiles covered whole by one
 // workgroup return).  The parts' workspace offsets are worked out once per
 // workgroup, in LDS.
 __global__ __launch_bounds__(256) void streamk_fixup_kernel(GemmParams p, StreamK sk,
@@ -131,7 +152,7 @@ __global__ __launch_bounds__(256) void streamk_fixup_kernel(GemmParams p, Stream
         part[j] = (int64_t)sk.slot(g0 + j, t) * R * R;
     __syncthreads();
     int bm, bn;
-    sk.coords(t, bm, bn);
+    sk.coords(sk.dp + t, bm, bn);
     const int r = (int)(blockIdx.x % kFixSplit) * (R / kFixSplit) + threadIdx.x / 64;
     const int c = 4 * (threadIdx.x % 64);
     const bool vec = p.ldc % 4 == 0 && reinterpret_cast<uintptr_t>(p.C) % 16 == 0;
