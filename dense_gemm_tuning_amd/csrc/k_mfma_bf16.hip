@@ -222,19 +222,20 @@ __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n
 #pragma unroll
             for (int r = 0; r < 16; ++r) acc[i][j][r] = 0.0f;
 
-    // One slice in flight.  The load is unconditional (past the last slice
-    // it reloads slice nk - 1, written to the buffer no iteration reads) so
-    // that the wait before the LDS write covers just this load; scheduling
-    // barriers keep the loads ahead of the MFMAs and the masking and writes
-    // after them.
+    // One slice in flight.  With guards the load is unconditional (past the
+    // last slice it reloads slice nk - 1, written to the buffer no iteration
+    // reads), so that the wait before the LDS write covers just this load,
+    // and scheduling barriers keep the loads ahead of the MFMAs and the
+    // masking and writes after them; whole tiles keep the compiler's own
+    // schedule (measured faster for them).
     const int nk = (p.K + BK - 1) / BK;
     load_slice(0);
     store_slice(0);
     __syncthreads();
     for (int t = 0; t < nk; ++t) {
         const int buf = t & 1;
-        load_slice(min(t + 1, nk - 1) * BK);
-        __builtin_amdgcn_sched_barrier(0);
+        if (kGuard || t + 1 < nk) load_slice(min(t + 1, nk - 1) * BK);
+        if constexpr (kGuard) __builtin_amdgcn_sched_barrier(0);
 #pragma unroll
         for (int s = 0; s < BK / 16; ++s) {
             // half-wave h supplies k = 16s + 8h .. +7 for both operands
@@ -256,8 +257,8 @@ __global__ __launch_bounds__(NT, 1) void mfma16_kernel(GemmParams p, int tiles_n
                 for (int tj = 0; tj < 4; ++tj)
                     acc[ti][tj] = mfma32x32x16<T>(a[ti], b[tj], acc[ti][tj]);
         }
-        __builtin_amdgcn_sched_barrier(0);
-        store_slice(buf ^ 1);
+        if constexpr (kGuard) __builtin_amdgcn_sched_barrier(0);
+        if (kGuard || t + 1 < nk) store_slice(buf ^ 1);
         __syncthreads();
     }
 
