@@ -199,12 +199,24 @@ __global__ __launch_bounds__(NT, T == 64 ? 4 : 2) void mfma_f32_kernel(GemmParam
         if constexpr (!TA) ra.read_all(As[buf], wm, h, r32, a);
         if constexpr (TB) rb.read_all(Bs[buf], wn, h, r32, b);
 #pragma unroll
+        for (int j = 0; j < 8; ++j)
+#pragma unroll
+            for (int x = 0; x < TM; ++x) {
+                if constexpr (TA) a[x][j] = ra.read_one(As[buf], wm, h, r32, x, j);
+                if constexpr (!TB) b[x][j] = rb.read_one(Bs[buf], wn, h, r32, x, j);
+            }
+        // 64-tiles: every operand read before the MFMAs, so that the LDS
+        // round trips overlap (a wave's 8 MFMAs a slice leave little to hide
+        // them behind; measured 4-8% faster).  128-tiles keep the compiler's
+        // interleaving (measured 1.5% faster for them).
+        if constexpr (T == 64) __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
         for (int j = 0; j < 8; ++j) {
             float aj[TM], bj[TM];
 #pragma unroll
             for (int x = 0; x < TM; ++x) {
-                aj[x] = TA ? ra.read_one(As[buf], wm, h, r32, x, j) : a[x][j];
-                bj[x] = TB ? b[x][j] : rb.read_one(Bs[buf], wn, h, r32, x, j);
+                aj[x] = a[x][j];
+                bj[x] = b[x][j];
             }
 #pragma unroll
             for (int ti = 0; ti < TM; ++ti)
