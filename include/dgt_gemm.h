@@ -135,9 +135,14 @@ enum gemm_variant {
                                    LDS tiles filled through registers by
                                    128-bit loads, double-buffered
                                    (dilfish.github.io 5.4's double buffer),
-                                   MFMA micro-tiles; any alignment.  GEMM_VARIANT_MFMA
-                                   uses it only for operands whose rows are
-                                   not 16-byte aligned                        */
+                                   MFMA micro-tiles, workgroup tiles of
+                                   128 x 128 (fp32) or 256 x 256 (16-bit
+                                   inputs); any alignment.  GEMM_VARIANT_MFMA
+                                   uses this kernel for operands the DMA
+                                   kernels do not take (rows not 16-byte
+                                   aligned, pitches past their limits) and,
+                                   on 64 x 64 tiles, for the small fp32
+                                   launches                                   */
 };
 
 /* C <- alpha*A*B + beta*C, fp32 inputs, fp32 accumulate/output. */
@@ -286,7 +291,9 @@ int64_t gemm_splitk_workspace_size(int dtype, int M, int N, int K, int splits);
  * 16-byte aligned, at least gemm_streamk_workspace_size bytes: two
  * 256 x 256 fp32 tiles per workgroup, 128 MiB at most) must not overlap A, B
  * or C and must stay untouched until the work on `stream` has finished; its
- * contents on return are unspecified.  Errors as for gemm_splitk. */
+ * contents on return are unspecified.  Errors as for gemm_splitk.
+ * gemm_f32 / gemm_bf16 / gemm_f16 and GEMM_VARIANT_AUTO take no workspace
+ * and never split K; for the shapes above this call is the faster form. */
 int gemm_streamk(int dtype, int trans_a, int trans_b, int M, int N, int K,
                  float alpha, const void* A, int lda, const void* B, int ldb,
                  float beta, float* C, int ldc, void* workspace,
