@@ -27,10 +27,11 @@
 // LDS reads; any fixed assignment of k to steps is valid because every
 // product lands in the same sum.
 //
-// LDS layout: a k-contiguous operand has its row pitch padded to 20 floats
-// (so 8 lanes reading 16 bytes from 8 consecutive rows hit 8 distinct bank
-// groups), an m/n-contiguous one to 132 floats (the two half-wavefronts read
-// rows 8 apart and land on opposite halves of the 64 banks).  Ragged
+// LDS layout: a k-contiguous operand keeps 64-byte rows with its 16-byte
+// chunks XOR-swizzled by row (kc_chunk), so that neither its 128-bit writes
+// nor its 128-bit reads meet bank conflicts; an m/n-contiguous one has its
+// rows padded to T + 4 floats (the two half-wavefronts read rows 8 apart and
+// land on opposite halves of the 64 banks).  Ragged
 // shapes: zero-filled loads outside A and B and masked stores
 // (dilfish.github.io 5.7; elainafan.one masked tiled listing); the
 // specialisation for shapes that are multiples of the tile skips the checks.
@@ -41,7 +42,17 @@ namespace dgt {
 namespace {
 
 constexpr int BK = 16, NT = 256;
-constexpr int KC_PITCH = BK + 4;    // floats, rows along k
+constexpr int KC_PITCH = BK;        // floats, rows along k (unpadded, chunks swizzled)
+
+// Position of 16-byte chunk c (k 4c .. 4c+3) within k-contiguous row `row`
+// in LDS.  Sixteen lanes of a 128-bit access meet in the same bank cycle;
+// with 64-byte rows the swizzle spreads both access patterns over all 64
+// banks: a write of 4 rows x 4 chunks (row % 4 gives the bank quarter,
+// the chunk its position in it) and a read of one chunk from 16
+// consecutive rows (row % 4 the quarter, row / 4 % 4 the XOR).  A padded
+// pitch cannot serve both: 20 floats make the reads distinct but send rows
+// 0 and 3 of a write to the same banks.
+__device__ __forceinline__ int kc_chunk(int row, int c) { return c ^ ((row >> 2) & 3); }
 
 // All ones when ok, else zero, through an empty asm statement the optimiser
 // cannot see into, applied when the chunk is written to LDS: the load stays
@@ -111,8 +122,8 @@ struct Chunk {
 
 // One operand's share of a K slice in LDS, for a T x T workgroup tile (T =
 // 128 or 64).  kKC (stored rows run along k: A untransposed, B transposed):
-// T mn-rows of 16 k, row pitch 20 floats, and a lane reads its 8 k of one
-// row as two 128-bit reads.  Otherwise (stored rows run along m / n): 16
+// T mn-rows of 16 k, 64 bytes each with swizzled chunks (kc_chunk), and a
+// lane reads its 8 k of one row as two 128-bit reads.  Otherwise (stored rows run along m / n): 16
 // k-rows of T, pitch T + 4, and a lane reads one float per k.  Each lane
 // moves T/64 16-byte chunks per slice.
 template <bool kVec, bool kGuard, bool kKC, int T>
@@ -143,7 +154,7 @@ struct OpF32 {
 #pragma unroll
         for (int c = 0; c < CH; ++c) {
             const int f = tid + NT * c;
-            float* d = kKC ? &dst[(f >> 2) * KC_PITCH + 4 * (f & 3)]
+            float* d = kKC ? &dst[(f >> 2) * KC_PITCH + 4 * kc_chunk(f >> 2, f & 3)]
                            : &dst[(f / (T / 4)) * MN_PITCH + 4 * (f % (T / 4))];
             *reinterpret_cast<float4*>(d) = r[c].value();
         }
@@ -153,9 +164,12 @@ struct OpF32 {
     __device__ void read_all(const float* src, int w, int h, int r32, float (&v)[TM][8]) const {
 #pragma unroll
         for (int t = 0; t < TM; ++t) {
-            const float* a = &src[(w * (T / 2) + t * 32 + r32) * KC_PITCH + 8 * h];
-            *reinterpret_cast<float4*>(&v[t][0]) = *reinterpret_cast<const float4*>(a);
-            *reinterpret_cast<float4*>(&v[t][4]) = *reinterpret_cast<const float4*>(a + 4);
+            const int row = w * (T / 2) + t * 32 + r32;
+            const float* a = &src[row * KC_PITCH];
+            *reinterpret_cast<float4*>(&v[t][0]) =
+                *reinterpret_cast<const float4*>(a + 4 * kc_chunk(row, 2 * h));
+            *reinterpret_cast<float4*>(&v[t][4]) =
+                *reinterpret_cast<const float4*>(a + 4 * kc_chunk(row, 2 * h + 1));
         }
     }
     // ... otherwise one j at a time.
