@@ -21,7 +21,7 @@ K=8192 (against HBM bandwidth: its time is the time to stream B once,
 dilfish.github.io 5.1 GEMV row), the BF16 square and skinny cases with a
 linear layer's operand storage (B stored N x K, A stored K x M), that
 layer's forward with its bias fused, a strided batch of 16 x 2048^3, and the
-split-K and one-GPU-share shapes, plus:
+split-K, stream-K and one-GPU-share shapes, plus:
   * "roofline": the dominant kernel's algorithmic FLOP (or bytes) per launch
     over its measured launch time, against the published MI355X peak, and
     the same against the peak scaled to the engine clock the workload runs
