@@ -99,14 +99,14 @@ DOMINANT = {
                      r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
     "bf16_8192_tn": ("mfma16_dma_kernel<BF16, TN>", "k_mfma_bf16_dma.hip",
                      r"mfma16_dma_kernel<\(dgt::In\)1, 256, true, false, false, false>"),
-    "bf16_skinny_8x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 1 row block, 8 waves>",
-                                    "k_skinny16_dma.hip",
-                                    r"skinny16_bt_dma_kernel<\(dgt::In\)1, 1, 8, 2, 128, false>"),
+    "bf16_skinny_8x28672x8192_nt": ("skinny_bt_dma_kernel<BF16, 1 row block, 8 waves>",
+                                    "k_skinny_dma.hip",
+                                    r"skinny_bt_dma_kernel<\(dgt::In\)1, 1, 8, 2, 256, false>"),
     "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
                                  r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
-    "bf16_decode_64x28672x8192_nt": ("skinny16_bt_dma_kernel<BF16, 4 row blocks, 8 waves>",
-                                     "k_skinny16_dma.hip",
-                                     r"skinny16_bt_dma_kernel<\(dgt::In\)1, 4, 8, 4, 64, true>"),
+    "bf16_decode_64x28672x8192_nt": ("skinny_bt_dma_kernel<BF16, 4 row blocks, 8 waves>",
+                                     "k_skinny_dma.hip",
+                                     r"skinny_bt_dma_kernel<\(dgt::In\)1, 4, 8, 4, 128, true>"),
     "f32_1000_splitk": ("mfma_f32_dma_kernel<NN, 128-tiles, edge> x 4 K slices + reduce (per call)",
                         "k_mfma_f32_dma.hip+k_splitk.hip",
                         r"mfma_f32_dma_kernel<128, false, false, true, (?:false|true)>"),

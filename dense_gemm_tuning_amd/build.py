@@ -19,7 +19,7 @@ LIBDIR = os.path.join(HERE, "lib")
 LIBPATH = os.path.join(LIBDIR, "libdgt_gemm.so")
 
 SOURCES = ["gemm_api.cpp", "k_naive.hip", "k_lds.hip", "k_mfma_f32.hip", "k_mfma_f32_dma.hip",
-           "k_mfma_bf16.hip", "k_mfma_bf16_dma.hip", "k_skinny16.hip", "k_skinny16_dma.hip",
+           "k_mfma_bf16.hip", "k_mfma_bf16_dma.hip", "k_skinny16.hip", "k_skinny_dma.hip",
            "k_skinny_f32.hip",
            "k_splitk.hip"]
 

@@ -105,11 +105,16 @@ hipError_t dispatch(DType t, int variant, const GemmParams& p, bool reads_ab, hi
                    : t == DType::BF16 ? dgt::launch_mfma16<In::BF16>(p, s)
                                       : dgt::launch_mfma16<In::F16>(p, s);
         case GEMM_VARIANT_SKINNY:
-            if (t == DType::F32) return dgt::launch_skinny_f32(p, s);
             // B stored N x K with A stored M x K: B streamed through LDS by copies
-            if (dgt::skinny16_bt_dma_eligible(p))
-                return t == DType::BF16 ? dgt::launch_skinny16_bt_dma<In::BF16>(p, s)
-                                        : dgt::launch_skinny16_bt_dma<In::F16>(p, s);
+            if (t == DType::F32) {
+                if (dgt::skinny_bt_dma_eligible<In::F32>(p))
+                    return dgt::launch_skinny_bt_dma<In::F32>(p, s);
+                return dgt::launch_skinny_f32(p, s);
+            }
+            if (t == DType::BF16 ? dgt::skinny_bt_dma_eligible<In::BF16>(p)
+                                 : dgt::skinny_bt_dma_eligible<In::F16>(p))
+                return t == DType::BF16 ? dgt::launch_skinny_bt_dma<In::BF16>(p, s)
+                                        : dgt::launch_skinny_bt_dma<In::F16>(p, s);
             return t == DType::BF16 ? dgt::launch_skinny16<In::BF16>(p, s)
                                     : dgt::launch_skinny16<In::F16>(p, s);
         case GEMM_VARIANT_MFMA_REGS:

@@ -193,8 +193,8 @@ hipError_t launch_splitk_reduce(const float* W, int splits, int M, int N, float 
 constexpr int64_t kScratchBytes = int64_t(64) << 20;
 hipError_t splitk_scratch(void** ptr);
 template <In T> hipError_t launch_skinny16(const GemmParams& p, hipStream_t s);
-bool skinny16_bt_dma_eligible(const GemmParams& p);
-template <In T> hipError_t launch_skinny16_bt_dma(const GemmParams& p, hipStream_t s);
+template <In T> bool skinny_bt_dma_eligible(const GemmParams& p);
+template <In T> hipError_t launch_skinny_bt_dma(const GemmParams& p, hipStream_t s);
 
 // Largest M the skinny (decode) path accepts: four blocks of 16 rows.
 constexpr int kSkinnyMaxM = 64;

@@ -1,8 +1,16 @@
-// k_skinny16_dma.hip -- the bandwidth-bound path for a linear layer's
-// decode-shaped product: 16-bit inputs, M <= 64 rows of A stored M x K and
-// the weight B stored N x K (every column of op(B) a stored row, k
-// contiguous).  Same reasoning as the register-staged skinny kernels: the
-// time is the time to stream B once.
+// k_skinny_dma.hip -- the bandwidth-bound path for a linear layer's
+// decode-shaped product: M <= 64 rows of A stored M x K and the weight B
+// stored N x K (every column of op(B) a stored row, k contiguous), 16-bit
+// or fp32 inputs.  Same reasoning as the register-staged skinny kernels:
+// the time is the time to stream B once.
+//
+// The kernel works in bytes: a step covers a 256- or 128-byte piece of each
+// stored row (128 or 64 k of 16-bit inputs, 64 or 32 of fp32), and a lane's
+// 16-byte chunk of A meets the same 16 bytes of B in one 16x16x32 product
+// (16-bit) or four 16x16x4 ones (fp32).  With fp32 B the register-staged
+// kernel's loads touch 16 stored rows with 64 bytes each per instruction;
+// through this kernel the same B streams 1.5-2x faster (28672 x 8192
+// weights: M = 8 142.5 against 219.9 us, M = 64 277.9 against 554.3).
 //
 // B never passes through registers: each wave copies its groups of B
 // straight into LDS with buffer loads that write LDS (one 16-byte piece per
@@ -16,9 +24,9 @@
 // register-staged waves with one or two).  So the configuration per row
 // count is the one with the most waves that fits without spilling (a
 // kernel that spills is also held to fewer concurrent waves by its scratch):
-//   M <= 32: eight waves, 128-deep steps, two stages (one group in flight),
+//   M <= 32: eight waves, 256-byte steps, two stages (one group in flight),
 //            A for the next step loaded a step ahead into a second buffer;
-//   M <= 64: eight waves, 64-deep steps (4-KiB groups, half the A
+//   M <= 64: eight waves, 128-byte steps (4-KiB groups, half the A
 //            registers), four stages, and one A buffer reloaded after each
 //            step's last MFMAs: at four row blocks the 128 accumulator
 //            registers leave no room for a second (with it the kernel
@@ -40,8 +48,9 @@
 // Operands through buffer descriptors: a 16-byte piece past a descriptor's
 // range reads as zeros.  Each group has a descriptor that ends at its last
 // valid stored row (k = K - 1), so rows past N read zeros; pieces at k >= K
-// (K a multiple of 8, so a piece is all inside or all outside) get an
-// offset at the range end and read zeros too, as do rows of A past M.
+// (K a multiple of the elements in 16 bytes, so a piece is all inside or
+// all outside) get an offset at the range end and read zeros too, as do
+// rows of A past M.
 #include <algorithm>
 
 #include "skinny_common.hpp"
@@ -57,25 +66,43 @@ constexpr int COLS = 128;        // columns (stored rows of B) per workgroup
 constexpr int GR = 32;           // stored rows per group (four groups a step)
 constexpr int kBPolicy = 2;      // cache policy of the B copies: nt (streamed once)
 
-// Geometry of a step SK deep in k (128 or 64): a group is GR stored rows x
-// SK k, one piece of ROWB bytes per row, copied by INSTR instructions of RPI
-// rows each (LPR lanes per row).  In LDS chunk c of local row r sits at
+// Geometry of a step whose row pieces are ROWB bytes (256 or 128: 128 or
+// 64 k of 16-bit inputs, 64 or 32 of fp32): a group is GR stored rows x one
+// piece, copied by INSTR instructions of RPI rows each (LPR lanes per row).  In LDS chunk c of local row r sits at
 // position c ^ swz(r), so that the operand reads (16 rows, one chunk) touch
 // 16 distinct 16-byte bank groups: with 256-byte rows 16 positions per row
 // serve; with 128-byte rows two rows share a 256-byte bank line, so rows r
 // and r + 8 (same line half) must differ: the swizzle uses r / 2.
-template <int SK>
+template <int ROWB_>
 struct Geo {
-    static_assert(SK == 128 || SK == 64, "a row piece is 256 or 128 bytes");
-    static constexpr int ROWB = 2 * SK;
+    static_assert(ROWB_ == 256 || ROWB_ == 128, "a row piece is 256 or 128 bytes");
+    static constexpr int ROWB = ROWB_;
     static constexpr int STAGE = GR * ROWB;           // bytes of one group
     static constexpr int INSTR = STAGE / 1024;        // copy instructions per group
     static constexpr int RPI = 1024 / ROWB;           // rows per copy instruction
     static constexpr int LPR = ROWB / 16;             // lanes per row
-    static constexpr int U = SK / 32;                 // 32-deep MFMA k-slices per step
+    static constexpr int U = ROWB / 64;               // 64-byte MFMA k-slices per step
     static constexpr int RED_ROWS = STAGE / (COLS * 4);  // C rows per reduction pass
-    __device__ static int swz(int r) { return SK == 128 ? (r & 15) : ((r >> 1) & 7); }
+    __device__ static int swz(int r) { return ROWB == 256 ? (r & 15) : ((r >> 1) & 7); }
 };
+
+// The products of one 16-byte chunk of A and of B per lane (lane group g =
+// l/16 holding the chunk's k): one 16x16x32 instruction for 16-bit inputs;
+// four 16x16x4 ones for fp32, the j-th taking element j of each chunk, so
+// that k-slot g of product j is the chunk's element j (every k of the 64
+// bytes lands in the sum once, as with the 16-bit form).
+template <In T>
+__device__ __forceinline__ floatx4 mfma_chunk(u32x4 a, u32x4 b, floatx4 c) {
+    if constexpr (T == In::F32) {
+#pragma unroll
+        for (int j = 0; j < 4; ++j)
+            c = __builtin_amdgcn_mfma_f32_16x16x4f32(__uint_as_float(a[j]), __uint_as_float(b[j]),
+                                                     c, 0, 0, 0);
+        return c;
+    } else {
+        return mfma16x16x32<T>(a, b, c);
+    }
+}
 
 // One 16-byte piece per lane of B into LDS: lane l's bytes at base + voff
 // land at lds + 16*l.
@@ -88,11 +115,15 @@ __device__ __forceinline__ void copy_b(const void* base, uint32_t range, uint8_t
 
 // NW waves (one K-range each), a ring of NS stages per wave (NS divides the
 // four groups of a step, so group cp of any step uses stage cp % NS), steps
-// SK deep; kSingleA: one register buffer of A operands, reloaded after each
-// step's last MFMAs (else two, the next step's loaded one step ahead).
-template <In T, int RB, int NW, int NS, int SK, bool kSingleA>
-__global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams p, int cols) {
-    using G = Geo<SK>;
+// of ROWB bytes per row (SK elements); kSingleA: one register buffer of A
+// operands, reloaded after each step's last MFMAs (else two, the next
+// step's loaded one step ahead).
+template <In T, int RB, int NW, int NS, int ROWB, bool kSingleA>
+__global__ __launch_bounds__(NW * 64, 1) void skinny_bt_dma_kernel(GemmParams p, int cols) {
+    using G = Geo<ROWB>;
+    constexpr int ESZ = T == In::F32 ? 4 : 2;  // bytes per element
+    constexpr int EPC = 16 / ESZ;              // elements per 16-byte chunk
+    constexpr int SK = ROWB / ESZ;             // k per step
     static_assert(NS == 2 || NS == 4, "a step's four groups map onto the ring");
     constexpr int D = NS - 1;  // groups copied ahead of the one being read
     constexpr int STAGE = G::STAGE;
@@ -114,7 +145,7 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
     // past the strip read zeros through the group descriptors.
     const int n0 = blockIdx.x * cols;
     const int nlim = min(n0 + cols, p.N);
-    const int64_t ldb2 = p.ldb * 2, lda2 = p.lda * 2;
+    const int64_t ldb2 = p.ldb * ESZ, lda2 = p.lda * ESZ;  // bytes
 
     // Group cp of a step: stored rows n0 + 32cp .. +31; its descriptor ends
     // at the last valid row's k = K - 1 (range 0 when no row is valid).
@@ -125,7 +156,7 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
         const int row0 = n0 + GR * cp;
         const int rows = min(GR, nlim - row0);
         gbase[cp] = static_cast<const uint8_t*>(p.B) + (int64_t)row0 * ldb2;
-        grange[cp] = rows <= 0 ? 0u : (uint32_t)((int64_t)(rows - 1) * ldb2 + 2 * (int64_t)p.K);
+        grange[cp] = rows <= 0 ? 0u : (uint32_t)((int64_t)(rows - 1) * ldb2 + ESZ * (int64_t)p.K);
     }
     // Instruction j of a group fills local rows RPI*j .. +RPI-1; lane l
     // writes row lr = RPI*j + l/LPR at position l%LPR, so it fetches chunk
@@ -137,12 +168,12 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
         const int lr = G::RPI * j + lane / G::LPR;
         const int c = (lane % G::LPR) ^ G::swz(lr);
         vrow[j] = (uint32_t)(lr * ldb2 + 16 * c);
-        kc[j] = 8 * c;
+        kc[j] = EPC * c;
     }
 
     // A: row 16rb + i of the RB row blocks; the descriptor covers rows 0 ..
     // M-1 (k = K - 1 of the last).
-    const uint32_t arange = (uint32_t)((int64_t)(p.M - 1) * lda2 + 2 * (int64_t)p.K);
+    const uint32_t arange = (uint32_t)((int64_t)(p.M - 1) * lda2 + ESZ * (int64_t)p.K);
     const __amdgpu_buffer_rsrc_t rsa =
         __builtin_amdgcn_make_buffer_rsrc(const_cast<void*>(p.A), 0, arange, kBufferRsrcW3);
     uint32_t arow[RB];
@@ -174,14 +205,15 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
             copy_b(gbase[cp], grange[cp], dst + 1024 * j, voff);
         }
     };
-    // RB x U loads: a[rb][u] = row 16rb + i, k = SK*s + 32u + 8g .. +7.
+    // RB x U loads: a[rb][u] = row 16rb + i, bytes 64u + 16g of the step's
+    // piece (k = SK*s + 4*EPC*u + EPC*g .. +EPC-1).
     auto load_a = [&](int s, u32x4 (&a)[RB][G::U]) {
         const int lim = p.K - SK * s;
 #pragma unroll
         for (int rb = 0; rb < RB; ++rb)
 #pragma unroll
             for (int u = 0; u < G::U; ++u) {
-                const bool ok = aok[rb] && 32 * u + 8 * g < lim;
+                const bool ok = aok[rb] && 4 * EPC * u + EPC * g < lim;
                 const uint32_t voff =
                     ok ? arow[rb] + (uint32_t)(G::ROWB * s + 64 * u + 16 * g) : arange;
                 a[rb][u] = __builtin_bit_cast(
@@ -208,7 +240,7 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
             for (int u = 0; u < G::U; ++u)
 #pragma unroll
                 for (int rb = 0; rb < RB; ++rb)
-                    acc[rb][2 * cp + b] = mfma16x16x32<T>(a[rb][u], bop[b][u], acc[rb][2 * cp + b]);
+                    acc[rb][2 * cp + b] = mfma_chunk<T>(a[rb][u], bop[b][u], acc[rb][2 * cp + b]);
     };
     // Before a copy overwrites a stage, this wave's reads of it must have
     // returned (they have: their MFMAs came first; the wait makes it explicit).
@@ -355,10 +387,10 @@ __global__ __launch_bounds__(NW * 64, 1) void skinny16_bt_dma_kernel(GemmParams 
 // re-reads A less.  So one row block keeps 128 on N = 28672 (224 strips
 // already saturate HBM: 71.8 us), four take 112 (256 strips, one per CU:
 // 83.5 us against 87.4 with 128), and a narrow N spreads over more CUs.
-int strip_cols(const GemmParams& p, int rb) {
+int strip_cols(const GemmParams& p, int rb, int esz) {
     constexpr int64_t kCUs = 256;
     const double hbm = 6.5e12, per_wg = 29e9 - (rb - 1) * (29e9 - 24e9) / 3.0;
-    const double bytes_col = 2.0 * p.K;  // one column of B over all of K
+    const double bytes_col = (double)esz * p.K;  // one column of B over all of K
     const double floor_s = bytes_col * p.N * p.batch / hbm;
     int best = COLS;
     double best_t = 0.0;
@@ -370,39 +402,44 @@ int strip_cols(const GemmParams& p, int rb) {
     return best;
 }
 
-template <In T, int RB, int NW, int NS, int SK, bool kSingleA>
+template <In T, int RB, int NW, int NS, int ROWB, bool kSingleA>
 hipError_t launch_cfg(const GemmParams& p, hipStream_t s) {
-    const int cols = strip_cols(p, RB);
+    const int cols = strip_cols(p, RB, T == In::F32 ? 4 : 2);
     const dim3 grid((p.N + cols - 1) / cols, p.batch), block(NW * 64);
-    hipLaunchKernelGGL((skinny16_bt_dma_kernel<T, RB, NW, NS, SK, kSingleA>), grid, block, 0, s,
-                       p, cols);
+    hipLaunchKernelGGL((skinny_bt_dma_kernel<T, RB, NW, NS, ROWB, kSingleA>), grid, block, 0,
+                       s, p, cols);
     return hipGetLastError();
 }
 
 template <In T, int RB>
 hipError_t launch_rb(const GemmParams& p, hipStream_t s) {
-    if constexpr (RB <= 2) return launch_cfg<T, RB, 8, 2, 128, false>(p, s);
-    else return launch_cfg<T, RB, 8, 4, 64, true>(p, s);
+    if constexpr (RB <= 2) return launch_cfg<T, RB, 8, 2, 256, false>(p, s);
+    else return launch_cfg<T, RB, 8, 4, 128, true>(p, s);
 }
 
 }  // namespace
 
-// A stored M x K and B stored N x K, 1 <= M <= 64, K a multiple of 8 (a
-// 16-byte piece is then all inside or all outside k < K), 16-byte aligned
-// rows, and every offset within a descriptor below 2^31 (at most 64 rows of
-// A or 32 of B per descriptor).
-bool skinny16_bt_dma_eligible(const GemmParams& p) {
-    if (p.ta || !p.tb || p.M < 1 || p.M > kSkinnyMaxM || p.N < 1 || p.K < 8 || !k_multiple(p, 8) ||
-        !operands_16b_aligned(p, 2) || p.lda < p.K || p.ldb < p.K)
+// A stored M x K and B stored N x K, 1 <= M <= 64, K a multiple of the
+// elements in 16 bytes (a 16-byte piece is then all inside or all outside
+// k < K), 16-byte aligned rows, and every offset within a descriptor below
+// 2^31 (at most 64 rows of A or 32 of B per descriptor).
+template <In T>
+bool skinny_bt_dma_eligible(const GemmParams& p) {
+    constexpr int esz = T == In::F32 ? 4 : 2, epc = 16 / esz;
+    if (p.ta || !p.tb || p.M < 1 || p.M > kSkinnyMaxM || p.N < 1 || p.K < epc ||
+        !k_multiple(p, epc) || !operands_16b_aligned(p, esz) || p.lda < p.K || p.ldb < p.K)
         return false;
     const int64_t lim = int64_t(1) << 31;
-    return (int64_t)(p.M - 1) * p.lda * 2 + 2 * (int64_t)p.K < lim &&
-           (int64_t)(GR - 1) * p.ldb * 2 + 2 * (int64_t)p.K < lim;
+    return (int64_t)(p.M - 1) * p.lda * esz + esz * (int64_t)p.K < lim &&
+           (int64_t)(GR - 1) * p.ldb * esz + esz * (int64_t)p.K < lim;
 }
+template bool skinny_bt_dma_eligible<In::F32>(const GemmParams&);
+template bool skinny_bt_dma_eligible<In::BF16>(const GemmParams&);
+template bool skinny_bt_dma_eligible<In::F16>(const GemmParams&);
 
 template <In T>
-hipError_t launch_skinny16_bt_dma(const GemmParams& p, hipStream_t s) {
-    if (!skinny16_bt_dma_eligible(p)) return hipErrorInvalidValue;
+hipError_t launch_skinny_bt_dma(const GemmParams& p, hipStream_t s) {
+    if (!skinny_bt_dma_eligible<T>(p)) return hipErrorInvalidValue;
     switch ((p.M + 15) / 16) {
         case 1: return launch_rb<T, 1>(p, s);
         case 2: return launch_rb<T, 2>(p, s);
@@ -411,7 +448,8 @@ hipError_t launch_skinny16_bt_dma(const GemmParams& p, hipStream_t s) {
         default: return hipErrorInvalidConfiguration;
     }
 }
-template hipError_t launch_skinny16_bt_dma<In::BF16>(const GemmParams&, hipStream_t);
-template hipError_t launch_skinny16_bt_dma<In::F16>(const GemmParams&, hipStream_t);
+template hipError_t launch_skinny_bt_dma<In::F32>(const GemmParams&, hipStream_t);
+template hipError_t launch_skinny_bt_dma<In::BF16>(const GemmParams&, hipStream_t);
+template hipError_t launch_skinny_bt_dma<In::F16>(const GemmParams&, hipStream_t);
 
 }  // namespace dgt

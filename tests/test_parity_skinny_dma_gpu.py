@@ -1,19 +1,22 @@
 """GPU parity for the skinny kernel that streams B through LDS by copies
-(16-bit inputs, A stored M x K, B stored N x K: a linear layer's weight),
-against the CPU oracle, through the C ABI.
+(A stored M x K, B stored N x K: a linear layer's weight; 16-bit and fp32
+inputs), against the CPU oracle, through the C ABI.
 
-The skinny rung takes that kernel when K is a multiple of 8 and every row
-is 16-byte aligned; each wave takes one K-range of a 128-column strip, eight
-waves per workgroup: 128-deep steps, a two-stage ring per wave and two A
-buffers for M <= 32; 64-deep steps, four stages and one A buffer above.
+The skinny rung takes that kernel when K is a multiple of the elements in
+16 bytes (8 for 16-bit inputs, 4 for fp32) and every row is 16-byte
+aligned; each wave takes one K-range of a 128-column strip, eight waves per
+workgroup: 256-byte row pieces per step (128 k of 16-bit inputs, 64 of
+fp32), a two-stage ring per wave and two A buffers for M <= 32; 128-byte
+pieces, four stages and one A buffer above.
 Covered: every row-block count (M = 1 .. 64, both configurations), ragged
 column strips (N not a multiple of 128, fewer
 columns than one group), K tails (K not a multiple of the 128-deep step,
 down to K = 8, where most waves have no step), integer inputs bit-exact
-for bf16 and f16; alpha / beta and the bias through the strided batch; row
-pitches padded with NaN (no k >= K may reach a product) and canaries around
-C; K not a multiple of 8 (the register-staged kernel takes it); real inputs
-within the gates at a decode-like size; run-to-run determinism.
+for every input type (fp32 also with K a multiple of 4 but not of 8);
+alpha / beta and the bias through the strided batch; row pitches padded
+with NaN (no k >= K may reach a product) and canaries around C; K not a
+multiple of 8 (16-bit) or 4 (fp32), which the register-staged kernels take;
+real inputs within the gates at a decode-like size; run-to-run determinism.
 """
 
 import numpy as np
@@ -29,7 +32,7 @@ import dense_gemm_tuning_amd as dgt  # noqa: E402
 
 pytestmark = pytest.mark.gpu
 
-DTYPES = ["bf16", "f16"]
+DTYPES = ["f32", "bf16", "f16"]
 
 
 @pytest.fixture(scope="module", autouse=True)
@@ -66,6 +69,22 @@ def test_integer_inputs_bit_exact(shape, dtype):
     assert st == 0, dgt.gemm_status_string(st)
     R = oracle.round_f32(oracle.gemm(A, B, None, 1.0, 0.0, dtype, trans_b=True))
     assert_bit_exact(C, R, f"skinny dma {dtype} {M}x{N}x{K}")
+
+
+# fp32 only: K a multiple of 4 but not of 8 (a 16-byte piece is 4 floats),
+# in both configurations, down to a single piece.
+F32_SHAPES = [(9, 200, 1004), (33, 333, 12), (50, 129, 260), (64, 100, 4), (2, 4099, 8196)]
+
+
+@pytest.mark.parametrize("shape", F32_SHAPES, ids=lambda s: "x".join(map(str, s)))
+def test_f32_k_multiple_of_4_bit_exact(shape):
+    M, N, K = shape
+    A, B = ints(6600 + M, M, K, "f32"), ints(6700 + N, N, K, "f32")
+    say(f"skinny dma f32 {M}x{N}x{K}")
+    st, C = run_gemm("skinny", "f32", A, B, None, 1.0, 0.0, trans_b=True)
+    assert st == 0, dgt.gemm_status_string(st)
+    R = oracle.round_f32(oracle.gemm(A, B, None, 1.0, 0.0, "f32", trans_b=True))
+    assert_bit_exact(C, R, f"skinny dma f32 {M}x{N}x{K}")
 
 
 @pytest.mark.parametrize("dtype", DTYPES)
@@ -126,35 +145,37 @@ def test_nan_padded_pitches_and_canaries(M, dtype):
     assert np.all(full[mask] == canary), "kernel wrote outside C"
 
 
-@pytest.mark.parametrize("K", [1001, 1004])
-def test_k_not_multiple_of_8_takes_register_kernel(K):
+@pytest.mark.parametrize("dtype,K", [("bf16", 1001), ("bf16", 1004), ("f32", 1001), ("f32", 1002)])
+def test_k_not_multiple_of_piece_takes_register_kernel(dtype, K):
     M, N = 40, 200
-    A, B = ints(6000 + K, M, K, "bf16"), ints(6100 + K, N, K, "bf16")
-    st, C = run_gemm("skinny", "bf16", A, B, None, 1.0, 0.0, trans_b=True)
+    A, B = ints(6000 + K, M, K, dtype), ints(6100 + K, N, K, dtype)
+    st, C = run_gemm("skinny", dtype, A, B, None, 1.0, 0.0, trans_b=True)
     assert st == 0
-    R = oracle.round_f32(oracle.gemm(A, B, None, 1.0, 0.0, "bf16", trans_b=True))
-    assert_bit_exact(C, R, f"K={K}")
+    R = oracle.round_f32(oracle.gemm(A, B, None, 1.0, 0.0, dtype, trans_b=True))
+    assert_bit_exact(C, R, f"{dtype} K={K}")
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M", [8, 32, 64])
-def test_real_inputs_decode_like(M):
+def test_real_inputs_decode_like(M, dtype):
     """Normal inputs (sigma 0.02, as a weight) at K = 8192, ragged N."""
     N, K = 2048 + 72, 8192
-    A = gi.draw(6200 + M, M, K, "normal", sigma=0.02, dtype="bf16")
-    B = gi.draw(6300 + M, N, K, "normal", sigma=0.02, dtype="bf16")
-    say(f"skinny dma real M={M}")
-    st, C = run_gemm("auto", "bf16", A, B, None, 1.0, 0.0, trans_b=True)
+    A = gi.draw(6200 + M, M, K, "normal", sigma=0.02, dtype=dtype)
+    B = gi.draw(6300 + M, N, K, "normal", sigma=0.02, dtype=dtype)
+    say(f"skinny dma real {dtype} M={M}")
+    st, C = run_gemm("auto", dtype, A, B, None, 1.0, 0.0, trans_b=True)
     assert st == 0
-    R = oracle.gemm(A, B, None, 1.0, 0.0, "bf16", trans_b=True)
-    assert_close(C, R, K, 1.0, 0.02, 0.02, what=f"decode-like M={M}")
+    R = oracle.gemm(A, B, None, 1.0, 0.0, dtype, trans_b=True)
+    assert_close(C, R, K, 1.0, 0.02, 0.02, what=f"decode-like {dtype} M={M}")
     assert np.all(np.isfinite(C))
 
 
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
 @pytest.mark.parametrize("M", [16, 40, 64])
-def test_deterministic(M):
+def test_deterministic(M, dtype):
     N, K = 1000, 4096
-    dA = to_dev(gi.draw(6400, M, K, "normal", dtype="bf16"), "bf16")
-    dB = to_dev(gi.draw(6500, N, K, "normal", dtype="bf16"), "bf16")
+    dA = to_dev(gi.draw(6400, M, K, "normal", dtype=dtype), dtype)
+    dB = to_dev(gi.draw(6500, N, K, "normal", dtype=dtype), dtype)
     outs = []
     for _ in range(2):
         C = torch.zeros((M, N), device="cuda")
