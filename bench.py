@@ -19,7 +19,8 @@ the ragged 1000^3 with alpha = 1.5, beta = 0.5), the FP32 4096^3 case
 fp16 peak, equal to bf16's), the skinny decode-shaped case M=8, N=28672,
 K=8192 (against HBM bandwidth: its time is the time to stream B once,
 dilfish.github.io 5.1 GEMV row), the BF16 square and skinny cases with a
-linear layer's operand storage (B stored N x K, A stored K x M), that
+linear layer's operand storage (B stored N x K, A stored K x M; the skinny
+one also with FP32 inputs), that
 layer's forward with its bias fused, a strided batch of 16 x 2048^3, and the
 split-K, stream-K and one-GPU-share shapes, plus:
   * "roofline": the dominant kernel's algorithmic FLOP (or bytes) per launch
@@ -70,7 +71,8 @@ HBM_PEAK_GBS = 8000.0
 
 PRIMARY = "bf16_8192"
 SECONDARY = ["f32_256", "f32_1000_ragged", "f32_4096", "f16_8192", "bf16_skinny_8x28672x8192",
-             "bf16_8192_nt", "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "bf16_linear_bias_8192_nt",
+             "bf16_8192_nt", "bf16_8192_tn", "bf16_skinny_8x28672x8192_nt", "f32_skinny_8x28672x8192_nt",
+             "bf16_linear_bias_8192_nt",
              "bf16_bmm_16x2048", "bf16_decode_64x28672x8192_nt", "f32_1000_splitk",
              "bf16_splitk_1024x1024x16384", "bf16_skinny_shard_8x3584x8192",
              "bf16_shard_8192x1024x8192", "bf16_streamk_6144x4096x8192", "f32_streamk_3000"]
@@ -104,6 +106,9 @@ DOMINANT = {
                                     r"skinny_bt_dma_kernel<\(dgt::In\)1, 1, 8, 2, 256, false>"),
     "bf16_linear_bias_8192_nt": ("mfma16_dma_kernel<BF16, NT> + bias", "k_mfma_bf16_dma.hip",
                                  r"mfma16_dma_kernel<\(dgt::In\)1, 256, false, true, false, false>"),
+    "f32_skinny_8x28672x8192_nt": ("skinny_bt_dma_kernel<F32, 1 row block, 8 waves>",
+                                   "k_skinny_dma.hip",
+                                   r"skinny_bt_dma_kernel<\(dgt::In\)0, 1, 8, 2, 256, false>"),
     "bf16_decode_64x28672x8192_nt": ("skinny_bt_dma_kernel<BF16, 4 row blocks, 8 waves>",
                                      "k_skinny_dma.hip",
                                      r"skinny_bt_dma_kernel<\(dgt::In\)1, 4, 8, 4, 128, true>"),

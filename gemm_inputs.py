@@ -209,6 +209,10 @@ WORKLOADS = {
     "bf16_skinny_8x28672x8192_nt": Workload("bf16_skinny_8x28672x8192_nt", "bf16",
                                             8, 28672, 8192, 1.0, 0.0, "normal",
                                             sigma=0.02, seed_base=9000, trans_b=True),
+    # The same decode product with fp32 inputs: 940 MB of weight streamed once.
+    "f32_skinny_8x28672x8192_nt": Workload("f32_skinny_8x28672x8192_nt", "f32",
+                                           8, 28672, 8192, 1.0, 0.0, "normal",
+                                           sigma=0.02, seed_base=19000, trans_b=True),
     # The linear layer's forward with its bias fused into the epilogue, and a
     # strided batch of independent products.
     "bf16_linear_bias_8192_nt": Workload("bf16_linear_bias_8192_nt", "bf16", 8192, 8192, 8192,

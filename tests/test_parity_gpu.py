@@ -225,7 +225,8 @@ def test_workload_configs(name):
 # so the device result must equal the oracle's bit for bit over all of C, at
 # the full sizes of the small, ragged, square and skinny workloads.
 @pytest.mark.parametrize("name", ["f32_256", "f32_1000_ragged", "f32_4096", "bf16_8192",
-                                  "bf16_skinny_8x28672x8192", "bf16_skinny_8x28672x8192_nt"])
+                                  "bf16_skinny_8x28672x8192", "bf16_skinny_8x28672x8192_nt",
+                                  "f32_skinny_8x28672x8192_nt"])
 def test_workload_integer_variants(name):
     w = gi.WORKLOADS[name].with_ints()
     A, B, C0 = gi.make_inputs(w)
