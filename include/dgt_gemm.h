@@ -116,7 +116,9 @@ enum gemm_variant {
                                    (256 x 256 or 128 x 128; 64 x 64 for fp32
                                    launches with at most 128 tiles of 128 x
                                    128) is chosen per launch                  */
-    GEMM_VARIANT_SKINNY = 4,    /* M <= 64: streams B once from HBM, A held in
+    GEMM_VARIANT_SKINNY = 4,    /* M <= 64: streams B once from HBM (copied
+                                   straight into LDS when B is stored N x K
+                                   with 16-byte aligned rows), A held in
                                    registers per step (up to four 16-row
                                    blocks), K split over waves and reduced
                                    in LDS (dilfish.github.io 5.1 GEMV row and
