@@ -82,8 +82,8 @@ SECONDARY = ["f32_256", "f32_1000_ragged", "f32_4096", "f16_8192", "bf16_skinny_
 # template arguments: input format, then vector / guard flags where the
 # kernel has them, then trans_a, trans_b; the DMA GEMM kernels' end with
 # their edge-tile and K-tail flags, false for whole tiles; the skinny DMA
-# kernel's are the row-block count, waves, ring stages, step depth and
-# whether A has one register buffer).
+# kernel's are the input format, row-block count, waves, ring stages, bytes
+# per row piece of a step and whether A has one register buffer).
 DOMINANT = {
     "f32_256": ("mfma_f32_kernel<NN, 64-tiles>", "k_mfma_f32.hip",
                 r"mfma_f32_kernel<true, false, false, false, 64>"),

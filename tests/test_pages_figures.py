@@ -97,3 +97,29 @@ def test_cpu_baseline_reports_accuracy_of_a_result():
     acc = bench.cpu_baseline(w, A, B, C0, target_s=0.0, c_gpu=bad)["accuracy"]
     assert abs(acc["max_abs"] - 0.5) < 1e-3
     assert acc["gate_max_abs"] == pytest.approx(1e-4 * np.sqrt(80))
+
+
+def _template_params(src, name):
+    """Template parameter count of __global__ kernel `name` in source text."""
+    import re
+    m = re.search(r"template\s*<([^>]*)>\s*__global__[^;{]*?\b" + name + r"\s*\(", src)
+    assert m, f"kernel {name} not found"
+    return len([p for p in m.group(1).split(",") if p.strip()])
+
+
+def test_dominant_kernels_exist_with_their_template_arity():
+    """Every bench workload names a dominant kernel whose rocprofv3 pattern
+    matches a kernel defined in the named source file, with as many template
+    arguments as the definition has (a renamed kernel or a changed template
+    would otherwise leave the bench's profile lookups silently empty)."""
+    import re
+    csrc = os.path.join(os.path.dirname(HERE), "dense_gemm_tuning_amd", "csrc")
+    for w in [bench.PRIMARY] + bench.SECONDARY:
+        assert w in bench.DOMINANT, w
+        _, srcs, pat = bench.DOMINANT[w]
+        text = "".join(open(os.path.join(csrc, f)).read() for f in srcs.split("+"))
+        m = re.match(r"(\w+)<(.*)>$", pat)
+        assert m, (w, pat)
+        name, args = m.group(1), m.group(2)
+        nargs = len(re.split(r",\s*", args.replace(r"\(dgt::In\)", "")))
+        assert _template_params(text, name) == nargs, (w, name, nargs)
