@@ -400,3 +400,39 @@ def gemm_split(A, B, C, alpha: float = 1.0, beta: float = 0.0, splits: int = 0,
     return gemm_splitk(dtype, trans_a, trans_b, M, N, K, float(alpha), A.data_ptr(), _ld(A),
                        B.data_ptr(), _ld(B), float(beta), C.data_ptr(), _ld(C), splits,
                        ws_ptr, ws_bytes, _stream_handle(stream))
+
+
+def gemm_stream(A, B, C, alpha: float = 1.0, beta: float = 0.0, workspace=None, stream=None,
+                trans_a: bool = False, trans_b: bool = False) -> int:
+    """Stream-K form of ``gemm`` on torch tensors (gemm_streamk).  ``workspace``
+    is a device tensor of at least gemm_streamk_workspace_size bytes; when
+    None one is allocated here with torch (the library itself allocates
+    nothing); a caller's workspace must be a contiguous GPU tensor on C's
+    device.  Shapes stream-K does not cover run as ``gemm``.  Returns the
+    status code."""
+    import torch
+
+    dtype = _dtype_code(A, B, C)
+    named = (("A", A), ("B", B), ("C", C))
+    _check_layout(named)
+    M, K = A.shape[::-1] if trans_a else A.shape
+    K2, N = B.shape[::-1] if trans_b else B.shape
+    if K2 != K or tuple(C.shape) != (M, N):
+        raise ValueError(f"shape mismatch: A {tuple(A.shape)}, B {tuple(B.shape)}, "
+                         f"C {tuple(C.shape)}")
+    if workspace is not None and not workspace.is_contiguous():
+        raise ValueError("workspace must be contiguous")
+    _check_device(named + ((("workspace", workspace),) if workspace is not None else ()),
+                  C.device)
+    need = gemm_streamk_workspace_size(dtype, M, N, K)
+    if need < 0:
+        return need
+    if workspace is None and need > 0:
+        workspace = torch.empty(need, dtype=torch.uint8, device=C.device)
+    ws_ptr, ws_bytes = 0, 0
+    if workspace is not None:
+        ws_ptr = workspace.data_ptr() if workspace.numel() > 0 else 0
+        ws_bytes = workspace.numel() * workspace.element_size()
+    return gemm_streamk(dtype, trans_a, trans_b, M, N, K, float(alpha), A.data_ptr(), _ld(A),
+                        B.data_ptr(), _ld(B), float(beta), C.data_ptr(), _ld(C), ws_ptr,
+                        ws_bytes, _stream_handle(stream))

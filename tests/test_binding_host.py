@@ -1,7 +1,7 @@
-"""The torch-facing calls of the binding (gemm, gemm_batched, gemm_split)
-reject host tensors, column-strided views and mis-shaped bias rows before
-anything reaches the library.  Runs without a GPU: the library loader is
-replaced by one that fails the test if it is ever reached."""
+"""The torch-facing calls of the binding (gemm, gemm_batched, gemm_split,
+gemm_stream) reject host tensors, column-strided views and mis-shaped bias
+rows before anything reaches the library.  Runs without a GPU: the library
+loader is replaced by one that fails the test if it is ever reached."""
 
 import pytest
 
@@ -48,6 +48,21 @@ def test_gemm_split_rejects_host_and_strided_tensors():
     ws = torch.zeros(64, dtype=torch.uint8)[::2]
     with pytest.raises(ValueError, match="contiguous"):
         dgt.gemm_split(A, B, C, splits=2, workspace=ws)
+
+
+def test_gemm_stream_rejects_host_and_strided_tensors():
+    A, B, C = torch.zeros(8, 4), torch.zeros(4, 6), torch.zeros(8, 6)
+    with pytest.raises(ValueError, match="GPU tensor"):
+        dgt.gemm_stream(A, B, C)
+    with pytest.raises(ValueError, match="unit column stride"):
+        dgt.gemm_stream(torch.zeros(8, 8)[:, ::2], B, C)
+    with pytest.raises(ValueError, match="dimensions"):
+        dgt.gemm_stream(A[None], B, C)
+    with pytest.raises(ValueError, match="shape mismatch"):
+        dgt.gemm_stream(A, torch.zeros(5, 6), C)
+    ws = torch.zeros(64, dtype=torch.uint8)[::2]
+    with pytest.raises(ValueError, match="contiguous"):
+        dgt.gemm_stream(A, B, C, workspace=ws)
 
 
 def test_gemm_batched_rejects_host_and_strided_tensors():

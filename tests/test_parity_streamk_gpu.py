@@ -12,7 +12,8 @@ partial last slice, and with alpha / beta; real inputs within the gates;
 run-to-run determinism; beta == 0 never reading a NaN-filled C; a padded C
 inside a canary band (the fix-up kernel writes only C); the calls stream-K
 does not cover (M <= 64, unaligned rows), which run as gemm_ex; a short
-workspace refused.
+workspace refused; the torch-facing gemm_stream, with its own workspace and
+with one it allocates, on stored-transposed operands.
 """
 
 import numpy as np
@@ -160,3 +161,27 @@ def test_streamk_short_workspace_refused():
     st, C, _ = run_streamk("bf16", A, B, None, M, N, K, 1.0, 0.0, ws_bytes=need - 1024)
     assert st == dgt.GEMM_ERR_WORKSPACE
     assert np.all(np.isnan(C)), "a refused call wrote C"
+
+
+@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+def test_gemm_stream_tensor_call(dtype):
+    """The torch-facing form: integer inputs bit-exact, A stored K x M and B
+    stored N x K, once with a caller's workspace and once with the one it
+    allocates."""
+    M, N, K = 1000, 1288, 1120
+    ta, tb = True, True
+    sa, sb = stored(M, N, K, ta, tb)
+    A = gi.draw(2450, *sa, "int", dtype=dtype)
+    B = gi.draw(2451, *sb, "int", dtype=dtype)
+    C0 = gi.draw(2452, M, N, "int")
+    R = oracle.round_f32(oracle.gemm(A, B, C0, 1.5, 0.5, dtype, trans_a=ta, trans_b=tb))
+    need = dgt.gemm_streamk_workspace_size(CODE[dtype], M, N, K)
+    assert need > 0
+    for ws in (torch.empty(need, dtype=torch.uint8, device="cuda"), None):
+        say(f"gemm_stream {dtype} {M}x{N}x{K} workspace {'given' if ws is not None else 'allocated'}")
+        dC = torch.from_numpy(C0.astype(np.float32)).cuda()
+        st = dgt.gemm_stream(to_dev(A, dtype), to_dev(B, dtype), dC, 1.5, 0.5, workspace=ws,
+                             trans_a=ta, trans_b=tb)
+        torch.cuda.synchronize()
+        assert st == 0, dgt.gemm_status_string(st)
+        assert_bit_exact(dC.cpu().numpy(), R, f"gemm_stream {dtype}")
